@@ -1,0 +1,163 @@
+/*
+ * gdn.h -- C ABI of libgdn: the chunked gated-delta-rule prefill (GDN and KDA) on MI355X.
+ *
+ * The operation (pages "split_prefill.rs" -- prefill_gdn_full, prefill_gdn_full_batched,
+ * prefill_gdn_full_batched_fla_varlen -- and "metrale_model_arch/glm5next_kda/prefill.rs"
+ * -- Glm5NextKdaLayer::prefill, prefill_with_pad_fill and its launch sequence conv_prefill,
+ * l2, split_widen, chunk_prepare, chunk_scan):
+ *
+ *   1. optional front end: causal depthwise conv1d over every channel of the packed
+ *      [q | k | v] rows (conv_k taps, no bias) followed by SiLU, starting from and
+ *      advancing a carried window of the last conv_k-1 raw inputs per channel;
+ *   2. optional L2 normalisation of q and k per token and head, q <- q / sqrt(|q|^2+eps),
+ *      k <- k / sqrt(|k|^2+eps), then q <- scale * q;
+ *   3. the gated delta rule, with S = h^T (dv x dk) per head and alpha_t = exp(g_t):
+ *        S_t = S_{t-1} diag(alpha_t) - beta_t (S_{t-1} diag(alpha_t) k_t - v_t) k_t^T,
+ *        o_t = S_t q_t,
+ *      evaluated chunk by chunk (cumulative log-gates, the beta-weighted WY/UT transform,
+ *      then the inter-chunk scan that carries h). alpha_t is one scalar per head (GDN) or
+ *      one value per key channel (KDA).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `p` is a DEVICE pointer; `p` is a host pointer.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
+ *     synchronise. The library never allocates caller-visible memory and keeps no state
+ *     between calls except lazily created per-device kernel handles.
+ *   - The caller owns every buffer. h and conv_state are read and then overwritten in
+ *     place. o is written only at real token rows: rows at or past a stream's end keep
+ *     their previous bytes.
+ *   - Positions at or past a stream's end (padding, or the tail of an allocation) are
+ *     never read; NaN or huge values there have no effect.
+ *   - Element types: q/k/v, the raw rows, conv_state and o are `p->dtype` (GDN_F32 or
+ *     GDN_BF16); g, beta, h and conv_w are float32.
+ *   - Errors: every check below runs on the host before anything is enqueued; on error
+ *     nothing is launched and no buffer changes (the pages refuse a bad token count before
+ *     any launch). GDN_E_HIP reports a failed launch.
+ *   - Not thread-safe per device for concurrent calls sharing one workspace.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define GDN_OK 0
+#define GDN_E_ARG (-1)         /* bad count, null pointer, bad stride, bad B            */
+#define GDN_E_UNSUPPORTED (-2) /* (dk, dv, chunk, dtype, conv_k) not compiled in        */
+#define GDN_E_WORKSPACE (-3)   /* ws_bytes smaller than gdn_workspace_bytes() requires  */
+#define GDN_E_HIP (-4)         /* a HIP launch or query failed                          */
+
+/* element types of q/k/v, raw rows, conv_state and o */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* call kinds for gdn_workspace_bytes */
+#define GDN_KIND_SINGLE 0
+#define GDN_KIND_BATCHED 1
+#define GDN_KIND_VARLEN 2
+
+typedef struct gdn_params {
+    int32_t H;      /* heads (q, k and v share the head count)                            */
+    int32_t dk;     /* key head dim: 64 or 128                                            */
+    int32_t dv;     /* value head dim: 64 or 128                                          */
+    int32_t chunk;  /* tokens per chunk: 64                                               */
+    float eps;      /* L2 eps for q and k; eps < 0: q and k are used as given (no L2)     */
+    float scale;    /* multiplies q after the optional L2 (normally 1/sqrt(dk))           */
+    int32_t dtype;  /* GDN_F32 or GDN_BF16                                                */
+    int32_t conv_k; /* 0: no front end; 2..4: causal depthwise conv taps + SiLU           */
+    int64_t ld_qkv; /* row stride, in elements, of the q, k and v rows                    */
+} gdn_params;
+
+/*
+ * Single stream of t tokens (pages: "split_prefill.rs" prefill_gdn_full;
+ * "metrale_model_arch/glm5next_kda/prefill.rs" Glm5NextKdaLayer::prefill, which refuses
+ * t == 0 or t above the workspace's token capacity before any launch).
+ *
+ *   q, k, v   row i of q is q + i*ld_qkv, head h at offset h*dk (k likewise, v at h*dv).
+ *             With the front end on, these are the raw conv inputs of the packed row
+ *             [q | k | v]: the conv channel of q element (h, c) is h*dk + c, of k element
+ *             H*dk + h*dk + c, of v element 2*H*dk + h*dv + c (cd = 2*H*dk + H*dv).
+ *   g         [t][H] float log-gates (kda_prefill: [t][H][dk], one per key channel).
+ *   beta      [t][H] float, used as given.
+ *   h         [H][dk][dv] float state, in/out.
+ *   conv_state [cd][conv_k-1] in dtype, oldest first, in/out (NULL iff conv_k == 0).
+ *   conv_w    [cd][conv_k] float taps; tap conv_k-1 multiplies the current token (NULL
+ *             iff conv_k == 0).
+ *   o         [t][H][dv] in dtype, out.
+ *   t         1 <= t <= the max_tokens the workspace was sized for.
+ *   ws        device workspace of ws_bytes >= gdn_workspace_bytes(p, 1, t, GDN_KIND_SINGLE)
+ *             (may be NULL when that size is 0).
+ */
+int gdn_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, float *h, void *conv_state,
+                const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* Same as gdn_prefill with the per-key-channel gate: g is [t][H][dk] (page
+ * "metrale_model_arch/glm5next_kda/prefill.rs", the KDA chunked prefill). */
+int kda_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, float *h, void *conv_state,
+                const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
+                void *stream);
+
+/*
+ * B streams of equal length t_per_stream lying back to back: stream b owns rows
+ * [b*t_per_stream, (b+1)*t_per_stream) of q/k/v/g/beta/o (page "split_prefill.rs",
+ * prefill_gdn_full_batched: one h-state pointer per stream, streams of equal length).
+ *   h_ptrs          device array of B device pointers, each to a [H][dk][dv] float state.
+ *   conv_state_ptrs device array of B device pointers to [cd][conv_k-1] windows (NULL iff
+ *                   conv_k == 0).
+ *   ws              >= gdn_workspace_bytes(p, B, B*t_per_stream, GDN_KIND_BATCHED).
+ * B >= 1 and t_per_stream >= 1, else GDN_E_ARG.
+ */
+int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *const *h_ptrs,
+                        void *const *conv_state_ptrs, const float *conv_w, void *o,
+                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
+ * B streams of different lengths described by cu_seqlens (page "split_prefill.rs",
+ * prefill_gdn_full_batched_fla_varlen): stream b owns rows [cu_seqlens[b],
+ * cu_seqlens[b+1]). Chunks restart at every stream start.
+ *   cu_seqlens   device int32 [B+1], cu_seqlens[0] == 0, non-decreasing,
+ *                cu_seqlens[B] == total_tokens. A zero-length stream is a no-op (its state
+ *                is left as it was). Violations are not detected (the host does not read
+ *                device memory) and give undefined results.
+ *   total_tokens host copy of cu_seqlens[B] (>= 1).
+ *   max_seqlen   host upper bound of the longest stream (1 <= max_seqlen <= total_tokens).
+ *   ws           >= gdn_workspace_bytes(p, B, total_tokens, GDN_KIND_VARLEN).
+ */
+int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, float *const *h_ptrs,
+                       void *const *conv_state_ptrs, const float *conv_w, void *o,
+                       const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,
+                       int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Per-chunk work table of a varlen call (the bookkeeping of
+ * prefill_gdn_full_batched_fla_varlen: total_nt = sum_b ceil(len_b/chunk) chunks,
+ * max_num_chunks = max_b ceil(len_b/chunk)). Writes, on `stream`, table[4*i .. 4*i+3] =
+ * {stream b, first row of the chunk, rows in the chunk, chunk index within b} for chunk
+ * i in stream-major order, and *count = total_nt. table holds max_entries rows; chunks
+ * beyond it are counted but not written. cu_seqlens as for gdn_prefill_varlen.
+ */
+int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t *table,
+                    int64_t max_entries, int32_t *count, void *stream);
+
+/* Bytes of device workspace a call of `kind` with B streams and up to max_tokens rows in
+ * total needs (0 if none). Returns 0 for invalid parameters. */
+size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
+
+/* Static description of a status code. */
+const char *gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

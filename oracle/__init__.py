@@ -126,7 +126,8 @@ def recurrence(q, k, v, g, beta, h0, cu_seqlens=None, l2=True, eps=1e-6, scale=N
     q, k: [N, H, dk]; v: [N, H, dv]; g: [N, H] (one log-gate per head) or [N, H, dk]
     (one per key channel); beta: [N, H]; h0: [B, H, dk, dv] (B = len(cu_seqlens) - 1).
     cu_seqlens: [B+1] prefix sums (None: one stream of all N rows).
-    l2: normalise q and k in the call (eps) and scale q (default 1/sqrt(dk)).
+    l2: normalise q and k in the call (eps). scale multiplies q either way (default
+    1/sqrt(dk) with l2, 1 without).
     Returns (o [N, H, dv], h [B, H, dk, dv]) in float64; rows past cu_seqlens[-1] of o are 0.
     """
     q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
@@ -137,7 +138,7 @@ def recurrence(q, k, v, g, beta, h0, cu_seqlens=None, l2=True, eps=1e-6, scale=N
     h = _f64(h0).reshape(B, H, dk, dv).copy()
     per_channel = 1 if g.ndim == 3 else 0
     if scale is None:
-        scale = 1.0 / np.sqrt(dk)
+        scale = 1.0 / np.sqrt(dk) if l2 else 1.0
     o = np.zeros((N, H, dv), np.float64)
     rc = _load().gdn_oracle_recurrence(
         B, cu.ctypes.data_as(_i64p), H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),

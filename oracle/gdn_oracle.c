@@ -105,7 +105,8 @@ static void l2_scale(double *dst, const double *src, int32_t n, double eps,
  *   q, k  [N][H][dk]   v [N][H][dv]
  *   g     [N][H] (gate_per_channel == 0) or [N][H][dk] (== 1), log decay
  *   beta  [N][H]
- *   l2    nonzero: normalise q and k (eps) and scale q; zero: use them as given
+ *   l2    nonzero: normalise q and k (eps); zero: use them as given
+ *   scale multiplies q in both cases (after the L2 when there is one)
  *   h     [B][H][dk][dv]  in: initial state of each stream, out: final state
  *   o     [N][H][dv]      out
  * Rows outside [cu[0], cu[B]) are never read or written.
@@ -146,7 +147,8 @@ int gdn_oracle_recurrence(int32_t B, const int64_t *cu, int32_t H, int32_t dk,
                 l2_scale(qn, qt, dk, eps, scale);
                 l2_scale(kn, kt, dk, eps, 1.0);
             } else {
-                memcpy(qn, qt, sizeof(double) * dk);
+                for (int32_t i = 0; i < dk; ++i)
+                    qn[i] = qt[i] * scale;
                 memcpy(kn, kt, sizeof(double) * dk);
             }
             /* S <- S diag(alpha): column i of S is row i of the stored h */
