@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked GDN/KDA prefill on one MI355X, printed as one JSON line.
+
+A step is one call of the C ABI over one batch of synthetic input: the whole path (front
+end when the workload has one, L2, chunk preparation, inter-chunk scan, state write-back).
+The default workload is GDN with the conv front end, 1 stream of T=4096 tokens, H=32,
+dk=dv=128, chunk 64 (seeded synthetic bf16 inputs). Inputs are resident in HBM when timing
+starts; several input copies are rotated so that a step never finds its inputs in the
+256 MB Infinity Cache from the previous step.
+
+Extra fields: ``roofline`` (the dominant kernel's algorithmic bytes per launch over its
+average duration, from hipEvents the library records on the call's stream during the timed
+steps) and ``cpu_baseline`` (the fp64 oracle on a bounded sample, on this host's cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "prefill tokens/s per GDN/KDA layer (H=32, d=128) + % of MFMA/HBM roofline"
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_depthwise_amd", "csrc", f)
+                  for f in ("gdn_kernels.hip", "gdn_api.cpp", "gdn_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(spec) -> dict:
+    """Bytes each kernel must move per launch (inputs read once, outputs written once)."""
+    N, H, dk, dv, B = spec.N, spec.H, spec.dk, spec.dv, spec.B
+    es = 2 if spec.dtype == "bf16" else 4
+    cd = spec.cd
+    g_bytes = N * H * (dk if spec.gate == "kda" else 1) * 4
+    state = 2 * B * H * dk * dv * 4  # h read + written
+    chunk = N * cd * es + g_bytes + N * H * 4 + N * H * dv * 4 + state
+    out = {"recur": chunk}
+    if spec.front_end:
+        # front: raw rows in, activations out (same element size), taps, windows read
+        out["front"] = 2 * N * cd * es + cd * spec.conv_k * 4 + B * cd * (spec.conv_k - 1) * es
+        out["state"] = 2 * B * cd * (spec.conv_k - 1) * es
+    return out
+
+
+def cpu_baseline(spec, inp, budget_s: float) -> dict:
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    H = spec.H
+    cu = inp["cu_seqlens"].numpy()
+    t0 = time.perf_counter()
+    oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk, dv=spec.dv,
+                   cu_seqlens=cu, conv_w=inp["conv_w"], conv_state=inp["conv_state"], heads=[0])
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(H, math.floor(budget_s / max(t1, 1e-3)))))
+    heads = list(range(n))
+    t0 = time.perf_counter()
+    oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk, dv=spec.dv,
+                   cu_seqlens=cu, conv_w=inp["conv_w"], conv_state=inp["conv_state"],
+                   heads=heads)
+    dt = time.perf_counter() - t0
+    # every head is independent and costs the same: the full layer takes dt * H / n
+    return {"value": spec.N / (dt * H / n), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "all %d tokens of the workload, %d of %d heads (fp64, %.1f s); "
+                      "full-layer time scaled by %d/%d" % (spec.N, n, H, dt, H, n)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from gated_delta_rule_depthwise_amd import binding as B
+    from gated_delta_rule_depthwise_amd import inputs
+    from gated_delta_rule_depthwise_amd.runner import Prefill
+
+    spec = inputs.config(args.config)
+    inp = inputs.make(spec)
+    dev = "cuda"
+    first = Prefill(inp, dev)
+    per_copy = sum(t.numel() * t.element_size() for t in
+                   (first.x, first.g, first.beta, first.o, first.ws))
+    copies = max(1, min(8, math.ceil((1 << 30) / per_copy)))
+    calls = [first] + [Prefill(inp, dev) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        rc = calls[i % copies]()
+        if rc != 0:
+            raise RuntimeError("libgdn status %d (%s)" % (rc, B.gdn_status_string(rc)))
+    torch.cuda.synchronize()
+    B.gdn_profile_read()          # drop anything recorded so far
+    B.gdn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rc = calls[i % copies]()
+        if rc != 0:
+            raise RuntimeError("libgdn status %d" % rc)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.gdn_profile_enable(False)
+    rc, ms, launches = B.gdn_profile_read()
+    assert rc == 0
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state"}
+    avg_ms = {names[i]: ms[i] / launches[i] for i in names if launches[i]}
+    dom = max(avg_ms, key=avg_ms.get)
+    alg = algorithmic_bytes(spec)
+    achieved = alg[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        ent = tr.get(spec.name, {}).get(dom)
+        if ent and ent.get("kernel_hash") == kernel_hash():
+            traffic = ent["bytes_per_launch"]
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    line = {
+        "metric": METRIC,
+        "value": spec.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; fp16 MFMA operands, fp32 accumulate/VALU; fp32 o",
+        "data": "synthetic (seeded; distributions of the workload description)",
+        "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
+                   "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
+                   "front_end": spec.front_end, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg[dom],
+                     "avg_launch_ms": avg_ms[dom]},
+        "stage_ms_per_step": avg_ms,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,388 @@
+// gdn_api.cpp -- the C ABI of libgdn: host-side validation, workspace carving and launches.
+//
+// Every check runs before anything is enqueued, so a refused call changes no buffer (page
+// "metrale_model_arch/glm5next_kda/prefill.rs": a call outside 1..=max_tokens tokens is
+// refused before a launch). Device memory is never read on the host.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+using gdn::ChunkArgs;
+using gdn::FrontArgs;
+using gdn::Streams;
+
+namespace {
+
+// ---- stage timing: hipEvents around each kernel of a call, on the call's stream ------
+namespace prof {
+std::atomic<bool> enabled{false};
+std::mutex mu;
+struct Rec {
+    int bucket;
+    hipEvent_t a, b;
+};
+std::vector<Rec> pending;
+std::vector<hipEvent_t> pool;
+
+hipEvent_t take()
+{
+    std::lock_guard<std::mutex> g(mu);
+    if (!pool.empty()) {
+        hipEvent_t e = pool.back();
+        pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+}  // namespace prof
+
+// Records the start of a bucket at construction and its end at done(), when enabled.
+struct Stage {
+    int bucket;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    Stage(int bucket_, hipStream_t s_) : bucket(bucket_), s(s_)
+    {
+        if (prof::enabled.load(std::memory_order_relaxed)) {
+            a = prof::take();
+            if (a && hipEventRecord(a, s) != hipSuccess)
+                a = nullptr;
+        }
+    }
+    void done()
+    {
+        if (!a)
+            return;
+        hipEvent_t b = prof::take();
+        if (b && hipEventRecord(b, s) == hipSuccess) {
+            std::lock_guard<std::mutex> g(prof::mu);
+            prof::pending.push_back({bucket, a, b});
+        }
+        a = nullptr;
+    }
+};
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t conv_dim(const gdn_params *p)
+{
+    return 2 * (int64_t)p->H * p->dk + (int64_t)p->H * p->dv;
+}
+
+// input kind of the chunk kernel: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
+int in_kind(const gdn_params *p)
+{
+    if (p->dtype != GDN_BF16)
+        return 0;
+    return p->conv_k > 0 ? 2 : 1;
+}
+
+// waves per workgroup: each wave owns 16 dv columns; the largest count that still gives
+// every CU a workgroup (B*H*dv/(16*nw) >= 256), else the smallest compiled one.
+int pick_waves(const gdn_params *p, int kda, int64_t BH)
+{
+    const int ik = in_kind(p);
+    static int forced = -1;
+    if (forced < 0) {
+        const char *e = getenv("GDN_WAVES");
+        forced = e ? atoi(e) : 0;
+    }
+    if (forced > 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, forced) &&
+        p->dv % (16 * forced) == 0)
+        return forced;
+    int best = 0;
+    for (int nw : {8, 4, 2, 1}) {
+        if (p->dv % (16 * nw) || !gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nw))
+            continue;
+        if (!best)
+            best = nw;
+        if (BH * (p->dv / (16 * nw)) >= 256)
+            return nw;
+        best = nw;
+    }
+    return best;
+}
+
+int check_params(const gdn_params *p, int kda)
+{
+    if (!p)
+        return GDN_E_ARG;
+    if (p->H < 1 || p->dk < 1 || p->dv < 1 || p->H > 4096)
+        return GDN_E_ARG;
+    if (!(p->eps == p->eps) || !(p->scale == p->scale))
+        return GDN_E_ARG;
+    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+        return GDN_E_UNSUPPORTED;
+    if (p->chunk != 64)
+        return GDN_E_UNSUPPORTED;
+    if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
+        return GDN_E_UNSUPPORTED;
+    if (pick_waves(p, kda, 1) == 0)
+        return GDN_E_UNSUPPORTED;
+    const int64_t vec = 16 / elem_bytes(p->dtype);
+    if (p->ld_qkv < (int64_t)p->H * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
+        p->ld_qkv % vec != 0)
+        return GDN_E_ARG;
+    return GDN_OK;
+}
+
+size_t front_bytes(const gdn_params *p, int64_t max_tokens)
+{
+    if (p->conv_k == 0)
+        return 0;
+    return align_up((size_t)max_tokens * (size_t)conv_dim(p) * elem_bytes(p->dtype));
+}
+
+struct Call {
+    const gdn_params *p;
+    int kda;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *h;
+    float *const *h_ptrs;
+    void *conv_state;
+    void *const *conv_state_ptrs;
+    const float *conv_w;
+    void *o;
+    Streams st;
+    int64_t N;
+    void *ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+int run(const Call &c)
+{
+    const gdn_params *p = c.p;
+    int rc = check_params(p, c.kda);
+    if (rc != GDN_OK)
+        return rc;
+    if (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.o || (!c.h && !c.h_ptrs))
+        return GDN_E_ARG;
+    if (!aligned16(c.q) || !aligned16(c.k) || !aligned16(c.v) || !aligned16(c.o))
+        return GDN_E_ARG;
+    const bool front = p->conv_k > 0;
+    if (front != (c.conv_w != nullptr) ||
+        front != (c.conv_state != nullptr || c.conv_state_ptrs != nullptr))
+        return GDN_E_ARG;
+    if (c.N < 1 || c.N > (int64_t)INT32_MAX)
+        return GDN_E_ARG;
+    const size_t need = front_bytes(p, c.N);
+    if (c.ws_bytes < need || (need && !c.ws))
+        return GDN_E_WORKSPACE;
+    if (need && !aligned16(c.ws))
+        return GDN_E_ARG;
+
+    const int64_t BH = (int64_t)c.st.B * p->H;
+    const int nw = pick_waves(p, c.kda, BH);
+    const int64_t grid = BH * (p->dv / (16 * nw));
+    if (grid > (int64_t)INT32_MAX)
+        return GDN_E_ARG;
+
+    ChunkArgs ca{};
+    ca.g = c.g;
+    ca.beta = c.beta;
+    ca.h = c.h;
+    ca.h_ptrs = c.h_ptrs;
+    ca.o = (float *)c.o;
+    ca.st = c.st;
+    ca.H = p->H;
+    ca.eps = p->eps;
+    FrontArgs fa{};
+    if (front) {
+        fa.q = c.q, fa.k = c.k, fa.v = c.v, fa.ld = p->ld_qkv;
+        fa.conv_w = c.conv_w;
+        fa.conv_state = c.conv_state;
+        fa.conv_state_ptrs = c.conv_state_ptrs;
+        fa.y = c.ws;
+        fa.st = c.st;
+        fa.N = c.N;
+        fa.H = p->H, fa.dk = p->dk, fa.dv = p->dv, fa.K = p->conv_k;
+        fa.do_l2 = p->eps >= 0.f;
+        fa.eps = p->eps;
+        fa.scale = p->scale;
+        Stage st(GDN_PROF_FRONT, c.stream);
+        if (gdn::launch_front(p->dtype, fa, c.stream) != hipSuccess)
+            return GDN_E_HIP;
+        st.done();
+        const size_t es = elem_bytes(p->dtype);
+        char *y = (char *)c.ws;
+        ca.q = y;
+        ca.k = y + (size_t)p->H * p->dk * es;
+        ca.v = y + (size_t)2 * p->H * p->dk * es;
+        ca.ld = conv_dim(p);
+        ca.do_l2 = 0;
+        ca.scale = 1.f;
+    } else {
+        ca.q = c.q, ca.k = c.k, ca.v = c.v, ca.ld = p->ld_qkv;
+        ca.do_l2 = p->eps >= 0.f;
+        ca.scale = p->scale;
+    }
+    {
+        Stage st(GDN_PROF_RECUR, c.stream);
+        if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, nw, ca, (int)grid, c.stream) !=
+            hipSuccess)
+            return GDN_E_HIP;
+        st.done();
+    }
+    if (front) {
+        Stage st(GDN_PROF_STATE, c.stream);
+        if (gdn::launch_conv_state(p->dtype, fa, c.stream) != hipSuccess)
+            return GDN_E_HIP;
+        st.done();
+    }
+    return GDN_OK;
+}
+
+int single(const gdn_params *p, int kda, const void *q, const void *k, const void *v,
+           const float *g, const float *beta, float *h, void *conv_state,
+           const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
+           void *stream)
+{
+    if (!h || t < 1)
+        return GDN_E_ARG;
+    Call c{};
+    c.p = p, c.kda = kda, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
+    c.h = h, c.conv_state = conv_state, c.conv_w = conv_w, c.o = o;
+    c.st = Streams{nullptr, t, 1};
+    c.N = t, c.ws = ws, c.ws_bytes = ws_bytes, c.stream = (hipStream_t)stream;
+    return run(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, float *h, void *conv_state,
+                const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
+                void *stream)
+{
+    return single(p, 0, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream);
+}
+
+int kda_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
+                const float *g, const float *beta, float *h, void *conv_state,
+                const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
+                void *stream)
+{
+    return single(p, 1, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream);
+}
+
+int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *const *h_ptrs,
+                        void *const *conv_state_ptrs, const float *conv_w, void *o,
+                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    if (B < 1 || t_per_stream < 1 || !h_ptrs)
+        return GDN_E_ARG;
+    if (t_per_stream > (int64_t)INT32_MAX / B)
+        return GDN_E_ARG;
+    Call c{};
+    c.p = p, c.kda = 0, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
+    c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
+    c.st = Streams{nullptr, t_per_stream, B};
+    c.N = (int64_t)B * t_per_stream, c.ws = ws, c.ws_bytes = ws_bytes;
+    c.stream = (hipStream_t)stream;
+    return run(c);
+}
+
+int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, float *const *h_ptrs,
+                       void *const *conv_state_ptrs, const float *conv_w, void *o,
+                       const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,
+                       int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream)
+{
+    if (B < 1 || !h_ptrs || !cu_seqlens || total_tokens < 1 || max_seqlen < 1 ||
+        max_seqlen > total_tokens)
+        return GDN_E_ARG;
+    Call c{};
+    c.p = p, c.kda = 0, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
+    c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
+    c.st = Streams{cu_seqlens, 0, B};
+    c.N = total_tokens, c.ws = ws, c.ws_bytes = ws_bytes, c.stream = (hipStream_t)stream;
+    return run(c);
+}
+
+int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t *table,
+                    int64_t max_entries, int32_t *count, void *stream)
+{
+    if (!cu_seqlens || B < 1 || chunk < 1 || !count || max_entries < 0 ||
+        (max_entries > 0 && !table))
+        return GDN_E_ARG;
+    if (gdn::launch_chunk_table(cu_seqlens, B, chunk, table, max_entries, count,
+                                (hipStream_t)stream) != hipSuccess)
+        return GDN_E_HIP;
+    return GDN_OK;
+}
+
+size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind)
+{
+    if (check_params(p, 0) != GDN_OK && check_params(p, 1) != GDN_OK)
+        return 0;
+    if (B < 1 || max_tokens < 1 || kind < GDN_KIND_SINGLE || kind > GDN_KIND_VARLEN)
+        return 0;
+    return front_bytes(p, max_tokens);
+}
+
+int gdn_profile_enable(int on)
+{
+    prof::enabled.store(on != 0);
+    return GDN_OK;
+}
+
+int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets)
+{
+    if (nbuckets < 0 || (nbuckets > 0 && (!ms_total || !launches)))
+        return GDN_E_ARG;
+    for (int32_t i = 0; i < nbuckets; ++i)
+        ms_total[i] = 0.0, launches[i] = 0;
+    std::vector<prof::Rec> recs;
+    {
+        std::lock_guard<std::mutex> g(prof::mu);
+        recs.swap(prof::pending);
+    }
+    int rc = GDN_OK;
+    for (const prof::Rec &r : recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            rc = GDN_E_HIP;
+        else if (r.bucket < nbuckets)
+            ms_total[r.bucket] += ms, launches[r.bucket] += 1;
+    }
+    std::lock_guard<std::mutex> g(prof::mu);
+    for (const prof::Rec &r : recs)
+        prof::pool.push_back(r.a), prof::pool.push_back(r.b);
+    return rc;
+}
+
+const char *gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_E_ARG: return "invalid argument";
+    case GDN_E_UNSUPPORTED: return "unsupported configuration";
+    case GDN_E_WORKSPACE: return "workspace too small";
+    case GDN_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+"""Device buffers for one workload and the C-ABI call that processes them.
+
+Plumbing only: torch allocates device memory and provides the stream; every step of the
+path runs inside libgdn's kernels (binding.py). Used by the tests and by bench.py.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class Prefill:
+    """One call of gdn_prefill / kda_prefill / gdn_prefill_batched / gdn_prefill_varlen.
+
+    ``inp`` is a dict from :func:`inputs.make`. ``mode`` is "single", "batched" or
+    "varlen" (default: single for one stream, batched for equal lengths, else varlen).
+    ``o_fill`` pre-fills the output so rows the call must not write can be checked.
+    """
+
+    def __init__(self, inp: dict, device="cuda", mode=None, o_fill=0.0, eps=None,
+                 scale=None):
+        spec = inp["spec"]
+        self.spec = spec
+        self.device = device
+        lens = list(spec.lengths)
+        if mode is None:
+            mode = "single" if len(lens) == 1 else (
+                "batched" if len(set(lens)) == 1 else "varlen")
+        if spec.gate == "kda" and mode != "single":
+            raise ValueError("the per-key-channel gate is exposed for single streams")
+        self.mode = mode
+        self.x = inp["x"].to(device)
+        self.g = inp["g"].to(device)
+        self.beta = inp["beta"].to(device)
+        self.h0 = inp["h0"].to(device)
+        self.h = self.h0.clone()
+        self.cu = inp["cu_seqlens"].to(device)
+        self.conv_w = None if inp["conv_w"] is None else inp["conv_w"].to(device)
+        self.conv_state0 = None if inp["conv_state"] is None else inp["conv_state"].to(device)
+        self.conv_state = None if self.conv_state0 is None else self.conv_state0.clone()
+        self.o = torch.full((spec.alloc, spec.H, spec.dv), o_fill, dtype=torch.float32,
+                            device=device)
+        self.h_ptrs = torch.tensor([self.h[b].data_ptr() for b in range(spec.B)],
+                                   dtype=torch.int64, device=device)
+        self.cs_ptrs = None if self.conv_state is None else torch.tensor(
+            [self.conv_state[b].data_ptr() for b in range(spec.B)], dtype=torch.int64,
+            device=device)
+        self.params = B.params(
+            spec.H, spec.dk, spec.dv, chunk=spec.chunk,
+            eps=spec.eps if eps is None else eps,
+            scale=spec.scale if scale is None else scale,
+            dtype=B.GDN_BF16 if spec.dtype == "bf16" else B.GDN_F32,
+            conv_k=spec.conv_k if spec.front_end else 0, ld_qkv=spec.cd)
+        kind = {"single": B.GDN_KIND_SINGLE, "batched": B.GDN_KIND_BATCHED,
+                "varlen": B.GDN_KIND_VARLEN}[mode]
+        self.ws_bytes = B.gdn_workspace_bytes(self.params, spec.B, spec.N, kind)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+        es = self.x.element_size()
+        base = self.x.data_ptr()
+        self.q_ptr = base
+        self.k_ptr = base + spec.H * spec.dk * es
+        self.v_ptr = base + 2 * spec.H * spec.dk * es
+
+    def reset(self):
+        """Restore the initial states (h, conv window)."""
+        self.h.copy_(self.h0)
+        if self.conv_state is not None:
+            self.conv_state.copy_(self.conv_state0)
+
+    def __call__(self, stream=None) -> int:
+        s = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        sp = self.spec
+        cs = None if self.conv_state is None else self.conv_state
+        if self.mode == "single":
+            fn = B.kda_prefill if sp.gate == "kda" else B.gdn_prefill
+            return fn(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g, self.beta,
+                      self.h, cs, self.conv_w, self.o, sp.N, self.ws, self.ws_bytes, s)
+        if self.mode == "batched":
+            return B.gdn_prefill_batched(self.params, self.q_ptr, self.k_ptr, self.v_ptr,
+                                         self.g, self.beta, self.h_ptrs, self.cs_ptrs,
+                                         self.conv_w, self.o, sp.B, sp.lengths[0], self.ws,
+                                         self.ws_bytes, s)
+        return B.gdn_prefill_varlen(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g,
+                                    self.beta, self.h_ptrs, self.cs_ptrs, self.conv_w, self.o,
+                                    self.cu, sp.B, sp.N, max(sp.lengths), self.ws,
+                                    self.ws_bytes, s)

@@ -28,8 +28,11 @@
  *     their previous bytes.
  *   - Positions at or past a stream's end (padding, or the tail of an allocation) are
  *     never read; NaN or huge values there have no effect.
- *   - Element types: q/k/v, the raw rows, conv_state and o are `p->dtype` (GDN_F32 or
- *     GDN_BF16); g, beta, h and conv_w are float32.
+ *   - Element types: q/k/v, the raw rows and conv_state are `p->dtype` (GDN_F32 or
+ *     GDN_BF16); o, g, beta, h and conv_w are float32. (o is float32 for bf16 inputs too:
+ *     rounding o itself to bf16 already costs about 2e-2 of max|error|/RMS on these
+ *     heavy-tailed outputs.) The dense products run on MFMA with fp32 accumulation, with
+ *     fp16 operands for bf16 inputs and fp32 operands for float32 inputs.
  *   - Errors: every check below runs on the host before anything is enqueued; on error
  *     nothing is launched and no buffer changes (the pages refuse a bad token count before
  *     any launch). GDN_E_HIP reports a failed launch.
@@ -52,7 +55,7 @@ extern "C" {
 #define GDN_E_WORKSPACE (-3)   /* ws_bytes smaller than gdn_workspace_bytes() requires  */
 #define GDN_E_HIP (-4)         /* a HIP launch or query failed                          */
 
-/* element types of q/k/v, raw rows, conv_state and o */
+/* element types of q/k/v, raw rows and conv_state */
 #define GDN_F32 0
 #define GDN_BF16 1
 
@@ -88,7 +91,7 @@ typedef struct gdn_params {
  *   conv_state [cd][conv_k-1] in dtype, oldest first, in/out (NULL iff conv_k == 0).
  *   conv_w    [cd][conv_k] float taps; tap conv_k-1 multiplies the current token (NULL
  *             iff conv_k == 0).
- *   o         [t][H][dv] in dtype, out.
+ *   o         [t][H][dv] float32, out (16-byte aligned).
  *   t         1 <= t <= the max_tokens the workspace was sized for.
  *   ws        device workspace of ws_bytes >= gdn_workspace_bytes(p, 1, t, GDN_KIND_SINGLE)
  *             (may be NULL when that size is 0).
@@ -149,6 +152,25 @@ int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const 
  */
 int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t *table,
                     int64_t max_entries, int32_t *count, void *stream);
+
+/*
+ * Stage timing, the counterpart of the pages' profile buckets around the KDA prefill's
+ * front end and recurrence (page "metrale_model_arch/glm5next_kda/prefill.rs",
+ * profile::start / profile::end with KDA_FRONT, KDA_RECUR, KDA_BACK). While enabled, every
+ * call records a hipEvent pair around each of its kernels on the call's stream:
+ *   GDN_PROF_FRONT  conv + SiLU + L2 kernel (front end calls only)
+ *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan)
+ *   GDN_PROF_STATE  the carried conv window update (front end calls only)
+ * gdn_profile_read waits for every recorded pair, writes the summed milliseconds and the
+ * launch count of buckets 0..nbuckets-1, and forgets the records. Host pointers; events
+ * are created once and reused. Enabling costs two event records per kernel.
+ */
+#define GDN_PROF_FRONT 0
+#define GDN_PROF_RECUR 1
+#define GDN_PROF_STATE 2
+#define GDN_PROF_BUCKETS 3
+int gdn_profile_enable(int on);
+int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 
 /* Bytes of device workspace a call of `kind` with B streams and up to max_tokens rows in
  * total needs (0 if none). Returns 0 for invalid parameters. */

@@ -1,0 +1,102 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/gdn.h declares,
+sizes workspaces, and refuses bad calls before any launch (CPU only: the refusals return
+before any HIP call, so fake device pointers are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_depthwise_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+FAKE = 1 << 20  # never dereferenced: every call below is refused on the host
+FAKE2 = FAKE + 4096
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+|kda_\w+)\s*\(", src,
+                                 flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.SO)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (B.GDN_OK, B.GDN_E_ARG, B.GDN_E_UNSUPPORTED, B.GDN_E_WORKSPACE, B.GDN_E_HIP):
+        assert B.gdn_status_string(code) not in ("", "unknown status")
+    assert B.gdn_status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes():
+    p = B.params(32, 128, 128, conv_k=4)
+    cd = 3 * 32 * 128
+    ws = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
+    assert ws >= 4096 * cd * 2 and ws % 256 == 0
+    assert B.gdn_workspace_bytes(B.params(32, 128, 128), 8, 16384, B.GDN_KIND_BATCHED) == 0
+    assert B.gdn_workspace_bytes(p, 0, 4096, B.GDN_KIND_SINGLE) == 0
+    assert B.gdn_workspace_bytes(p, 1, 0, B.GDN_KIND_SINGLE) == 0
+    assert B.gdn_workspace_bytes(B.params(32, 96, 128), 1, 10, B.GDN_KIND_SINGLE) == 0
+
+
+def _single(p, t=10, ws=None, ws_bytes=0, h=FAKE, g=FAKE, cs=None, cw=None, q=FAKE):
+    return B.gdn_prefill(p, q, FAKE, FAKE, g, FAKE, h, cs, cw, FAKE, t, ws, ws_bytes, None)
+
+
+def test_refusals_before_launch():
+    p = B.params(2, 64, 64, dtype=B.GDN_F32)
+    assert _single(p, t=0) == B.GDN_E_ARG                   # zero tokens
+    assert _single(p, t=-5) == B.GDN_E_ARG
+    assert _single(p, h=None) == B.GDN_E_ARG                 # null state
+    assert _single(p, g=None) == B.GDN_E_ARG
+    assert _single(p, q=FAKE + 2) == B.GDN_E_ARG             # misaligned rows
+    assert _single(B.params(2, 64, 64, chunk=32)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 96, 96)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 64, 64, dtype=7)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 64, 64, conv_k=5)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 64, 64, ld_qkv=100)) == B.GDN_E_ARG    # ld < H*dk
+    assert _single(B.params(2, 64, 64, ld_qkv=388)) == B.GDN_E_ARG    # ld not 16-byte rows
+    assert _single(B.params(0, 64, 64)) == B.GDN_E_ARG
+    nan = B.params(2, 64, 64, scale=float("nan"))
+    assert _single(nan) == B.GDN_E_ARG
+    # front end: conv pointers required, and a workspace large enough for t tokens
+    pf = B.params(2, 64, 64, conv_k=4)
+    assert _single(pf) == B.GDN_E_ARG
+    need = B.gdn_workspace_bytes(pf, 1, 10, B.GDN_KIND_SINGLE)
+    assert _single(pf, cs=FAKE, cw=FAKE, ws=FAKE, ws_bytes=need - 1) == B.GDN_E_WORKSPACE
+    assert _single(pf, t=11, cs=FAKE, cw=FAKE, ws=FAKE, ws_bytes=need) == B.GDN_E_WORKSPACE
+    assert _single(pf, cs=FAKE, cw=None, ws=FAKE, ws_bytes=need) == B.GDN_E_ARG
+
+
+def test_batched_and_varlen_refusals():
+    p = B.params(2, 64, 64)
+    assert B.gdn_prefill_batched(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 0,
+                                 10, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_batched(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 2,
+                                 0, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_batched(p, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2,
+                                 5, None, 0, None) == B.GDN_E_ARG
+    args = [p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE]
+    assert B.gdn_prefill_varlen(*args, None, 2, 10, 5, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_varlen(*args, FAKE2, 0, 10, 5, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_varlen(*args, FAKE2, 2, 0, 1, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_varlen(*args, FAKE2, 2, 10, 11, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_varlen(*args, FAKE2, 2, 10, 0, None, 0, None) == B.GDN_E_ARG
+    assert B.gdn_chunk_table(None, 2, 64, FAKE, 10, FAKE, None) == B.GDN_E_ARG
+    assert B.gdn_chunk_table(FAKE, 0, 64, FAKE, 10, FAKE, None) == B.GDN_E_ARG
+    assert B.gdn_chunk_table(FAKE, 2, 0, FAKE, 10, FAKE, None) == B.GDN_E_ARG
+
+
+def test_params_struct_layout():
+    assert ctypes.sizeof(B.gdn_params) == 40
+    assert B.gdn_params.ld_qkv.offset == 32
