@@ -92,28 +92,33 @@ int in_kind(const gdn_params *p)
     return p->conv_k > 0 ? 2 : 1;
 }
 
-// waves per workgroup: each wave owns 16 dv columns; the largest count that still gives
-// every CU a workgroup (B*H*dv/(16*nw) >= 256), else the smallest compiled one.
-int pick_waves(const gdn_params *p, int kda, int64_t BH)
+// Workgroup shape: dv columns per workgroup and waves per workgroup. The widest compiled
+// slice that still gives every CU a workgroup (B*H*dv/nv >= 256), else the narrowest one;
+// the first compiled wave count for it. GDN_COLS / GDN_WAVES force a compiled shape.
+struct Shape {
+    int nv, waves;
+};
+
+Shape pick_shape(const gdn_params *p, int kda, int64_t BH)
 {
     const int ik = in_kind(p);
-    static int forced = -1;
-    if (forced < 0) {
-        const char *e = getenv("GDN_WAVES");
-        forced = e ? atoi(e) : 0;
+    static int fcols = -1, fwaves = -1;
+    if (fcols < 0) {
+        const char *e = getenv("GDN_COLS");
+        fcols = e ? atoi(e) : 0;
+        e = getenv("GDN_WAVES");
+        fwaves = e ? atoi(e) : 0;
     }
-    if (forced > 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, forced) &&
-        p->dv % (16 * forced) == 0)
-        return forced;
-    int best = 0;
-    for (int nw : {8, 4, 2, 1}) {
-        if (p->dv % (16 * nw) || !gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nw))
+    if (fcols > 0 && p->dv % fcols == 0 &&
+        gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves))
+        return Shape{fcols, fwaves};
+    Shape best{0, 0};
+    for (int nv : {128, 64}) {
+        if (p->dv % nv || !gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0))
             continue;
-        if (!best)
-            best = nw;
-        if (BH * (p->dv / (16 * nw)) >= 256)
-            return nw;
-        best = nw;
+        best = Shape{nv, 0};
+        if (BH * (p->dv / nv) >= 256)
+            return best;
     }
     return best;
 }
@@ -132,7 +137,7 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_UNSUPPORTED;
     if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
         return GDN_E_UNSUPPORTED;
-    if (pick_waves(p, kda, 1) == 0)
+    if (pick_shape(p, kda, 1).nv == 0)
         return GDN_E_UNSUPPORTED;
     const int64_t vec = 16 / elem_bytes(p->dtype);
     if (p->ld_qkv < (int64_t)p->H * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
@@ -189,8 +194,8 @@ int run(const Call &c)
         return GDN_E_ARG;
 
     const int64_t BH = (int64_t)c.st.B * p->H;
-    const int nw = pick_waves(p, c.kda, BH);
-    const int64_t grid = BH * (p->dv / (16 * nw));
+    const Shape sh = pick_shape(p, c.kda, BH);
+    const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
 
@@ -235,7 +240,8 @@ int run(const Call &c)
     }
     {
         Stage st(GDN_PROF_RECUR, c.stream);
-        if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, nw, ca, (int)grid, c.stream) !=
+        if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca, (int)grid,
+                              c.stream) !=
             hipSuccess)
             return GDN_E_HIP;
         st.done();

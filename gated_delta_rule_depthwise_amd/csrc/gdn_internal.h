@@ -49,12 +49,14 @@ struct FrontArgs {
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
 // new carried conv windows; must run after every kernel that reads the old ones
 hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
-// in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end
-hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nw, const ChunkArgs &a,
-                        int grid, hipStream_t s);
+// in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end;
+// nv: dv columns per workgroup (the grid is B * H * dv / nv workgroups); waves: waves per
+// workgroup, 0 = the first compiled instance of that width
+hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
+                        const ChunkArgs &a, int grid, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
-// 1 if the (in_kind, dk, dv, kda, nw) instance exists.
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nw);
+// 1 if the (in_kind, dk, dv, kda, nv, waves) instance exists.
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves);
 
 }  // namespace gdn

@@ -265,56 +265,69 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
     init_window(t0);
 
     TOUT *y = (TOUT *)a.y;
-    for (int64_t t = t0; t < t1; ++t) {
-        if (t >= eb) {  // the next non-empty stream starts at t
-            do {
-                ++b;
-                stream_bounds(a.st, b, sb, eb);
-            } while (eb <= t);
-            init_window(t);
-        }
-        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (active)
-            load8<T>(src + t * a.ld, x);
-        float z[FRONT_CPT];
+    constexpr int RB = 4;  // rows loaded together (memory-level parallelism)
+    for (int64_t tb = t0; tb < t1; tb += RB) {
+        float xs[RB][8];
 #pragma unroll
-        for (int i = 0; i < FRONT_CPT; ++i) {
-            float acc = w[K - 1][i] * x[i];
+        for (int u = 0; u < RB; ++u) {
 #pragma unroll
-            for (int j = 0; j < W; ++j)
-                acc += w[j][i] * win[j][i];
-            z[i] = acc / (1.f + __expf(-acc));
+            for (int i = 0; i < 8; ++i)
+                xs[u][i] = 0.f;
+            if (active && tb + u < t1)
+                load8<T>(src + (tb + u) * a.ld, xs[u]);
         }
 #pragma unroll
-        for (int j = 0; j + 1 < W; ++j)
+        for (int u = 0; u < RB; ++u) {
+            const int64_t t = tb + u;
+            if (t >= t1)
+                break;  // uniform over the block
+            if (t >= eb) {  // the next non-empty stream starts at t
+                do {
+                    ++b;
+                    stream_bounds(a.st, b, sb, eb);
+                } while (eb <= t);
+                init_window(t);
+            }
+            float z[FRONT_CPT];
 #pragma unroll
-            for (int i = 0; i < FRONT_CPT; ++i)
-                win[j][i] = win[j + 1][i];
-        if (W > 0) {
+            for (int i = 0; i < FRONT_CPT; ++i) {
+                float acc = w[K - 1][i] * xs[u][i];
 #pragma unroll
-            for (int i = 0; i < FRONT_CPT; ++i)
-                win[W > 0 ? W - 1 : 0][i] = x[i];
-        }
-        if (a.do_l2) {  // uniform; q and k heads are whole aligned lane groups
-            float ss = 0.f;
+                for (int j = 0; j < W; ++j)
+                    acc += w[j][i] * win[j][i];
+                z[i] = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));  // SiLU
+            }
 #pragma unroll
-            for (int i = 0; i < FRONT_CPT; ++i)
-                ss += z[i] * z[i];
-            for (int m = 1; m < lanes_per_head; m <<= 1)
-                ss += __shfl_xor(ss, m);
-            if (sec < 2) {
-                const float inv = rsqrtf(ss + a.eps) * (sec == 0 ? a.scale : 1.f);
+            for (int j = 0; j + 1 < W; ++j)
 #pragma unroll
                 for (int i = 0; i < FRONT_CPT; ++i)
-                    z[i] *= inv;
-            }
-        } else if (sec == 0) {
+                    win[j][i] = win[j + 1][i];
+            if (W > 0) {
 #pragma unroll
-            for (int i = 0; i < FRONT_CPT; ++i)
-                z[i] *= a.scale;
+                for (int i = 0; i < FRONT_CPT; ++i)
+                    win[W > 0 ? W - 1 : 0][i] = xs[u][i];
+            }
+            if (a.do_l2) {  // uniform; q and k heads are whole aligned lane groups
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < FRONT_CPT; ++i)
+                    ss += z[i] * z[i];
+                for (int m = 1; m < lanes_per_head; m <<= 1)
+                    ss += __shfl_xor(ss, m);
+                if (sec < 2) {
+                    const float inv = rsqrtf(ss + a.eps) * (sec == 0 ? a.scale : 1.f);
+#pragma unroll
+                    for (int i = 0; i < FRONT_CPT; ++i)
+                        z[i] *= inv;
+                }
+            } else if (sec == 0) {
+#pragma unroll
+                for (int i = 0; i < FRONT_CPT; ++i)
+                    z[i] *= a.scale;
+            }
+            if (active)
+                store8<TOUT>(y + t * (int64_t)cd + c0, z);
         }
-        if (active)
-            store8<TOUT>(y + t * (int64_t)cd + c0, z);
     }
 }
 
@@ -417,86 +430,173 @@ hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s)
 
 constexpr int CH = 64;  // chunk length
 
-template <typename T, int DK, int DV, int NW, bool KDA>
+template <typename T, int DK, int DV, int NW, int NCB>
 struct ChunkCfg {
-    static constexpr int NV = 16 * NW;  // dv columns per workgroup
-    static constexpr int PAD = 16 / (int)sizeof(T);
-    static constexpr int LDQ = DK + PAD;  // Qs, Ks, Ws: [64][LDQ]
-    static constexpr int LDT = CH + PAD;  // KTs [DK][LDT], VTs [NV][LDT], Ps/Tb/Tba [64][LDT]
+    static constexpr int NV = 16 * NW * NCB;  // dv columns per workgroup (16*NCB per wave)
+    // fp16 operands: T = (I+M)^-1 and P are applied as fp16 hi + lo pairs, and the
+    // right-hand operands of T X and P U too, which keeps those products at about fp32
+    // accuracy; fp32 operands need no split
+    static constexpr bool SPLIT = sizeof(T) == 2;
+    // Row strides of the operand tiles are 8 dwords past a multiple of 32, so fragment
+    // reads (16 rows x 4 column pieces), transposed column reads and 16-byte row writes
+    // spread evenly over the LDS banks. The fp32 solve tiles use 4 dwords past a multiple
+    // of 32, which keeps the D-layout stores (rows 4g+i) and 16-byte fragment reads even.
+    static constexpr int PAD = 32 / (int)sizeof(T);
+    static constexpr int LDQ = DK + PAD;  // Qs, Ks: [64][LDQ]
+    static constexpr int LDV = NV + PAD;  // Vs: [64][LDV]
+    static constexpr int LDT = CH + PAD;  // P and T operand tiles: [64][LDT]
     static constexpr int LDF = CH + 4;    // Ms, Tf: [64][LDF] float
     static constexpr int SZ_Q = CH * LDQ * (int)sizeof(T);
-    static constexpr int SZ_KT = DK * LDT * (int)sizeof(T);
-    static constexpr int SZ_VT = NV * LDT * (int)sizeof(T);
+    static constexpr int SZ_V = CH * LDV * (int)sizeof(T);
     static constexpr int SZ_P = CH * LDT * (int)sizeof(T);
     static constexpr int SZ_F = CH * LDF * 4;
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + SZ_Q;
-    static constexpr int OFF_W = OFF_K + SZ_Q;  // Ms aliases Ws (dead before Ws is built)
-    static constexpr int OFF_KT = OFF_W + (SZ_Q > SZ_F ? SZ_Q : SZ_F);
-    static constexpr int OFF_VT = OFF_KT + SZ_KT;
-    static constexpr int OFF_P = OFF_VT + SZ_VT;
-    static constexpr int OFF_TB = OFF_P + SZ_P;
-    static constexpr int OFF_TBA = OFF_TB + SZ_P;
-    // fp16 operands: T is applied as an fp16 hi + lo pair (two MFMAs), which keeps the
-    // WY factors at about fp32 accuracy; fp32 operands need no split
-    static constexpr bool SPLIT = sizeof(T) == 2;
-    static constexpr int OFF_TBL = OFF_TBA + SZ_P;
-    static constexpr int OFF_TBAL = OFF_TBL + (SPLIT ? SZ_P : 0);
-    static constexpr int OFF_TF = OFF_TBAL + (SPLIT ? SZ_P : 0);
-    static constexpr int OFF_G = OFF_TF + SZ_F;  // gam[64], bet[64]
+    static constexpr int OFF_V = OFF_K + SZ_Q;
+    static constexpr int OFF_P = OFF_V + SZ_V;
+    static constexpr int OFF_PL = OFF_P + SZ_P;
+    static constexpr int OFF_TB = OFF_PL + (SPLIT ? SZ_P : 0);
+    static constexpr int OFF_TBL = OFF_TB + SZ_P;
+    static constexpr int OFF_M = OFF_TBL + (SPLIT ? SZ_P : 0);
+    static constexpr int OFF_TF = OFF_M + SZ_F;
+    static constexpr int OFF_G = OFF_TF + SZ_F;  // graw[64], bet[64]
     static constexpr int BYTES = OFF_G + 2 * CH * 4;
 };
 
-// T_IJ = -T_II * sum_{K=J}^{I-1} M_IK T_KJ for one 16x16 block (one wave, fp32 MFMA).
-template <int LDF>
-__device__ __forceinline__ void solve_block(const float *Ms, float *Tf, int I, int J, int lane)
+// Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
+// lane (g, c) gets X[k0 + kappa(g, i)][n0 + c], i = 0..7, with kappa as in ld_frag.
+// fp16 tiles use the gfx950 LDS transpose read: within each 16-lane group, output lane j,
+// element i comes from source lane 4i + j/4, element j%4; so source lane s of group g
+// addresses row k0 + 4g + s/4, columns n0 + 4(s%4) .. +3, and the second read adds 16 rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f16x8 ld_frag_t(const f16 *X, int ld, int k0, int n0, int lane)
+{
+    const int g = lane >> 4, s = lane & 15;
+    const f16 *p0 = X + (k0 + 4 * g + (s >> 2)) * ld + n0 + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 16 * ld));
+    const f16x4 flo = __builtin_bit_cast(f16x4, lo), fhi = __builtin_bit_cast(f16x4, hi);
+    return __builtin_shufflevector(flo, fhi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x8 ld_frag_t(const float *X, int ld, int k0, int n0, int lane)
 {
     const int g = lane >> 4, c = lane & 15;
-    f32x4 y = zero4();
-    for (int Kb = J; Kb < I; ++Kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float av = Ms[(16 * I + c) * LDF + 16 * Kb + 4 * g + i];
-            const float bv = Tf[(16 * Kb + 4 * g + i) * LDF + 16 * J + c];
-            y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, y, 0, 0, 0);
-        }
-    }
-    f32x4 t = zero4();
+    const float *p = X + (k0 + 4 * g) * ld + n0 + c;
+    f32x8 f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float av = Tf[(16 * I + c) * LDF + 16 * I + 4 * g + i];
-        t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, y[i], t, 0, 0, 0);
+        f[i] = p[i * ld];
+        f[4 + i] = p[(16 + i) * ld];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        Tf[(16 * I + 4 * g + i) * LDF + 16 * J + c] = -t[i];
+    return f;
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, bool KDA>
+// raw 16-byte vector -> floats
+__device__ __forceinline__ void unpack(const bf16 *, const uint4 &u, float (&x)[8])
+{
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack(const f16 *, const uint4 &u, float (&x)[8])
+{
+    const f16x8 v = __builtin_bit_cast(f16x8, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        x[i] = (float)v[i];
+}
+__device__ __forceinline__ void unpack(const float *, const uint4 &u, float (&x)[4])
+{
+    x[0] = __uint_as_float(u.x), x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z), x[3] = __uint_as_float(u.w);
+}
+
+// d += A B for 16x16 blocks with a 16-deep contraction in about fp32 accuracy:
+// a[i] = A[c][4g+i], b[i] = B[4g+i][c] (lane = 16g + c); d in the same D layout.
+template <bool SPLIT>
+__device__ __forceinline__ void mm16(f32x4 &d, const f32x4 &a, const f32x4 &b)
+{
+    if constexpr (SPLIT) {
+        f16x4 ah, al, bh, bl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ah[i] = (f16)a[i];
+            al[i] = (f16)(a[i] - (float)ah[i]);
+            bh[i] = (f16)b[i];
+            bl[i] = (f16)(b[i] - (float)bh[i]);
+        }
+        d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, d, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], d, 0, 0, 0);
+    }
+}
+
+// A-operand fragment of 16x16 block (I, K) of a row-major fp32 tile: a[i] = X[16I+c][16K+4g+i]
+__device__ __forceinline__ f32x4 blk_a(const float *X, int ld, int I, int K, int lane)
+{
+    return *reinterpret_cast<const f32x4 *>(X + (16 * I + (lane & 15)) * ld + 16 * K +
+                                            4 * (lane >> 4));
+}
+// B-operand fragment of block (K, J): b[i] = X[16K+4g+i][16J+c]
+__device__ __forceinline__ f32x4 blk_b(const float *X, int ld, int K, int J, int lane)
+{
+    const float *p = X + (16 * K + 4 * (lane >> 4)) * ld + 16 * J + (lane & 15);
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+
+// hi + lo operand pair of the B operand built from two D-layout accumulators
+template <typename T>
+__device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
+                                           typename Tr<T>::frag &hi, typename Tr<T>::frag &lo)
+{
+    hi = pack<T>(d0, d1);
+    if constexpr (sizeof(T) == 2) {
+        f32x4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r0[i] = d0[i] - (float)hi[i];
+            r1[i] = d1[i] - (float)hi[4 + i];
+        }
+        lo = pack<T>(r0, r1);
+    }
+}
+
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
 __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
-    using C = ChunkCfg<T, DK, DV, NW, KDA>;
-    constexpr int NV = C::NV, LDQ = C::LDQ, LDT = C::LDT, LDF = C::LDF;
+    static_assert(NW == 4, "4 waves per workgroup (one per SIMD)");
+    using C = ChunkCfg<T, DK, DV, NW, NCB>;
+    constexpr int NV = C::NV, LDQ = C::LDQ, LDV = C::LDV, LDT = C::LDT, LDF = C::LDF;
+    constexpr bool SPLIT = C::SPLIT;
     constexpr int VEC = Tr<T>::VEC;
     constexpr int NT = NW * 64;
     typedef typename Tr<T>::frag frag;
+    // row -> lane maps of the 16-byte loads
+    constexpr int LPR = DK / VEC, RPW = 64 / LPR, NQK = 2 * CH / (NW * RPW);
+    constexpr int LPV = NV / VEC, RPV = 64 / LPV, NVV = CH / (NW * RPV);
+    static_assert(NQK * NW * RPW == 2 * CH && NVV * NW * RPV == CH, "load map");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     T *Qs = (T *)(smem + C::OFF_Q);
     T *Ks = (T *)(smem + C::OFF_K);
-    T *Ws = (T *)(smem + C::OFF_W);
-    float *Ms = (float *)(smem + C::OFF_W);
-    T *KTs = (T *)(smem + C::OFF_KT);
-    T *VTs = (T *)(smem + C::OFF_VT);
+    T *Vs = (T *)(smem + C::OFF_V);
     T *Ps = (T *)(smem + C::OFF_P);
+    T *Psl = (T *)(smem + C::OFF_PL);
     T *Tb = (T *)(smem + C::OFF_TB);
-    T *Tba = (T *)(smem + C::OFF_TBA);
-    T *Tbl = (T *)(smem + C::OFF_TBL);    // lo parts (fp16 operands only)
-    T *Tbal = (T *)(smem + C::OFF_TBAL);
+    T *Tbl = (T *)(smem + C::OFF_TBL);
+    float *Ms = (float *)(smem + C::OFF_M);
     float *Tf = (float *)(smem + C::OFF_TF);
-    float *gam = (float *)(smem + C::OFF_G);
-    float *bet = gam + CH;
+    float *graw = (float *)(smem + C::OFF_G);
+    float *bet = graw + CH;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -508,272 +608,343 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     float *hp = (a.h_ptrs ? a.h_ptrs[b] : a.h) + (int64_t)head * DK * DV;
-    const int colw = slice * NV + wave * 16;  // this wave's first dv column
+    const int colw = slice * NV + wave * 16 * NCB;  // this wave's first dv column
 
     const TIN *qg = (const TIN *)a.q + head * DK;
     const TIN *kg = (const TIN *)a.k + head * DK;
     const TIN *vg = (const TIN *)a.v + head * DV + slice * NV;
-    float *og = (float *)a.o + head * DV + colw + c16;
+    float *og = a.o + head * DV + colw + c16;  // + 16 cb for column block cb
     const int64_t ld = a.ld;
 
-    // P's blocks above the diagonal that the 32-deep steps touch stay zero
+    // blocks above the diagonal that the 32-deep steps over P and Tb touch stay 0
     for (int idx = tid; idx < 2 * 256; idx += NT) {
         const int blk = idx >> 8, e = idx & 255;
-        const int r = 32 * blk + (e >> 4), s = 32 * blk + 16 + (e & 15);
-        Ps[r * LDT + s] = (T)0.f;
+        const int off = (32 * blk + (e >> 4)) * LDT + 32 * blk + 16 + (e & 15);
+        Ps[off] = (T)0.f, Tb[off] = (T)0.f;
+        if constexpr (SPLIT)
+            Psl[off] = (T)0.f, Tbl[off] = (T)0.f;
     }
 
-    // state, D layout: hs[mb][i] = h[16 mb + 4 g + i][colw + c]
-    f32x4 hs[DK / 16];
+    // state, D layout: hs[cb][mb][i] = h[16 mb + 4 g + i][colw + 16 cb + c]
+    f32x4 hs[NCB][DK / 16];
 #pragma unroll
-    for (int mb = 0; mb < DK / 16; ++mb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            hs[mb][i] = hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + c16];
+        for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hs[cb][mb][i] = hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + 16 * cb + c16];
+
+    // Raw 16-byte vectors of the next chunk, loaded one chunk ahead so that the HBM latency
+    // hides behind a whole chunk of work. Rows at or past the stream's end are never read.
+    uint4 pq[NQK], pv[NVV];
+    float pg = 0.f, pb = 0.f;
+    auto prefetch = [&](int64_t c0, int Lc) {
+#pragma unroll
+        for (int it = 0; it < NQK; ++it) {
+            const int rr = wave * RPW + lane / LPR + it * NW * RPW;
+            const int r = rr & (CH - 1);
+            const TIN *src = (rr >= CH ? kg : qg) + (c0 + r) * ld + (lane % LPR) * VEC;
+            pq[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < NVV; ++it) {
+            const int r = wave * RPV + lane / LPV + it * NW * RPV;
+            const TIN *src = vg + (c0 + r) * ld + (lane % LPV) * VEC;
+            pv[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < CH) {
+            pg = tid < Lc ? a.g[(c0 + tid) * H + head] : 0.f;
+            pb = tid < Lc ? a.beta[(c0 + tid) * H + head] : 0.f;
+        }
+    };
+    if (start < end)
+        prefetch(start, (int)min((int64_t)CH, end - start));
 
     for (int64_t cs = start; cs < end; cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
 
-        // ---- A: load q, k (L2, scale), v^T, g, beta; rows >= L read as 0 -------------
-        {
-            constexpr int LPR = DK / VEC, RPW = 64 / LPR;
-            for (int rr = wave * RPW + lane / LPR; rr < 2 * CH; rr += NW * RPW) {
-                const bool isk = rr >= CH;
-                const int r = rr & (CH - 1);
-                const int c0 = (lane % LPR) * VEC;
-                float x[VEC];
+        // ---- A: registers -> LDS: q, k (L2, scale), v, raw gates, beta -----------------
+#pragma unroll
+        for (int it = 0; it < NQK; ++it) {
+            const int rr = wave * RPW + lane / LPR + it * NW * RPW;
+            const bool isk = rr >= CH;
+            const int r = rr & (CH - 1);
+            const int c0 = (lane % LPR) * VEC;
+            float x[VEC];
+            unpack((const TIN *)nullptr, pq[it], x);
+            float mul = isk ? 1.f : a.scale;
+            if (a.do_l2) {
+                float ss = 0.f;
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
-                    x[i] = 0.f;
-                if (r < L)
-                    load_vec((isk ? kg : qg) + (cs + r) * ld + c0, x);
-                float mul = isk ? 1.f : a.scale;
-                if (a.do_l2) {
-                    float ss = 0.f;
+                    ss += x[i] * x[i];
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i)
-                        ss += x[i] * x[i];
-#pragma unroll
-                    for (int m = 1; m < LPR; m <<= 1)
-                        ss += __shfl_xor(ss, m);
-                    mul = r < L ? mul * rsqrtf(ss + a.eps) : 0.f;
-                }
-#pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    x[i] *= mul;
-                store_vec((isk ? Ks : Qs) + r * LDQ + c0, x);
-                if (isk) {
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i)
-                        KTs[(c0 + i) * LDT + r] = (T)x[i];
-                }
+                for (int m = 1; m < LPR; m <<= 1)
+                    ss += __shfl_xor(ss, m);
+                mul = r < L ? mul * rsqrtf(ss + a.eps) : 0.f;
             }
-            constexpr int LPV = NV / VEC, RPV = 64 / LPV;
-            for (int r = wave * RPV + lane / LPV; r < CH; r += NW * RPV) {
-                const int c0 = (lane % LPV) * VEC;
-                float x[VEC];
 #pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    x[i] = 0.f;
-                if (r < L)
-                    load_vec(vg + (cs + r) * ld + c0, x);
-#pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    VTs[(c0 + i) * LDT + r] = (T)x[i];
-            }
-            if (tid < CH) {
-                const bool ok = tid < L;
-                gam[tid] = ok ? a.g[(cs + tid) * H + head] : 0.f;
-                bet[tid] = ok ? a.beta[(cs + tid) * H + head] : 0.f;
-            }
+            for (int i = 0; i < VEC; ++i)
+                x[i] *= mul;
+            store_vec((isk ? Ks : Qs) + r * LDQ + c0, x);
         }
+#pragma unroll
+        for (int it = 0; it < NVV; ++it) {
+            const int r = wave * RPV + lane / LPV + it * NW * RPV;
+            float x[VEC];
+            unpack((const TIN *)nullptr, pv[it], x);
+            store_vec(Vs + r * LDV + (lane % LPV) * VEC, x);
+        }
+        if (tid < CH) {
+            graw[tid] = pg;
+            bet[tid] = pb;
+        }
+        if (cs + CH < end)
+            prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH));
         __syncthreads();
 
-        // ---- B: cumulative log-gate (inclusive scan over the chunk) --------------------
-        if (wave == 0) {
-            float x = gam[lane];
+        // ---- B: cumulative log-gate; lane r of every wave holds Gamma_r -----------------
+        float gam = graw[lane];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off)
-                    x += y;
-            }
-            gam[lane] = x;
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gam, off);
+            if (lane >= off)
+                gam += y;
         }
-        __syncthreads();
-
-        // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
-        {
-            for (int task = wave; task < 20; task += NW) {
-                const bool isq = task >= 10;
-                const int p = isq ? task - 10 : task;
-                const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-                const int J = p - I * (I + 1) / 2;
-                const T *As = isq ? Qs : Ks;
-                f32x4 acc = zero4();
+        const float gC = __shfl(gam, CH - 1);
+        float gr[4][4];  // Gamma at the D-layout rows 16I + 4g + i of this lane
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    mma(acc, ld_frag(As, LDQ, 16 * I, 32 * kb, lane),
-                        ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane));
-                const int s = 16 * J + c16;
-                const float gs = gam[s];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * g4 + i;
-                    const float dec = __expf(fminf(gam[r] - gs, 0.f));
-                    if (isq)
-                        Ps[r * LDT + s] = (T)(s <= r ? dec * acc[i] : 0.f);
-                    else
-                        Ms[r * LDF + s] = s < r ? bet[r] * dec * acc[i] : 0.f;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- D: T = (I + M)^-1 by 16x16 block substitution -----------------------------
-        if (wave == 0) {  // diagonal blocks: lane -> (block lane/16, column lane%16)
-            const int base = 16 * g4, j = c16;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = r == j ? 1.f : 0.f;
-#pragma unroll
-                for (int t = 0; t < r; ++t)
-                    s -= Ms[(base + r) * LDF + base + t] * x[t];
-                x[r] = s;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                Tf[(base + r) * LDF + base + j] = x[r];
-        }
-        __syncthreads();
-        for (int I = 1 + wave; I <= 3; I += NW)
-            solve_block<LDF>(Ms, Tf, I, I - 1, lane);
-        __syncthreads();
-        for (int I = 2 + wave; I <= 3; I += NW)
-            solve_block<LDF>(Ms, Tf, I, I - 2, lane);
-        __syncthreads();
-        if (wave == 0)
-            solve_block<LDF>(Ms, Tf, 3, 0, lane);
-        __syncthreads();
-        // Tb = T diag(beta), Tba = T diag(beta . a), zero above the diagonal
-        for (int idx = tid; idx < CH * CH; idx += NT) {
-            const int r = idx >> 6, s = idx & 63;
-            const float t = s <= r ? Tf[r * LDF + s] : 0.f;
-            const float tb = t * bet[s];
-            const float tba = tb * __expf(gam[s]);
-            const T tb_hi = (T)tb, tba_hi = (T)tba;
-            Tb[r * LDT + s] = tb_hi;
-            Tba[r * LDT + s] = tba_hi;
-            if constexpr (C::SPLIT) {
-                Tbl[r * LDT + s] = (T)(tb - (float)tb_hi);
-                Tbal[r * LDT + s] = (T)(tba - (float)tba_hi);
-            }
-        }
-        __syncthreads();
-
-        // ---- E: W = Tba K (shared), U~ = Tb V (per wave) -------------------------------
-        for (int task = wave; task < 4 * (DK / 16); task += NW) {
-            const int I = task & 3, nb = task >> 2;
-            f32x4 acc = zero4();
-            for (int kb = 0; kb <= (I >> 1); ++kb) {
-                const frag kt = ld_frag(KTs, LDT, 16 * nb, 32 * kb, lane);
-                mma(acc, ld_frag(Tba, LDT, 16 * I, 32 * kb, lane), kt);
-                if constexpr (C::SPLIT)
-                    mma(acc, ld_frag(Tbal, LDT, 16 * I, 32 * kb, lane), kt);
-            }
+        for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                Ws[(16 * I + 4 * g4 + i) * LDQ + 16 * nb + c16] = (T)acc[i];
-        }
-        f32x4 ut[4];
-        {
-            const frag vt0 = ld_frag(VTs, LDT, 16 * wave, 0, lane);
-            const frag vt1 = ld_frag(VTs, LDT, 16 * wave, 32, lane);
+                gr[I][i] = __shfl(gam, 16 * I + 4 * g4 + i);
+        float gcol[4];   // Gamma at the D-layout columns 16J + c of this lane
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                ut[I] = zero4();
-                mma(ut[I], ld_frag(Tb, LDT, 16 * I, 0, lane), vt0);
-                if constexpr (C::SPLIT)
-                    mma(ut[I], ld_frag(Tbl, LDT, 16 * I, 0, lane), vt0);
-                if (I >= 2) {
-                    mma(ut[I], ld_frag(Tb, LDT, 16 * I, 32, lane), vt1);
-                    if constexpr (C::SPLIT)
-                        mma(ut[I], ld_frag(Tbl, LDT, 16 * I, 32, lane), vt1);
+        for (int J = 0; J < 4; ++J)
+            gcol[J] = __shfl(gam, 16 * J + c16);
+
+        // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
+        // 20 lower blocks (10 of K K^T, 10 of Q K^T); wave w takes tasks w, w+4, ..., w+16
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int task = wave + NW * j;
+            const bool isq = task >= 10;
+            const int p = isq ? task - 10 : task;
+            const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+            const int J = p - I * (I + 1) / 2;
+            const T *As = isq ? Qs : Ks;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb)
+                mma(acc, ld_frag(As, LDQ, 16 * I, 32 * kb, lane),
+                    ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane));
+            const int s = 16 * J + c16;
+            float gs = gcol[0];
+#pragma unroll
+            for (int jj = 1; jj < 4; ++jj)
+                gs = J == jj ? gcol[jj] : gs;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * I + 4 * g4 + i;
+                float grr = gr[0][i];
+#pragma unroll
+                for (int ii = 1; ii < 4; ++ii)
+                    grr = I == ii ? gr[ii][i] : grr;
+                const float dec = __expf(fminf(grr - gs, 0.f));
+                if (isq) {
+                    const float pv_ = s <= r ? dec * acc[i] : 0.f;
+                    const T hi = (T)pv_;
+                    Ps[r * LDT + s] = hi;
+                    if constexpr (SPLIT)
+                        Psl[r * LDT + s] = (T)(pv_ - (float)hi);
+                } else {
+                    Ms[r * LDF + s] = s < r ? bet[r] * dec * acc[i] : 0.f;
                 }
             }
         }
         __syncthreads();
 
-        // ---- F: state products for this wave's 16 columns ------------------------------
+        // ---- D: T = (I + M)^-1, each block also stored as Tb = T diag(beta) (hi + lo) ---
+        auto put_t = [&](int r, int s, float t) {
+            Tf[r * LDF + s] = t;
+            const float tb = t * bet[s];
+            const T hi = (T)tb;
+            Tb[r * LDT + s] = hi;
+            if constexpr (SPLIT)
+                Tbl[r * LDT + s] = (T)(tb - (float)hi);
+        };
         {
+            // Diagonal block I = wave: with N = -M_II (strictly lower, so N^16 = 0),
+            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8). Powers are formed on MFMA;
+            // an A operand that is not in LDS yet is written to this wave's own block of Tf
+            // (free until the block's inverse is stored there) and read back.
+            const int I = wave, base = 16 * I;
+            float *scr = Tf + base * LDF + base;
+            const f32x4 mI = blk_a(Ms, LDF, I, I, lane);   // A layout of M_II
+            const f32x4 mIb = blk_b(Ms, LDF, I, I, lane);  // D layout of M_II
+            f32x4 na, nb;                                  // N in A and D layouts
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                na[i] = -mI[i], nb[i] = -mIb[i];
+            auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    scr[(4 * g4 + i) * LDF + c16] = d[i];
+                return blk_a(Tf, LDF, I, I, lane);
+            };
+            f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
+            mm16<SPLIT>(n2, na, nb);  // N^2
+            mm16<SPLIT>(n3, na, n2);  // N^3
+            const f32x4 n2a = to_a(n2);
+            mm16<SPLIT>(n4, n2a, n2);  // N^4
+            const f32x4 n4a = to_a(n4);
+            mm16<SPLIT>(n8, n4a, n4);  // N^8
+            const f32x4 n8a = to_a(n8);
+            f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x[i] = ((4 * g4 + i) == c16 ? 1.f : 0.f) + nb[i] + n2[i] + n3[i];
+            f32x4 y = x;
+            mm16<SPLIT>(y, n4a, x);  // (I + N^4) X
+            f32x4 z = y;
+            mm16<SPLIT>(z, n8a, y);  // (I + N^8) Y
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                put_t(base + 4 * g4 + i, base + c16, z[i]);
+        }
+        __syncthreads();
+        if (wave < 3) {  // column block J = wave: T_IJ = -T_II sum_{K=J}^{I-1} M_IK T_KJ
+            const int J = wave;
+            for (int I = J + 1; I < 4; ++I) {
+                f32x4 y = zero4();
+                for (int K = J; K < I; ++K)
+                    mm16<SPLIT>(y, blk_a(Ms, LDF, I, K, lane), blk_b(Tf, LDF, K, J, lane));
+                f32x4 t = zero4();
+                mm16<SPLIT>(t, blk_a(Tf, LDF, I, I, lane), y);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    put_t(16 * I + 4 * g4 + i, 16 * J + c16, -t[i]);
+            }
+        }
+        __syncthreads();
+
+        // ---- F: state products for this wave's 16*NCB columns -------------------------
+        //   X = V - diag(a) K h,  U = T diag(beta) X,  O = diag(a) Q h + P U,
+        //   h <- a_C h + K^T diag(a_C / a) U
+        float ar[4][4], dr[4][4];  // a_r = e^Gamma_r and a_C / a_r at this lane's rows
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ar[I][i] = __expf(gr[I][i]);
+                dr[I][i] = __expf(gC - gr[I][i]);
+            }
+        const float aC = __expf(gC);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int vc = 16 * (wave * NCB + cb);  // this block's columns within Vs
             frag hf[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
-                hf[kb] = pack<T>(hs[2 * kb], hs[2 * kb + 1]);
-            f32x4 u[4], o[4];
+                hf[kb] = pack<T>(hs[cb][2 * kb], hs[cb][2 * kb + 1]);
+            f32x4 x[4], o[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                f32x4 wh = zero4(), qh = zero4();
+                f32x4 kh = zero4(), qh = zero4();
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    mma(wh, ld_frag(Ws, LDQ, 16 * I, 32 * kb, lane), hf[kb]);
+                    mma(kh, ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane), hf[kb]);
                     mma(qh, ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane), hf[kb]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * g4 + i;
-                    u[I][i] = ut[I][i] - wh[i];
-                    o[I][i] = qh[i] * __expf(gam[r]);
+                    const float v = (float)Vs[(16 * I + 4 * g4 + i) * LDV + vc + c16];
+                    x[I][i] = v - ar[I][i] * kh[i];
+                    o[I][i] = ar[I][i] * qh[i];
                 }
             }
-            const frag uf0 = pack<T>(u[0], u[1]), uf1 = pack<T>(u[2], u[3]);
+            // U = Tb X with Tb and X as hi + lo pairs
+            frag xh[2], xl[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                pack_split<T>(x[2 * kb], x[2 * kb + 1], xh[kb], xl[kb]);
+            f32x4 u[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                mma(o[I], ld_frag(Ps, LDT, 16 * I, 0, lane), uf0);
-                if (I >= 2)
-                    mma(o[I], ld_frag(Ps, LDT, 16 * I, 32, lane), uf1);
+                u[I] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb > (I >> 1))
+                        continue;
+                    const frag th = ld_frag(Tb, LDT, 16 * I, 32 * kb, lane);
+                    mma(u[I], th, xh[kb]);
+                    if constexpr (SPLIT) {
+                        mma(u[I], th, xl[kb]);
+                        mma(u[I], ld_frag(Tbl, LDT, 16 * I, 32 * kb, lane), xh[kb]);
+                    }
+                }
+            }
+            // O += P U with P and U as hi + lo pairs
+            frag uh[2], ul[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                pack_split<T>(u[2 * kb], u[2 * kb + 1], uh[kb], ul[kb]);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb > (I >> 1))
+                        continue;
+                    const frag ph = ld_frag(Ps, LDT, 16 * I, 32 * kb, lane);
+                    mma(o[I], ph, uh[kb]);
+                    if constexpr (SPLIT) {
+                        mma(o[I], ph, ul[kb]);
+                        mma(o[I], ld_frag(Psl, LDT, 16 * I, 32 * kb, lane), uh[kb]);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * I + 4 * g4 + i;
                     if (r < L)
-                        og[(cs + r) * (int64_t)H * DV] = o[I][i];
+                        og[(cs + r) * (int64_t)H * DV + 16 * cb] = o[I][i];
                 }
             }
-            const float gC = gam[CH - 1];
-            const float aC = __expf(gC);
+            // h <- a_C h + K^T (diag(a_C / a) U)
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    u[I][i] *= __expf(gC - gam[16 * I + 4 * g4 + i]);
+                    u[I][i] *= dr[I][i];
             const frag vf0 = pack<T>(u[0], u[1]), vf1 = pack<T>(u[2], u[3]);
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    hs[mb][i] *= aC;
-                mma(hs[mb], ld_frag(KTs, LDT, 16 * mb, 0, lane), vf0);
-                mma(hs[mb], ld_frag(KTs, LDT, 16 * mb, 32, lane), vf1);
+                    hs[cb][mb][i] *= aC;
+                mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 0, 16 * mb, lane), vf0);
+                mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 32, 16 * mb, lane), vf1);
             }
         }
         __syncthreads();
     }
 
 #pragma unroll
-    for (int mb = 0; mb < DK / 16; ++mb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + c16] = hs[mb][i];
+        for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + 16 * cb + c16] = hs[cb][mb][i];
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, bool KDA>
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
-    using C = ChunkCfg<T, DK, DV, NW, KDA>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
-    auto kern = chunk_kernel<TIN, T, DK, DV, NW, KDA>;
+    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA>;
     static bool attr_set = false;  // per instance; same value on every device
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -786,39 +957,36 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
     return hipGetLastError();
 }
 
-// Instances: (input element, operand type, input kind, dk, dv, waves per workgroup).
-// Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations of the front end.
-#define GDN_CHUNK_INSTANCES(X)          \
-    X(bf16, f16, 1, 128, 128, 8)        \
-    X(bf16, f16, 1, 128, 128, 4)        \
-    X(bf16, f16, 1, 128, 128, 2)        \
-    X(bf16, f16, 1, 128, 128, 1)        \
-    X(f16, f16, 2, 128, 128, 8)         \
-    X(f16, f16, 2, 128, 128, 4)         \
-    X(f16, f16, 2, 128, 128, 2)         \
-    X(f16, f16, 2, 128, 128, 1)         \
-    X(bf16, f16, 1, 64, 64, 4)          \
-    X(bf16, f16, 1, 64, 64, 1)          \
-    X(f16, f16, 2, 64, 64, 4)           \
-    X(f16, f16, 2, 64, 64, 1)           \
-    X(float, float, 0, 64, 64, 4)       \
-    X(float, float, 0, 64, 64, 1)
+// Instances: (input element, operand type, input kind, dk, dv, waves, column blocks of 16
+// per wave). Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations of the front end.
+// A workgroup covers NW * NCB * 16 dv columns of one (stream, head).
+#define GDN_CHUNK_INSTANCES(X)            \
+    X(bf16, f16, 1, 128, 128, 4, 2)       \
+    X(bf16, f16, 1, 128, 128, 4, 1)       \
+    X(f16, f16, 2, 128, 128, 4, 2)        \
+    X(f16, f16, 2, 128, 128, 4, 1)        \
+    X(bf16, f16, 1, 64, 64, 4, 1)         \
+    X(f16, f16, 2, 64, 64, 4, 1)          \
+    X(float, float, 0, 64, 64, 4, 1)
 
-hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nw, const ChunkArgs &a,
-                        int grid, hipStream_t s)
+// nv: dv columns per workgroup; waves: 0 = the default for that width
+hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
+                        const ChunkArgs &a, int grid, hipStream_t s)
 {
-#define X(TIN, T, IK, DK, DV, NW)                                    \
-    if (in_kind == IK && dk == DK && dv == DV && nw == NW && !kda)   \
-        return launch_chunk_t<TIN, T, DK, DV, NW, false>(a, grid, s);
+#define X(TIN, T, IK, DK, DV, NW, NCB)                                                 \
+    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda &&        \
+        (waves == 0 || waves == NW))                                                   \
+        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, false>(a, grid, s);
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nw)
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves)
 {
-#define X(TIN, T, IK, DK, DV, NW)                                   \
-    if (in_kind == IK && dk == DK && dv == DV && nw == NW && !kda)  \
+#define X(TIN, T, IK, DK, DV, NW, NCB)                                                 \
+    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda &&        \
+        (waves == 0 || waves == NW))                                                   \
         return 1;
     GDN_CHUNK_INSTANCES(X)
 #undef X
