@@ -27,7 +27,7 @@ GDN_KIND_VARLEN = 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",
-           "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
+           "kda_prefill_batched", "kda_prefill_varlen", "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
            "gdn_status_string")
 GDN_PROF_FRONT = 0
 GDN_PROF_RECUR = 1
@@ -63,10 +63,13 @@ def load(path: str = SO):
         single = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
         lib.gdn_prefill.argtypes = single
         lib.kda_prefill.argtypes = single
-        lib.gdn_prefill_batched.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                            _i32, _i64, _vp, _sz, _vp]
-        lib.gdn_prefill_varlen.argtypes = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                           _vp, _i32, _i64, _i32, _vp, _sz, _vp]
+        batched = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz, _vp]
+        varlen = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp,
+                  _sz, _vp]
+        lib.gdn_prefill_batched.argtypes = batched
+        lib.kda_prefill_batched.argtypes = batched
+        lib.gdn_prefill_varlen.argtypes = varlen
+        lib.kda_prefill_varlen.argtypes = varlen
         lib.gdn_chunk_table.argtypes = [_vp, _i32, _i32, _vp, _i64, _vp, _vp]
         lib.gdn_profile_enable.argtypes = [ctypes.c_int]
         lib.gdn_profile_enable.restype = ctypes.c_int
@@ -77,7 +80,8 @@ def load(path: str = SO):
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
-                     "gdn_prefill_varlen", "gdn_chunk_table"):
+                     "gdn_prefill_varlen", "kda_prefill_batched", "kda_prefill_varlen",
+                     "gdn_chunk_table"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -121,6 +125,21 @@ def gdn_prefill_batched(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o,
 def gdn_prefill_varlen(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, cu_seqlens,
                        B, total_tokens, max_seqlen, ws, ws_bytes, stream):
     return load().gdn_prefill_varlen(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                     _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o),
+                                     _p(cu_seqlens), B, total_tokens, max_seqlen, _p(ws),
+                                     ws_bytes, stream)
+
+
+def kda_prefill_batched(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B,
+                        t_per_stream, ws, ws_bytes, stream):
+    return load().kda_prefill_batched(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                      _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o), B,
+                                      t_per_stream, _p(ws), ws_bytes, stream)
+
+
+def kda_prefill_varlen(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, cu_seqlens,
+                       B, total_tokens, max_seqlen, ws, ws_bytes, stream):
+    return load().kda_prefill_varlen(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
                                      _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o),
                                      _p(cu_seqlens), B, total_tokens, max_seqlen, _p(ws),
                                      ws_bytes, stream)

@@ -179,7 +179,8 @@ int run(const Call &c)
         return rc;
     if (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.o || (!c.h && !c.h_ptrs))
         return GDN_E_ARG;
-    if (!aligned16(c.q) || !aligned16(c.k) || !aligned16(c.v) || !aligned16(c.o))
+    if (!aligned16(c.q) || !aligned16(c.k) || !aligned16(c.v) || !aligned16(c.o) ||
+        (c.kda && !aligned16(c.g)))
         return GDN_E_ARG;
     const bool front = p->conv_k > 0;
     if (front != (c.conv_w != nullptr) ||
@@ -290,23 +291,61 @@ int kda_prefill(const gdn_params *p, const void *q, const void *k, const void *v
     return single(p, 1, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream);
 }
 
-int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
-                        const float *g, const float *beta, float *const *h_ptrs,
-                        void *const *conv_state_ptrs, const float *conv_w, void *o,
-                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
-                        void *stream)
+namespace {
+int batched(const gdn_params *p, int kda, const void *q, const void *k, const void *v,
+            const float *g, const float *beta, float *const *h_ptrs,
+            void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+            int64_t t_per_stream, void *ws, size_t ws_bytes, void *stream)
 {
     if (B < 1 || t_per_stream < 1 || !h_ptrs)
         return GDN_E_ARG;
     if (t_per_stream > (int64_t)INT32_MAX / B)
         return GDN_E_ARG;
     Call c{};
-    c.p = p, c.kda = 0, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
+    c.p = p, c.kda = kda, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
     c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
     c.st = Streams{nullptr, t_per_stream, B};
     c.N = (int64_t)B * t_per_stream, c.ws = ws, c.ws_bytes = ws_bytes;
     c.stream = (hipStream_t)stream;
     return run(c);
+}
+
+int varlen(const gdn_params *p, int kda, const void *q, const void *k, const void *v,
+           const float *g, const float *beta, float *const *h_ptrs,
+           void *const *conv_state_ptrs, const float *conv_w, void *o,
+           const int32_t *cu_seqlens, int32_t B, int64_t total_tokens, int32_t max_seqlen,
+           void *ws, size_t ws_bytes, void *stream)
+{
+    if (B < 1 || !h_ptrs || !cu_seqlens || total_tokens < 1 || max_seqlen < 1 ||
+        max_seqlen > total_tokens)
+        return GDN_E_ARG;
+    Call c{};
+    c.p = p, c.kda = kda, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
+    c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
+    c.st = Streams{cu_seqlens, 0, B};
+    c.N = total_tokens, c.ws = ws, c.ws_bytes = ws_bytes, c.stream = (hipStream_t)stream;
+    return run(c);
+}
+}  // namespace
+
+int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *const *h_ptrs,
+                        void *const *conv_state_ptrs, const float *conv_w, void *o,
+                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    return batched(p, 0, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B,
+                   t_per_stream, ws, ws_bytes, stream);
+}
+
+int kda_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *const *h_ptrs,
+                        void *const *conv_state_ptrs, const float *conv_w, void *o,
+                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    return batched(p, 1, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B,
+                   t_per_stream, ws, ws_bytes, stream);
 }
 
 int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
@@ -315,15 +354,18 @@ int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const 
                        const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,
                        int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream)
 {
-    if (B < 1 || !h_ptrs || !cu_seqlens || total_tokens < 1 || max_seqlen < 1 ||
-        max_seqlen > total_tokens)
-        return GDN_E_ARG;
-    Call c{};
-    c.p = p, c.kda = 0, c.q = q, c.k = k, c.v = v, c.g = g, c.beta = beta;
-    c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
-    c.st = Streams{cu_seqlens, 0, B};
-    c.N = total_tokens, c.ws = ws, c.ws_bytes = ws_bytes, c.stream = (hipStream_t)stream;
-    return run(c);
+    return varlen(p, 0, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, cu_seqlens, B,
+                  total_tokens, max_seqlen, ws, ws_bytes, stream);
+}
+
+int kda_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, float *const *h_ptrs,
+                       void *const *conv_state_ptrs, const float *conv_w, void *o,
+                       const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,
+                       int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream)
+{
+    return varlen(p, 1, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, cu_seqlens, B,
+                  total_tokens, max_seqlen, ws, ws_bytes, stream);
 }
 
 int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t *table,

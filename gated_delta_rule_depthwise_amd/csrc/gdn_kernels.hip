@@ -31,6 +31,7 @@
 namespace gdn {
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
@@ -430,7 +431,7 @@ hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s)
 
 constexpr int CH = 64;  // chunk length
 
-template <typename T, int DK, int DV, int NW, int NCB>
+template <typename T, int DK, int DV, int NW, int NCB, bool KDA>
 struct ChunkCfg {
     static constexpr int NV = 16 * NW * NCB;  // dv columns per workgroup (16*NCB per wave)
     // fp16 operands: T = (I+M)^-1 and P are applied as fp16 hi + lo pairs, and the
@@ -446,6 +447,7 @@ struct ChunkCfg {
     static constexpr int LDV = NV + PAD;  // Vs: [64][LDV]
     static constexpr int LDT = CH + PAD;  // P and T operand tiles: [64][LDT]
     static constexpr int LDF = CH + 4;    // Ms, Tf: [64][LDF] float
+    static constexpr int LDG = DK + 4;    // per-channel gate: Gk [64][LDG] float
     static constexpr int SZ_Q = CH * LDQ * (int)sizeof(T);
     static constexpr int SZ_V = CH * LDV * (int)sizeof(T);
     static constexpr int SZ_P = CH * LDT * (int)sizeof(T);
@@ -459,8 +461,11 @@ struct ChunkCfg {
     static constexpr int OFF_TBL = OFF_TB + SZ_P;
     static constexpr int OFF_M = OFF_TBL + (SPLIT ? SZ_P : 0);
     static constexpr int OFF_TF = OFF_M + SZ_F;
-    static constexpr int OFF_G = OFF_TF + SZ_F;  // graw[64], bet[64]
+    static constexpr int OFF_GK = OFF_TF + SZ_F;  // per-channel cumulative log-gates
+    static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);  // graw[64], bet[64]
     static constexpr int BYTES = OFF_G + 2 * CH * 4;
+    // the gated K^T tile of the per-channel-gate state update reuses Ms + Tf
+    static_assert(!KDA || SZ_Q <= 2 * SZ_F, "gated tile fits the solve scratch");
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -574,8 +579,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
     static_assert(NW == 4, "4 waves per workgroup (one per SIMD)");
-    using C = ChunkCfg<T, DK, DV, NW, NCB>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
     constexpr int NV = C::NV, LDQ = C::LDQ, LDV = C::LDV, LDT = C::LDT, LDF = C::LDF;
+    constexpr int LDG = C::LDG;
     constexpr bool SPLIT = C::SPLIT;
     constexpr int VEC = Tr<T>::VEC;
     constexpr int NT = NW * 64;
@@ -584,6 +590,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     constexpr int LPR = DK / VEC, RPW = 64 / LPR, NQK = 2 * CH / (NW * RPW);
     constexpr int LPV = NV / VEC, RPV = 64 / LPV, NVV = CH / (NW * RPV);
     static_assert(NQK * NW * RPW == 2 * CH && NVV * NW * RPV == CH, "load map");
+    // per-channel gate rows (fp32): 16-byte pieces per row and rows per wave pass
+    constexpr int GPR = DK * 4 / 16, GRW = 64 / GPR, NGK = KDA ? CH / (NW * GRW) : 1;
+    static_assert(!KDA || NGK * NW * GRW == CH, "gate load map");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     T *Qs = (T *)(smem + C::OFF_Q);
@@ -595,6 +604,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     T *Tbl = (T *)(smem + C::OFF_TBL);
     float *Ms = (float *)(smem + C::OFF_M);
     float *Tf = (float *)(smem + C::OFF_TF);
+    float *Gk = (float *)(smem + C::OFF_GK);  // per-channel gate only
     float *graw = (float *)(smem + C::OFF_G);
     float *bet = graw + CH;
 
@@ -637,7 +647,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 
     // Raw 16-byte vectors of the next chunk, loaded one chunk ahead so that the HBM latency
     // hides behind a whole chunk of work. Rows at or past the stream's end are never read.
-    uint4 pq[NQK], pv[NVV];
+    uint4 pq[NQK], pv[NVV], pgk[NGK];
     float pg = 0.f, pb = 0.f;
     auto prefetch = [&](int64_t c0, int Lc) {
 #pragma unroll
@@ -653,8 +663,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             const TIN *src = vg + (c0 + r) * ld + (lane % LPV) * VEC;
             pv[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
         }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int it = 0; it < NGK; ++it) {
+                const int r = wave * GRW + lane / GPR + it * NW * GRW;
+                const float *src = a.g + ((c0 + r) * H + head) * DK + (lane % GPR) * 4;
+                pgk[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
+            }
+        }
         if (tid < CH) {
-            pg = tid < Lc ? a.g[(c0 + tid) * H + head] : 0.f;
+            if constexpr (!KDA)
+                pg = tid < Lc ? a.g[(c0 + tid) * H + head] : 0.f;
             pb = tid < Lc ? a.beta[(c0 + tid) * H + head] : 0.f;
         }
     };
@@ -696,6 +715,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             unpack((const TIN *)nullptr, pv[it], x);
             store_vec(Vs + r * LDV + (lane % LPV) * VEC, x);
         }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int it = 0; it < NGK; ++it) {
+                const int r = wave * GRW + lane / GPR + it * NW * GRW;
+                *reinterpret_cast<uint4 *>(Gk + r * LDG + (lane % GPR) * 4) = pgk[it];
+            }
+        }
         if (tid < CH) {
             graw[tid] = pg;
             bet[tid] = pb;
@@ -705,6 +731,33 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
         __syncthreads();
 
         // ---- B: cumulative log-gate; lane r of every wave holds Gamma_r -----------------
+        if constexpr (KDA) {
+            // per channel, in place in Gk: each thread scans CH/PARTS rows of one channel,
+            // then adds the totals of the parts above it
+            constexpr int PARTS = NT / DK, RP = CH / PARTS;
+            const int c = tid % DK, part = tid / DK;
+            float xs[RP];
+            float run = 0.f;
+#pragma unroll
+            for (int j = 0; j < RP; ++j) {
+                run += Gk[(part * RP + j) * LDG + c];
+                xs[j] = run;
+            }
+#pragma unroll
+            for (int j = 0; j < RP; ++j)
+                Gk[(part * RP + j) * LDG + c] = xs[j];
+            __syncthreads();
+            float add = 0.f;
+            for (int pp = 0; pp < part; ++pp)
+                add += Gk[(pp * RP + RP - 1) * LDG + c];
+            __syncthreads();
+            if (part > 0) {
+#pragma unroll
+                for (int j = 0; j < RP; ++j)
+                    Gk[(part * RP + j) * LDG + c] = xs[j] + add;
+            }
+            __syncthreads();
+        }
         float gam = graw[lane];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -735,10 +788,79 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             const int J = p - I * (I + 1) / 2;
             const T *As = isq ? Qs : Ks;
             f32x4 acc = zero4();
+            if constexpr (!KDA) {
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                mma(acc, ld_frag(As, LDQ, 16 * I, 32 * kb, lane),
-                    ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane));
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    mma(acc, ld_frag(As, LDQ, 16 * I, 32 * kb, lane),
+                        ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane));
+            } else if (I != J) {
+                // off-diagonal block: reference row b = 16I (first row of block I), so
+                // both factors e^(G_r - G_b) (r >= b) and e^(G_b - G_s) (s < b) are <= 1
+                const float *gb = Gk + 16 * I * LDG;
+                const float *gr_ = Gk + (16 * I + c16) * LDG;
+                const float *gs_ = Gk + (16 * J + c16) * LDG;
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    frag fa = ld_frag(As, LDQ, 16 * I, 32 * kb, lane);
+                    frag fb = ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane);
+                    const int c0 = 32 * kb + 4 * g4;
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gb + c0);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(gb + c0 + 16);
+                    const f32x4 r0 = *reinterpret_cast<const f32x4 *>(gr_ + c0);
+                    const f32x4 r1 = *reinterpret_cast<const f32x4 *>(gr_ + c0 + 16);
+                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(gs_ + c0);
+                    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(gs_ + c0 + 16);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        fa[i] = (T)((float)fa[i] * __expf(r0[i] - b0[i]));
+                        fa[4 + i] = (T)((float)fa[4 + i] * __expf(r1[i] - b1[i]));
+                        fb[i] = (T)((float)fb[i] * __expf(b0[i] - s0[i]));
+                        fb[4 + i] = (T)((float)fb[4 + i] * __expf(b1[i] - s1[i]));
+                    }
+                    mma(acc, fa, fb);
+                }
+            } else {
+                // diagonal block: mid-block reference m = 16I + 8, so each factor spans at
+                // most 8 tokens of decay (exponents clamped at 80); the gated operands can
+                // exceed the fp16 range, so they go in fp32 range: fp32 MFMA for fp32 tiles,
+                // bf16 hi + lo pairs (about 16 mantissa bits) for fp16 tiles
+                const float *gm = Gk + (16 * I + 8) * LDG;
+                const float *grs = Gk + (16 * I + c16) * LDG;
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int kb = 0; kb < DK / 32; ++kb) {
+                        const frag xa = ld_frag(As, LDQ, 16 * I, 32 * kb, lane);
+                        const frag xb = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
+                        const int c0 = 32 * kb + 4 * g4;
+                        bf16x8 ah, al, bh, bl;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int ch = c0 + (i < 4 ? i : 12 + i);
+                            const float d = grs[ch] - gm[ch];
+                            const float av = (float)xa[i] * __expf(fminf(d, 80.f));
+                            const float bv = (float)xb[i] * __expf(fminf(-d, 80.f));
+                            ah[i] = (bf16)av;
+                            al[i] = (bf16)(av - (float)ah[i]);
+                            bh[i] = (bf16)bv;
+                            bl[i] = (bf16)(bv - (float)bh[i]);
+                        }
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                    }
+                } else {
+                    const T *xr = As + (16 * I + c16) * LDQ;
+                    const T *ks = Ks + (16 * I + c16) * LDQ;
+#pragma unroll 8
+                    for (int j4 = 0; j4 < DK / 4; ++j4) {
+                        const int ch = 4 * j4 + g4;
+                        const float d = grs[ch] - gm[ch];
+                        const float av = (float)xr[ch] * __expf(fminf(d, 80.f));
+                        const float bv = (float)ks[ch] * __expf(fminf(-d, 80.f));
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                    }
+                }
+            }
             const int s = 16 * J + c16;
             float gs = gcol[0];
 #pragma unroll
@@ -751,7 +873,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 #pragma unroll
                 for (int ii = 1; ii < 4; ++ii)
                     grr = I == ii ? gr[ii][i] : grr;
-                const float dec = __expf(fminf(grr - gs, 0.f));
+                // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside acc);
+                // the masked upper part is discarded by the selects below
+                const float dec = KDA ? 1.f : __expf(grr - gs);
                 if (isq) {
                     const float pv_ = s <= r ? dec * acc[i] : 0.f;
                     const T hi = (T)pv_;
@@ -828,6 +952,26 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             }
         }
         __syncthreads();
+        T *Kd = (T *)(smem + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms + Tf
+        if constexpr (KDA) {
+            // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1
+            for (int idx = tid; idx < CH * (DK / VEC); idx += NT) {
+                const int r = idx / (DK / VEC), c0 = (idx % (DK / VEC)) * VEC;
+                T *kp = Ks + r * LDQ + c0;
+                T *qp = Qs + r * LDQ + c0;
+                T *dp = Kd + r * LDQ + c0;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const float gg = Gk[r * LDG + c0 + i];
+                    const float gcc = Gk[(CH - 1) * LDG + c0 + i];
+                    const float kv = (float)kp[i], qv = (float)qp[i];
+                    dp[i] = (T)(kv * __expf(gcc - gg));
+                    kp[i] = (T)(kv * __expf(gg));
+                    qp[i] = (T)(qv * __expf(gg));
+                }
+            }
+            __syncthreads();
+        }
 
         // ---- F: state products for this wave's 16*NCB columns -------------------------
         //   X = V - diag(a) K h,  U = T diag(beta) X,  O = diag(a) Q h + P U,
@@ -860,8 +1004,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float v = (float)Vs[(16 * I + 4 * g4 + i) * LDV + vc + c16];
-                    x[I][i] = v - ar[I][i] * kh[i];
-                    o[I][i] = ar[I][i] * qh[i];
+                    const float arr = KDA ? 1.f : ar[I][i];  // gated tiles carry e^G
+                    x[I][i] = v - arr * kh[i];
+                    o[I][i] = arr * qh[i];
                 }
             }
             // U = Tb X with Tb and X as hi + lo pairs
@@ -910,20 +1055,32 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                         og[(cs + r) * (int64_t)H * DV + 16 * cb] = o[I][i];
                 }
             }
-            // h <- a_C h + K^T (diag(a_C / a) U)
+            // h <- a_C h + K^T (diag(a_C / a) U); per-channel gate:
+            // h <- diag(e^G_C) h + (K . e^(G_C - G))^T U
+            if constexpr (!KDA) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+                for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    u[I][i] *= dr[I][i];
+                    for (int i = 0; i < 4; ++i)
+                        u[I][i] *= dr[I][i];
+            }
             const frag vf0 = pack<T>(u[0], u[1]), vf1 = pack<T>(u[2], u[3]);
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb) {
+                if constexpr (KDA) {
+                    const float *gcr = Gk + (CH - 1) * LDG + 16 * mb + 4 * g4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    hs[cb][mb][i] *= aC;
-                mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 0, 16 * mb, lane), vf0);
-                mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 32, 16 * mb, lane), vf1);
+                    for (int i = 0; i < 4; ++i)
+                        hs[cb][mb][i] *= __expf(gcr[i]);
+                    mma(hs[cb][mb], ld_frag_t(Kd, LDQ, 0, 16 * mb, lane), vf0);
+                    mma(hs[cb][mb], ld_frag_t(Kd, LDQ, 32, 16 * mb, lane), vf1);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        hs[cb][mb][i] *= aC;
+                    mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 0, 16 * mb, lane), vf0);
+                    mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 32, 16 * mb, lane), vf1);
+                }
             }
         }
         __syncthreads();
@@ -941,7 +1098,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
-    using C = ChunkCfg<T, DK, DV, NW, NCB>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
     auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA>;
@@ -958,25 +1115,30 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 }
 
 // Instances: (input element, operand type, input kind, dk, dv, waves, column blocks of 16
-// per wave). Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations of the front end.
-// A workgroup covers NW * NCB * 16 dv columns of one (stream, head).
-#define GDN_CHUNK_INSTANCES(X)            \
-    X(bf16, f16, 1, 128, 128, 4, 2)       \
-    X(bf16, f16, 1, 128, 128, 4, 1)       \
-    X(f16, f16, 2, 128, 128, 4, 2)        \
-    X(f16, f16, 2, 128, 128, 4, 1)        \
-    X(bf16, f16, 1, 64, 64, 4, 1)         \
-    X(f16, f16, 2, 64, 64, 4, 1)          \
-    X(float, float, 0, 64, 64, 4, 1)
+// per wave, per-channel gate). Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
+// of the front end. A workgroup covers NW * NCB * 16 dv columns of one (stream, head).
+#define GDN_CHUNK_INSTANCES(X)                   \
+    X(bf16, f16, 1, 128, 128, 4, 2, false)       \
+    X(bf16, f16, 1, 128, 128, 4, 1, false)       \
+    X(f16, f16, 2, 128, 128, 4, 2, false)        \
+    X(f16, f16, 2, 128, 128, 4, 1, false)        \
+    X(bf16, f16, 1, 64, 64, 4, 1, false)         \
+    X(f16, f16, 2, 64, 64, 4, 1, false)          \
+    X(float, float, 0, 64, 64, 4, 1, false)      \
+    X(bf16, f16, 1, 128, 128, 4, 1, true)        \
+    X(f16, f16, 2, 128, 128, 4, 1, true)         \
+    X(bf16, f16, 1, 64, 64, 4, 1, true)          \
+    X(f16, f16, 2, 64, 64, 4, 1, true)           \
+    X(float, float, 0, 64, 64, 4, 1, true)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
                         const ChunkArgs &a, int grid, hipStream_t s)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB)                                                 \
-    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda &&        \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD)                                             \
+    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
         (waves == 0 || waves == NW))                                                   \
-        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, false>(a, grid, s);
+        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD>(a, grid, s);
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return hipErrorInvalidValue;
@@ -984,8 +1146,8 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 
 int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB)                                                 \
-    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda &&        \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD)                                             \
+    if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
         (waves == 0 || waves == NW))                                                   \
         return 1;
     GDN_CHUNK_INSTANCES(X)

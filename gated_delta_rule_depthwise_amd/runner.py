@@ -27,8 +27,6 @@ class Prefill:
         if mode is None:
             mode = "single" if len(lens) == 1 else (
                 "batched" if len(set(lens)) == 1 else "varlen")
-        if spec.gate == "kda" and mode != "single":
-            raise ValueError("the per-key-channel gate is exposed for single streams")
         self.mode = mode
         self.x = inp["x"].to(device)
         self.g = inp["g"].to(device)
@@ -76,12 +74,13 @@ class Prefill:
             fn = B.kda_prefill if sp.gate == "kda" else B.gdn_prefill
             return fn(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g, self.beta,
                       self.h, cs, self.conv_w, self.o, sp.N, self.ws, self.ws_bytes, s)
+        kda = sp.gate == "kda"
         if self.mode == "batched":
-            return B.gdn_prefill_batched(self.params, self.q_ptr, self.k_ptr, self.v_ptr,
-                                         self.g, self.beta, self.h_ptrs, self.cs_ptrs,
-                                         self.conv_w, self.o, sp.B, sp.lengths[0], self.ws,
-                                         self.ws_bytes, s)
-        return B.gdn_prefill_varlen(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g,
-                                    self.beta, self.h_ptrs, self.cs_ptrs, self.conv_w, self.o,
-                                    self.cu, sp.B, sp.N, max(sp.lengths), self.ws,
-                                    self.ws_bytes, s)
+            fn = B.kda_prefill_batched if kda else B.gdn_prefill_batched
+            return fn(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g, self.beta,
+                      self.h_ptrs, self.cs_ptrs, self.conv_w, self.o, sp.B, sp.lengths[0],
+                      self.ws, self.ws_bytes, s)
+        fn = B.kda_prefill_varlen if kda else B.gdn_prefill_varlen
+        return fn(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g, self.beta,
+                  self.h_ptrs, self.cs_ptrs, self.conv_w, self.o, self.cu, sp.B, sp.N,
+                  max(sp.lengths), self.ws, self.ws_bytes, s)

@@ -101,7 +101,8 @@ int gdn_prefill(const gdn_params *p, const void *q, const void *k, const void *v
                 const float *conv_w, void *o, int64_t t, void *ws, size_t ws_bytes,
                 void *stream);
 
-/* Same as gdn_prefill with the per-key-channel gate: g is [t][H][dk] (page
+/* Same as gdn_prefill with the per-key-channel gate: g is [t][H][dk], 16-byte aligned, and
+ * must be a decay (g <= 0; see kda_prefill_batched) (page
  * "metrale_model_arch/glm5next_kda/prefill.rs", the KDA chunked prefill). */
 int kda_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, float *h, void *conv_state,
@@ -137,6 +138,25 @@ int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const
  *   ws           >= gdn_workspace_bytes(p, B, total_tokens, GDN_KIND_VARLEN).
  */
 int gdn_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, float *const *h_ptrs,
+                       void *const *conv_state_ptrs, const float *conv_w, void *o,
+                       const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,
+                       int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The per-key-channel gate for equal-length and varlen streams: as gdn_prefill_batched and
+ * gdn_prefill_varlen with g [rows][H][dk] (one log-gate per key channel, 16-byte aligned).
+ * The gate must be a decay, g <= 0: chunk products are factored at 16-token block
+ * boundaries with factors e^(G_r - G_ref) <= 1 held in fp16, and the diagonal 16x16 blocks
+ * in fp32 with a mid-block reference whose exponents are clamped at 80 (a decay stronger
+ * than e^-80 over 8 tokens of one channel is flushed).
+ */
+int kda_prefill_batched(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *const *h_ptrs,
+                        void *const *conv_state_ptrs, const float *conv_w, void *o,
+                        int32_t B, int64_t t_per_stream, void *ws, size_t ws_bytes,
+                        void *stream);
+int kda_prefill_varlen(const gdn_params *p, const void *q, const void *k, const void *v,
                        const float *g, const float *beta, float *const *h_ptrs,
                        void *const *conv_state_ptrs, const float *conv_w, void *o,
                        const int32_t *cu_seqlens, int32_t B, int64_t total_tokens,

@@ -24,7 +24,11 @@ def rel_err(got, ref):
 
 
 def spec_small(base: int, **kw):
-    return dataclasses.replace(inputs.config(base), **kw)
+    """Workload ``base`` with some fields replaced; the name records the changes."""
+    tag = ",".join("%s=%s" % (k, v if k != "lengths" else (v if len(v) < 5 else "%d streams" % len(v)))
+                   for k, v in sorted(kw.items()) if k != "seed")
+    spec = dataclasses.replace(inputs.config(base), **kw)
+    return dataclasses.replace(spec, name="cfg%d[%s]" % (base, tag))
 
 
 def run_gpu(inp, mode=None, o_fill=SENTINEL, **kw):

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gated_delta_rule_depthwise_amd import inputs
-from tests.gpu_util import compare, run_gpu, run_oracle
+from tests.gpu_util import compare, rel_err, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -40,3 +40,35 @@ def test_config3_batched_8x2048():
 @pytest.mark.parametrize("fill", [float("nan"), 1e30])
 def test_config4_varlen_tails(fill):
     _full(4, heads=[0, 31], fill=fill)
+
+
+def test_config5_kda_one_shot_and_4_calls():
+    """KDA, T=16384 with the front end: one call, and 4 calls of 4096 carrying the conv
+    window and h; both match the oracle and each other."""
+    spec = inputs.config(5)
+    inp = inputs.make(spec)
+    one = run_gpu(inp)
+    ref = run_oracle(inp, heads=[0, 31])
+    e_o, e_h = compare(one, ref, heads=[0, 31])
+    print("%s one-shot: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
+    import dataclasses
+    h, cs = inp["h0"], inp["conv_state"]
+    parts = []
+    for s0 in range(0, 16384, 4096):
+        sub = dataclasses.replace(spec, lengths=[4096])
+        d = {"spec": sub, "x": torch.zeros(sub.alloc, spec.cd, dtype=inp["x"].dtype),
+             "g": torch.zeros((sub.alloc,) + tuple(inp["g"].shape[1:])),
+             "beta": torch.zeros(sub.alloc, spec.H), "h0": h, "conv_w": inp["conv_w"],
+             "conv_state": cs, "cu_seqlens": torch.tensor([0, 4096], dtype=torch.int32)}
+        d["x"][:4096] = inp["x"][s0:s0 + 4096]
+        d["g"][:4096] = inp["g"][s0:s0 + 4096]
+        d["beta"][:4096] = inp["beta"][s0:s0 + 4096]
+        c = run_gpu(d)
+        parts.append(c.o[:4096].cpu())
+        h, cs = c.h.cpu(), c.conv_state.cpu()
+    o4 = torch.cat(parts)
+    sel = [0, 31]
+    assert rel_err(o4[:, sel].numpy(), ref["o"]) < 2e-2
+    assert rel_err(h[:, sel].numpy(), ref["h"]) < 2e-2
+    assert rel_err(o4.numpy(), one.o[:16384].cpu().numpy()) < 2e-2
+    assert torch.equal(cs, one.conv_state.cpu())
