@@ -452,20 +452,18 @@ struct ChunkCfg {
     static constexpr int SZ_V = CH * LDV * (int)sizeof(T);
     static constexpr int SZ_P = CH * LDT * (int)sizeof(T);
     static constexpr int SZ_F = CH * LDF * 4;
+    static constexpr int SZ_MS = SZ_F > SZ_Q ? SZ_F : SZ_Q;  // the KDA gated K^T tile reuses it
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + SZ_Q;
     static constexpr int OFF_V = OFF_K + SZ_Q;
-    static constexpr int OFF_P = OFF_V + SZ_V;
-    static constexpr int OFF_PL = OFF_P + SZ_P;
-    static constexpr int OFF_TB = OFF_PL + (SPLIT ? SZ_P : 0);
-    static constexpr int OFF_TBL = OFF_TB + SZ_P;
-    static constexpr int OFF_M = OFF_TBL + (SPLIT ? SZ_P : 0);
-    static constexpr int OFF_TF = OFF_M + SZ_F;
-    static constexpr int OFF_GK = OFF_TF + SZ_F;  // per-channel cumulative log-gates
+    static constexpr int OFF_P = OFF_V + SZ_V;                    // P (hi)
+    static constexpr int OFF_PL = OFF_P + SZ_P;                   // P (lo)
+    static constexpr int OFF_MT = OFF_PL + (SPLIT ? SZ_P : 0);    // M_IJ (J<I), T_II (hi)
+    static constexpr int OFF_MTL = OFF_MT + SZ_P;                 // same (lo)
+    static constexpr int OFF_M = OFF_MTL + (SPLIT ? SZ_P : 0);    // diagonal blocks of M, fp32
+    static constexpr int OFF_GK = OFF_M + SZ_MS;  // per-channel cumulative log-gates
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);  // graw[64], bet[64]
     static constexpr int BYTES = OFF_G + 2 * CH * 4;
-    // the gated K^T tile of the per-channel-gate state update reuses Ms + Tf
-    static_assert(!KDA || SZ_Q <= 2 * SZ_F, "gated tile fits the solve scratch");
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -557,6 +555,46 @@ __device__ __forceinline__ f32x4 blk_b(const float *X, int ld, int K, int J, int
     return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
+// A-operand fragment of 16x16 block (I, J) of a row-major operand tile (16-deep products):
+// a[i] = X[16I+c][16J+4g+i], returned as fp32 values
+__device__ __forceinline__ f32x4 blk_a16(const f16 *X, int ld, int I, int J, int lane)
+{
+    const f16x4 v = *reinterpret_cast<const f16x4 *>(X + (16 * I + (lane & 15)) * ld + 16 * J +
+                                                     4 * (lane >> 4));
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 blk_a16(const float *X, int ld, int I, int J, int lane)
+{
+    return blk_a(X, ld, I, J, lane);
+}
+
+// d += A B (16x16 blocks, 16-deep) with A given as a stored hi + lo pair of operand tiles and
+// B an fp32 D-layout value split here into hi + lo; fp32 tiles use fp32 MFMA directly.
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *Xh, const f16 *Xl, int ld, int I,
+                                         int J, const f32x4 &b, int lane)
+{
+    const int off = (16 * I + (lane & 15)) * ld + 16 * J + 4 * (lane >> 4);
+    const f16x4 ah = *reinterpret_cast<const f16x4 *>(Xh + off);
+    const f16x4 al = *reinterpret_cast<const f16x4 *>(Xl + off);
+    f16x4 bh, bl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bh[i] = (f16)b[i];
+        bl[i] = (f16)(b[i] - (float)bh[i]);
+    }
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const float *Xh, const float *, int ld, int I,
+                                         int J, const f32x4 &b, int lane)
+{
+    const f32x4 a = blk_a(Xh, ld, I, J, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], d, 0, 0, 0);
+}
+
 // hi + lo operand pair of the B operand built from two D-layout accumulators
 template <typename T>
 __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
@@ -600,10 +638,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     T *Vs = (T *)(smem + C::OFF_V);
     T *Ps = (T *)(smem + C::OFF_P);
     T *Psl = (T *)(smem + C::OFF_PL);
-    T *Tb = (T *)(smem + C::OFF_TB);
-    T *Tbl = (T *)(smem + C::OFF_TBL);
+    T *MTh = (T *)(smem + C::OFF_MT);
+    T *MTl = (T *)(smem + C::OFF_MTL);
     float *Ms = (float *)(smem + C::OFF_M);
-    float *Tf = (float *)(smem + C::OFF_TF);
     float *Gk = (float *)(smem + C::OFF_GK);  // per-channel gate only
     float *graw = (float *)(smem + C::OFF_G);
     float *bet = graw + CH;
@@ -626,13 +663,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     float *og = a.o + head * DV + colw + c16;  // + 16 cb for column block cb
     const int64_t ld = a.ld;
 
-    // blocks above the diagonal that the 32-deep steps over P and Tb touch stay 0
+    // blocks above the diagonal that the 32-deep steps over P touch stay 0
     for (int idx = tid; idx < 2 * 256; idx += NT) {
         const int blk = idx >> 8, e = idx & 255;
         const int off = (32 * blk + (e >> 4)) * LDT + 32 * blk + 16 + (e & 15);
-        Ps[off] = (T)0.f, Tb[off] = (T)0.f;
+        Ps[off] = (T)0.f;
         if constexpr (SPLIT)
-            Psl[off] = (T)0.f, Tbl[off] = (T)0.f;
+            Psl[off] = (T)0.f;
     }
 
     // state, D layout: hs[cb][mb][i] = h[16 mb + 4 g + i][colw + 16 cb + c]
@@ -778,21 +815,24 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             gcol[J] = __shfl(gam, 16 * J + c16);
 
         // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
-        // 20 lower blocks (10 of K K^T, 10 of Q K^T); wave w takes tasks w, w+4, ..., w+16
+        // The 10 lower 16x16 blocks (I, J); wave w takes blocks w, w+4, w+8. Both products of
+        // a block share the K_J operand. Diagonal blocks of M go to Ms (fp32) for the
+        // inversion; off-diagonal ones to the MT tiles as hi + lo operands; P to Ps/Psl.
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int task = wave + NW * j;
-            const bool isq = task >= 10;
-            const int p = isq ? task - 10 : task;
+        for (int jb = 0; jb < 3; ++jb) {
+            const int p = wave + NW * jb;
+            if (p >= 10)
+                break;
             const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
             const int J = p - I * (I + 1) / 2;
-            const T *As = isq ? Qs : Ks;
-            f32x4 acc = zero4();
+            f32x4 am = zero4(), ap = zero4();
             if constexpr (!KDA) {
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    mma(acc, ld_frag(As, LDQ, 16 * I, 32 * kb, lane),
-                        ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane));
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const frag fb = ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane);
+                    mma(am, ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane), fb);
+                    mma(ap, ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane), fb);
+                }
             } else if (I != J) {
                 // off-diagonal block: reference row b = 16I (first row of block I), so
                 // both factors e^(G_r - G_b) (r >= b) and e^(G_b - G_s) (s < b) are <= 1
@@ -801,7 +841,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                 const float *gs_ = Gk + (16 * J + c16) * LDG;
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    frag fa = ld_frag(As, LDQ, 16 * I, 32 * kb, lane);
+                    frag fk = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
+                    frag fq = ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane);
                     frag fb = ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane);
                     const int c0 = 32 * kb + 4 * g4;
                     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gb + c0);
@@ -812,12 +853,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(gs_ + c0 + 16);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        fa[i] = (T)((float)fa[i] * __expf(r0[i] - b0[i]));
-                        fa[4 + i] = (T)((float)fa[4 + i] * __expf(r1[i] - b1[i]));
+                        const float ea = __expf(r0[i] - b0[i]), ea1 = __expf(r1[i] - b1[i]);
+                        fk[i] = (T)((float)fk[i] * ea);
+                        fk[4 + i] = (T)((float)fk[4 + i] * ea1);
+                        fq[i] = (T)((float)fq[i] * ea);
+                        fq[4 + i] = (T)((float)fq[4 + i] * ea1);
                         fb[i] = (T)((float)fb[i] * __expf(b0[i] - s0[i]));
                         fb[4 + i] = (T)((float)fb[4 + i] * __expf(b1[i] - s1[i]));
                     }
-                    mma(acc, fa, fb);
+                    mma(am, fk, fb);
+                    mma(ap, fq, fb);
                 }
             } else {
                 // diagonal block: mid-block reference m = 16I + 8, so each factor spans at
@@ -829,35 +874,44 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                 if constexpr (SPLIT) {
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb) {
-                        const frag xa = ld_frag(As, LDQ, 16 * I, 32 * kb, lane);
-                        const frag xb = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
+                        const frag xk = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
+                        const frag xq = ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane);
                         const int c0 = 32 * kb + 4 * g4;
-                        bf16x8 ah, al, bh, bl;
+                        bf16x8 kh_, kl_, qh_, ql_, bh, bl;
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
                             const int ch = c0 + (i < 4 ? i : 12 + i);
                             const float d = grs[ch] - gm[ch];
-                            const float av = (float)xa[i] * __expf(fminf(d, 80.f));
-                            const float bv = (float)xb[i] * __expf(fminf(-d, 80.f));
-                            ah[i] = (bf16)av;
-                            al[i] = (bf16)(av - (float)ah[i]);
+                            const float ea = __expf(fminf(d, 80.f));
+                            const float kv = (float)xk[i] * ea, qv = (float)xq[i] * ea;
+                            const float bv = (float)xk[i] * __expf(fminf(-d, 80.f));
+                            kh_[i] = (bf16)kv;
+                            kl_[i] = (bf16)(kv - (float)kh_[i]);
+                            qh_[i] = (bf16)qv;
+                            ql_[i] = (bf16)(qv - (float)qh_[i]);
                             bh[i] = (bf16)bv;
                             bl[i] = (bf16)(bv - (float)bh[i]);
                         }
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bh, am, 0, 0, 0);
+                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bl, am, 0, 0, 0);
+                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl_, bh, am, 0, 0, 0);
+                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bh, ap, 0, 0, 0);
+                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bl, ap, 0, 0, 0);
+                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql_, bh, ap, 0, 0, 0);
                     }
                 } else {
-                    const T *xr = As + (16 * I + c16) * LDQ;
-                    const T *ks = Ks + (16 * I + c16) * LDQ;
+                    const T *kr = Ks + (16 * I + c16) * LDQ;
+                    const T *qr = Qs + (16 * I + c16) * LDQ;
 #pragma unroll 8
                     for (int j4 = 0; j4 < DK / 4; ++j4) {
                         const int ch = 4 * j4 + g4;
                         const float d = grs[ch] - gm[ch];
-                        const float av = (float)xr[ch] * __expf(fminf(d, 80.f));
-                        const float bv = (float)ks[ch] * __expf(fminf(-d, 80.f));
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                        const float ea = __expf(fminf(d, 80.f));
+                        const float bv = (float)kr[ch] * __expf(fminf(-d, 80.f));
+                        am = __builtin_amdgcn_mfma_f32_16x16x4f32((float)kr[ch] * ea, bv, am, 0,
+                                                                  0, 0);
+                        ap = __builtin_amdgcn_mfma_f32_16x16x4f32((float)qr[ch] * ea, bv, ap, 0,
+                                                                  0, 0);
                     }
                 }
             }
@@ -873,38 +927,35 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 #pragma unroll
                 for (int ii = 1; ii < 4; ++ii)
                     grr = I == ii ? gr[ii][i] : grr;
-                // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside acc);
-                // the masked upper part is discarded by the selects below
+                // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside the
+                // products); the masked upper part is discarded by the selects below
                 const float dec = KDA ? 1.f : __expf(grr - gs);
-                if (isq) {
-                    const float pv_ = s <= r ? dec * acc[i] : 0.f;
-                    const T hi = (T)pv_;
-                    Ps[r * LDT + s] = hi;
-                    if constexpr (SPLIT)
-                        Psl[r * LDT + s] = (T)(pv_ - (float)hi);
+                const float pv_ = s <= r ? dec * ap[i] : 0.f;
+                const T phi = (T)pv_;
+                Ps[r * LDT + s] = phi;
+                if constexpr (SPLIT)
+                    Psl[r * LDT + s] = (T)(pv_ - (float)phi);
+                const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
+                if (I == J) {
+                    Ms[r * LDF + s] = mv;
                 } else {
-                    Ms[r * LDF + s] = s < r ? bet[r] * dec * acc[i] : 0.f;
+                    const T mhi = (T)mv;
+                    MTh[r * LDT + s] = mhi;
+                    if constexpr (SPLIT)
+                        MTl[r * LDT + s] = (T)(mv - (float)mhi);
                 }
             }
         }
         __syncthreads();
 
-        // ---- D: T = (I + M)^-1, each block also stored as Tb = T diag(beta) (hi + lo) ---
-        auto put_t = [&](int r, int s, float t) {
-            Tf[r * LDF + s] = t;
-            const float tb = t * bet[s];
-            const T hi = (T)tb;
-            Tb[r * LDT + s] = hi;
-            if constexpr (SPLIT)
-                Tbl[r * LDT + s] = (T)(tb - (float)hi);
-        };
+        // ---- D: T_II = (I + M_II)^-1 for the 4 diagonal blocks (one per wave) -----------
         {
-            // Diagonal block I = wave: with N = -M_II (strictly lower, so N^16 = 0),
-            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8). Powers are formed on MFMA;
-            // an A operand that is not in LDS yet is written to this wave's own block of Tf
-            // (free until the block's inverse is stored there) and read back.
+            // With N = -M_II (strictly lower, so N^16 = 0),
+            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8). Powers are formed on MFMA; an
+            // A operand that is not in LDS yet is written to this wave's own block of Ms
+            // (already read) and read back.
             const int I = wave, base = 16 * I;
-            float *scr = Tf + base * LDF + base;
+            float *scr = Ms + base * LDF + base;
             const f32x4 mI = blk_a(Ms, LDF, I, I, lane);   // A layout of M_II
             const f32x4 mIb = blk_b(Ms, LDF, I, I, lane);  // D layout of M_II
             f32x4 na, nb;                                  // N in A and D layouts
@@ -915,7 +966,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     scr[(4 * g4 + i) * LDF + c16] = d[i];
-                return blk_a(Tf, LDF, I, I, lane);
+                return blk_a(Ms, LDF, I, I, lane);
             };
             f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
             mm16<SPLIT>(n2, na, nb);  // N^2
@@ -934,25 +985,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             f32x4 z = y;
             mm16<SPLIT>(z, n8a, y);  // (I + N^8) Y
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                put_t(base + 4 * g4 + i, base + c16, z[i]);
-        }
-        __syncthreads();
-        if (wave < 3) {  // column block J = wave: T_IJ = -T_II sum_{K=J}^{I-1} M_IK T_KJ
-            const int J = wave;
-            for (int I = J + 1; I < 4; ++I) {
-                f32x4 y = zero4();
-                for (int K = J; K < I; ++K)
-                    mm16<SPLIT>(y, blk_a(Ms, LDF, I, K, lane), blk_b(Tf, LDF, K, J, lane));
-                f32x4 t = zero4();
-                mm16<SPLIT>(t, blk_a(Tf, LDF, I, I, lane), y);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    put_t(16 * I + 4 * g4 + i, 16 * J + c16, -t[i]);
+            for (int i = 0; i < 4; ++i) {
+                const int off = (base + 4 * g4 + i) * LDT + base + c16;
+                const T hi = (T)z[i];
+                MTh[off] = hi;
+                if constexpr (SPLIT)
+                    MTl[off] = (T)(z[i] - (float)hi);
             }
         }
         __syncthreads();
-        T *Kd = (T *)(smem + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms + Tf
+        T *Kd = (T *)(smem + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms
         if constexpr (KDA) {
             // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1
             for (int idx = tid; idx < CH * (DK / VEC); idx += NT) {
@@ -1009,26 +1051,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                     o[I][i] = arr * qh[i];
                 }
             }
-            // U = Tb X with Tb and X as hi + lo pairs
-            frag xh[2], xl[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                pack_split<T>(x[2 * kb], x[2 * kb + 1], xh[kb], xl[kb]);
+            // U = T diag(beta) X by block forward substitution on (I + M) U = diag(beta) X:
+            // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), operands as hi + lo pairs
             f32x4 u[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                u[I] = zero4();
+                f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    if (kb > (I >> 1))
-                        continue;
-                    const frag th = ld_frag(Tb, LDT, 16 * I, 32 * kb, lane);
-                    mma(u[I], th, xh[kb]);
-                    if constexpr (SPLIT) {
-                        mma(u[I], th, xl[kb]);
-                        mma(u[I], ld_frag(Tbl, LDT, 16 * I, 32 * kb, lane), xh[kb]);
-                    }
-                }
+                for (int J = 0; J < I; ++J)
+                    mm16_pre(acc, MTh, MTl, LDT, I, J, u[J], lane);
+                f32x4 z;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    z[i] = bet[16 * I + 4 * g4 + i] * x[I][i] - acc[i];
+                u[I] = zero4();
+                mm16_pre(u[I], MTh, MTl, LDT, I, I, z, lane);
             }
             // O += P U with P and U as hi + lo pairs
             frag uh[2], ul[2];
