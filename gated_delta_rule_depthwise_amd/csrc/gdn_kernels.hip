@@ -613,10 +613,11 @@ __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
 }
 
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
-__global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
+__global__ void __launch_bounds__(NW * 64)
+    __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
-    static_assert(NW == 4, "4 waves per workgroup (one per SIMD)");
+    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
     constexpr int NV = C::NV, LDQ = C::LDQ, LDV = C::LDV, LDT = C::LDT, LDF = C::LDF;
     constexpr int LDG = C::LDG;
@@ -633,20 +634,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     static_assert(!KDA || NGK * NW * GRW == CH, "gate load map");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T *Qs = (T *)(smem + C::OFF_Q);
-    T *Ks = (T *)(smem + C::OFF_K);
-    T *Vs = (T *)(smem + C::OFF_V);
-    T *Ps = (T *)(smem + C::OFF_P);
-    T *Psl = (T *)(smem + C::OFF_PL);
-    T *MTh = (T *)(smem + C::OFF_MT);
-    T *MTl = (T *)(smem + C::OFF_MTL);
-    float *Ms = (float *)(smem + C::OFF_M);
-    float *Gk = (float *)(smem + C::OFF_GK);  // per-channel gate only
-    float *graw = (float *)(smem + C::OFF_G);
-    float *bet = graw + CH;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g4 = lane >> 4, c16 = lane & 15;
+    const int tid0 = threadIdx.x, lane0 = tid0 & 63;
+    const int wave0 = __builtin_amdgcn_readfirstlane(tid0 >> 6);
 
     const int H = a.H;
     const int BH = a.st.B * H;
@@ -655,21 +645,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     float *hp = (a.h_ptrs ? a.h_ptrs[b] : a.h) + (int64_t)head * DK * DV;
-    const int colw = slice * NV + wave * 16 * NCB;  // this wave's first dv column
+    const int colw = slice * NV + wave0 * 16 * NCB;  // this wave's first dv column
 
     const TIN *qg = (const TIN *)a.q + head * DK;
     const TIN *kg = (const TIN *)a.k + head * DK;
     const TIN *vg = (const TIN *)a.v + head * DV + slice * NV;
-    float *og = a.o + head * DV + colw + c16;  // + 16 cb for column block cb
+    float *ob = a.o + head * DV + colw;  // + 16 cb + lane column for column block cb
     const int64_t ld = a.ld;
 
     // blocks above the diagonal that the 32-deep steps over P touch stay 0
-    for (int idx = tid; idx < 2 * 256; idx += NT) {
+    for (int idx = tid0; idx < 2 * 256; idx += NT) {
         const int blk = idx >> 8, e = idx & 255;
         const int off = (32 * blk + (e >> 4)) * LDT + 32 * blk + 16 + (e & 15);
-        Ps[off] = (T)0.f;
+        ((T *)(smem + C::OFF_P))[off] = (T)0.f;
         if constexpr (SPLIT)
-            Psl[off] = (T)0.f;
+            ((T *)(smem + C::OFF_PL))[off] = (T)0.f;
     }
 
     // state, D layout: hs[cb][mb][i] = h[16 mb + 4 g + i][colw + 16 cb + c]
@@ -680,13 +670,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
         for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hs[cb][mb][i] = hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + 16 * cb + c16];
+                hs[cb][mb][i] = hp[(int64_t)(16 * mb + 4 * (lane0 >> 4) + i) * DV + colw +
+                                   16 * cb + (lane0 & 15)];
 
     // Raw 16-byte vectors of the next chunk, loaded one chunk ahead so that the HBM latency
     // hides behind a whole chunk of work. Rows at or past the stream's end are never read.
     uint4 pq[NQK], pv[NVV], pgk[NGK];
     float pg = 0.f, pb = 0.f;
-    auto prefetch = [&](int64_t c0, int Lc) {
+    auto prefetch = [&](int64_t c0, int Lc, int tid, int lane, int wave) {
 #pragma unroll
         for (int it = 0; it < NQK; ++it) {
             const int rr = wave * RPW + lane / LPR + it * NW * RPW;
@@ -715,10 +706,29 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
         }
     };
     if (start < end)
-        prefetch(start, (int)min((int64_t)CH, end - start));
+        prefetch(start, (int)min((int64_t)CH, end - start), tid0, lane0, wave0);
 
     for (int64_t cs = start; cs < end; cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
+        // Thread coordinates and tile addresses are re-derived from opaque copies in every
+        // chunk: otherwise the compiler hoists each per-lane LDS address out of the loop
+        // and holds a register for every one of them across all stages.
+        int zo = 0, tz = threadIdx.x;
+        asm volatile("" : "+s"(zo));
+        asm volatile("" : "+v"(tz));
+        const int tid = tz, lane = tz & 63, g4 = lane >> 4, c16 = lane & 15;
+        const int wave = __builtin_amdgcn_readfirstlane(tz >> 6);
+        T *Qs = (T *)(smem + zo + C::OFF_Q);
+        T *Ks = (T *)(smem + zo + C::OFF_K);
+        T *Vs = (T *)(smem + zo + C::OFF_V);
+        T *Ps = (T *)(smem + zo + C::OFF_P);
+        T *Psl = (T *)(smem + zo + C::OFF_PL);
+        T *MTh = (T *)(smem + zo + C::OFF_MT);
+        T *MTl = (T *)(smem + zo + C::OFF_MTL);
+        float *Ms = (float *)(smem + zo + C::OFF_M);
+        float *Gk = (float *)(smem + zo + C::OFF_GK);
+        float *graw = (float *)(smem + zo + C::OFF_G);
+        float *bet = graw + CH;
 
         // ---- A: registers -> LDS: q, k (L2, scale), v, raw gates, beta -----------------
 #pragma unroll
@@ -764,7 +774,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             bet[tid] = pb;
         }
         if (cs + CH < end)
-            prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH));
+            prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH), tid, lane, wave);
         __syncthreads();
 
         // ---- B: cumulative log-gate; lane r of every wave holds Gamma_r -----------------
@@ -815,11 +825,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             gcol[J] = __shfl(gam, 16 * J + c16);
 
         // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
-        // The 10 lower 16x16 blocks (I, J); wave w takes blocks w, w+4, w+8. Both products of
+        // The 10 lower 16x16 blocks (I, J); wave w takes blocks w, w+NW, ... Both products of
         // a block share the K_J operand. Diagonal blocks of M go to Ms (fp32) for the
         // inversion; off-diagonal ones to the MT tiles as hi + lo operands; P to Ps/Psl.
 #pragma unroll
-        for (int jb = 0; jb < 3; ++jb) {
+        for (int jb = 0; jb < (10 + NW - 1) / NW; ++jb) {
             const int p = wave + NW * jb;
             if (p >= 10)
                 break;
@@ -949,7 +959,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
         __syncthreads();
 
         // ---- D: T_II = (I + M_II)^-1 for the 4 diagonal blocks (one per wave) -----------
-        {
+        if (wave < 4) {
             // With N = -M_II (strictly lower, so N^16 = 0),
             // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8). Powers are formed on MFMA; an
             // A operand that is not in LDS yet is written to this wave's own block of Ms
@@ -994,7 +1004,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
             }
         }
         __syncthreads();
-        T *Kd = (T *)(smem + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms
+        T *Kd = (T *)(smem + zo + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms
         if constexpr (KDA) {
             // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1
             for (int idx = tid; idx < CH * (DK / VEC); idx += NT) {
@@ -1089,7 +1099,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * I + 4 * g4 + i;
                     if (r < L)
-                        og[(cs + r) * (int64_t)H * DV + 16 * cb] = o[I][i];
+                        ob[(cs + r) * (int64_t)H * DV + 16 * cb + c16] = o[I][i];
                 }
             }
             // h <- a_C h + K^T (diag(a_C / a) U); per-channel gate:
@@ -1129,7 +1139,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_kernel(const ChunkArgs a)
         for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hp[(int64_t)(16 * mb + 4 * g4 + i) * DV + colw + 16 * cb + c16] = hs[cb][mb][i];
+                hp[(int64_t)(16 * mb + 4 * (lane0 >> 4) + i) * DV + colw + 16 * cb + (lane0 & 15)] =
+                    hs[cb][mb][i];
 }
 
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
@@ -1155,14 +1166,18 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 // per wave, per-channel gate). Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
 // of the front end. A workgroup covers NW * NCB * 16 dv columns of one (stream, head).
 #define GDN_CHUNK_INSTANCES(X)                   \
+    X(bf16, f16, 1, 128, 128, 8, 1, false)       \
     X(bf16, f16, 1, 128, 128, 4, 2, false)       \
     X(bf16, f16, 1, 128, 128, 4, 1, false)       \
+    X(f16, f16, 2, 128, 128, 8, 1, false)        \
     X(f16, f16, 2, 128, 128, 4, 2, false)        \
     X(f16, f16, 2, 128, 128, 4, 1, false)        \
     X(bf16, f16, 1, 64, 64, 4, 1, false)         \
     X(f16, f16, 2, 64, 64, 4, 1, false)          \
     X(float, float, 0, 64, 64, 4, 1, false)      \
+    X(bf16, f16, 1, 128, 128, 8, 1, true)        \
     X(bf16, f16, 1, 128, 128, 4, 1, true)        \
+    X(f16, f16, 2, 128, 128, 8, 1, true)         \
     X(f16, f16, 2, 128, 128, 4, 1, true)         \
     X(bf16, f16, 1, 64, 64, 4, 1, true)          \
     X(f16, f16, 2, 64, 64, 4, 1, true)           \
