@@ -112,15 +112,15 @@ Shape pick_shape(const gdn_params *p, int kda, int64_t BH)
     if (fcols > 0 && p->dv % fcols == 0 &&
         gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves))
         return Shape{fcols, fwaves};
-    Shape best{0, 0};
+    // The widest instance: one workgroup per (stream, head) computes the chunk
+    // preparation once for all its columns, and 8-wave instances hide latency with two
+    // waves per SIMD.
+    (void)BH;
     for (int nv : {128, 64}) {
-        if (p->dv % nv || !gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0))
-            continue;
-        best = Shape{nv, 0};
-        if (BH * (p->dv / nv) >= 256)
-            return best;
+        if (p->dv % nv == 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0))
+            return Shape{nv, 0};
     }
-    return best;
+    return Shape{0, 0};
 }
 
 int check_params(const gdn_params *p, int kda)

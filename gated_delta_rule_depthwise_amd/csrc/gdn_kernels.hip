@@ -70,6 +70,50 @@ __device__ __forceinline__ void mma(f32x4 &d, const f32x8 &a, const f32x8 &b)
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Cross-lane moves on DPP: a VALU operand modifier, so a reduction or scan step costs a few
+// cycles instead of an LDS round trip per step. A lane whose source falls outside its row
+// reads 0.
+namespace dpp {
+constexpr int QUAD_XOR1 = 0xB1, QUAD_XOR2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+constexpr int ROW_SHR = 0x110, ROW_MIRROR = 0x140, ROW_HALF_MIRROR = 0x141;
+constexpr int ROW_BCAST15 = 0x142, ROW_BCAST31 = 0x143;
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float mov(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf,
+                                           true));
+}
+}  // namespace dpp
+
+// Sum over aligned groups of N lanes, N in {4, 8, 16}; every lane of a group gets the same
+// bits (each step adds the same two partial sums in both lanes).
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(N == 4 || N == 8 || N == 16, "DPP groups are quads, half rows or rows");
+    x += dpp::mov<dpp::QUAD_XOR1>(x);
+    x += dpp::mov<dpp::QUAD_XOR2>(x);
+    if constexpr (N >= 8)
+        x += dpp::mov<dpp::ROW_HALF_MIRROR>(x);
+    if constexpr (N >= 16)
+        x += dpp::mov<dpp::ROW_MIRROR>(x);
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: a scan within each row of 16 lanes,
+// then the totals of rows 0 and 2 into rows 1 and 3, then that of rows 0-1 into rows 2-3.
+__device__ __forceinline__ float wave_scan(float x)
+{
+    x += dpp::mov<dpp::ROW_SHR + 1>(x);
+    x += dpp::mov<dpp::ROW_SHR + 2>(x);
+    x += dpp::mov<dpp::ROW_SHR + 4>(x);
+    x += dpp::mov<dpp::ROW_SHR + 8>(x);
+    x += dpp::mov<dpp::ROW_BCAST15, 0xa>(x);
+    x += dpp::mov<dpp::ROW_BCAST31, 0xc>(x);
+    return x;
+}
+
 // 16 bytes of global memory -> floats (8 for 2-byte types, 4 for float)
 __device__ __forceinline__ void load_vec(const bf16 *p, float (&x)[8])
 {
@@ -107,6 +151,15 @@ __device__ __forceinline__ void store_vec(float *p, const float (&x)[4])
 {
     *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
+// 4 floats -> 4 elements (8 or 16 bytes)
+__device__ __forceinline__ void store_vec4(f16 *p, const float (&x)[4])
+{
+    *reinterpret_cast<f16x4 *>(p) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+}
+__device__ __forceinline__ void store_vec4(float *p, const float (&x)[4])
+{
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
 
 // Operand fragment from a row-major LDS tile X[row][k] (row stride ld elements):
 // row = row0 + (lane & 15), k = k0 + 4g + {0..3} and k0 + 16 + 4g + {0..3}.
@@ -123,6 +176,39 @@ __device__ __forceinline__ f32x8 ld_frag(const float *X, int ld, int row0, int k
     const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
     const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 16);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Q/K operand tiles [64][DK]. Rows are padded to 8 dwords past a multiple of 32 banks,
+// which suits the transposed reads (4 rows x 4 chunks of 4 elements per 16 lanes). For the
+// row-wise fragment reads (16 consecutive rows at one chunk) the chunks of row r are
+// permuted as ch ^ ((r / 4) mod 4): rows r and r + 4 then land 2 dwords apart instead of on
+// the same banks. The permutation touches the low 2 bits of the chunk index only, so the
+// offsets between the chunks a lane reads stay compile-time constants.
+template <typename T, int DK>
+struct QK {
+    static constexpr bool SWZ = sizeof(T) == 2;
+    static constexpr int LD = DK + 32 / (int)sizeof(T);
+    // element offset of the chunk holding elements (r, 4 ch .. 4 ch + 3)
+    __device__ static __forceinline__ int at(int r, int ch)
+    {
+        return r * LD + (SWZ ? (ch ^ ((r >> 2) & 3)) : ch) * 4;
+    }
+};
+
+// ld_frag for a Q/K tile
+template <int DK>
+__device__ __forceinline__ f16x8 ld_frag_qk(const f16 *X, int row0, int k0, int lane)
+{
+    using L = QK<f16, DK>;
+    const int r = row0 + (lane & 15), ch = k0 / 4 + (lane >> 4);
+    const f16x4 lo = *reinterpret_cast<const f16x4 *>(X + L::at(r, ch));
+    const f16x4 hi = *reinterpret_cast<const f16x4 *>(X + L::at(r, ch + 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int DK>
+__device__ __forceinline__ f32x8 ld_frag_qk(const float *X, int row0, int k0, int lane)
+{
+    return ld_frag(X, QK<float, DK>::LD, row0, k0, lane);
 }
 
 // B operand of a 32-deep block from the accumulators of its two 16-row halves.
@@ -313,8 +399,13 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
 #pragma unroll
                 for (int i = 0; i < FRONT_CPT; ++i)
                     ss += z[i] * z[i];
-                for (int m = 1; m < lanes_per_head; m <<= 1)
-                    ss += __shfl_xor(ss, m);
+                if (lanes_per_head == 16)
+                    ss = group_sum<16>(ss);
+                else if (lanes_per_head == 8)
+                    ss = group_sum<8>(ss);
+                else
+                    for (int m = 1; m < lanes_per_head; m <<= 1)
+                        ss += __shfl_xor(ss, m);
                 if (sec < 2) {
                     const float inv = rsqrtf(ss + a.eps) * (sec == 0 ? a.scale : 1.f);
 #pragma unroll
@@ -438,14 +529,15 @@ struct ChunkCfg {
     // right-hand operands of T X and P U too, which keeps those products at about fp32
     // accuracy; fp32 operands need no split
     static constexpr bool SPLIT = sizeof(T) == 2;
-    // Row strides of the operand tiles are 8 dwords past a multiple of 32, so fragment
-    // reads (16 rows x 4 column pieces), transposed column reads and 16-byte row writes
-    // spread evenly over the LDS banks. The fp32 solve tiles use 4 dwords past a multiple
-    // of 32, which keeps the D-layout stores (rows 4g+i) and 16-byte fragment reads even.
+    // Row strides. 16-bit tiles: P and M operand tiles 2 dwords past a multiple of 32, so
+    // a fragment read (16 rows at one 8-byte piece) and a D-layout store (4 rows 4 apart,
+    // 8 dwords each) touch distinct banks; V 4 dwords past, so the D-layout element reads
+    // of rows 4 apart fall in separate halves of the banks. Q and K are permuted instead
+    // of padded (see QK). fp32 tiles: 8 dwords past.
     static constexpr int PAD = 32 / (int)sizeof(T);
-    static constexpr int LDQ = DK + PAD;  // Qs, Ks: [64][LDQ]
-    static constexpr int LDV = NV + PAD;  // Vs: [64][LDV]
-    static constexpr int LDT = CH + PAD;  // P and T operand tiles: [64][LDT]
+    static constexpr int LDQ = QK<T, DK>::LD;                  // Qs, Ks: [64][LDQ]
+    static constexpr int LDV = NV + (SPLIT ? 8 : PAD);         // Vs: [64][LDV]
+    static constexpr int LDT = CH + (SPLIT ? 4 : PAD);         // P and M operand tiles
     static constexpr int LDF = CH + 4;    // Ms, Tf: [64][LDF] float
     static constexpr int LDG = DK + 4;    // per-channel gate: Gk [64][LDG] float
     static constexpr int SZ_Q = CH * LDQ * (int)sizeof(T);
@@ -463,7 +555,11 @@ struct ChunkCfg {
     static constexpr int OFF_M = OFF_MTL + (SPLIT ? SZ_P : 0);    // diagonal blocks of M, fp32
     static constexpr int OFF_GK = OFF_M + SZ_MS;  // per-channel cumulative log-gates
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);  // graw[64], bet[64]
-    static constexpr int BYTES = OFF_G + 2 * CH * 4;
+    static constexpr int LDO = NV + 16;  // o rows (fp32): 4 rows of a D-layout write hit 32 banks
+    static constexpr int OFF_O = OFF_G + 2 * CH * 4;
+    // o is staged in LDS when it fits (not with the per-channel gate tile at 128 columns)
+    static constexpr bool STAGE_O = OFF_O + CH * LDO * 4 <= 160 * 1024;
+    static constexpr int BYTES = OFF_O + (STAGE_O ? CH * LDO * 4 : 0);
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -493,6 +589,26 @@ __device__ __forceinline__ f32x8 ld_frag_t(const float *X, int ld, int k0, int n
         f[4 + i] = p[(16 + i) * ld];
     }
     return f;
+}
+
+// ld_frag_t for a Q/K tile
+template <int DK>
+__device__ __forceinline__ f16x8 ld_frag_t_qk(const f16 *X, int k0, int n0, int lane)
+{
+    using L = QK<f16, DK>;
+    const int g = lane >> 4, s = lane & 15;
+    const int r = k0 + 4 * g + (s >> 2), ch = n0 / 4 + (s & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + L::at(r, ch)));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + L::at(r + 16, ch)));
+    const f16x4 flo = __builtin_bit_cast(f16x4, lo), fhi = __builtin_bit_cast(f16x4, hi);
+    return __builtin_shufflevector(flo, fhi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int DK>
+__device__ __forceinline__ f32x8 ld_frag_t_qk(const float *X, int k0, int n0, int lane)
+{
+    return ld_frag_t(X, QK<float, DK>::LD, k0, n0, lane);
 }
 
 // raw 16-byte vector -> floats
@@ -620,7 +736,7 @@ __global__ void __launch_bounds__(NW * 64)
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
     constexpr int NV = C::NV, LDQ = C::LDQ, LDV = C::LDV, LDT = C::LDT, LDF = C::LDF;
-    constexpr int LDG = C::LDG;
+    constexpr int LDG = C::LDG, LDO = C::LDO;
     constexpr bool SPLIT = C::SPLIT;
     constexpr int VEC = Tr<T>::VEC;
     constexpr int NT = NW * 64;
@@ -650,7 +766,7 @@ __global__ void __launch_bounds__(NW * 64)
     const TIN *qg = (const TIN *)a.q + head * DK;
     const TIN *kg = (const TIN *)a.k + head * DK;
     const TIN *vg = (const TIN *)a.v + head * DV + slice * NV;
-    float *ob = a.o + head * DV + colw;  // + 16 cb + lane column for column block cb
+    float *ob = a.o + head * DV + slice * NV;  // this workgroup's o columns
     const int64_t ld = a.ld;
 
     // blocks above the diagonal that the 32-deep steps over P touch stay 0
@@ -708,6 +824,22 @@ __global__ void __launch_bounds__(NW * 64)
     if (start < end)
         prefetch(start, (int)min((int64_t)CH, end - start), tid0, lane0, wave0);
 
+    // o of a chunk is staged in LDS and written out during the next chunk, right after the
+    // wait for that chunk's prefetched rows: vector loads and stores share one completion
+    // counter, so stores issued at the end of a chunk would hold up that wait. Full rows
+    // go out as 16-byte stores.
+    auto flush_o = [&](const float *Os, int64_t c0, int Lc, int tid) {
+        constexpr int V4 = NV / 4, RPP = NT / V4;
+        static_assert(NT % V4 == 0 && CH % RPP == 0, "o row map");
+#pragma unroll
+        for (int r0 = 0; r0 < CH; r0 += RPP) {
+            const int r = r0 + tid / V4, j = tid % V4;
+            if (r < Lc)
+                *reinterpret_cast<float4 *>(ob + (c0 + r) * (int64_t)H * DV + 4 * j) =
+                    *reinterpret_cast<const float4 *>(Os + r * LDO + 4 * j);
+        }
+    };
+
     for (int64_t cs = start; cs < end; cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
         // Thread coordinates and tile addresses are re-derived from opaque copies in every
@@ -729,6 +861,7 @@ __global__ void __launch_bounds__(NW * 64)
         float *Gk = (float *)(smem + zo + C::OFF_GK);
         float *graw = (float *)(smem + zo + C::OFF_G);
         float *bet = graw + CH;
+        float *Os = (float *)(smem + zo + C::OFF_O);
 
         // ---- A: registers -> LDS: q, k (L2, scale), v, raw gates, beta -----------------
 #pragma unroll
@@ -745,15 +878,24 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     ss += x[i] * x[i];
+                if constexpr (LPR == 4 || LPR == 8 || LPR == 16) {
+                    ss = group_sum<LPR>(ss);
+                } else {
 #pragma unroll
-                for (int m = 1; m < LPR; m <<= 1)
-                    ss += __shfl_xor(ss, m);
+                    for (int m = 1; m < LPR; m <<= 1)
+                        ss += __shfl_xor(ss, m);
+                }
                 mul = r < L ? mul * rsqrtf(ss + a.eps) : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
                 x[i] *= mul;
-            store_vec((isk ? Ks : Qs) + r * LDQ + c0, x);
+            T *dst = isk ? Ks : Qs;
+#pragma unroll
+            for (int h = 0; h < VEC / 4; ++h) {  // 4-element chunks of the Q/K layout
+                const float y[4] = {x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
+                store_vec4(dst + QK<T, DK>::at(r, c0 / 4 + h), y);
+            }
         }
 #pragma unroll
         for (int it = 0; it < NVV; ++it) {
@@ -773,6 +915,8 @@ __global__ void __launch_bounds__(NW * 64)
             graw[tid] = pg;
             bet[tid] = pb;
         }
+        if (C::STAGE_O && cs > start)
+            flush_o(Os, cs - CH, CH, tid);  // only the last chunk of a stream is partial
         if (cs + CH < end)
             prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH), tid, lane, wave);
         __syncthreads();
@@ -805,14 +949,9 @@ __global__ void __launch_bounds__(NW * 64)
             }
             __syncthreads();
         }
-        float gam = graw[lane];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(gam, off);
-            if (lane >= off)
-                gam += y;
-        }
-        const float gC = __shfl(gam, CH - 1);
+        const float gam = wave_scan(graw[lane]);
+        const float gC = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), CH - 1));
         float gr[4][4];  // Gamma at the D-layout rows 16I + 4g + i of this lane
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -839,9 +978,9 @@ __global__ void __launch_bounds__(NW * 64)
             if constexpr (!KDA) {
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    const frag fb = ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane);
-                    mma(am, ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane), fb);
-                    mma(ap, ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane), fb);
+                    const frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
+                    mma(am, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), fb);
+                    mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
                 }
             } else if (I != J) {
                 // off-diagonal block: reference row b = 16I (first row of block I), so
@@ -851,9 +990,9 @@ __global__ void __launch_bounds__(NW * 64)
                 const float *gs_ = Gk + (16 * J + c16) * LDG;
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    frag fk = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
-                    frag fq = ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane);
-                    frag fb = ld_frag(Ks, LDQ, 16 * J, 32 * kb, lane);
+                    frag fk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
+                    frag fq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
+                    frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
                     const int c0 = 32 * kb + 4 * g4;
                     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gb + c0);
                     const f32x4 b1 = *reinterpret_cast<const f32x4 *>(gb + c0 + 16);
@@ -884,8 +1023,8 @@ __global__ void __launch_bounds__(NW * 64)
                 if constexpr (SPLIT) {
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb) {
-                        const frag xk = ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane);
-                        const frag xq = ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane);
+                        const frag xk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
+                        const frag xq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
                         const int c0 = 32 * kb + 4 * g4;
                         bf16x8 kh_, kl_, qh_, ql_, bh, bl;
 #pragma unroll
@@ -1007,13 +1146,14 @@ __global__ void __launch_bounds__(NW * 64)
         T *Kd = (T *)(smem + zo + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms
         if constexpr (KDA) {
             // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1
-            for (int idx = tid; idx < CH * (DK / VEC); idx += NT) {
-                const int r = idx / (DK / VEC), c0 = (idx % (DK / VEC)) * VEC;
-                T *kp = Ks + r * LDQ + c0;
-                T *qp = Qs + r * LDQ + c0;
-                T *dp = Kd + r * LDQ + c0;
+            for (int idx = tid; idx < CH * (DK / 4); idx += NT) {
+                const int r = idx / (DK / 4), c0 = (idx % (DK / 4)) * 4;
+                const int off = QK<T, DK>::at(r, c0 / 4);
+                T *kp = Ks + off;
+                T *qp = Qs + off;
+                T *dp = Kd + off;
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) {
+                for (int i = 0; i < 4; ++i) {
                     const float gg = Gk[r * LDG + c0 + i];
                     const float gcc = Gk[(CH - 1) * LDG + c0 + i];
                     const float kv = (float)kp[i], qv = (float)qp[i];
@@ -1050,8 +1190,8 @@ __global__ void __launch_bounds__(NW * 64)
                 f32x4 kh = zero4(), qh = zero4();
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    mma(kh, ld_frag(Ks, LDQ, 16 * I, 32 * kb, lane), hf[kb]);
-                    mma(qh, ld_frag(Qs, LDQ, 16 * I, 32 * kb, lane), hf[kb]);
+                    mma(kh, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), hf[kb]);
+                    mma(qh, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), hf[kb]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1097,9 +1237,11 @@ __global__ void __launch_bounds__(NW * 64)
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * g4 + i;
-                    if (r < L)
-                        ob[(cs + r) * (int64_t)H * DV + 16 * cb + c16] = o[I][i];
+                    const int r = 16 * I + 4 * g4 + i, col = 16 * (wave * NCB + cb) + c16;
+                    if constexpr (C::STAGE_O)
+                        Os[r * LDO + col] = o[I][i];
+                    else if (r < L)
+                        ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
                 }
             }
             // h <- a_C h + K^T (diag(a_C / a) U); per-channel gate:
@@ -1119,18 +1261,22 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         hs[cb][mb][i] *= __expf(gcr[i]);
-                    mma(hs[cb][mb], ld_frag_t(Kd, LDQ, 0, 16 * mb, lane), vf0);
-                    mma(hs[cb][mb], ld_frag_t(Kd, LDQ, 32, 16 * mb, lane), vf1);
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kd, 0, 16 * mb, lane), vf0);
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kd, 32, 16 * mb, lane), vf1);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         hs[cb][mb][i] *= aC;
-                    mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 0, 16 * mb, lane), vf0);
-                    mma(hs[cb][mb], ld_frag_t(Ks, LDQ, 32, 16 * mb, lane), vf1);
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Ks, 0, 16 * mb, lane), vf0);
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Ks, 32, 16 * mb, lane), vf1);
                 }
             }
         }
         __syncthreads();
+    }
+    if (C::STAGE_O && start < end) {  // the last chunk's o (the loop ends on a barrier)
+        const int64_t last = start + (end - start - 1) / CH * CH;
+        flush_o((const float *)(smem + C::OFF_O), last, (int)(end - last), tid0);
     }
 
 #pragma unroll
