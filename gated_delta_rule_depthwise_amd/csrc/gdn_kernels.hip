@@ -711,6 +711,28 @@ __device__ __forceinline__ void mm16_pre(f32x4 &d, const float *Xh, const float 
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], d, 0, 0, 0);
 }
 
+// The same with B given as a ready hi + lo pair
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *Xh, const f16 *Xl, int ld, int I,
+                                         int J, const f16x4 &bh, const f16x4 &bl, int lane)
+{
+    const int off = (16 * I + (lane & 15)) * ld + 16 * J + 4 * (lane >> 4);
+    const f16x4 ah = *reinterpret_cast<const f16x4 *>(Xh + off);
+    const f16x4 al = *reinterpret_cast<const f16x4 *>(Xl + off);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, d, 0, 0, 0);
+}
+
+// fp32 D-layout value -> fp16 hi + lo
+__device__ __forceinline__ void split4(const f32x4 &x, f16x4 &hi, f16x4 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (f16)x[i];
+        lo[i] = (f16)(x[i] - (float)hi[i]);
+    }
+}
+
 // hi + lo operand pair of the B operand built from two D-layout accumulators
 template <typename T>
 __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
@@ -725,6 +747,22 @@ __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
             r1[i] = d1[i] - (float)hi[4 + i];
         }
         lo = pack<T>(r0, r1);
+    }
+}
+
+// Block (numbered row by row over the 10 lower 16x16 blocks of a chunk) handled as task j
+// of a wave in the preparation stage, or -1. Diagonal blocks (0, 2, 5, 9) come first on
+// waves 0-3, which also invert them.
+template <int NW>
+__device__ __forceinline__ int block_task(int wave, int j)
+{
+    if constexpr (NW == 8) {
+        constexpr int tab[8][2] = {{0, -1}, {2, -1}, {5, -1}, {9, -1},
+                                   {1, 6},  {3, 7},  {4, -1}, {8, -1}};
+        return tab[wave][j];
+    } else {
+        constexpr int tab[4][3] = {{0, 1, 3}, {2, 4, 6}, {5, 7, -1}, {9, 8, -1}};
+        return tab[wave][j];
     }
 }
 
@@ -911,8 +949,8 @@ __global__ void __launch_bounds__(NW * 64)
                 *reinterpret_cast<uint4 *>(Gk + r * LDG + (lane % GPR) * 4) = pgk[it];
             }
         }
-        if (tid < CH) {
-            graw[tid] = pg;
+        if (tid < CH) {  // wave 0: Gamma = inclusive prefix sum of the log-gates
+            graw[tid] = wave_scan(pg);
             bet[tid] = pb;
         }
         if (C::STAGE_O && cs > start)
@@ -949,28 +987,31 @@ __global__ void __launch_bounds__(NW * 64)
             }
             __syncthreads();
         }
-        const float gam = wave_scan(graw[lane]);
-        const float gC = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), CH - 1));
+        const float gC = graw[CH - 1];  // graw holds Gamma (written in stage A)
         float gr[4][4];  // Gamma at the D-layout rows 16I + 4g + i of this lane
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(graw + 16 * I + 4 * g4);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                gr[I][i] = __shfl(gam, 16 * I + 4 * g4 + i);
+                gr[I][i] = v[i];
+        }
         float gcol[4];   // Gamma at the D-layout columns 16J + c of this lane
 #pragma unroll
         for (int J = 0; J < 4; ++J)
-            gcol[J] = __shfl(gam, 16 * J + c16);
+            gcol[J] = graw[16 * J + c16];
 
         // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
-        // The 10 lower 16x16 blocks (I, J); wave w takes blocks w, w+NW, ... Both products of
-        // a block share the K_J operand. Diagonal blocks of M go to Ms (fp32) for the
-        // inversion; off-diagonal ones to the MT tiles as hi + lo operands; P to Ps/Psl.
+        // The 10 lower 16x16 blocks (I, J), numbered row by row. Waves 0-3 each take one
+        // diagonal block and invert it right away, T_II = (I + M_II)^-1; the 6 blocks below
+        // the diagonal are spread over the other waves (8 waves) or the same ones (4 waves).
+        // Both products of a block share the K_J operand. T_II and the off-diagonal M_IJ go
+        // to the MT tiles as hi + lo operands, P to Ps/Psl.
+        constexpr int NJ = NW == 8 ? 2 : 3;
 #pragma unroll
-        for (int jb = 0; jb < (10 + NW - 1) / NW; ++jb) {
-            const int p = wave + NW * jb;
-            if (p >= 10)
+        for (int jb = 0; jb < NJ; ++jb) {
+            const int p = block_task<NW>(wave, jb);
+            if (p < 0)
                 break;
             const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
             const int J = p - I * (I + 1) / 2;
@@ -1085,61 +1126,55 @@ __global__ void __launch_bounds__(NW * 64)
                 if constexpr (SPLIT)
                     Psl[r * LDT + s] = (T)(pv_ - (float)phi);
                 const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
-                if (I == J) {
-                    Ms[r * LDF + s] = mv;
-                } else {
+                am[i] = mv;
+                if (I != J) {
                     const T mhi = (T)mv;
                     MTh[r * LDT + s] = mhi;
                     if constexpr (SPLIT)
                         MTl[r * LDT + s] = (T)(mv - (float)mhi);
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- D: T_II = (I + M_II)^-1 for the 4 diagonal blocks (one per wave) -----------
-        if (wave < 4) {
-            // With N = -M_II (strictly lower, so N^16 = 0),
-            // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8). Powers are formed on MFMA; an
-            // A operand that is not in LDS yet is written to this wave's own block of Ms
-            // (already read) and read back.
-            const int I = wave, base = 16 * I;
-            float *scr = Ms + base * LDF + base;
-            const f32x4 mI = blk_a(Ms, LDF, I, I, lane);   // A layout of M_II
-            const f32x4 mIb = blk_b(Ms, LDF, I, I, lane);  // D layout of M_II
-            f32x4 na, nb;                                  // N in A and D layouts
+            if (I == J) {
+                // T_II = (I - N)^-1 with N = -M_II strictly lower (N^16 = 0):
+                // (I + N)(I + N^2)(I + N^4)(I + N^8), the powers on MFMA. A-layout operands
+                // go through this block's own corner of Ms (no other wave touches it).
+                const int base = 16 * I;
+                float *scr = Ms + base * LDF + base;
+                auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                na[i] = -mI[i], nb[i] = -mIb[i];
-            auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
+                    for (int i = 0; i < 4; ++i)
+                        scr[(4 * g4 + i) * LDF + c16] = d[i];
+                    return blk_a(Ms, LDF, I, I, lane);
+                };
+                f32x4 nb;  // N, D layout
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    scr[(4 * g4 + i) * LDF + c16] = d[i];
-                return blk_a(Ms, LDF, I, I, lane);
-            };
-            f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
-            mm16<SPLIT>(n2, na, nb);  // N^2
-            mm16<SPLIT>(n3, na, n2);  // N^3
-            const f32x4 n2a = to_a(n2);
-            mm16<SPLIT>(n4, n2a, n2);  // N^4
-            const f32x4 n4a = to_a(n4);
-            mm16<SPLIT>(n8, n4a, n4);  // N^8
-            const f32x4 n8a = to_a(n8);
-            f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
+                    nb[i] = -am[i];
+                const f32x4 na = to_a(nb);
+                f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
+                mm16<SPLIT>(n2, na, nb);  // N^2
+                mm16<SPLIT>(n3, na, n2);  // N^3
+                const f32x4 n2a = to_a(n2);
+                mm16<SPLIT>(n4, n2a, n2);  // N^4
+                const f32x4 n4a = to_a(n4);
+                mm16<SPLIT>(n8, n4a, n4);  // N^8
+                const f32x4 n8a = to_a(n8);
+                f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                x[i] = ((4 * g4 + i) == c16 ? 1.f : 0.f) + nb[i] + n2[i] + n3[i];
-            f32x4 y = x;
-            mm16<SPLIT>(y, n4a, x);  // (I + N^4) X
-            f32x4 z = y;
-            mm16<SPLIT>(z, n8a, y);  // (I + N^8) Y
+                for (int i = 0; i < 4; ++i)
+                    x[i] = ((4 * g4 + i) == c16 ? 1.f : 0.f) + nb[i] + n2[i] + n3[i];
+                f32x4 y = x;
+                mm16<SPLIT>(y, n4a, x);  // (I + N^4) X
+                f32x4 z = y;
+                mm16<SPLIT>(z, n8a, y);  // (I + N^8) Y
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int off = (base + 4 * g4 + i) * LDT + base + c16;
-                const T hi = (T)z[i];
-                MTh[off] = hi;
-                if constexpr (SPLIT)
-                    MTl[off] = (T)(z[i] - (float)hi);
+                for (int i = 0; i < 4; ++i) {
+                    const int off = (base + 4 * g4 + i) * LDT + base + c16;
+                    const T hi = (T)z[i];
+                    MTh[off] = hi;
+                    if constexpr (SPLIT)
+                        MTl[off] = (T)(z[i] - (float)hi);
+                }
             }
         }
         __syncthreads();
@@ -1203,25 +1238,42 @@ __global__ void __launch_bounds__(NW * 64)
             }
             // U = T diag(beta) X by block forward substitution on (I + M) U = diag(beta) X:
             // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), operands as hi + lo pairs
+            // (fp16 operands: each U block is split into hi + lo once, for the later blocks
+            // and for P U)
             f32x4 u[4];
+            f16x4 uhs[4], uls[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int J = 0; J < I; ++J)
-                    mm16_pre(acc, MTh, MTl, LDT, I, J, u[J], lane);
+                for (int J = 0; J < I; ++J) {
+                    if constexpr (SPLIT)
+                        mm16_pre(acc, MTh, MTl, LDT, I, J, uhs[J], uls[J], lane);
+                    else
+                        mm16_pre(acc, MTh, MTl, LDT, I, J, u[J], lane);
+                }
                 f32x4 z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     z[i] = bet[16 * I + 4 * g4 + i] * x[I][i] - acc[i];
                 u[I] = zero4();
                 mm16_pre(u[I], MTh, MTl, LDT, I, I, z, lane);
+                if constexpr (SPLIT)
+                    split4(u[I], uhs[I], uls[I]);
             }
             // O += P U with P and U as hi + lo pairs
             frag uh[2], ul[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                pack_split<T>(u[2 * kb], u[2 * kb + 1], uh[kb], ul[kb]);
+            for (int kb = 0; kb < 2; ++kb) {
+                if constexpr (SPLIT) {
+                    uh[kb] = __builtin_shufflevector(uhs[2 * kb], uhs[2 * kb + 1], 0, 1, 2, 3, 4,
+                                                     5, 6, 7);
+                    ul[kb] = __builtin_shufflevector(uls[2 * kb], uls[2 * kb + 1], 0, 1, 2, 3, 4,
+                                                     5, 6, 7);
+                } else {
+                    pack_split<T>(u[2 * kb], u[2 * kb + 1], uh[kb], ul[kb]);
+                }
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
 #pragma unroll
