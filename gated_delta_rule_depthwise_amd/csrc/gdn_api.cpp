@@ -92,9 +92,8 @@ int in_kind(const gdn_params *p)
     return p->conv_k > 0 ? 2 : 1;
 }
 
-// Workgroup shape: dv columns per workgroup and waves per workgroup. The widest compiled
-// slice that still gives every CU a workgroup (B*H*dv/nv >= 256), else the narrowest one;
-// the first compiled wave count for it. GDN_COLS / GDN_WAVES force a compiled shape.
+// Workgroup shape: dv columns per workgroup and waves per workgroup (the widest compiled
+// instance). GDN_COLS / GDN_WAVES force a compiled shape.
 struct Shape {
     int nv, waves;
 };
@@ -153,6 +152,85 @@ size_t front_bytes(const gdn_params *p, int64_t max_tokens)
     return align_up((size_t)max_tokens * (size_t)conv_dim(p) * elem_bytes(p->dtype));
 }
 
+// ---- segmented scan of long streams -----------------------------------------------------
+// With few (stream, head) pairs most CUs would idle while each workgroup walks its stream
+// chunk by chunk. Streams of equal length are then cut into S segments: one launch runs
+// segment 0 and, for every inner segment, its end state from h = 0 and its dk x dk
+// transition (the same recurrence from h = I with v = 0); a small kernel chains
+// h_{s+1} = A_s h_s + b_s; a second launch runs segments 1..S-1 from their start states.
+constexpr int kMaxSeg = 12;
+
+int cu_count()
+{
+    static std::atomic<int> cached{0};
+    int n = cached.load();
+    if (n > 0)
+        return n;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    cached.store(n);
+    return n;
+}
+
+struct SegPlan {
+    int S;            // 0: no segmentation
+    int64_t seg_len;  // tokens
+};
+
+// Cost in chunk steps of a launch of `wgs` one-per-CU workgroups that each walk `chunks`.
+double waves_cost(int64_t wgs, int64_t chunks, int ncu)
+{
+    return (double)((wgs + ncu - 1) / ncu) * (double)chunks;
+}
+
+SegPlan seg_plan(const gdn_params *p, int32_t B, int64_t tps, int nslices, int ncu)
+{
+    SegPlan none{0, 0};
+    if (p->dk != p->dv || p->chunk != 64 || tps < 1)
+        return none;
+    const int64_t nc = (tps + 63) / 64;
+    static int force = -1;  // GDN_SEG: 0 never segments, S >= 3 asks for S segments
+    if (force < 0) {
+        const char *e = getenv("GDN_SEG");
+        force = e ? atoi(e) : 0x7fffffff;
+    }
+    if (force == 0)
+        return none;
+    if (force >= 3 && force <= kMaxSeg && force != 0x7fffffff) {
+        const int64_t L = (nc + force - 1) / force;
+        const int Se = (int)((nc + L - 1) / L);
+        return Se >= 3 ? SegPlan{Se, L * 64} : none;
+    }
+    const int64_t U = (int64_t)B * p->H * nslices;
+    const double base = waves_cost(U, nc, ncu);
+    double best = 0.8 * base;  // segment only for a clear gain
+    SegPlan plan = none;
+    for (int S = 3; S <= kMaxSeg && S <= nc; ++S) {
+        const int64_t L = (nc + S - 1) / S;
+        const int Se = (int)((nc + L - 1) / L);
+        if (Se < 3)
+            continue;
+        // the chain of S-2 steps of (dk x dk) x (dk x 16) products costs about a
+        // quarter of a chunk step each
+        const double cost = waves_cost((2 * (int64_t)Se - 3) * U, L, ncu) +
+                            waves_cost((int64_t)(Se - 1) * U, L, ncu) + 0.25 * (Se - 2);
+        if (cost < best)
+            best = cost, plan = SegPlan{Se, L * 64};
+    }
+    return plan;
+}
+
+size_t seg_bytes(const gdn_params *p, int32_t B, int S)
+{
+    if (S < 3)
+        return 0;
+    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S};
+    return align_up((size_t)lay.total() * sizeof(float));
+}
+
 struct Call {
     const gdn_params *p;
     int kda;
@@ -199,6 +277,14 @@ int run(const Call &c)
     const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
+    // segmented scan when it pays and the workspace has room for its states
+    SegPlan sp{0, 0};
+    if (!c.st.cu) {
+        sp = seg_plan(p, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
+        if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.st.B, sp.S) ||
+                     grid * (2 * sp.S - 3) > (int64_t)INT32_MAX))
+            sp = SegPlan{0, 0};
+    }
 
     ChunkArgs ca{};
     ca.g = c.g;
@@ -241,10 +327,29 @@ int run(const Call &c)
     }
     {
         Stage st(GDN_PROF_RECUR, c.stream);
-        if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca, (int)grid,
-                              c.stream) !=
-            hipSuccess)
-            return GDN_E_HIP;
+        if (!sp.S) {
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+                                  (int)grid, c.stream) != hipSuccess)
+                return GDN_E_HIP;
+        } else {
+            ca.nseg = sp.S;
+            ca.seg_len = sp.seg_len;
+            ca.seg_ws = (float *)((char *)c.ws + need);
+            ca.pass = 1;
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+                                  (int)(grid * (2 * sp.S - 3)), c.stream) != hipSuccess)
+                return GDN_E_HIP;
+            gdn::CombineArgs cb{};
+            cb.seg_ws = ca.seg_ws;
+            cb.lay = gdn::SegLayout{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S};
+            cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
+            if (gdn::launch_combine(cb, c.stream) != hipSuccess)
+                return GDN_E_HIP;
+            ca.pass = 2;
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+                                  (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
+                return GDN_E_HIP;
+        }
         st.done();
     }
     if (front) {
@@ -386,7 +491,16 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
         return 0;
     if (B < 1 || max_tokens < 1 || kind < GDN_KIND_SINGLE || kind > GDN_KIND_VARLEN)
         return 0;
-    return front_bytes(p, max_tokens);
+    // room for any segment plan a call of up to max_tokens can make: only calls with fewer
+    // (stream, head, slice) workgroups than CUs ever segment
+    size_t seg = 0;
+    Shape sh = pick_shape(p, 0, 1);
+    if (sh.nv == 0)
+        sh = pick_shape(p, 1, 1);
+    if (kind != GDN_KIND_VARLEN && p->dk == p->dv && sh.nv > 0 &&
+        (int64_t)B * p->H * (p->dv / sh.nv) < cu_count() && max_tokens / B >= 3 * 64)
+        seg = seg_bytes(p, B, kMaxSeg);
+    return front_bytes(p, max_tokens) + seg;
 }
 
 int gdn_profile_enable(int on)

@@ -28,6 +28,40 @@ struct ChunkArgs {
     int32_t do_l2;          // normalise q and k rows on load
     float eps;
     float scale;            // multiplies q on load
+    // Segmented scan of long streams (see SegLayout). pass 0: each workgroup walks a whole
+    // stream. pass 1: job 0 runs segment 0 from the stream's state (o written, end state to
+    // slot H(b, 1)); jobs 1..S-2 run segment j from h = 0 (end state to slot B(b, j)); jobs
+    // S-1..2S-4 run segment j-(S-2) from h = I with v = 0 (end state, the segment's
+    // transition, to slot A(b, j-(S-2))). pass 2: job j runs segment j+1 from slot H(b, j+1)
+    // (o written; the last segment's end state to the stream's state).
+    int32_t pass;
+    int32_t nseg;           // S
+    int64_t seg_len;        // tokens per segment, a multiple of the chunk
+    float *seg_ws;
+};
+
+// Slots of the segmented scan, each one [H][dk][dv] fp32 (dk == dv): H(b, s), s = 1..S-1;
+// B(b, s) and A(b, s), s = 1..S-2.
+struct SegLayout {
+    int64_t slot;  // floats per slot
+    int32_t B, S;
+    __host__ __device__ int64_t h(int b, int s) const { return ((int64_t)b * (S - 1) + s - 1) * slot; }
+    __host__ __device__ int64_t bs(int b, int s) const
+    {
+        return ((int64_t)B * (S - 1) + (int64_t)b * (S - 2) + s - 1) * slot;
+    }
+    __host__ __device__ int64_t as(int b, int s) const
+    {
+        return ((int64_t)B * (S - 1) + (int64_t)B * (S - 2) + (int64_t)b * (S - 2) + s - 1) * slot;
+    }
+    __host__ __device__ int64_t total() const { return (int64_t)B * (3 * S - 5) * slot; }
+};
+
+// h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).
+struct CombineArgs {
+    float *seg_ws;
+    SegLayout lay;
+    int32_t H, dk, dv;
 };
 
 // Front end: conv + SiLU (+ L2 and scale of q, k) over every channel of the packed rows.
@@ -54,6 +88,7 @@ hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
 // workgroup, 0 = the first compiled instance of that width
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
                         const ChunkArgs &a, int grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
 // 1 if the (in_kind, dk, dv, kda, nv, waves) instance exists.

@@ -794,11 +794,41 @@ __global__ void __launch_bounds__(NW * 64)
 
     const int H = a.H;
     const int BH = a.st.B * H;
-    const int slice = blockIdx.x / BH, bh = blockIdx.x - slice * BH;
+    constexpr int NS = DV / NV;  // dv slices
+    const int job = blockIdx.x / (BH * NS), jr = blockIdx.x - job * (BH * NS);
+    const int slice = jr / BH, bh = jr - slice * BH;
     const int b = bh / H, head = bh - b * H;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
-    float *hp = (a.h_ptrs ? a.h_ptrs[b] : a.h) + (int64_t)head * DK * DV;
+    float *state = (a.h_ptrs ? a.h_ptrs[b] : a.h);
+    // segmented scan: this job's rows, where its state comes from and goes to
+    const float *hin = state;  // nullptr: start from 0
+    float *hout = state;       // nullptr: the end state is not needed
+    bool h_ident = false, v_zero = false, write_o = true;
+    if (a.pass != 0) {
+        const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg};
+        const int S = a.nseg;
+        int seg;
+        if (a.pass == 1) {
+            seg = job <= S - 2 ? job : job - (S - 2);
+            if (job > 0) {
+                hin = nullptr;
+                write_o = false;
+                h_ident = v_zero = job > S - 2;
+            }
+            hout = a.seg_ws + (job == 0 ? lay.h(b, 1) : job <= S - 2 ? lay.bs(b, seg)
+                                                                       : lay.as(b, seg));
+        } else {
+            seg = job + 1;
+            hin = a.seg_ws + lay.h(b, seg);
+            if (seg < S - 1)
+                hout = nullptr;
+        }
+        const int64_t s0 = start;
+        start = min(s0 + seg * a.seg_len, end);
+        end = min(start + a.seg_len, end);
+    }
+    const int64_t hoff = (int64_t)head * DK * DV;
     const int colw = slice * NV + wave0 * 16 * NCB;  // this wave's first dv column
 
     const TIN *qg = (const TIN *)a.q + head * DK;
@@ -823,9 +853,12 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                hs[cb][mb][i] = hp[(int64_t)(16 * mb + 4 * (lane0 >> 4) + i) * DV + colw +
-                                   16 * cb + (lane0 & 15)];
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mb + 4 * (lane0 >> 4) + i;
+                const int col = colw + 16 * cb + (lane0 & 15);
+                hs[cb][mb][i] = hin ? hin[hoff + (int64_t)row * DV + col]
+                                    : (h_ident && row == col ? 1.f : 0.f);
+            }
 
     // Raw 16-byte vectors of the next chunk, loaded one chunk ahead so that the HBM latency
     // hides behind a whole chunk of work. Rows at or past the stream's end are never read.
@@ -843,7 +876,8 @@ __global__ void __launch_bounds__(NW * 64)
         for (int it = 0; it < NVV; ++it) {
             const int r = wave * RPV + lane / LPV + it * NW * RPV;
             const TIN *src = vg + (c0 + r) * ld + (lane % LPV) * VEC;
-            pv[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
+            pv[it] = r < Lc && !v_zero ? *reinterpret_cast<const uint4 *>(src)
+                                       : make_uint4(0, 0, 0, 0);
         }
         if constexpr (KDA) {
 #pragma unroll
@@ -953,7 +987,7 @@ __global__ void __launch_bounds__(NW * 64)
             graw[tid] = wave_scan(pg);
             bet[tid] = pb;
         }
-        if (C::STAGE_O && cs > start)
+        if (C::STAGE_O && write_o && cs > start)
             flush_o(Os, cs - CH, CH, tid);  // only the last chunk of a stream is partial
         if (cs + CH < end)
             prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH), tid, lane, wave);
@@ -1292,7 +1326,7 @@ __global__ void __launch_bounds__(NW * 64)
                     const int r = 16 * I + 4 * g4 + i, col = 16 * (wave * NCB + cb) + c16;
                     if constexpr (C::STAGE_O)
                         Os[r * LDO + col] = o[I][i];
-                    else if (r < L)
+                    else if (r < L && write_o)
                         ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
                 }
             }
@@ -1326,19 +1360,21 @@ __global__ void __launch_bounds__(NW * 64)
         }
         __syncthreads();
     }
-    if (C::STAGE_O && start < end) {  // the last chunk's o (the loop ends on a barrier)
+    if (C::STAGE_O && write_o && start < end) {  // the last chunk's o (loop ends on a barrier)
         const int64_t last = start + (end - start - 1) / CH * CH;
         flush_o((const float *)(smem + C::OFF_O), last, (int)(end - last), tid0);
     }
 
+    if (hout) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int mb = 0; mb < DK / 16; ++mb)
+            for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                hp[(int64_t)(16 * mb + 4 * (lane0 >> 4) + i) * DV + colw + 16 * cb + (lane0 & 15)] =
-                    hs[cb][mb][i];
+                for (int i = 0; i < 4; ++i)
+                    hout[hoff + (int64_t)(16 * mb + 4 * (lane0 >> 4) + i) * DV + colw + 16 * cb +
+                         (lane0 & 15)] = hs[cb][mb][i];
+    }
 }
 
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
@@ -1403,6 +1439,75 @@ int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int wave
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return 0;
+}
+
+// ------------------------------------------------------------------------------------
+// segmented scan: chain the segment maps, h(b, s+1) = A(b, s) h(b, s) + B(b, s)
+
+constexpr int CB_THREADS = 256;
+
+// One workgroup per (stream, head, 16 state columns). The 16 columns of h(b, s) sit in LDS;
+// wave w computes row blocks w, w+4 of the next state with fp32 MFMA, A read from memory.
+__global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a)
+{
+    __shared__ float hsm[128][20];  // dk <= 128; 20 floats: rows 4 apart 16 banks apart
+    const int ncb = a.dv / 16;
+    const int cbk = blockIdx.x % ncb, bh = blockIdx.x / ncb;
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int64_t hoff = (int64_t)head * a.dk * a.dv;
+    const int col0 = 16 * cbk, nrb = a.dk / 16;
+    const float *h1 = a.seg_ws + a.lay.h(b, 1) + hoff;
+    for (int idx = tid; idx < a.dk * 16; idx += CB_THREADS)
+        hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * a.dv + col0 + (idx & 15)];
+    __syncthreads();
+    for (int s = 1; s <= a.lay.S - 2; ++s) {
+        const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk] (dk == dv)
+        const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
+        float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
+        f32x4 acc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int rb = wave + 4 * j;
+            if (rb < nrb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * a.dv + col0 + c16];
+                for (int kb = 0; kb < nrb; ++kb) {
+                    const f32x4 av = blk_a(A, a.dk, rb, kb, lane);
+                    const f32x4 bv = f32x4{hsm[16 * kb + 4 * g4][c16], hsm[16 * kb + 4 * g4 + 1][c16],
+                                           hsm[16 * kb + 4 * g4 + 2][c16],
+                                           hsm[16 * kb + 4 * g4 + 3][c16]};
+                    mm16<false>(acc[j], av, bv);
+                }
+            }
+        }
+        __syncthreads();  // every wave has read h(b, s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int rb = wave + 4 * j;
+            if (rb < nrb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * g4 + i;
+                    hsm[r][c16] = acc[j][i];
+                    Hn[(int64_t)r * a.dv + col0 + c16] = acc[j][i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
+{
+    if (a.dk > 128 || a.dk % 16 || a.dv % 16 || a.dk != a.dv || a.lay.S < 3)
+        return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)a.lay.B * a.H * (a.dv / 16);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(CB_THREADS), 0, s, a);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------
