@@ -28,7 +28,7 @@ GDN_KIND_VARLEN = 2
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",
            "kda_prefill_batched", "kda_prefill_varlen", "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
-           "gdn_status_string")
+           "gdn_segments", "gdn_status_string")
 GDN_PROF_FRONT = 0
 GDN_PROF_RECUR = 1
 GDN_PROF_STATE = 2
@@ -77,6 +77,8 @@ def load(path: str = SO):
         lib.gdn_profile_read.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [_pp, _i32, _i64, _i32]
         lib.gdn_workspace_bytes.restype = _sz
+        lib.gdn_segments.argtypes = [_pp, _i32, _i32, _i64, _sz]
+        lib.gdn_segments.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
@@ -164,6 +166,10 @@ def gdn_profile_read(nbuckets=GDN_PROF_BUCKETS):
 
 def gdn_workspace_bytes(p, B, max_tokens, kind):
     return int(load().gdn_workspace_bytes(ctypes.byref(p), B, max_tokens, kind))
+
+
+def gdn_segments(p, kind, B, t_per_stream, ws_bytes):
+    return int(load().gdn_segments(ctypes.byref(p), kind, B, t_per_stream, ws_bytes))
 
 
 def gdn_status_string(status):

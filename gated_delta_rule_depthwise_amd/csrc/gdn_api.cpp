@@ -503,6 +503,25 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
     return front_bytes(p, max_tokens) + seg;
 }
 
+int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
+                 size_t ws_bytes)
+{
+    int rc0 = check_params(p, 0), rc1 = check_params(p, 1);
+    if (rc0 != GDN_OK && rc1 != GDN_OK)
+        return rc0;
+    if (B < 1 || t_per_stream < 1 || kind < GDN_KIND_SINGLE || kind > GDN_KIND_VARLEN ||
+        (kind == GDN_KIND_SINGLE && B != 1))
+        return GDN_E_ARG;
+    if (kind == GDN_KIND_VARLEN)
+        return 0;
+    const Shape sh = pick_shape(p, rc0 == GDN_OK ? 0 : 1, (int64_t)B * p->H);
+    const SegPlan sp = seg_plan(p, B, t_per_stream, p->dv / sh.nv, cu_count());
+    const size_t need = front_bytes(p, (int64_t)B * t_per_stream);
+    if (sp.S && ws_bytes >= need + seg_bytes(p, B, sp.S))
+        return sp.S;
+    return 0;
+}
+
 int gdn_profile_enable(int on)
 {
     prof::enabled.store(on != 0);

@@ -16,10 +16,11 @@ class Prefill:
     ``inp`` is a dict from :func:`inputs.make`. ``mode`` is "single", "batched" or
     "varlen" (default: single for one stream, batched for equal lengths, else varlen).
     ``o_fill`` pre-fills the output so rows the call must not write can be checked.
+    ``segmented=False`` gives the call a workspace without room for segment states.
     """
 
     def __init__(self, inp: dict, device="cuda", mode=None, o_fill=0.0, eps=None,
-                 scale=None):
+                 scale=None, segmented=True):
         spec = inp["spec"]
         self.spec = spec
         self.device = device
@@ -52,7 +53,11 @@ class Prefill:
             conv_k=spec.conv_k if spec.front_end else 0, ld_qkv=spec.cd)
         kind = {"single": B.GDN_KIND_SINGLE, "batched": B.GDN_KIND_BATCHED,
                 "varlen": B.GDN_KIND_VARLEN}[mode]
-        self.ws_bytes = B.gdn_workspace_bytes(self.params, spec.B, spec.N, kind)
+        self.kind = kind
+        # segmented=False sizes the workspace for the front end only, which makes a single
+        # or batched call run its scan unsegmented
+        self.ws_bytes = B.gdn_workspace_bytes(
+            self.params, spec.B, spec.N, kind if segmented else B.GDN_KIND_VARLEN)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
         es = self.x.element_size()
         base = self.x.data_ptr()

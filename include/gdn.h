@@ -193,8 +193,28 @@ int gdn_profile_enable(int on);
 int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 
 /* Bytes of device workspace a call of `kind` with B streams and up to max_tokens rows in
- * total needs (0 if none). Returns 0 for invalid parameters. */
+ * total needs (0 if none). Returns 0 for invalid parameters.
+ *
+ * The workspace holds the front end's activations and, for single and batched calls with
+ * fewer (stream, head) work units than the device has compute units, the states of the
+ * segmented scan: each stream is cut into S segments of whole chunks; one launch runs
+ * segment 0 and gives, for every inner segment, its end state from a zero state and its
+ * dk x dk transition (the end state from the identity with v = 0); a chain over the
+ * segments turns these into each segment's start state; a second launch runs segments
+ * 1..S-1 from their start states. (The pages' chunked scan carries h serially across a
+ * stream's chunks; the recurrence is affine in h, so the segment maps compose exactly up
+ * to rounding.) A call whose ws_bytes covers the front end but not the segment states runs
+ * unsegmented. */
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
+
+/* Segments per stream (S >= 3, or 0 for an unsegmented scan) that a single (kind
+ * GDN_KIND_SINGLE, B = 1) or batched (GDN_KIND_BATCHED) call with these parameters,
+ * t_per_stream tokens per stream and ws_bytes of workspace would use on the current device;
+ * always 0 for GDN_KIND_VARLEN. Negative status for invalid arguments. Host only; enqueues
+ * nothing. The environment variable GDN_SEG (read once) overrides the choice: 0 never
+ * segments, 3..12 asks for that many segments. */
+int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
+                 size_t ws_bytes);
 
 /* Static description of a status code. */
 const char *gdn_status_string(int status);

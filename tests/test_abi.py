@@ -49,6 +49,35 @@ def test_workspace_bytes():
     assert B.gdn_workspace_bytes(B.params(32, 96, 128), 1, 10, B.GDN_KIND_SINGLE) == 0
 
 
+def test_segment_plan():
+    """Few (stream, head) units and long streams: the scan is segmented, and the workspace
+    has room for the segment states; a workspace without that room, varlen calls and calls
+    that already fill the device run unsegmented."""
+    p = B.params(32, 128, 128, conv_k=4)           # one stream, 32 heads
+    full = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
+    front = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN)
+    assert front == 4096 * 3 * 32 * 128 * 2
+    S = B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 4096, full)
+    assert 3 <= S <= 12
+    # the states: per slot [H][dk][dv] fp32, 3S-5 slots
+    assert full - front >= (3 * S - 5) * 32 * 128 * 128 * 4
+    assert B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 4096, front) == 0
+    assert B.gdn_segments(p, B.GDN_KIND_VARLEN, 1, 4096, full) == 0
+    assert B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 100, full) == 0   # two chunks
+    pb = B.params(32, 128, 128)                    # 8 streams x 32 heads fill 256 CUs
+    assert B.gdn_workspace_bytes(pb, 8, 16384, B.GDN_KIND_BATCHED) == 0
+    assert B.gdn_segments(pb, B.GDN_KIND_BATCHED, 8, 2048, 1 << 40) == 0
+    pk = B.params(32, 128, 128, conv_k=4)          # long KDA stream
+    wk = B.gdn_workspace_bytes(pk, 1, 16384, B.GDN_KIND_SINGLE)
+    assert B.gdn_segments(pk, B.GDN_KIND_SINGLE, 1, 16384, wk) >= 3
+    # no compiled instance: the status of the refused call
+    pr = B.params(4, 64, 128, dtype=B.GDN_BF16)
+    assert B.gdn_segments(pr, B.GDN_KIND_SINGLE, 1, 4096, 1 << 40) == B.GDN_E_UNSUPPORTED
+    assert B.gdn_segments(p, B.GDN_KIND_SINGLE, 2, 4096, full) == B.GDN_E_ARG
+    assert B.gdn_segments(p, B.GDN_KIND_BATCHED, 0, 4096, full) == B.GDN_E_ARG
+    assert B.gdn_segments(p, 7, 1, 4096, full) == B.GDN_E_ARG
+
+
 def _single(p, t=10, ws=None, ws_bytes=0, h=FAKE, g=FAKE, cs=None, cw=None, q=FAKE):
     return B.gdn_prefill(p, q, FAKE, FAKE, g, FAKE, h, cs, cw, FAKE, t, ws, ws_bytes, None)
 

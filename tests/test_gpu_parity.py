@@ -33,8 +33,8 @@ def test_f32_ragged_lengths(T):
 
 
 @pytest.mark.parametrize("H", [2, 64, 128, 256])
-def test_bf16_single_stream_all_wave_counts(H):
-    """H picks the waves per workgroup (1, 2, 4, 8), so every compiled bf16 instance runs."""
+def test_bf16_single_stream_head_counts(H):
+    """From a segmented scan (2 heads) to one or more workgroups per CU (256 heads)."""
     heads = None if H <= 4 else [0, H // 2 + 1, H - 1]
     _case(spec_small(3, lengths=[130], H=H, seed=20 + H), heads=heads)
 
@@ -159,3 +159,37 @@ def test_deterministic_run_to_run():
     a = run_gpu(inp)
     b = run_gpu(inp)
     assert torch.equal(a.o, b.o) and torch.equal(a.h, b.h)
+
+
+SEG_CASES = {
+    "gdn-front-T1000": lambda: spec_small(2, lengths=[1000], H=2, seed=50),
+    "gdn-bf16-T777-H4": lambda: spec_small(3, lengths=[777], H=4, seed=51),
+    "batched-2x640": lambda: spec_small(3, lengths=[640, 640], H=2, seed=52),
+    "kda-T900": lambda: spec_small(5, lengths=[900], H=2, seed=53),
+    "f32-d64-T700": lambda: spec_small(1, lengths=[700], H=2, h0_std=0.1, seed=54),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SEG_CASES))
+def test_segmented_scan_matches_serial_scan(case):
+    """Few heads and a long stream: the call segments its scan (the segment maps chained
+    into start states). It matches the oracle, as does the serial scan the same inputs
+    take when the workspace has no room for segment states, and the two agree."""
+    from gated_delta_rule_depthwise_amd import binding as B
+    spec = SEG_CASES[case]()
+    inp = inputs.make(spec)
+    seg = run_gpu(inp)
+    ser = run_gpu(inp, segmented=False)
+    tps = spec.N // spec.B
+    S = B.gdn_segments(seg.params, seg.kind, spec.B, tps, seg.ws_bytes)
+    assert S >= 3, "expected a segmented plan"
+    assert B.gdn_segments(ser.params, ser.kind, spec.B, tps, ser.ws_bytes) == 0
+    ref = run_oracle(inp)
+    e_seg = compare(seg, ref)
+    e_ser = compare(ser, ref)
+    tol = 1e-4 if spec.dtype == "f32" else 2e-2
+    d_o = rel_err(seg.o[:spec.N].cpu().numpy(), ser.o[:spec.N].cpu().numpy())
+    d_h = rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy())
+    print("%s S=%d seg err(o)=%.3g err(h)=%.3g serial err(o)=%.3g err(h)=%.3g |seg-serial| "
+          "o %.3g h %.3g" % (spec.name, S, *e_seg, *e_ser, d_o, d_h), flush=True)
+    assert d_o <= tol and d_h <= tol
