@@ -45,14 +45,17 @@ struct ChunkArgs {
 struct SegLayout {
     int64_t slot;  // floats per slot
     int32_t B, S;
-    __host__ __device__ int64_t h(int b, int s) const { return ((int64_t)b * (S - 1) + s - 1) * slot; }
+    __host__ __device__ int64_t h(int b, int s) const
+    {
+        return ((int64_t)b * (S - 1) + s - 1) * slot;
+    }
     __host__ __device__ int64_t bs(int b, int s) const
     {
         return ((int64_t)B * (S - 1) + (int64_t)b * (S - 2) + s - 1) * slot;
     }
     __host__ __device__ int64_t as(int b, int s) const
     {
-        return ((int64_t)B * (S - 1) + (int64_t)B * (S - 2) + (int64_t)b * (S - 2) + s - 1) * slot;
+        return ((int64_t)B * (2 * S - 3) + (int64_t)b * (S - 2) + s - 1) * slot;
     }
     __host__ __device__ int64_t total() const { return (int64_t)B * (3 * S - 5) * slot; }
 };

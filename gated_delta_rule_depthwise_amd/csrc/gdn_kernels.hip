@@ -870,7 +870,8 @@ __global__ void __launch_bounds__(NW * 64)
             const int rr = wave * RPW + lane / LPR + it * NW * RPW;
             const int r = rr & (CH - 1);
             const TIN *src = (rr >= CH ? kg : qg) + (c0 + r) * ld + (lane % LPR) * VEC;
-            pq[it] = r < Lc ? *reinterpret_cast<const uint4 *>(src) : make_uint4(0, 0, 0, 0);
+            pq[it] = r < Lc && (rr >= CH || write_o) ? *reinterpret_cast<const uint4 *>(src)
+                                                     : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int it = 0; it < NVV; ++it) {
@@ -1055,7 +1056,8 @@ __global__ void __launch_bounds__(NW * 64)
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
                     mma(am, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), fb);
-                    mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
+                    if (write_o)  // P is only needed for o
+                        mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
                 }
             } else if (I != J) {
                 // off-diagonal block: reference row b = 16I (first row of block I), so
@@ -1086,7 +1088,8 @@ __global__ void __launch_bounds__(NW * 64)
                         fb[4 + i] = (T)((float)fb[4 + i] * __expf(b1[i] - s1[i]));
                     }
                     mma(am, fk, fb);
-                    mma(ap, fq, fb);
+                    if (write_o)
+                        mma(ap, fq, fb);
                 }
             } else {
                 // diagonal block: mid-block reference m = 16I + 8, so each factor spans at
@@ -1119,9 +1122,11 @@ __global__ void __launch_bounds__(NW * 64)
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bh, am, 0, 0, 0);
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bl, am, 0, 0, 0);
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl_, bh, am, 0, 0, 0);
-                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bh, ap, 0, 0, 0);
-                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bl, ap, 0, 0, 0);
-                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql_, bh, ap, 0, 0, 0);
+                        if (write_o) {
+                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bh, ap, 0, 0, 0);
+                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bl, ap, 0, 0, 0);
+                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql_, bh, ap, 0, 0, 0);
+                        }
                     }
                 } else {
                     const T *kr = Ks + (16 * I + c16) * LDQ;
@@ -1154,11 +1159,13 @@ __global__ void __launch_bounds__(NW * 64)
                 // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside the
                 // products); the masked upper part is discarded by the selects below
                 const float dec = KDA ? 1.f : __expf(grr - gs);
-                const float pv_ = s <= r ? dec * ap[i] : 0.f;
-                const T phi = (T)pv_;
-                Ps[r * LDT + s] = phi;
-                if constexpr (SPLIT)
-                    Psl[r * LDT + s] = (T)(pv_ - (float)phi);
+                if (write_o) {
+                    const float pv_ = s <= r ? dec * ap[i] : 0.f;
+                    const T phi = (T)pv_;
+                    Ps[r * LDT + s] = phi;
+                    if constexpr (SPLIT)
+                        Psl[r * LDT + s] = (T)(pv_ - (float)phi);
+                }
                 const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
                 am[i] = mv;
                 if (I != J) {
@@ -1260,7 +1267,8 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     mma(kh, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), hf[kb]);
-                    mma(qh, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), hf[kb]);
+                    if (write_o)
+                        mma(qh, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), hf[kb]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1296,38 +1304,40 @@ __global__ void __launch_bounds__(NW * 64)
                     split4(u[I], uhs[I], uls[I]);
             }
             // O += P U with P and U as hi + lo pairs
-            frag uh[2], ul[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if constexpr (SPLIT) {
-                    uh[kb] = __builtin_shufflevector(uhs[2 * kb], uhs[2 * kb + 1], 0, 1, 2, 3, 4,
-                                                     5, 6, 7);
-                    ul[kb] = __builtin_shufflevector(uls[2 * kb], uls[2 * kb + 1], 0, 1, 2, 3, 4,
-                                                     5, 6, 7);
-                } else {
-                    pack_split<T>(u[2 * kb], u[2 * kb + 1], uh[kb], ul[kb]);
-                }
-            }
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            if (write_o) {
+                frag uh[2], ul[2];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    if (kb > (I >> 1))
-                        continue;
-                    const frag ph = ld_frag(Ps, LDT, 16 * I, 32 * kb, lane);
-                    mma(o[I], ph, uh[kb]);
                     if constexpr (SPLIT) {
-                        mma(o[I], ph, ul[kb]);
-                        mma(o[I], ld_frag(Psl, LDT, 16 * I, 32 * kb, lane), uh[kb]);
+                        uh[kb] = __builtin_shufflevector(uhs[2 * kb], uhs[2 * kb + 1], 0, 1, 2,
+                                                         3, 4, 5, 6, 7);
+                        ul[kb] = __builtin_shufflevector(uls[2 * kb], uls[2 * kb + 1], 0, 1, 2,
+                                                         3, 4, 5, 6, 7);
+                    } else {
+                        pack_split<T>(u[2 * kb], u[2 * kb + 1], uh[kb], ul[kb]);
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * g4 + i, col = 16 * (wave * NCB + cb) + c16;
-                    if constexpr (C::STAGE_O)
-                        Os[r * LDO + col] = o[I][i];
-                    else if (r < L && write_o)
-                        ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
+                for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        if (kb > (I >> 1))
+                            continue;
+                        const frag ph = ld_frag(Ps, LDT, 16 * I, 32 * kb, lane);
+                        mma(o[I], ph, uh[kb]);
+                        if constexpr (SPLIT) {
+                            mma(o[I], ph, ul[kb]);
+                            mma(o[I], ld_frag(Psl, LDT, 16 * I, 32 * kb, lane), uh[kb]);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * I + 4 * g4 + i, col = 16 * (wave * NCB + cb) + c16;
+                        if constexpr (C::STAGE_O)
+                            Os[r * LDO + col] = o[I][i];
+                        else if (r < L)
+                            ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
+                    }
                 }
             }
             // h <- a_C h + K^T (diag(a_C / a) U); per-channel gate:
@@ -1477,9 +1487,8 @@ __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a
                     acc[j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * a.dv + col0 + c16];
                 for (int kb = 0; kb < nrb; ++kb) {
                     const f32x4 av = blk_a(A, a.dk, rb, kb, lane);
-                    const f32x4 bv = f32x4{hsm[16 * kb + 4 * g4][c16], hsm[16 * kb + 4 * g4 + 1][c16],
-                                           hsm[16 * kb + 4 * g4 + 2][c16],
-                                           hsm[16 * kb + 4 * g4 + 3][c16]};
+                    const float *hc = &hsm[16 * kb + 4 * g4][c16];
+                    const f32x4 bv = f32x4{hc[0], hc[20], hc[40], hc[60]};
                     mm16<false>(acc[j], av, bv);
                 }
             }

@@ -46,7 +46,9 @@ class Spec:
     chunk: int = 64
     dtype: str = "bf16"               # "bf16" | "f32" (q/k/v, conv state, o)
     gate: str = "gdn"                 # "gdn" (per head) | "kda" (per key channel)
-    gate_dist: str = "softplus"       # "softplus": -softplus(N(0,1)); "uniform": U(-0.5,-0.01)
+    # "softplus": -softplus(N(0,1)); "uniform": U(-0.5,-0.01); "slow": U(-0.02,-1e-4), a
+    # decay weak enough that the state carries over many chunks
+    gate_dist: str = "softplus"
     front_end: bool = False           # raw packed QKV + conv1d(K) + SiLU
     conv_k: int = 4
     h0_std: float = 0.1               # 0 -> zero initial state
@@ -110,6 +112,8 @@ def make(spec: Spec) -> dict:
     gshape = (N, H) if spec.gate == "gdn" else (N, H, dk)
     if spec.gate_dist == "softplus":
         g = -_softplus(_normal(rng, gshape))
+    elif spec.gate_dist == "slow":
+        g = rng.uniform(-0.02, -1e-4, size=gshape).astype(np.float32)
     else:
         g = rng.uniform(-0.5, -0.01, size=gshape).astype(np.float32)
     gt = torch.full((alloc,) + gshape[1:], spec.pad_fill, dtype=torch.float32)

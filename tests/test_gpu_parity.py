@@ -161,12 +161,14 @@ def test_deterministic_run_to_run():
     assert torch.equal(a.o, b.o) and torch.equal(a.h, b.h)
 
 
-SEG_CASES = {
-    "gdn-front-T1000": lambda: spec_small(2, lengths=[1000], H=2, seed=50),
-    "gdn-bf16-T777-H4": lambda: spec_small(3, lengths=[777], H=4, seed=51),
-    "batched-2x640": lambda: spec_small(3, lengths=[640, 640], H=2, seed=52),
-    "kda-T900": lambda: spec_small(5, lengths=[900], H=2, seed=53),
-    "f32-d64-T700": lambda: spec_small(1, lengths=[700], H=2, h0_std=0.1, seed=54),
+SEG_CASES = {  # slow decay, so that every segment's start state matters
+    "gdn-front-T1000": lambda: spec_small(2, lengths=[1000], H=2, gate_dist="slow", seed=50),
+    "gdn-front-T4096-H4": lambda: spec_small(2, lengths=[4096], H=4, gate_dist="slow", seed=55),
+    "gdn-bf16-T777-H4": lambda: spec_small(3, lengths=[777], H=4, gate_dist="slow", seed=51),
+    "batched-2x640": lambda: spec_small(3, lengths=[640, 640], H=2, gate_dist="slow", seed=52),
+    "kda-T900": lambda: spec_small(5, lengths=[900], H=2, gate_dist="slow", seed=53),
+    "f32-d64-T700": lambda: spec_small(1, lengths=[700], H=2, h0_std=0.1, gate_dist="slow",
+                                       seed=54),
 }
 
 
@@ -193,3 +195,4 @@ def test_segmented_scan_matches_serial_scan(case):
     print("%s S=%d seg err(o)=%.3g err(h)=%.3g serial err(o)=%.3g err(h)=%.3g |seg-serial| "
           "o %.3g h %.3g" % (spec.name, S, *e_seg, *e_ser, d_o, d_h), flush=True)
     assert d_o <= tol and d_h <= tol
+    assert d_o > 0, "the two scans should differ in rounding: is the state carried?"
