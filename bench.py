@@ -136,6 +136,10 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
 
+    # the chunk scan: one chunk_kernel launch, or (segmented scan) pass 1 + the chain of
+    # segment maps + pass 2, timed together as one stage
+    segs = B.gdn_segments(first.params, first.kind, spec.B, spec.N // spec.B, first.ws_bytes) \
+        if first.kind != B.GDN_KIND_VARLEN else 0
     names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state"}
     avg_ms = {names[i]: ms[i] / launches[i] for i in names if launches[i]}
     dom = max(avg_ms, key=avg_ms.get)
@@ -165,7 +169,11 @@ def main() -> int:
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
                    "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
                    "front_end": spec.front_end, "input_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": dom if not (dom == "recur" and segs) else
+                     "recur: chunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
+                     "(segmented scan, %d segments)" % segs,
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg[dom],
                      "avg_launch_ms": avg_ms[dom]},

@@ -308,6 +308,16 @@ int run(const Call &c)
         fa.do_l2 = p->eps >= 0.f;
         fa.eps = p->eps;
         fa.scale = p->scale;
+        // Tiles long enough that the grid is about one round of workgroups (3 per CU at
+        // the front kernel's occupancy), at least 32 tokens: a tile's window set-up and
+        // its first loads are paid once per tile.
+        {
+            const int64_t groups = (conv_dim(p) / 8 + 255) / 256;
+            const int64_t target = 3 * (int64_t)cu_count();
+            int64_t rows = (c.N * groups + target - 1) / target;
+            rows = (rows + 3) / 4 * 4;
+            fa.tile_rows = (int32_t)(rows < 32 ? 32 : rows > 4096 ? 4096 : rows);
+        }
         Stage st(GDN_PROF_FRONT, c.stream);
         if (gdn::launch_front(p->dtype, fa, c.stream) != hipSuccess)
             return GDN_E_HIP;

@@ -80,6 +80,7 @@ struct FrontArgs {
     int32_t H, dk, dv, K;
     int32_t do_l2;
     float eps, scale;
+    int32_t tile_rows;      // tokens per workgroup tile: a multiple of 4, >= 32
 };
 
 // Launchers (defined in gdn_kernels.hip). Return hipSuccess or the launch error.

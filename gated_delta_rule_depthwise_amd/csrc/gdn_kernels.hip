@@ -247,7 +247,7 @@ __device__ __forceinline__ void stream_bounds(const Streams &s, int b, int64_t &
 // front end: conv + SiLU (+ L2, scale)
 
 constexpr int FRONT_THREADS = 256;
-constexpr int FRONT_ROWS = 32;  // tokens per tile
+constexpr int FRONT_ROWS = 32;  // fewest tokens per tile
 constexpr int FRONT_CPT = 8;    // channels per thread
 
 template <typename T>
@@ -317,8 +317,8 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
         for (int i = 0; i < FRONT_CPT; ++i)
             w[j][i] = active ? a.conv_w[(int64_t)(c0 + i) * K + j] : 0.f;
 
-    const int64_t t0 = (int64_t)blockIdx.y * FRONT_ROWS;
-    const int64_t t1 = min(t0 + FRONT_ROWS, a.N);
+    const int64_t t0 = (int64_t)blockIdx.y * a.tile_rows;
+    const int64_t t1 = min(t0 + a.tile_rows, a.N);
     if (t0 >= t1)
         return;  // uniform over the block
 
@@ -352,17 +352,28 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
     init_window(t0);
 
     TOUT *y = (TOUT *)a.y;
-    constexpr int RB = 4;  // rows loaded together (memory-level parallelism)
-    for (int64_t tb = t0; tb < t1; tb += RB) {
-        float xs[RB][8];
+    constexpr int RB = 4;  // rows per batch; the next batch is in flight while one is used
+    float xn[RB][8];
+    auto load_batch = [&](int64_t tb) {
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                xs[u][i] = 0.f;
+                xn[u][i] = 0.f;
             if (active && tb + u < t1)
-                load8<T>(src + (tb + u) * a.ld, xs[u]);
+                load8<T>(src + (tb + u) * a.ld, xn[u]);
         }
+    };
+    load_batch(t0);
+    for (int64_t tb = t0; tb < t1; tb += RB) {
+        float xs[RB][8];
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                xs[u][i] = xn[u][i];
+        if (tb + RB < t1)
+            load_batch(tb + RB);
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
             const int64_t t = tb + u;
@@ -468,8 +479,10 @@ hipError_t launch_front_tk(const FrontArgs &a, hipStream_t s)
 {
     const int cd = 2 * a.H * a.dk + a.H * a.dv;
     const int groups = cd / FRONT_CPT;
+    if (a.tile_rows < FRONT_ROWS || a.tile_rows % 4)
+        return hipErrorInvalidValue;
     dim3 grid((groups + FRONT_THREADS - 1) / FRONT_THREADS,
-              (unsigned)((a.N + FRONT_ROWS - 1) / FRONT_ROWS));
+              (unsigned)((a.N + a.tile_rows - 1) / a.tile_rows));
     hipLaunchKernelGGL((front_kernel<T, TOUT, K>), grid, dim3(FRONT_THREADS), 0, s, a);
     return hipGetLastError();
 }
@@ -1457,52 +1470,73 @@ int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int wave
 constexpr int CB_THREADS = 256;
 
 // One workgroup per (stream, head, 16 state columns). The 16 columns of h(b, s) sit in LDS;
-// wave w computes row blocks w, w+4 of the next state with fp32 MFMA, A read from memory.
+// wave w computes row blocks w, w+4 of the next state with fp32 MFMA. The A and B blocks a
+// wave needs for step s+1 are loaded into registers while step s computes, so each step
+// waits on memory once at most.
+template <int DK>
 __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a)
 {
-    __shared__ float hsm[128][20];  // dk <= 128; 20 floats: rows 4 apart 16 banks apart
+    constexpr int NRB = DK / 16, RBW = (NRB + 3) / 4;  // row blocks, per wave
+    __shared__ float hsm[DK][20];  // 20 floats: rows 4 apart 16 banks apart
     const int ncb = a.dv / 16;
     const int cbk = blockIdx.x % ncb, bh = blockIdx.x / ncb;
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, c16 = lane & 15;
-    const int64_t hoff = (int64_t)head * a.dk * a.dv;
-    const int col0 = 16 * cbk, nrb = a.dk / 16;
+    const int64_t hoff = (int64_t)head * DK * DK;
+    const int col0 = 16 * cbk;
+    const int S = a.lay.S;
     const float *h1 = a.seg_ws + a.lay.h(b, 1) + hoff;
-    for (int idx = tid; idx < a.dk * 16; idx += CB_THREADS)
-        hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * a.dv + col0 + (idx & 15)];
-    __syncthreads();
-    for (int s = 1; s <= a.lay.S - 2; ++s) {
-        const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk] (dk == dv)
+    for (int idx = tid; idx < DK * 16; idx += CB_THREADS)
+        hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
+
+    f32x4 av[RBW][NRB], bv[RBW];  // A blocks and B rows of the next step
+    auto load = [&](int s) {
+        const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk]
         const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
-        float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
-        f32x4 acc[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < RBW; ++j) {
             const int rb = wave + 4 * j;
-            if (rb < nrb) {
+            if (rb < NRB) {
+#pragma unroll
+                for (int kb = 0; kb < NRB; ++kb)
+                    av[j][kb] = blk_a(A, DK, rb, kb, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * a.dv + col0 + c16];
-                for (int kb = 0; kb < nrb; ++kb) {
-                    const f32x4 av = blk_a(A, a.dk, rb, kb, lane);
+                    bv[j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
+            }
+        }
+    };
+    load(1);
+    __syncthreads();
+    for (int s = 1; s <= S - 2; ++s) {
+        f32x4 acc[RBW];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave + 4 * j;
+            acc[j] = bv[j];
+            if (rb < NRB) {
+#pragma unroll
+                for (int kb = 0; kb < NRB; ++kb) {
                     const float *hc = &hsm[16 * kb + 4 * g4][c16];
-                    const f32x4 bv = f32x4{hc[0], hc[20], hc[40], hc[60]};
-                    mm16<false>(acc[j], av, bv);
+                    mm16<false>(acc[j], av[j][kb], f32x4{hc[0], hc[20], hc[40], hc[60]});
                 }
             }
         }
+        if (s + 1 <= S - 2)
+            load(s + 1);
         __syncthreads();  // every wave has read h(b, s)
+        float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < RBW; ++j) {
             const int rb = wave + 4 * j;
-            if (rb < nrb) {
+            if (rb < NRB) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * rb + 4 * g4 + i;
                     hsm[r][c16] = acc[j][i];
-                    Hn[(int64_t)r * a.dv + col0 + c16] = acc[j][i];
+                    Hn[(int64_t)r * DK + col0 + c16] = acc[j][i];
                 }
             }
         }
@@ -1515,7 +1549,12 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
     if (a.dk > 128 || a.dk % 16 || a.dv % 16 || a.dk != a.dv || a.lay.S < 3)
         return hipErrorInvalidValue;
     const int64_t grid = (int64_t)a.lay.B * a.H * (a.dv / 16);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(CB_THREADS), 0, s, a);
+    if (a.dk == 128)
+        hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)grid), dim3(CB_THREADS), 0, s, a);
+    else if (a.dk == 64)
+        hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)grid), dim3(CB_THREADS), 0, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
