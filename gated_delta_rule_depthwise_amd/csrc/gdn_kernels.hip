@@ -598,9 +598,8 @@ struct ChunkCfg {
     static constexpr int OFF_V = OFF_K + SZ_Q;
     static constexpr int OFF_P = OFF_V + SZ_V;                    // P (hi)
     static constexpr int OFF_PL = OFF_P + SZ_P;                   // P (lo)
-    static constexpr int OFF_MT = OFF_PL + (SPLIT ? SZ_P : 0);    // M_IJ (J<I), T_II (hi)
-    static constexpr int OFF_MTL = OFF_MT + SZ_P;                 // same (lo)
-    static constexpr int OFF_M = OFF_MTL + (SPLIT ? SZ_P : 0);    // diagonal blocks of M, fp32
+    static constexpr int OFF_MT = OFF_PL + (SPLIT ? SZ_P : 0);    // M_IJ (J<I), T_II
+    static constexpr int OFF_M = OFF_MT + SZ_P;                   // diagonal blocks of M, fp32
     static constexpr int OFF_GK = OFF_M + SZ_MS;  // per-channel cumulative log-gates
     // Gamma[64], beta[64], a = e^Gamma [64], a_C / a [64]
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);
@@ -711,43 +710,37 @@ __device__ __forceinline__ f32x4 blk_a16(const float *X, int ld, int I, int J, i
     return blk_a(X, ld, I, J, lane);
 }
 
-// d += A B (16x16 blocks, 16-deep) with A given as a stored hi + lo pair of operand tiles and
-// B an fp32 D-layout value split here into hi + lo; fp32 tiles use fp32 MFMA directly.
-__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *Xh, const f16 *Xl, int ld, int I,
-                                         int J, const f32x4 &b, int lane)
+// d += A B for 16x16 blocks (16-deep): A block (I, J) of a stored operand tile, B an fp32
+// D-layout value given as an fp16 hi + lo pair (or split here). A is a single fp16 operand:
+// its rounding adds no measurable error to o or h (the M blocks below the diagonal and the
+// inverted diagonal blocks enter U only through products with the split right-hand side),
+// while rounding B does. fp32 tiles use fp32 MFMA directly.
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, int J,
+                                         const f16x4 &bh, const f16x4 &bl, int lane)
 {
-    const int off = (16 * I + (lane & 15)) * ld + 16 * J + 4 * (lane >> 4);
-    const f16x4 ah = *reinterpret_cast<const f16x4 *>(Xh + off);
-    const f16x4 al = *reinterpret_cast<const f16x4 *>(Xl + off);
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(X + (16 * I + (lane & 15)) * ld + 16 * J +
+                                                    4 * (lane >> 4));
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bh, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bl, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, int J,
+                                         const f32x4 &b, int lane)
+{
     f16x4 bh, bl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         bh[i] = (f16)b[i];
         bl[i] = (f16)(b[i] - (float)bh[i]);
     }
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, d, 0, 0, 0);
+    mm16_pre(d, X, ld, I, J, bh, bl, lane);
 }
-__device__ __forceinline__ void mm16_pre(f32x4 &d, const float *Xh, const float *, int ld, int I,
-                                         int J, const f32x4 &b, int lane)
+__device__ __forceinline__ void mm16_pre(f32x4 &d, const float *X, int ld, int I, int J,
+                                         const f32x4 &b, int lane)
 {
-    const f32x4 a = blk_a(Xh, ld, I, J, lane);
+    const f32x4 a = blk_a(X, ld, I, J, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], d, 0, 0, 0);
-}
-
-// The same with B given as a ready hi + lo pair
-__device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *Xh, const f16 *Xl, int ld, int I,
-                                         int J, const f16x4 &bh, const f16x4 &bl, int lane)
-{
-    const int off = (16 * I + (lane & 15)) * ld + 16 * J + 4 * (lane >> 4);
-    const f16x4 ah = *reinterpret_cast<const f16x4 *>(Xh + off);
-    const f16x4 al = *reinterpret_cast<const f16x4 *>(Xl + off);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bl, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(al, bh, d, 0, 0, 0);
 }
 
 // fp32 D-layout value -> fp16 hi + lo
@@ -977,7 +970,6 @@ __global__ void __launch_bounds__(NW * 64)
         T *Ps = (T *)(smem + zo + C::OFF_P);
         T *Psl = (T *)(smem + zo + C::OFF_PL);
         T *MTh = (T *)(smem + zo + C::OFF_MT);
-        T *MTl = (T *)(smem + zo + C::OFF_MTL);
         float *Ms = (float *)(smem + zo + C::OFF_M);
         float *Gk = (float *)(smem + zo + C::OFF_GK);
         float *graw = (float *)(smem + zo + C::OFF_G);
@@ -1099,7 +1091,7 @@ __global__ void __launch_bounds__(NW * 64)
         // diagonal block and invert it right away, T_II = (I + M_II)^-1; the 6 blocks below
         // the diagonal are spread over the other waves (8 waves) or the same ones (4 waves).
         // Both products of a block share the K_J operand. T_II and the off-diagonal M_IJ go
-        // to the MT tiles as hi + lo operands, P to Ps/Psl.
+        // to the MT tile (fp16), P to Ps/Psl as an fp16 hi + lo pair.
         constexpr int NJ = NW == 8 ? 2 : 3;
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
@@ -1226,12 +1218,8 @@ __global__ void __launch_bounds__(NW * 64)
                 }
                 const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
                 am[i] = mv;
-                if (I != J) {
-                    const T mhi = (T)mv;
-                    MTh[r * LDT + s] = mhi;
-                    if constexpr (SPLIT)
-                        MTl[r * LDT + s] = (T)(mv - (float)mhi);
-                }
+                if (I != J)
+                    MTh[r * LDT + s] = (T)mv;
             }
             if (I == J) {
                 // T_II = (I - N)^-1 with N = -M_II strictly lower (N^16 = 0):
@@ -1268,13 +1256,8 @@ __global__ void __launch_bounds__(NW * 64)
                 f32x4 z = y;
                 mm16<false>(z, n8a, y);  // (I + N^8) Y
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int off = (base + 4 * g4 + i) * LDT + base + c16;
-                    const T hi = (T)z[i];
-                    MTh[off] = hi;
-                    if constexpr (SPLIT)
-                        MTl[off] = (T)(z[i] - (float)hi);
-                }
+                for (int i = 0; i < 4; ++i)
+                    MTh[(base + 4 * g4 + i) * LDT + base + c16] = (T)z[i];
             }
         }
         __syncthreads();
@@ -1342,7 +1325,7 @@ __global__ void __launch_bounds__(NW * 64)
                 }
             }
             // U = T diag(beta) X by block forward substitution on (I + M) U = diag(beta) X:
-            // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), operands as hi + lo pairs
+            // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), right-hand sides as hi + lo pairs
             // (fp16 operands: each U block is split into hi + lo once, for the later blocks
             // and for P U)
             f32x4 u[4];
@@ -1353,16 +1336,16 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                 for (int J = 0; J < I; ++J) {
                     if constexpr (SPLIT)
-                        mm16_pre(acc, MTh, MTl, LDT, I, J, uhs[J], uls[J], lane);
+                        mm16_pre(acc, MTh, LDT, I, J, uhs[J], uls[J], lane);
                     else
-                        mm16_pre(acc, MTh, MTl, LDT, I, J, u[J], lane);
+                        mm16_pre(acc, MTh, LDT, I, J, u[J], lane);
                 }
                 f32x4 z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     z[i] = bet[16 * I + 4 * g4 + i] * x[I][i] - acc[i];
                 u[I] = zero4();
-                mm16_pre(u[I], MTh, MTl, LDT, I, I, z, lane);
+                mm16_pre(u[I], MTh, LDT, I, I, z, lane);
                 if constexpr (SPLIT)
                     split4(u[I], uhs[I], uls[I]);
             }
