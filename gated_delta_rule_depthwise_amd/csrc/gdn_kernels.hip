@@ -770,18 +770,20 @@ __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
     }
 }
 
-// Block (numbered row by row over the 10 lower 16x16 blocks of a chunk) handled as task j
-// of a wave in the preparation stage, or -1. Diagonal blocks (0, 2, 5, 9) come first on
-// waves 0-3, which also invert them.
+// Task j of a wave in the preparation stage, or -1: block b (numbered row by row over the
+// 10 lower 16x16 blocks of a chunk) + 16 * part, part 0 = both products of the block,
+// 1 = M only, 2 = P only. Diagonal blocks (0, 2, 5, 9) come first on waves 0-3, which
+// also invert them; two blocks below the diagonal are split between two waves so that
+// the waves without an inversion carry about as much as the ones with.
 template <int NW>
 __device__ __forceinline__ int block_task(int wave, int j)
 {
     if constexpr (NW == 8) {
-        constexpr int tab[8][2] = {{0, -1}, {2, -1}, {5, -1}, {9, -1},
-                                   {1, 6},  {3, 7},  {4, -1}, {8, -1}};
+        constexpr int tab[8][2] = {{0, -1}, {2, -1}, {5, -1},      {9, -1},
+                                   {1, 22}, {3, 23}, {4, 38}, {8, 39}};
         return tab[wave][j];
     } else {
-        constexpr int tab[4][3] = {{0, 1, 3}, {2, 4, 6}, {5, 7, -1}, {9, 8, -1}};
+        constexpr int tab[4][3] = {{0, 1, 19}, {2, 4, 22}, {5, 7, 35}, {9, 8, 38}};
         return tab[wave][j];
     }
 }
@@ -1086,6 +1088,12 @@ __global__ void __launch_bounds__(NW * 64)
         if (C::STAGE_O && write_o && cs > start)
             flush_o(Os, cs - CH, CH, tid);  // only the last chunk of a stream is partial
 
+        // Two waves share a SIMD and the older one wins every issue slot: without help the
+        // second wave of each SIMD (waves 4-7) reaches each barrier last. They get the
+        // higher priority from here to the end of the K h / Q h products.
+        if (NW == 8 && wave >= 4)
+            __builtin_amdgcn_s_setprio(1);
+
         // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
         // The 10 lower 16x16 blocks (I, J), numbered row by row. Waves 0-3 each take one
         // diagonal block and invert it right away, T_II = (I + M_II)^-1; the 6 blocks below
@@ -1095,9 +1103,11 @@ __global__ void __launch_bounds__(NW * 64)
         constexpr int NJ = NW == 8 ? 2 : 3;
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
-            const int p = block_task<NW>(wave, jb);
-            if (p < 0)
+            const int code = block_task<NW>(wave, jb);
+            if (code < 0)
                 break;
+            const int p = code & 15, part = code >> 4;
+            const bool do_m = part != 2, do_p = part != 1 && write_o;  // P only feeds o
             const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
             const int J = p - I * (I + 1) / 2;
             f32x4 am = zero4(), ap = zero4();
@@ -1105,8 +1115,9 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
-                    mma(am, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), fb);
-                    if (write_o)  // P is only needed for o
+                    if (do_m)
+                        mma(am, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), fb);
+                    if (do_p)
                         mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
                 }
             } else if (I != J) {
@@ -1137,8 +1148,9 @@ __global__ void __launch_bounds__(NW * 64)
                         fb[i] = (T)((float)fb[i] * __expf(b0[i] - s0[i]));
                         fb[4 + i] = (T)((float)fb[4 + i] * __expf(b1[i] - s1[i]));
                     }
-                    mma(am, fk, fb);
-                    if (write_o)
+                    if (do_m)
+                        mma(am, fk, fb);
+                    if (do_p)
                         mma(ap, fq, fb);
                 }
             } else {
@@ -1172,7 +1184,7 @@ __global__ void __launch_bounds__(NW * 64)
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bh, am, 0, 0, 0);
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bl, am, 0, 0, 0);
                         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl_, bh, am, 0, 0, 0);
-                        if (write_o) {
+                        if (do_p) {
                             ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bh, ap, 0, 0, 0);
                             ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bl, ap, 0, 0, 0);
                             ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql_, bh, ap, 0, 0, 0);
@@ -1209,7 +1221,7 @@ __global__ void __launch_bounds__(NW * 64)
                 // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside the
                 // products); the masked upper part is discarded by the selects below
                 const float dec = KDA ? 1.f : __expf(grr - gs);
-                if (write_o) {
+                if (do_p) {
                     const float pv_ = s <= r ? dec * ap[i] : 0.f;
                     const T phi = (T)pv_;
                     Ps[r * LDT + s] = phi;
@@ -1218,7 +1230,7 @@ __global__ void __launch_bounds__(NW * 64)
                 }
                 const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
                 am[i] = mv;
-                if (I != J)
+                if (I != J && do_m)
                     MTh[r * LDT + s] = (T)mv;
             }
             if (I == J) {
@@ -1324,6 +1336,8 @@ __global__ void __launch_bounds__(NW * 64)
                     o[I][i] = arr * qh[i];
                 }
             }
+            if (NW == 8 && wave >= 4 && cb == NCB - 1)
+                __builtin_amdgcn_s_setprio(0);
             // U = T diag(beta) X by block forward substitution on (I + M) U = diag(beta) X:
             // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), right-hand sides as hi + lo pairs
             // (fp16 operands: each U block is split into hi + lo once, for the later blocks
