@@ -1525,8 +1525,11 @@ __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a
 {
     constexpr int NRB = DK / 16, RBW = (NRB + 3) / 4;  // row blocks, per wave
     __shared__ float hsm[DK][20];  // 20 floats: rows 4 apart 16 banks apart
-    const int ncb = a.dv / 16;
-    const int cbk = blockIdx.x % ncb, bh = blockIdx.x / ncb;
+    // Workgroups go to the 8 XCDs round-robin by index: with the column block as the slow
+    // index, the column blocks of one (stream, head) share an XCD (B*H a multiple of 8),
+    // so that XCD's L2 serves that head's A to all of them.
+    const int BH = a.lay.B * a.H;
+    const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
