@@ -1541,8 +1541,10 @@ __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a
     for (int idx = tid; idx < DK * 16; idx += CB_THREADS)
         hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
 
-    f32x4 av[RBW][NRB], bv[RBW];  // A blocks and B rows of the next step
-    auto load = [&](int s) {
+    // A blocks and B rows of the next two steps (ring of 2), so a step's loads have two
+    // steps' time to arrive
+    f32x4 av[2][RBW][NRB], bv[2][RBW];
+    auto load = [&](int s, int slot) {
         const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk]
         const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
 #pragma unroll
@@ -1551,31 +1553,29 @@ __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a
             if (rb < NRB) {
 #pragma unroll
                 for (int kb = 0; kb < NRB; ++kb)
-                    av[j][kb] = blk_a(A, DK, rb, kb, lane);
+                    av[slot][j][kb] = blk_a(A, DK, rb, kb, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    bv[j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
+                    bv[slot][j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
             }
         }
     };
-    load(1);
-    __syncthreads();
-    for (int s = 1; s <= S - 2; ++s) {
+    auto step = [&](int s, int slot) {
         f32x4 acc[RBW];
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int rb = wave + 4 * j;
-            acc[j] = bv[j];
+            acc[j] = bv[slot][j];
             if (rb < NRB) {
 #pragma unroll
                 for (int kb = 0; kb < NRB; ++kb) {
                     const float *hc = &hsm[16 * kb + 4 * g4][c16];
-                    mm16<false>(acc[j], av[j][kb], f32x4{hc[0], hc[20], hc[40], hc[60]});
+                    mm16<false>(acc[j], av[slot][j][kb], f32x4{hc[0], hc[20], hc[40], hc[60]});
                 }
             }
         }
-        if (s + 1 <= S - 2)
-            load(s + 1);
+        if (s + 2 <= S - 2)
+            load(s + 2, slot);
         __syncthreads();  // every wave has read h(b, s)
         float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
 #pragma unroll
@@ -1591,6 +1591,16 @@ __global__ void __launch_bounds__(CB_THREADS) combine_kernel(const CombineArgs a
             }
         }
         __syncthreads();
+    };
+    load(1, 0);
+    if (S - 2 >= 2)
+        load(2, 1);
+    __syncthreads();
+    // the ring slot is a compile-time index: steps go in pairs
+    for (int s = 1; s <= S - 2; s += 2) {
+        step(s, 0);
+        if (s + 1 <= S - 2)
+            step(s + 1, 1);
     }
 }
 
