@@ -8,6 +8,10 @@ dk=dv=128, chunk 64 (seeded synthetic bf16 inputs). Inputs are resident in HBM w
 starts; several input copies are rotated so that a step never finds its inputs in the
 256 MB Infinity Cache from the previous step.
 
+``--decode gdn|kda`` times the decode step instead: one call advances 64 streams by one
+token each (front end, one recurrence step on each stream's 2 MiB state, window update);
+the value is decoded tokens/s.
+
 Extra fields: ``roofline`` (the dominant kernel's algorithmic bytes per launch over its
 average duration, from hipEvents the library records on the call's stream during the timed
 steps) and ``cpu_baseline`` (the fp64 oracle on a bounded sample, on this host's cores).
@@ -27,15 +31,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "prefill tokens/s per GDN/KDA layer (H=32, d=128) + % of MFMA/HBM roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_depthwise_amd", "csrc", f)
-                  for f in ("gdn_kernels.hip", "gdn_api.cpp", "gdn_internal.h")]
+DECODE_METRIC = ("decode tokens/s per GDN/KDA layer (one token per stream, H=32, d=128) "
+                 "+ % of HBM roofline")
+CSRC = os.path.join(ROOT, "gated_delta_rule_depthwise_amd", "csrc")
+# the sources a kernel's traffic depends on (device code and the host code launching it)
+KERNEL_SOURCES = {"prefill": ("gdn_kernels.hip", "gdn_api.cpp", "gdn_internal.h"),
+                  "decode": ("gdn_decode.hip", "gdn_api.cpp", "gdn_internal.h")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_hash() -> str:
+def kernel_hash(which: str = "prefill") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for f in KERNEL_SOURCES[which]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -55,6 +63,18 @@ def algorithmic_bytes(spec) -> dict:
     return out
 
 
+def decode_bytes(spec) -> dict:
+    """Bytes one decode launch must move: every state read and written once, the token
+    rows, windows (read + written), taps, gates, beta and o."""
+    B, H, dk, dv, cd = spec.B, spec.H, spec.dk, spec.dv, spec.cd
+    es = 2 if spec.dtype == "bf16" else 4
+    n = 2 * B * H * dk * dv * 4 + B * cd * es + B * H * (dk if spec.gate == "kda" else 1) * 4
+    n += B * H * 4 + B * H * dv * 4
+    if spec.front_end:
+        n += 2 * B * cd * (spec.conv_k - 1) * es + cd * spec.conv_k * 4
+    return {"recur": n}
+
+
 def cpu_baseline(spec, inp, budget_s: float) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -72,6 +92,19 @@ def cpu_baseline(spec, inp, budget_s: float) -> dict:
                    cu_seqlens=cu, conv_w=inp["conv_w"], conv_state=inp["conv_state"],
                    heads=heads)
     dt = time.perf_counter() - t0
+    if n == H and dt < budget_s / 3:
+        # a small workload (a decode batch): repeat the whole layer to fill the budget
+        reps = int(min(1000, math.floor(budget_s / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk,
+                           dv=spec.dv, cu_seqlens=cu, conv_w=inp["conv_w"],
+                           conv_state=inp["conv_state"])
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": spec.N / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "the whole workload (%d tokens, %d heads, fp64) %d times, %.1f s"
+                          % (spec.N, H, reps, dt * reps)}
     # every head is independent and costs the same: the full layer takes dt * H / n
     return {"value": spec.N / (dt * H / n), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
@@ -89,6 +122,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--decode", choices=("gdn", "kda"), default=None,
+                    help="time the decode step (64 streams, one token each) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -98,16 +133,23 @@ def main() -> int:
     import torch
     from gated_delta_rule_depthwise_amd import binding as B
     from gated_delta_rule_depthwise_amd import inputs
-    from gated_delta_rule_depthwise_amd.runner import Prefill
+    from gated_delta_rule_depthwise_amd.runner import Decode, Prefill
 
-    spec = inputs.config(args.config)
-    inp = inputs.make(spec)
     dev = "cuda"
-    first = Prefill(inp, dev)
-    per_copy = sum(t.numel() * t.element_size() for t in
-                   (first.x, first.g, first.beta, first.o, first.ws))
+    if args.decode:
+        spec = inputs.decode_config(64, gate=args.decode)
+        inp = inputs.make(spec)
+        first = Decode(inp, dev)
+        per_copy = sum(t.numel() * t.element_size() for t in
+                       (first.x, first.g, first.beta, first.o, first.h))
+    else:
+        spec = inputs.config(args.config)
+        inp = inputs.make(spec)
+        first = Prefill(inp, dev)
+        per_copy = sum(t.numel() * t.element_size() for t in
+                       (first.x, first.g, first.beta, first.o, first.ws))
     copies = max(1, min(8, math.ceil((1 << 30) / per_copy)))
-    calls = [first] + [Prefill(inp, dev) for _ in range(copies - 1)]
+    calls = [first] + [type(first)(inp, dev) for _ in range(copies - 1)]
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -138,23 +180,33 @@ def main() -> int:
 
     # the chunk scan: one chunk_kernel launch, or (segmented scan) pass 1 + the chain of
     # segment maps + pass 2, timed together as one stage
-    segs = B.gdn_segments(first.params, first.kind, spec.B, spec.N // spec.B, first.ws_bytes) \
-        if first.kind != B.GDN_KIND_VARLEN else 0
+    segs = 0
+    if not args.decode and first.kind != B.GDN_KIND_VARLEN:
+        segs = B.gdn_segments(first.params, first.kind, spec.B, spec.N // spec.B,
+                              first.ws_bytes)
     names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state"}
     avg_ms = {names[i]: ms[i] / launches[i] for i in names if launches[i]}
     dom = max(avg_ms, key=avg_ms.get)
-    alg = algorithmic_bytes(spec)
+    alg = decode_bytes(spec) if args.decode else algorithmic_bytes(spec)
     achieved = alg[dom] / (avg_ms[dom] * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         ent = tr.get(spec.name, {}).get(dom)
-        if ent and ent.get("kernel_hash") == kernel_hash():
+        if ent and ent.get("kernel_hash") == kernel_hash("decode" if args.decode else
+                                                         "prefill"):
             traffic = ent["bytes_per_launch"]
+    if args.decode:
+        kname = "decode_kernel (front end + one recurrence step + window update, fused)"
+    elif dom == "recur" and segs:
+        kname = ("recur: chunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
+                 "(segmented scan, %d segments)" % segs)
+    else:
+        kname = dom
 
     ms_per_step = elapsed * 1e3 / args.steps
     line = {
-        "metric": METRIC,
+        "metric": DECODE_METRIC if args.decode else METRIC,
         "value": spec.N / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -164,15 +216,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in; fp16 MFMA operands, fp32 accumulate/VALU; fp32 o",
+        "dtype": "bf16 in; fp32 arithmetic; fp32 o" if args.decode else
+                 "bf16 in; fp16 MFMA operands, fp32 accumulate/VALU; fp32 o",
         "data": "synthetic (seeded; distributions of the workload description)",
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
                    "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
                    "front_end": spec.front_end, "input_copies_rotated": copies},
         "roofline": {"bound": "hbm",
-                     "kernel": dom if not (dom == "recur" and segs) else
-                     "recur: chunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
-                     "(segmented scan, %d segments)" % segs,
+                     "kernel": kname,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg[dom],

@@ -27,7 +27,8 @@ GDN_KIND_VARLEN = 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",
-           "kda_prefill_batched", "kda_prefill_varlen", "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
+           "kda_prefill_batched", "kda_prefill_varlen", "gdn_decode", "kda_decode",
+           "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
            "gdn_segments", "gdn_status_string")
 GDN_PROF_FRONT = 0
 GDN_PROF_RECUR = 1
@@ -70,6 +71,9 @@ def load(path: str = SO):
         lib.kda_prefill_batched.argtypes = batched
         lib.gdn_prefill_varlen.argtypes = varlen
         lib.kda_prefill_varlen.argtypes = varlen
+        decode = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
+        lib.gdn_decode.argtypes = decode
+        lib.kda_decode.argtypes = decode
         lib.gdn_chunk_table.argtypes = [_vp, _i32, _i32, _vp, _i64, _vp, _vp]
         lib.gdn_profile_enable.argtypes = [ctypes.c_int]
         lib.gdn_profile_enable.restype = ctypes.c_int
@@ -83,7 +87,7 @@ def load(path: str = SO):
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
                      "gdn_prefill_varlen", "kda_prefill_batched", "kda_prefill_varlen",
-                     "gdn_chunk_table"):
+                     "gdn_decode", "kda_decode", "gdn_chunk_table"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -145,6 +149,16 @@ def kda_prefill_varlen(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, 
                                      _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o),
                                      _p(cu_seqlens), B, total_tokens, max_seqlen, _p(ws),
                                      ws_bytes, stream)
+
+
+def gdn_decode(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B, stream):
+    return load().gdn_decode(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                             _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o), B, stream)
+
+
+def kda_decode(p, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B, stream):
+    return load().kda_decode(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                             _p(h_ptrs), _p(conv_state_ptrs), _p(conv_w), _p(o), B, stream)
 
 
 def gdn_chunk_table(cu_seqlens, B, chunk, table, max_entries, count, stream):

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SO = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_decode.hip"),
+           os.path.join(CSRC, "gdn_api.cpp")]
 
 
 def hipcc() -> str:

@@ -483,6 +483,60 @@ int kda_prefill_varlen(const gdn_params *p, const void *q, const void *k, const 
                   total_tokens, max_seqlen, ws, ws_bytes, stream);
 }
 
+namespace {
+int decode(const gdn_params *p, int kda, const void *q, const void *k, const void *v,
+           const float *g, const float *beta, float *const *h_ptrs,
+           void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+           void *stream)
+{
+    int rc = check_params(p, kda);
+    if (rc != GDN_OK)
+        return rc;
+    if (p->dk != p->dv || (p->dk != 64 && p->dk != 128))
+        return GDN_E_UNSUPPORTED;
+    if (B < 1 || (int64_t)B * p->H > (int64_t)INT32_MAX)
+        return GDN_E_ARG;
+    if (!q || !k || !v || !g || !beta || !h_ptrs || !o)
+        return GDN_E_ARG;
+    if (!aligned16(o))
+        return GDN_E_ARG;
+    const bool front = p->conv_k > 0;
+    if (front != (conv_w != nullptr) || front != (conv_state_ptrs != nullptr))
+        return GDN_E_ARG;
+    gdn::DecodeArgs a{};
+    a.q = q, a.k = k, a.v = v, a.ld = p->ld_qkv;
+    a.g = g, a.beta = beta, a.h_ptrs = h_ptrs;
+    a.conv_state_ptrs = conv_state_ptrs, a.conv_w = conv_w;
+    a.o = (float *)o;
+    a.B = B, a.H = p->H, a.dk = p->dk, a.dv = p->dv, a.K = p->conv_k;
+    a.do_l2 = p->eps >= 0.f;
+    a.eps = p->eps;
+    a.scale = p->scale;
+    // one fused launch: front end, recurrence step and window update
+    Stage st(GDN_PROF_RECUR, (hipStream_t)stream);
+    if (gdn::launch_decode(p->dtype, kda, a, (hipStream_t)stream) != hipSuccess)
+        return GDN_E_HIP;
+    st.done();
+    return GDN_OK;
+}
+}  // namespace
+
+int gdn_decode(const gdn_params *p, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, float *const *h_ptrs,
+               void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+               void *stream)
+{
+    return decode(p, 0, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B, stream);
+}
+
+int kda_decode(const gdn_params *p, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, float *const *h_ptrs,
+               void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+               void *stream)
+{
+    return decode(p, 1, q, k, v, g, beta, h_ptrs, conv_state_ptrs, conv_w, o, B, stream);
+}
+
 int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t *table,
                     int64_t max_entries, int32_t *count, void *stream)
 {

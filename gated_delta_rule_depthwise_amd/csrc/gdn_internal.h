@@ -83,7 +83,24 @@ struct FrontArgs {
     int32_t tile_rows;      // tokens per workgroup tile: a multiple of 4, >= 32
 };
 
-// Launchers (defined in gdn_kernels.hip). Return hipSuccess or the launch error.
+// One decode step: a single token per stream through the front end (optional), L2 and the
+// recurrence, h updated in place.
+struct DecodeArgs {
+    const void *q, *k, *v;           // row b (stream b's token): q + b*ld + h*dk, ...
+    int64_t ld;
+    const float *g;                  // [B][H] or [B][H][dk]
+    const float *beta;               // [B][H]
+    float *const *h_ptrs;            // per-stream [H][dk][dv]
+    void *const *conv_state_ptrs;    // per-stream [cd][K-1] (K > 0)
+    const float *conv_w;             // [cd][K] (K > 0)
+    float *o;                        // [B][H][dv]
+    int32_t B, H, dk, dv, K;
+    int32_t do_l2;
+    float eps, scale;
+};
+
+// Launchers (defined in gdn_kernels.hip and gdn_decode.hip). Return hipSuccess or the
+// launch error.
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
 // new carried conv windows; must run after every kernel that reads the old ones
 hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
@@ -93,6 +110,7 @@ hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
                         const ChunkArgs &a, int grid, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
 // 1 if the (in_kind, dk, dv, kda, nv, waves) instance exists.

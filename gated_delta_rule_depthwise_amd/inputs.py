@@ -198,3 +198,10 @@ def config(i: int, pad_fill: float = 0.0) -> Spec:
         return Spec("kda-frontend-T16384-H32-d128-bf16", [16384], gate="kda",
                     front_end=True, seed=5, pad_fill=pad_fill)
     raise ValueError(i)
+
+
+def decode_config(B: int = 64, gate: str = "gdn", pad_fill: float = 0.0) -> Spec:
+    """A decode batch: B streams with one new token each (row b is stream b's token), the
+    front end on, H=32, dk=dv=128, bf16, carried states h0 ~ N(0, 0.1)."""
+    return Spec("%s-decode-B%d-H32-d128-bf16" % (gate, B), [1] * B, gate=gate,
+                front_end=True, seed=6, pad_fill=pad_fill)

@@ -89,3 +89,72 @@ class Prefill:
         return fn(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g, self.beta,
                   self.h_ptrs, self.cs_ptrs, self.conv_w, self.o, self.cu, sp.B, sp.N,
                   max(sp.lengths), self.ws, self.ws_bytes, s)
+
+
+class Decode:
+    """One call of gdn_decode / kda_decode: row b of ``inp`` is stream b's new token.
+
+    ``inp`` is a dict from :func:`inputs.make` whose streams all have length 1. The states
+    h (``[B, H, dk, dv]``) and the conv windows are updated in place by every call; ``o`` is
+    ``[B, H, dv]``. ``step(t, ...)`` points the call at other token rows (see there).
+    """
+
+    def __init__(self, inp: dict, device="cuda", o_fill=0.0, eps=None, scale=None):
+        spec = inp["spec"]
+        self.spec = spec
+        self.device = device
+        self.x = inp["x"].to(device)
+        self.g = inp["g"].to(device)
+        self.beta = inp["beta"].to(device)
+        self.h0 = inp["h0"].to(device)
+        self.h = self.h0.clone()
+        self.conv_w = None if inp["conv_w"] is None else inp["conv_w"].to(device)
+        self.conv_state0 = None if inp["conv_state"] is None else inp["conv_state"].to(device)
+        self.conv_state = None if self.conv_state0 is None else self.conv_state0.clone()
+        self.o = torch.full((spec.B, spec.H, spec.dv), o_fill, dtype=torch.float32,
+                            device=device)
+        self.h_ptrs = torch.tensor([self.h[b].data_ptr() for b in range(spec.B)],
+                                   dtype=torch.int64, device=device)
+        self.cs_ptrs = None if self.conv_state is None else torch.tensor(
+            [self.conv_state[b].data_ptr() for b in range(spec.B)], dtype=torch.int64,
+            device=device)
+        self.eps = spec.eps if eps is None else eps
+        self.scale = spec.scale if scale is None else scale
+        self.params = self._params(spec.cd)
+        es = self.x.element_size()
+        base = self.x.data_ptr()
+        self.q_ptr = base
+        self.k_ptr = base + spec.H * spec.dk * es
+        self.v_ptr = base + 2 * spec.H * spec.dk * es
+
+    def _params(self, ld):
+        sp = self.spec
+        return B.params(sp.H, sp.dk, sp.dv, chunk=sp.chunk, eps=self.eps, scale=self.scale,
+                        dtype=B.GDN_BF16 if sp.dtype == "bf16" else B.GDN_F32,
+                        conv_k=sp.conv_k if sp.front_end else 0, ld_qkv=ld)
+
+    def reset(self):
+        """Restore the initial states (h, conv window)."""
+        self.h.copy_(self.h0)
+        if self.conv_state is not None:
+            self.conv_state.copy_(self.conv_state0)
+
+    def _call(self, p, q, k, v, g, beta, stream):
+        s = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        fn = B.kda_decode if self.spec.gate == "kda" else B.gdn_decode
+        return fn(p, q, k, v, g, beta, self.h_ptrs, self.cs_ptrs, self.conv_w, self.o,
+                  self.spec.B, s)
+
+    def __call__(self, stream=None) -> int:
+        return self._call(self.params, self.q_ptr, self.k_ptr, self.v_ptr, self.g,
+                          self.beta, stream)
+
+    def step(self, x, t, T, g, beta, stream=None) -> int:
+        """Decode token t of T per stream from prefill-layout rows: stream b's token is row
+        b*T + t of ``x`` (a device tensor of packed rows; the row stride between streams
+        is T rows); ``g`` and ``beta`` hold this step's [B, H(, dk)] values."""
+        sp = self.spec
+        es = x.element_size()
+        base = x.data_ptr() + t * sp.cd * es
+        return self._call(self._params(T * sp.cd), base, base + sp.H * sp.dk * es,
+                          base + 2 * sp.H * sp.dk * es, g, beta, stream)

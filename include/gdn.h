@@ -163,6 +163,32 @@ int kda_prefill_varlen(const gdn_params *p, const void *q, const void *k, const 
                        int32_t max_seqlen, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * One decode step: a single new token for each of B streams (page
+ * "metrale_model_arch/glm5next_kda/prefill.rs" names decode_k, the single-token step, beside
+ * the prefill's profile buckets). The token goes through the same steps as a prefill row:
+ * the optional front end (advancing each stream's window by one raw input), the optional
+ * L2 and q scale, then one step of the recurrence on the stream's state, and o_t = S_t q_t.
+ * The result equals a varlen prefill with cu_seqlens = {0, 1, ..., B}.
+ *   q, k, v   row b (stream b's token) at q + b*ld_qkv; head and channel layout as for
+ *             gdn_prefill.
+ *   g         [B][H] float log-gates (kda_decode: [B][H][dk]); beta [B][H] float.
+ *   h_ptrs    device array of B device pointers, each to a [H][dk][dv] float state,
+ *             16-byte aligned, in/out. The B states must not overlap.
+ *   conv_state_ptrs, conv_w  as for gdn_prefill_batched (NULL iff conv_k == 0).
+ *   o         [B][H][dv] float32, out (16-byte aligned).
+ * dk == dv, 64 or 128 (else GDN_E_UNSUPPORTED); B >= 1. No workspace. The step is one
+ * kernel; with profiling enabled it is recorded in GDN_PROF_RECUR.
+ */
+int gdn_decode(const gdn_params *p, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, float *const *h_ptrs,
+               void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+               void *stream);
+int kda_decode(const gdn_params *p, const void *q, const void *k, const void *v,
+               const float *g, const float *beta, float *const *h_ptrs,
+               void *const *conv_state_ptrs, const float *conv_w, void *o, int32_t B,
+               void *stream);
+
+/*
  * Per-chunk work table of a varlen call (the bookkeeping of
  * prefill_gdn_full_batched_fla_varlen: total_nt = sum_b ceil(len_b/chunk) chunks,
  * max_num_chunks = max_b ceil(len_b/chunk)). Writes, on `stream`, table[4*i .. 4*i+3] =

@@ -126,6 +126,22 @@ def test_batched_and_varlen_refusals():
     assert B.gdn_chunk_table(FAKE, 2, 0, FAKE, 10, FAKE, None) == B.GDN_E_ARG
 
 
+def test_decode_refusals():
+    p = B.params(2, 64, 64)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE]
+    assert B.gdn_decode(p, *args, 0, None) == B.GDN_E_ARG                 # no streams
+    assert B.kda_decode(p, *args, -1, None) == B.GDN_E_ARG
+    assert B.gdn_decode(p, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2,
+                        None) == B.GDN_E_ARG                               # null h_ptrs
+    assert B.gdn_decode(p, *args[:-1], FAKE + 4, 2, None) == B.GDN_E_ARG   # misaligned o
+    assert B.gdn_decode(B.params(2, 64, 128), *args, 2, None) == B.GDN_E_UNSUPPORTED
+    assert B.gdn_decode(B.params(2, 96, 96), *args, 2, None) == B.GDN_E_UNSUPPORTED
+    assert B.gdn_decode(B.params(2, 64, 64, dtype=7), *args, 2, None) == B.GDN_E_UNSUPPORTED
+    pf = B.params(2, 64, 64, conv_k=4)                                     # conv pointers
+    assert B.gdn_decode(pf, *args, 2, None) == B.GDN_E_ARG
+    assert B.gdn_decode(pf, *args[:6], FAKE, None, FAKE, 2, None) == B.GDN_E_ARG
+
+
 def test_params_struct_layout():
     assert ctypes.sizeof(B.gdn_params) == 40
     assert B.gdn_params.ld_qkv.offset == 32
