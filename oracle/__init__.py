@@ -26,6 +26,12 @@ What each function computes, and the passages it follows:
   ``prefill_with_pad_fill`` from conv_prefill to chunk_scan. Rows at or past a stream's end
   are never read.
 
+* :func:`gated_rmsnorm` -- the output gate that opens phase 3 (page "split_prefill.rs",
+  ``prefill_phase3``: gated RMSNorm of the GDN output with Z): per token and head,
+  y = o / sqrt(mean(o^2) + eps) * w * silu(z) over the dv values, one weight per value
+  channel. The pages name the operation only; normalising before gating, eps inside the
+  root and a [dv] weight shared by the heads are the reading taken.
+
 Parity of the conv tap orientation is unpinned by the pages: it follows the convention of
 ``torch.nn.functional.conv1d`` (tap K-1 multiplies the current token).
 """
@@ -74,6 +80,9 @@ def _load():
             _dp, _dp, _dp, _dp, ctypes.c_int32, _dp, ctypes.c_int32, ctypes.c_double,
             ctypes.c_double, _dp, _dp]
         lib.gdn_oracle_recurrence.restype = ctypes.c_int
+        lib.gdn_oracle_gated_rmsnorm.argtypes = [
+            ctypes.c_int64, ctypes.c_int32, _dp, _dp, _dp, ctypes.c_double, _dp]
+        lib.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
         lib.gdn_oracle_num_threads.argtypes = []
         lib.gdn_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -146,6 +155,25 @@ def recurrence(q, k, v, g, beta, h0, cu_seqlens=None, l2=True, eps=1e-6, scale=N
     if rc != 0:
         raise RuntimeError("gdn_oracle_recurrence failed: %d" % rc)
     return o, h
+
+
+def gated_rmsnorm(o, z, w, eps=1e-6):
+    """Gated RMSNorm over the last axis: o / sqrt(mean(o^2) + eps) * w * silu(z).
+
+    o, z: [..., dv] (same shape); w: [dv]. Returns float64 of o's shape.
+    """
+    o = _f64(o)
+    z = _f64(z)
+    w = _f64(w)
+    dv = o.shape[-1]
+    assert z.shape == o.shape and w.shape == (dv,)
+    y = np.empty_like(o)
+    rows = o.size // dv
+    rc = _load().gdn_oracle_gated_rmsnorm(rows, dv, _ptr(o), _ptr(z), _ptr(w), float(eps),
+                                           _ptr(y))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_gated_rmsnorm failed: %d" % rc)
+    return y
 
 
 def prefill(x, g, beta, h0, *, H, dk, dv, cu_seqlens=None, conv_w=None, conv_state=None,

@@ -26,12 +26,19 @@
  *       o_t = S q_t
  *   alpha_t is one scalar per head (GDN) or one value per key channel (KDA).
  *
+ *   output gate (page "split_prefill.rs", prefill_phase3: the gated RMSNorm of the GDN
+ *   output with Z comes first in phase 3): per token and head, over the dv values of o,
+ *       y_j = o_j / sqrt(mean_j o_j^2 + eps) * w_j * silu(z_j),   silu(z) = z / (1 + e^-z)
+ *   with one weight per value channel shared by every head.
+ *
  * Readings where the pages are silent:
  *   - conv taps follow the cross-correlation convention: tap K-1 multiplies the current
  *     token, tap 0 the token K-1 steps back;
  *   - the conv window holds raw (pre-conv) inputs, oldest first, [C][K-1];
  *   - g is the log of the decay; the decay is applied before the delta update;
- *   - beta is used as given (already through its sigmoid).
+ *   - beta is used as given (already through its sigmoid);
+ *   - the gated RMSNorm normalises before gating (the norm sees o alone), over one head's
+ *     dv values, with eps inside the square root and a [dv] weight.
  *
  * Parity of the conv tap orientation is unpinned by the pages (only the library
  * convention of torch.nn.functional.conv1d pins it).
@@ -185,6 +192,27 @@ int gdn_oracle_recurrence(int32_t B, const int64_t *cu, int32_t H, int32_t dk,
 }
 
 /* Threads the OpenMP runtime will use for the loops above (for reporting). */
+/* Gated RMSNorm of rows of dv values: y = o / sqrt(mean(o^2) + eps) * w * silu(z). */
+int gdn_oracle_gated_rmsnorm(int64_t rows, int32_t dv, const double *o, const double *z,
+                             const double *w, double eps, double *y)
+{
+    if (rows < 0 || dv < 1 || !o || !z || !w || !y || !(eps >= 0.0))
+        return ORACLE_EARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *orow = o + r * dv, *zrow = z + r * dv;
+        double ss = 0.0;
+        for (int32_t j = 0; j < dv; ++j)
+            ss += orow[j] * orow[j];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        for (int32_t j = 0; j < dv; ++j) {
+            const double zj = zrow[j];
+            y[r * dv + j] = orow[j] * inv * w[j] * (zj / (1.0 + exp(-zj)));
+        }
+    }
+    return ORACLE_OK;
+}
+
 int gdn_oracle_num_threads(void)
 {
     int n = 1;

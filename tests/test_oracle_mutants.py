@@ -34,6 +34,12 @@ MUTANTS = {
     "silu_sign": ("y[t * C + c] = z / (1.0 + exp(-z));",
                   "y[t * C + c] = z / (1.0 + exp(z));"),
     "kda_channel_index": ("g[(t * H + hd) * dk + i]", "g[(t * H + hd) * dk]"),
+    "norm_sum_not_mean": ("sqrt(ss / dv + eps)", "sqrt(ss + eps)"),
+    "norm_eps_outside": ("sqrt(ss / dv + eps)", "(sqrt(ss / dv) + eps)"),
+    "gate_silu_sign": ("(zj / (1.0 + exp(-zj)))", "(zj / (1.0 + exp(zj)))"),
+    "gate_weight_index": ("* w[j] *", "* w[0] *"),
+    "gate_before_norm": ("ss += orow[j] * orow[j];",
+                         "ss += orow[j] * orow[j] * zrow[j] * zrow[j];"),
     "output_before_update": ("/* o = S q */", "/* o = S q */ for (int32_t i2 = 0; "
                              "i2 < dk; ++i2) for (int32_t j2 = 0; j2 < dv; ++j2) "
                              "S[(int64_t)i2 * dv + j2] += bt * e[j2] * kn[i2];"),
@@ -57,6 +63,9 @@ def _pin_calls():
         pins.test_l2_properties,
         lambda: pins.test_conv_matches_torch_conv1d(37),
         lambda: pins.test_conv_matches_torch_conv1d(2),
+        pins.test_gated_rmsnorm_hand_worked,
+        pins.test_gated_rmsnorm_matches_torch,
+        pins.test_gated_rmsnorm_invariants,
     ]
 
 
@@ -72,7 +81,8 @@ def test_mutant_is_caught(name, tmp_path):
                     str(so), "-lm"], check=True)
     real = oracle._load()
     lib = ctypes.CDLL(str(so))
-    for fn in ("gdn_oracle_conv_silu", "gdn_oracle_recurrence", "gdn_oracle_num_threads"):
+    for fn in ("gdn_oracle_conv_silu", "gdn_oracle_recurrence", "gdn_oracle_gated_rmsnorm",
+               "gdn_oracle_num_threads"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     oracle._lib = lib

@@ -228,6 +228,51 @@ def test_conv_split_equals_one_shot():
 
 
 # ---------------------------------------------------------------------------------------
+# output gate (gated RMSNorm)
+
+
+def test_gated_rmsnorm_hand_worked():
+    # o = (3, 4): mean square 12.5, root 5 / sqrt(2); w = (1, 2); z = (0, ln 3):
+    # sigmoid(ln 3) = 3/4, so silu = (0, 0.75 ln 3); y = (0, 2 * 4 sqrt(2) / 5 * 0.75 ln 3)
+    # = (0, 1.2 sqrt(2) ln 3), worked by hand
+    y = oracle.gated_rmsnorm(np.array([[3.0, 4.0]]), np.array([[0.0, np.log(3.0)]]),
+                             np.array([1.0, 2.0]), eps=0.0)
+    assert y[0, 0] == 0.0
+    assert abs(y[0, 1] - 1.2 * np.sqrt(2.0) * np.log(3.0)) < 1e-14
+    # eps enters beside the mean square: o = (1, 1), eps = 3 -> 1 / sqrt(1 + 3) = 0.5;
+    # z = 40: silu(40) = 40 to double precision
+    y = oracle.gated_rmsnorm(np.ones((1, 2)), np.full((1, 2), 40.0), np.ones(2), eps=3.0)
+    np.testing.assert_allclose(y, [[20.0, 20.0]], rtol=1e-15)
+
+
+def test_gated_rmsnorm_matches_torch():
+    """torch's rms_norm (weight over the last axis) times torch's silu, in float64; a large
+    eps so its place in the formula matters."""
+    rng = np.random.default_rng(31)
+    o = rng.standard_normal((5, 3, 64))
+    z = 2.0 * rng.standard_normal((5, 3, 64))
+    w = 1.0 + 0.3 * rng.standard_normal(64)
+    for eps in (1e-6, 0.5):
+        y = oracle.gated_rmsnorm(o, z, w, eps)
+        ref = F.rms_norm(torch.tensor(o), (64,), weight=torch.tensor(w), eps=eps) * \
+            F.silu(torch.tensor(z))
+        np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_gated_rmsnorm_invariants():
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((4, 16))
+    z = rng.standard_normal((4, 16))
+    w = rng.standard_normal(16)
+    # scale invariance with eps = 0; a constant row normalises to its sign
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * o, z, w, 0.0),
+                               oracle.gated_rmsnorm(o, z, w, 0.0), rtol=1e-12)
+    c = np.full((1, 16), -2.5)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(c, z[:1], w, 0.0),
+                               -w * z[:1] / (1.0 + np.exp(-z[:1])), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
 # invariants of the whole path
 
 
