@@ -3,6 +3,7 @@
 // Every check runs before anything is enqueued, so a refused call changes no buffer (page
 // "metrale_model_arch/glm5next_kda/prefill.rs": a call outside 1..=max_tokens tokens is
 // refused before a launch). Device memory is never read on the host.
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -108,15 +109,16 @@ Shape pick_shape(const gdn_params *p, int kda, int64_t BH)
         e = getenv("GDN_WAVES");
         fwaves = e ? atoi(e) : 0;
     }
-    if (fcols > 0 && p->dv % fcols == 0 &&
-        gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves))
+    // the output gate needs whole o rows per workgroup: the overrides do not apply
+    if (!p->z && fcols > 0 && p->dv % fcols == 0 &&
+        gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves, 0))
         return Shape{fcols, fwaves};
     // The widest instance: one workgroup per (stream, head) computes the chunk
     // preparation once for all its columns, and 8-wave instances hide latency with two
     // waves per SIMD.
     (void)BH;
     for (int nv : {128, 64}) {
-        if (p->dv % nv == 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0))
+        if (p->dv % nv == 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0, 0))
             return Shape{nv, 0};
     }
     return Shape{0, 0};
@@ -136,12 +138,21 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_UNSUPPORTED;
     if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
         return GDN_E_UNSUPPORTED;
-    if (pick_shape(p, kda, 1).nv == 0)
+    const Shape sh = pick_shape(p, kda, 1);
+    if (sh.nv == 0)
         return GDN_E_UNSUPPORTED;
     const int64_t vec = 16 / elem_bytes(p->dtype);
     if (p->ld_qkv < (int64_t)p->H * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
         p->ld_qkv % vec != 0)
         return GDN_E_ARG;
+    if (p->z) {  // output gate
+        if (sh.nv != p->dv)
+            return GDN_E_UNSUPPORTED;
+        if (!p->norm_w || !aligned16(p->z) || !aligned16(p->norm_w) ||
+            p->ld_z < (int64_t)p->H * p->dv || p->ld_z % vec != 0 ||
+            !(p->norm_eps >= 0.f) || !(p->norm_eps < INFINITY))
+            return GDN_E_ARG;
+    }
     return GDN_OK;
 }
 
@@ -274,6 +285,9 @@ int run(const Call &c)
 
     const int64_t BH = (int64_t)c.st.B * p->H;
     const Shape sh = pick_shape(p, c.kda, BH);
+    // the output gate rides in the o flush where the instance stages o, else its own pass
+    const int fused = p->z && gdn::chunk_instance_exists(in_kind(p), p->dk, p->dv, c.kda,
+                                                         sh.nv, sh.waves, 1);
     const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
@@ -295,6 +309,12 @@ int run(const Call &c)
     ca.st = c.st;
     ca.H = p->H;
     ca.eps = p->eps;
+    if (fused) {
+        ca.z = p->z;
+        ca.ld_z = p->ld_z;
+        ca.norm_w = p->norm_w;
+        ca.norm_eps = p->norm_eps;
+    }
     FrontArgs fa{};
     if (front) {
         fa.q = c.q, fa.k = c.k, fa.v = c.v, fa.ld = p->ld_qkv;
@@ -338,7 +358,7 @@ int run(const Call &c)
     {
         Stage st(GDN_PROF_RECUR, c.stream);
         if (!sp.S) {
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)grid, c.stream) != hipSuccess)
                 return GDN_E_HIP;
         } else {
@@ -346,7 +366,7 @@ int run(const Call &c)
             ca.seg_len = sp.seg_len;
             ca.seg_ws = (float *)((char *)c.ws + need);
             ca.pass = 1;
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * (2 * sp.S - 3)), c.stream) != hipSuccess)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
@@ -356,10 +376,24 @@ int run(const Call &c)
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;
             ca.pass = 2;
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, ca,
+            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
                 return GDN_E_HIP;
         }
+        st.done();
+    }
+    if (p->z && !fused) {
+        gdn::GateArgs ga{};
+        ga.o = (float *)c.o;
+        ga.z = p->z;
+        ga.ld_z = p->ld_z;
+        ga.w = p->norm_w;
+        ga.N = c.N;
+        ga.H = p->H, ga.dv = p->dv;
+        ga.eps = p->norm_eps;
+        Stage st(GDN_PROF_GATE, c.stream);
+        if (gdn::launch_gate(p->dtype, ga, c.stream) != hipSuccess)
+            return GDN_E_HIP;
         st.done();
     }
     if (front) {
@@ -512,6 +546,10 @@ int decode(const gdn_params *p, int kda, const void *q, const void *k, const voi
     a.do_l2 = p->eps >= 0.f;
     a.eps = p->eps;
     a.scale = p->scale;
+    a.z = p->z;
+    a.ld_z = p->ld_z;
+    a.norm_w = p->norm_w;
+    a.norm_eps = p->norm_eps;
     // one fused launch: front end, recurrence step and window update
     Stage st(GDN_PROF_RECUR, (hipStream_t)stream);
     if (gdn::launch_decode(p->dtype, kda, a, (hipStream_t)stream) != hipSuccess)

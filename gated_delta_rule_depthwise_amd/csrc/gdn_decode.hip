@@ -9,7 +9,8 @@
 // The step reads and writes the whole state once, so it is bound by HBM on h. One
 // workgroup per (stream, head) holds its head's state in registers: each lane owns 4
 // adjacent columns of every P-th row, so one wave instruction moves whole rows of h as
-// 16-byte lanes. All arithmetic is fp32.
+// 16-byte lanes. All arithmetic is fp32. With the output gate on, o leaves as
+// o / sqrt(mean(o^2) + eps) * w * silu(z) over the head's dv values.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,20 @@ __device__ __forceinline__ void store_nt(float *p, float4 v)
 {
     const nt4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, (nt4 *)p);
+}
+
+// 4 adjacent values of the output gate's z as floats
+__device__ __forceinline__ float4 load4(const float *p) { return *(const float4 *)p; }
+__device__ __forceinline__ float4 load4(const bf16 *p)
+{
+    const uint2 u = *(const uint2 *)p;
+    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+
+__device__ __forceinline__ float silu(float x)
+{
+    return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
 // Sum over the 64 lanes of a wave, every lane gets the result.
@@ -75,6 +90,13 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
     for (int r = 0; r < RP; ++r)
         hr[r] = load_nt(hp + (int64_t)(p + r * P) * DV);
 
+    // output gate operands of this lane's 4 columns (the lanes that finish o)
+    float4 zv = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
+    if (a.z && p == 0) {
+        zv = load4((const T *)a.z + (int64_t)b * a.ld_z + (int64_t)head * DV + 4 * jc);
+        wv = *(const float4 *)(a.norm_w + 4 * jc);
+    }
+
     // front end (or the given activations) for this head's q, k and v channels
     for (int c = tid; c < 2 * DK + DV; c += DEC_THREADS) {
         const int sec = c < DK ? 0 : c < 2 * DK ? 1 : 2;
@@ -100,7 +122,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
             for (int i = 0; i + 1 < W; ++i)
                 win[i] = old[i + 1];
             win[W - 1] = raw;
-            x = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));  // SiLU
+            x = silu(acc);
         }
         (sec == 0 ? sq : sec == 1 ? sk : sv)[e] = x;
     }
@@ -168,6 +190,15 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
         for (int pp = 1; pp < P; ++pp) {
             const float4 t = red[pp][jc];
             o.x += t.x, o.y += t.y, o.z += t.z, o.w += t.w;
+        }
+        if (a.z) {  // o <- o / sqrt(mean(o^2) + eps) * w * silu(z); the row is lanes 0..CPR-1
+            float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+            for (int m = 1; m < CPR; m <<= 1)
+                ss += __shfl_xor(ss, m);
+            const float inv = rsqrtf(ss * (1.f / DV) + a.norm_eps);
+            o.x *= inv * wv.x * silu(zv.x), o.y *= inv * wv.y * silu(zv.y);
+            o.z *= inv * wv.z * silu(zv.z), o.w *= inv * wv.w * silu(zv.w);
         }
         *(float4 *)(a.o + ((int64_t)b * H + head) * DV + 4 * jc) = o;
     }

@@ -38,6 +38,22 @@ struct ChunkArgs {
     int32_t nseg;           // S
     int64_t seg_len;        // tokens per segment, a multiple of the chunk
     float *seg_ws;
+    // output gate (fused instances): o <- o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
+    const void *z;          // row r of head h: z + r*ld_z + h*dv (bf16, or float for f32)
+    int64_t ld_z;
+    const float *norm_w;    // [dv]
+    float norm_eps;
+};
+
+// The output gate as a separate pass over rows [0, N) of o, all heads.
+struct GateArgs {
+    float *o;               // [N][H][dv], in/out
+    const void *z;
+    int64_t ld_z;
+    const float *w;         // [dv]
+    int64_t N;
+    int32_t H, dv;
+    float eps;
 };
 
 // Slots of the segmented scan, each one [H][dk][dv] fp32 (dk == dv): H(b, s), s = 1..S-1;
@@ -97,6 +113,10 @@ struct DecodeArgs {
     int32_t B, H, dk, dv, K;
     int32_t do_l2;
     float eps, scale;
+    const void *z;                   // output gate (nullptr: off): row b at z + b*ld_z
+    int64_t ld_z;
+    const float *norm_w;             // [dv]
+    float norm_eps;
 };
 
 // Launchers (defined in gdn_kernels.hip and gdn_decode.hip). Return hipSuccess or the
@@ -106,14 +126,17 @@ hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
 hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
 // in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end;
 // nv: dv columns per workgroup (the grid is B * H * dv / nv workgroups); waves: waves per
-// workgroup, 0 = the first compiled instance of that width
-hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
+// workgroup, 0 = the first compiled instance of that width; gate: the instance with the
+// output gate fused into its o flush (ChunkArgs z, ld_z, norm_w, norm_eps)
+hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
                         const ChunkArgs &a, int grid, hipStream_t s);
+// the output gate as its own pass (dtype: element type of z, GDN_F32 or GDN_BF16)
+hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
-// 1 if the (in_kind, dk, dv, kda, nv, waves) instance exists.
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves);
+// 1 if the (in_kind, dk, dv, kda, nv, waves, gate) instance exists.
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate);
 
 }  // namespace gdn

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -566,6 +568,95 @@ hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s)
 }
 
 // ------------------------------------------------------------------------------------
+// output gate: y = o / sqrt(mean(o^2) + eps) * w * silu(z) over the dv values of a row
+
+// 4 adjacent z values: one 8-byte load (bf16) or one 16-byte load (float)
+template <typename TZ>
+struct Z4;
+template <>
+struct Z4<bf16> {
+    typedef uint2 raw;
+    __device__ static raw load(const bf16 *p) { return *reinterpret_cast<const uint2 *>(p); }
+    __device__ static raw zero() { return make_uint2(0, 0); }
+    __device__ static float4 get(const raw &u)
+    {
+        return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    }
+};
+template <>
+struct Z4<float> {
+    typedef float4 raw;
+    __device__ static raw load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+    __device__ static raw zero() { return float4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ static float4 get(const raw &u) { return u; }
+};
+
+__device__ __forceinline__ float silu(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
+// o (4 values of a row) times inv_rms * w * silu(z)
+__device__ __forceinline__ float4 gate4(float4 o, float inv_rms, float4 w, float4 z)
+{
+    return float4{o.x * inv_rms * w.x * silu(z.x), o.y * inv_rms * w.y * silu(z.y),
+                  o.z * inv_rms * w.z * silu(z.z), o.w * inv_rms * w.w * silu(z.w)};
+}
+
+// Sum over aligned groups of N lanes (N a power of two <= 64).
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x)
+{
+#pragma unroll
+    for (int m = 1; m < N; m <<= 1)
+        x += __shfl_xor(x, m);
+    return x;
+}
+
+// Separate pass for instances that cannot stage whole o rows: rows [0, N) x H heads of o
+// gated in place. One 32- or 16-lane group per (row, head), 4 values per lane.
+template <typename TZ, int DV>
+__global__ void __launch_bounds__(256) gate_kernel(const GateArgs a)
+{
+    constexpr int LPI = DV / 4, IPB = 256 / LPI;  // lanes per item, items per block
+    const int64_t item = (int64_t)blockIdx.x * IPB + threadIdx.x / LPI;
+    const int j = threadIdx.x % LPI;
+    const bool live = item < a.N * a.H;
+    const int64_t row = live ? item / a.H : 0, head = live ? item - row * a.H : 0;
+    float *op = a.o + (row * a.H + head) * DV + 4 * j;
+    float4 o = live ? *reinterpret_cast<const float4 *>(op) : float4{0.f, 0.f, 0.f, 0.f};
+    const typename Z4<TZ>::raw z =
+        live ? Z4<TZ>::load((const TZ *)a.z + row * a.ld_z + head * DV + 4 * j) : Z4<TZ>::zero();
+    const float4 w = *reinterpret_cast<const float4 *>(a.w + 4 * j);
+    const float ss = lane_group_sum<LPI>(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+    o = gate4(o, rsqrtf(ss * (1.f / DV) + a.eps), w, Z4<TZ>::get(z));
+    if (live)
+        *reinterpret_cast<float4 *>(op) = o;
+}
+
+hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
+{
+    const int64_t items = a.N * a.H;
+    if (a.dv == 128) {
+        const unsigned g = (unsigned)((items + 7) / 8);
+        if (dtype)
+            hipLaunchKernelGGL((gate_kernel<bf16, 128>), dim3(g), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((gate_kernel<float, 128>), dim3(g), dim3(256), 0, s, a);
+    } else if (a.dv == 64) {
+        const unsigned g = (unsigned)((items + 15) / 16);
+        if (dtype)
+            hipLaunchKernelGGL((gate_kernel<bf16, 64>), dim3(g), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((gate_kernel<float, 64>), dim3(g), dim3(256), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
 // fused chunk kernel
 
 constexpr int CH = 64;  // chunk length
@@ -788,13 +879,17 @@ __device__ __forceinline__ int block_task(int wave, int j)
     }
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE>
 __global__ void __launch_bounds__(NW * 64)
     __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
+    // the output gate normalises whole o rows, which the staged o holds
+    static_assert(!GATE || (C::STAGE_O && C::NV == DV), "output gate needs staged o rows");
+    // z comes in the caller's element type (bf16 also when the operands are fp16)
+    typedef typename std::conditional<sizeof(TIN) == 4, float, bf16>::type TZ;
     constexpr int NV = C::NV, LDQ = C::LDQ, LDV = C::LDV, LDT = C::LDT, LDF = C::LDF;
     constexpr int LDG = C::LDG, LDO = C::LDO;
     constexpr bool SPLIT = C::SPLIT;
@@ -944,15 +1039,35 @@ __global__ void __launch_bounds__(NW * 64)
     // stage: vector loads and stores share one completion counter, so stores issued at the
     // end of a chunk would hold up the wait for the next chunk's rows. Full rows go out as
     // 16-byte stores.
-    auto flush_o = [&](const float *Os, int64_t c0, int Lc, int tid) {
-        constexpr int V4 = NV / 4, RPP = NT / V4;
-        static_assert(NT % V4 == 0 && CH % RPP == 0, "o row map");
+    // With the output gate, the z values of the staged rows and the norm weights of this
+    // lane's 4 columns are loaded at the end of the chunk that computes o, so their latency
+    // hides behind the barrier and the next chunk's first stages.
+    constexpr int V4 = NV / 4, RPP = NT / V4, NZ = GATE ? CH / RPP : 1;
+    static_assert(NT % V4 == 0 && CH % RPP == 0 && 64 % V4 == 0, "o row map");
+    typename Z4<TZ>::raw zr[NZ];
+    float4 wr = {0.f, 0.f, 0.f, 0.f};
+    const TZ *zg = GATE ? (const TZ *)a.z + head * DV : nullptr;
+    auto load_z = [&](int64_t c0, int Lc, int tid) {
+        const int j = tid % V4;
 #pragma unroll
-        for (int r0 = 0; r0 < CH; r0 += RPP) {
-            const int r = r0 + tid / V4, j = tid % V4;
+        for (int it = 0; it < NZ; ++it) {
+            const int r = it * RPP + tid / V4;
+            zr[it] = r < Lc ? Z4<TZ>::load(zg + (c0 + r) * a.ld_z + 4 * j) : Z4<TZ>::zero();
+        }
+        wr = *reinterpret_cast<const float4 *>(a.norm_w + 4 * j);
+    };
+    auto flush_o = [&](const float *Os, int64_t c0, int Lc, int tid) {
+#pragma unroll
+        for (int it = 0; it < CH / RPP; ++it) {
+            const int r = it * RPP + tid / V4, j = tid % V4;
+            float4 o = *reinterpret_cast<const float4 *>(Os + r * LDO + 4 * j);
+            if constexpr (GATE) {  // every lane takes part in the row sums
+                const float ss =
+                    lane_group_sum<V4>(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+                o = gate4(o, rsqrtf(ss * (1.f / DV) + a.norm_eps), wr, Z4<TZ>::get(zr[it]));
+            }
             if (r < Lc)
-                *reinterpret_cast<float4 *>(ob + (c0 + r) * (int64_t)H * DV + 4 * j) =
-                    *reinterpret_cast<const float4 *>(Os + r * LDO + 4 * j);
+                *reinterpret_cast<float4 *>(ob + (c0 + r) * (int64_t)H * DV + 4 * j) = o;
         }
     };
 
@@ -1428,6 +1543,10 @@ __global__ void __launch_bounds__(NW * 64)
                 }
             }
         }
+        if constexpr (GATE) {
+            if (write_o)
+                load_z(cs, L, tid);
+        }
         __syncthreads();
     }
     if (C::STAGE_O && write_o && start < end) {  // the last chunk's o (loop ends on a barrier)
@@ -1447,13 +1566,13 @@ __global__ void __launch_bounds__(NW * 64)
     }
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA>
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
     using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
-    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA>;
+    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE>;
     static bool attr_set = false;  // per instance; same value on every device
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -1467,44 +1586,56 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 }
 
 // Instances: (input element, operand type, input kind, dk, dv, waves, column blocks of 16
-// per wave, per-channel gate). Input kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
-// of the front end. A workgroup covers NW * NCB * 16 dv columns of one (stream, head).
-#define GDN_CHUNK_INSTANCES(X)                   \
-    X(bf16, f16, 1, 128, 128, 8, 1, false)       \
-    X(bf16, f16, 1, 128, 128, 4, 2, false)       \
-    X(bf16, f16, 1, 128, 128, 4, 1, false)       \
-    X(f16, f16, 2, 128, 128, 8, 1, false)        \
-    X(f16, f16, 2, 128, 128, 4, 2, false)        \
-    X(f16, f16, 2, 128, 128, 4, 1, false)        \
-    X(bf16, f16, 1, 64, 64, 4, 1, false)         \
-    X(f16, f16, 2, 64, 64, 4, 1, false)          \
-    X(float, float, 0, 64, 64, 4, 1, false)      \
-    X(bf16, f16, 1, 128, 128, 8, 1, true)        \
-    X(bf16, f16, 1, 128, 128, 4, 1, true)        \
-    X(f16, f16, 2, 128, 128, 8, 1, true)         \
-    X(f16, f16, 2, 128, 128, 4, 1, true)         \
-    X(bf16, f16, 1, 64, 64, 4, 1, true)          \
-    X(f16, f16, 2, 64, 64, 4, 1, true)           \
-    X(float, float, 0, 64, 64, 4, 1, true)
+// per wave, per-channel gate, output gate fused). Input kind: 0 = f32 rows, 1 = bf16 rows,
+// 2 = fp16 activations of the front end. A workgroup covers NW * NCB * 16 dv columns of one
+// (stream, head). The default (widest) shapes that stage o also come with the output gate
+// fused into the o flush; the per-channel-gate instance at 128 columns does not stage o,
+// and gates o in a separate pass (gate_kernel).
+#define GDN_CHUNK_INSTANCES(X)                          \
+    X(bf16, f16, 1, 128, 128, 8, 1, false, false)       \
+    X(bf16, f16, 1, 128, 128, 4, 2, false, false)       \
+    X(bf16, f16, 1, 128, 128, 4, 1, false, false)       \
+    X(f16, f16, 2, 128, 128, 8, 1, false, false)        \
+    X(f16, f16, 2, 128, 128, 4, 2, false, false)        \
+    X(f16, f16, 2, 128, 128, 4, 1, false, false)        \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, false)         \
+    X(f16, f16, 2, 64, 64, 4, 1, false, false)          \
+    X(float, float, 0, 64, 64, 4, 1, false, false)      \
+    X(bf16, f16, 1, 128, 128, 8, 1, true, false)        \
+    X(bf16, f16, 1, 128, 128, 4, 1, true, false)        \
+    X(f16, f16, 2, 128, 128, 8, 1, true, false)         \
+    X(f16, f16, 2, 128, 128, 4, 1, true, false)         \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, false)          \
+    X(f16, f16, 2, 64, 64, 4, 1, true, false)           \
+    X(float, float, 0, 64, 64, 4, 1, true, false)       \
+    X(bf16, f16, 1, 128, 128, 8, 1, false, true)        \
+    X(f16, f16, 2, 128, 128, 8, 1, false, true)         \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, true)          \
+    X(f16, f16, 2, 64, 64, 4, 1, false, true)           \
+    X(float, float, 0, 64, 64, 4, 1, false, true)       \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, true)           \
+    X(f16, f16, 2, 64, 64, 4, 1, true, true)            \
+    X(float, float, 0, 64, 64, 4, 1, true, true)
 
-// nv: dv columns per workgroup; waves: 0 = the default for that width
-hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
+// nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
+// with the output gate fused
+hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
                         const ChunkArgs &a, int grid, hipStream_t s)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD)                                             \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G)                                          \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
-        (waves == 0 || waves == NW))                                                   \
-        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD>(a, grid, s);
+        (waves == 0 || waves == NW) && !gate == !G)                                    \
+        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD, G>(a, grid, s);
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves)
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD)                                             \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G)                                          \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
-        (waves == 0 || waves == NW))                                                   \
+        (waves == 0 || waves == NW) && !gate == !G)                                    \
         return 1;
     GDN_CHUNK_INSTANCES(X)
 #undef X

@@ -15,6 +15,7 @@ Layouts (all row-major, rows = tokens of every stream back to back):
 * ``conv_w``     [cd, K] f32 and ``conv_state`` [B, cd, K-1] in the dtype of ``x``
   (front end only).
 * ``cu_seqlens`` [B+1] int32.
+* ``z`` [alloc, H, dv] in the dtype of ``x`` and ``norm_w`` [dv] f32 (output gate only).
 
 ``alloc`` = round_up(N, chunk) + chunk rows; rows ``[N, alloc)`` of every per-token array
 hold ``pad_fill`` (0, NaN, 1e30, ...), so a kernel that read past a stream's end would
@@ -23,7 +24,7 @@ see it.
 Distributions (second parameter of N(.,.) is the standard deviation):
 q, k, v ~ N(0,1); conv weights ~ N(0, 0.5); carried conv state ~ N(0, 1);
 beta = sigmoid(N(0,1)); g = -softplus(N(0,1)) or Uniform(-0.5, -0.01);
-h0 = 0 or N(0, 0.1).
+h0 = 0 or N(0, 0.1); output gate: z ~ N(0, 1), norm_w ~ Uniform(0.5, 1.5).
 """
 from __future__ import annotations
 
@@ -55,6 +56,8 @@ class Spec:
     seed: int = 0
     pad_fill: float = 0.0
     eps: float = 1e-6
+    out_gate: bool = False            # gated RMSNorm of o with z (z, norm_w drawn last)
+    norm_eps: float = 1e-6
 
     @property
     def B(self) -> int:
@@ -138,6 +141,16 @@ def make(spec: Spec) -> dict:
         out["conv_w"] = None
         out["conv_state"] = None
 
+    if spec.out_gate:
+        z = torch.from_numpy(_normal(rng, (N, H, dv))).to(td)
+        zt = torch.full((alloc, H, dv), spec.pad_fill, dtype=td)
+        zt[:N] = z
+        out["z"] = zt
+        out["norm_w"] = torch.from_numpy(rng.uniform(0.5, 1.5, size=dv).astype(np.float32))
+    else:
+        out["z"] = None
+        out["norm_w"] = None
+
     cu = np.zeros(spec.B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(spec.lengths, dtype=np.int64))
     out["cu_seqlens"] = torch.from_numpy(cu)
@@ -150,7 +163,9 @@ def refill_tails(inp: dict, value: float) -> dict:
     res = dict(inp)
     res["spec"] = spec
     N = spec.N
-    for key in ("x", "g", "beta"):
+    for key in ("x", "g", "beta", "z"):
+        if inp.get(key) is None:
+            continue
         t = inp[key].clone()
         t[N:] = value
         res[key] = t

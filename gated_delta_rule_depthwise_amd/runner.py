@@ -45,12 +45,15 @@ class Prefill:
         self.cs_ptrs = None if self.conv_state is None else torch.tensor(
             [self.conv_state[b].data_ptr() for b in range(spec.B)], dtype=torch.int64,
             device=device)
+        self.z = None if inp.get("z") is None else inp["z"].to(device)
+        self.norm_w = None if inp.get("norm_w") is None else inp["norm_w"].to(device)
         self.params = B.params(
             spec.H, spec.dk, spec.dv, chunk=spec.chunk,
             eps=spec.eps if eps is None else eps,
             scale=spec.scale if scale is None else scale,
             dtype=B.GDN_BF16 if spec.dtype == "bf16" else B.GDN_F32,
-            conv_k=spec.conv_k if spec.front_end else 0, ld_qkv=spec.cd)
+            conv_k=spec.conv_k if spec.front_end else 0, ld_qkv=spec.cd,
+            z=self.z, norm_w=self.norm_w, norm_eps=spec.norm_eps)
         kind = {"single": B.GDN_KIND_SINGLE, "batched": B.GDN_KIND_BATCHED,
                 "varlen": B.GDN_KIND_VARLEN}[mode]
         self.kind = kind
@@ -120,6 +123,8 @@ class Decode:
             device=device)
         self.eps = spec.eps if eps is None else eps
         self.scale = spec.scale if scale is None else scale
+        self.z = None if inp.get("z") is None else inp["z"].to(device)
+        self.norm_w = None if inp.get("norm_w") is None else inp["norm_w"].to(device)
         self.params = self._params(spec.cd)
         es = self.x.element_size()
         base = self.x.data_ptr()
@@ -127,11 +132,13 @@ class Decode:
         self.k_ptr = base + spec.H * spec.dk * es
         self.v_ptr = base + 2 * spec.H * spec.dk * es
 
-    def _params(self, ld):
+    def _params(self, ld, z=None, ld_z=None):
         sp = self.spec
         return B.params(sp.H, sp.dk, sp.dv, chunk=sp.chunk, eps=self.eps, scale=self.scale,
                         dtype=B.GDN_BF16 if sp.dtype == "bf16" else B.GDN_F32,
-                        conv_k=sp.conv_k if sp.front_end else 0, ld_qkv=ld)
+                        conv_k=sp.conv_k if sp.front_end else 0, ld_qkv=ld,
+                        z=self.z if z is None else z, norm_w=self.norm_w, ld_z=ld_z,
+                        norm_eps=sp.norm_eps)
 
     def reset(self):
         """Restore the initial states (h, conv window)."""
@@ -152,9 +159,13 @@ class Decode:
     def step(self, x, t, T, g, beta, stream=None) -> int:
         """Decode token t of T per stream from prefill-layout rows: stream b's token is row
         b*T + t of ``x`` (a device tensor of packed rows; the row stride between streams
-        is T rows); ``g`` and ``beta`` hold this step's [B, H(, dk)] values."""
+        is T rows); ``g`` and ``beta`` hold this step's [B, H(, dk)] values. With the
+        output gate, ``self.z`` must hold the T rows per stream in the same layout."""
         sp = self.spec
         es = x.element_size()
         base = x.data_ptr() + t * sp.cd * es
-        return self._call(self._params(T * sp.cd), base, base + sp.H * sp.dk * es,
-                          base + 2 * sp.H * sp.dk * es, g, beta, stream)
+        # the output gate's z in the same prefill layout: stream b's row b*T + t
+        zp = None if self.z is None else self.z.data_ptr() + t * sp.H * sp.dv * es
+        p = self._params(T * sp.cd, zp, T * sp.H * sp.dv)
+        return self._call(p, base, base + sp.H * sp.dk * es, base + 2 * sp.H * sp.dk * es,
+                          g, beta, stream)

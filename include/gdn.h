@@ -74,6 +74,18 @@ typedef struct gdn_params {
     int32_t dtype;  /* GDN_F32 or GDN_BF16                                                */
     int32_t conv_k; /* 0: no front end; 2..4: causal depthwise conv taps + SiLU           */
     int64_t ld_qkv; /* row stride, in elements, of the q, k and v rows                    */
+    /* Optional output gate, the gated RMSNorm that opens the next phase (page
+     * "split_prefill.rs", prefill_phase3: gated RMSNorm of the GDN output with Z). With z
+     * non-NULL, every o row of every head leaves as
+     *     y = o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z),   silu(z) = z / (1+e^-z),
+     * the mean over that head's dv values, instead of o itself. Zero-initialise the struct
+     * (or set z = NULL) to leave o ungated.                                               */
+    const void *z;        /* DEVICE, rows like o: row r, head h at z + r*ld_z + h*dv, in
+                             dtype; 16-byte aligned. NULL = no gate.                       */
+    const float *norm_w;  /* DEVICE [dv] float weights shared by the heads, 16-byte aligned */
+    int64_t ld_z;         /* row stride of z in elements (>= H*dv, 16-byte multiple)       */
+    float norm_eps;       /* >= 0, finite                                                   */
+    int32_t reserved;     /* 0                                                              */
 } gdn_params;
 
 /*
@@ -207,6 +219,9 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
  *   GDN_PROF_FRONT  conv + SiLU + L2 kernel (front end calls only)
  *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan)
  *   GDN_PROF_STATE  the carried conv window update (front end calls only)
+ *   GDN_PROF_GATE   the output gate when it runs as its own pass (the per-key-channel gate
+ *                   at dk = dv = 128; elsewhere it is fused into the o flush of the chunk
+ *                   kernel or the decode kernel and nothing is recorded here)
  * gdn_profile_read waits for every recorded pair, writes the summed milliseconds and the
  * launch count of buckets 0..nbuckets-1, and forgets the records. Host pointers; events
  * are created once and reused. Enabling costs two event records per kernel.
@@ -214,7 +229,8 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
 #define GDN_PROF_FRONT 0
 #define GDN_PROF_RECUR 1
 #define GDN_PROF_STATE 2
-#define GDN_PROF_BUCKETS 3
+#define GDN_PROF_GATE 3
+#define GDN_PROF_BUCKETS 4
 int gdn_profile_enable(int on);
 int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 

@@ -49,14 +49,15 @@ def run_oracle(inp, heads=None, eps=None, scale=None, l2=None):
         scale=spec.scale if scale is None else scale, heads=heads)
 
 
-def compare(call, ref, heads=None, tol=None):
-    """Parity of o (real rows), every final h and the conv windows; returns the errors."""
+def compare(call, ref, heads=None, tol=None, o_metric=None):
+    """Parity of o (real rows), every final h and the conv windows; returns the errors.
+    ``o_metric(got, ref)`` replaces max|got - ref| / RMS(ref) for o."""
     spec = call.spec
     heads = list(range(spec.H)) if heads is None else list(heads)
     tol = TOL[spec.dtype] if tol is None else tol
     N = spec.N
     o = call.o[:N, heads].float().cpu().numpy()
-    e_o = rel_err(o, ref["o"])
+    e_o = (o_metric or rel_err)(o, ref["o"])
     h = call.h[:, heads].cpu().numpy()
     e_h = rel_err(h, ref["h"])
     assert e_o <= tol, "o error %.3g > %.3g" % (e_o, tol)

@@ -142,6 +142,35 @@ def test_decode_refusals():
     assert B.gdn_decode(pf, *args[:6], FAKE, None, FAKE, 2, None) == B.GDN_E_ARG
 
 
+def test_output_gate_refusals():
+    ok = dict(z=FAKE, norm_w=FAKE2)
+    p = B.params(2, 64, 64, dtype=B.GDN_F32, **ok)
+    assert _single(p, t=0) == B.GDN_E_ARG   # the usual checks still come first
+    for kw in (dict(norm_w=None), dict(z=FAKE + 4), dict(norm_w=FAKE2 + 4),
+               dict(ld_z=2 * 64 - 4), dict(ld_z=2 * 64 + 1), dict(norm_eps=-1.0),
+               dict(norm_eps=float("nan")), dict(norm_eps=float("inf"))):
+        args = dict(ok, **kw)
+        assert _single(B.params(2, 64, 64, dtype=B.GDN_F32, **args)) == B.GDN_E_ARG, kw
+        pd = B.params(2, 64, 64, dtype=B.GDN_F32, **args)
+        assert B.gdn_decode(pd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 2,
+                            None) == B.GDN_E_ARG, kw
+
+
 def test_params_struct_layout():
-    assert ctypes.sizeof(B.gdn_params) == 40
-    assert B.gdn_params.ld_qkv.offset == 32
+    """The ctypes struct matches include/gdn.h as a C compiler lays it out."""
+    import subprocess
+    import tempfile
+    fields = [f[0] for f in B.gdn_params._fields_]
+    prog = "#include <stddef.h>\n#include <stdio.h>\n#include \"gdn.h\"\nint main(void) {\n"
+    prog += '  printf("%zu\\n", sizeof(gdn_params));\n'
+    for f in fields:
+        prog += '  printf("%%zu\\n", offsetof(gdn_params, %s));\n' % f
+    prog += "  return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(B.gdn_params) == 72
+    assert out[1:] == [getattr(B.gdn_params, f).offset for f in fields]
