@@ -47,6 +47,12 @@ def kernel_hash(which: str = "prefill") -> str:
     return h.hexdigest()[:16]
 
 
+def gate_fused(spec) -> bool:
+    """The output gate rides in the chunk kernel's o flush except for the per-key-channel
+    instances at dk = dv = 128 and in fp32, which gate in a pass of their own."""
+    return not (spec.gate == "kda" and (spec.dk == 128 or spec.dtype == "f32"))
+
+
 def algorithmic_bytes(spec) -> dict:
     """Bytes each kernel must move per launch (inputs read once, outputs written once)."""
     N, H, dk, dv, B = spec.N, spec.H, spec.dk, spec.dv, spec.B
@@ -56,6 +62,12 @@ def algorithmic_bytes(spec) -> dict:
     state = 2 * B * H * dk * dv * 4  # h read + written
     chunk = N * cd * es + g_bytes + N * H * 4 + N * H * dv * 4 + state
     out = {"recur": chunk}
+    if spec.out_gate:
+        zw = N * H * dv * es + dv * 4  # z and the norm weights
+        if gate_fused(spec):
+            out["recur"] += zw
+        else:  # o read back and rewritten
+            out["gate"] = zw + 2 * N * H * dv * 4
     if spec.front_end:
         # front: raw rows in, activations out (same element size), taps, windows read
         out["front"] = 2 * N * cd * es + cd * spec.conv_k * 4 + B * cd * (spec.conv_k - 1) * es
@@ -70,6 +82,8 @@ def decode_bytes(spec) -> dict:
     es = 2 if spec.dtype == "bf16" else 4
     n = 2 * B * H * dk * dv * 4 + B * cd * es + B * H * (dk if spec.gate == "kda" else 1) * 4
     n += B * H * 4 + B * H * dv * 4
+    if spec.out_gate:
+        n += B * H * dv * es + dv * 4
     if spec.front_end:
         n += 2 * B * cd * (spec.conv_k - 1) * es + cd * spec.conv_k * 4
     return {"recur": n}
@@ -77,29 +91,32 @@ def decode_bytes(spec) -> dict:
 
 def cpu_baseline(spec, inp, budget_s: float) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload."""
-    import numpy as np
     import oracle
     H = spec.H
     cu = inp["cu_seqlens"].numpy()
+
+    def run(heads):
+        r = oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk,
+                           dv=spec.dv, cu_seqlens=cu, conv_w=inp["conv_w"],
+                           conv_state=inp["conv_state"], heads=heads)
+        if spec.out_gate:
+            oracle.gated_rmsnorm(r["o"], inp["z"][:spec.N][:, heads], inp["norm_w"],
+                                 spec.norm_eps)
+
     t0 = time.perf_counter()
-    oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk, dv=spec.dv,
-                   cu_seqlens=cu, conv_w=inp["conv_w"], conv_state=inp["conv_state"], heads=[0])
+    run([0])
     t1 = time.perf_counter() - t0
     n = int(max(1, min(H, math.floor(budget_s / max(t1, 1e-3)))))
     heads = list(range(n))
     t0 = time.perf_counter()
-    oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk, dv=spec.dv,
-                   cu_seqlens=cu, conv_w=inp["conv_w"], conv_state=inp["conv_state"],
-                   heads=heads)
+    run(heads)
     dt = time.perf_counter() - t0
     if n == H and dt < budget_s / 3:
         # a small workload (a decode batch): repeat the whole layer to fill the budget
         reps = int(min(1000, math.floor(budget_s / max(dt, 1e-3))))
         t0 = time.perf_counter()
         for _ in range(reps):
-            oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk,
-                           dv=spec.dv, cu_seqlens=cu, conv_w=inp["conv_w"],
-                           conv_state=inp["conv_state"])
+            run(heads)
         dt = (time.perf_counter() - t0) / reps
         return {"value": spec.N / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
                 "kind": "oracle",
@@ -124,6 +141,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--decode", choices=("gdn", "kda"), default=None,
                     help="time the decode step (64 streams, one token each) instead")
+    ap.add_argument("--gate", action="store_true",
+                    help="with the output gate (gated RMSNorm of o with z)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -135,15 +154,20 @@ def main() -> int:
     from gated_delta_rule_depthwise_amd import inputs
     from gated_delta_rule_depthwise_amd.runner import Decode, Prefill
 
+    import dataclasses
     dev = "cuda"
     if args.decode:
         spec = inputs.decode_config(64, gate=args.decode)
+        if args.gate:
+            spec = dataclasses.replace(spec, out_gate=True, name=spec.name + "-gated")
         inp = inputs.make(spec)
         first = Decode(inp, dev)
         per_copy = sum(t.numel() * t.element_size() for t in
                        (first.x, first.g, first.beta, first.o, first.h))
     else:
         spec = inputs.config(args.config)
+        if args.gate:
+            spec = dataclasses.replace(spec, out_gate=True, name=spec.name + "-gated")
         inp = inputs.make(spec)
         first = Prefill(inp, dev)
         per_copy = sum(t.numel() * t.element_size() for t in
@@ -184,7 +208,8 @@ def main() -> int:
     if not args.decode and first.kind != B.GDN_KIND_VARLEN:
         segs = B.gdn_segments(first.params, first.kind, spec.B, spec.N // spec.B,
                               first.ws_bytes)
-    names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state"}
+    names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state",
+             B.GDN_PROF_GATE: "gate"}
     avg_ms = {names[i]: ms[i] / launches[i] for i in names if launches[i]}
     dom = max(avg_ms, key=avg_ms.get)
     alg = decode_bytes(spec) if args.decode else algorithmic_bytes(spec)
@@ -221,7 +246,8 @@ def main() -> int:
         "data": "synthetic (seeded; distributions of the workload description)",
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
                    "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
-                   "front_end": spec.front_end, "input_copies_rotated": copies},
+                   "front_end": spec.front_end, "output_gate": spec.out_gate,
+                   "input_copies_rotated": copies},
         "roofline": {"bound": "hbm",
                      "kernel": kname,
                      "achieved": achieved,

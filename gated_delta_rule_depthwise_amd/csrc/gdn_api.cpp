@@ -286,8 +286,14 @@ int run(const Call &c)
     const int64_t BH = (int64_t)c.st.B * p->H;
     const Shape sh = pick_shape(p, c.kda, BH);
     // the output gate rides in the o flush where the instance stages o, else its own pass
-    const int fused = p->z && gdn::chunk_instance_exists(in_kind(p), p->dk, p->dv, c.kda,
-                                                         sh.nv, sh.waves, 1);
+    // (GDN_GATE_PASS=1, read once, forces the pass)
+    static const bool force_pass = [] {
+        const char *e = getenv("GDN_GATE_PASS");
+        return e && atoi(e) != 0;
+    }();
+    const int fused = p->z && !force_pass &&
+                      gdn::chunk_instance_exists(in_kind(p), p->dk, p->dv, c.kda, sh.nv,
+                                                 sh.waves, 1);
     const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;

@@ -661,7 +661,7 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
 
 constexpr int CH = 64;  // chunk length
 
-template <typename T, int DK, int DV, int NW, int NCB, bool KDA>
+template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false>
 struct ChunkCfg {
     static constexpr int NV = 16 * NW * NCB;  // dv columns per workgroup (16*NCB per wave)
     // fp16 operands: T = (I+M)^-1 and P are applied as fp16 hi + lo pairs, and the
@@ -698,7 +698,12 @@ struct ChunkCfg {
     static constexpr int OFF_O = OFF_G + 4 * CH * 4;
     // o is staged in LDS when it fits (not with the per-channel gate tile at 128 columns)
     static constexpr bool STAGE_O = OFF_O + CH * LDO * 4 <= 160 * 1024;
-    static constexpr int BYTES = OFF_O + (STAGE_O ? CH * LDO * 4 : 0);
+    // output gate: the z rows of a chunk (the caller's element type, as wide as T) and the
+    // norm weights of the NV columns
+    static constexpr int OFF_Z = OFF_O + (STAGE_O ? CH * LDO * 4 : 0);
+    static constexpr int ZROW = NV * (int)sizeof(T);
+    static constexpr int OFF_W = OFF_Z + (GATE ? CH * ZROW : 0);
+    static constexpr int BYTES = OFF_W + (GATE ? NV * 4 : 0);
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -885,7 +890,7 @@ __global__ void __launch_bounds__(NW * 64)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE>;
     // the output gate normalises whole o rows, which the staged o holds
     static_assert(!GATE || (C::STAGE_O && C::NV == DV), "output gate needs staged o rows");
     // z comes in the caller's element type (bf16 also when the operands are fp16)
@@ -1039,35 +1044,67 @@ __global__ void __launch_bounds__(NW * 64)
     // stage: vector loads and stores share one completion counter, so stores issued at the
     // end of a chunk would hold up the wait for the next chunk's rows. Full rows go out as
     // 16-byte stores.
-    // With the output gate, the z values of the staged rows and the norm weights of this
-    // lane's 4 columns are loaded at the end of the chunk that computes o, so their latency
-    // hides behind the barrier and the next chunk's first stages.
-    constexpr int V4 = NV / 4, RPP = NT / V4, NZ = GATE ? CH / RPP : 1;
-    static_assert(NT % V4 == 0 && CH % RPP == 0 && 64 % V4 == 0, "o row map");
-    typename Z4<TZ>::raw zr[NZ];
-    float4 wr = {0.f, 0.f, 0.f, 0.f};
+    // Output gate: the z rows of a chunk go straight from HBM into the z tile with LDS-DMA
+    // loads issued beside the next chunk's prefetch (no registers held; the chunk start's
+    // wait for the prefetch covers them); the flush of that chunk's o reads them from LDS.
+    // One 16-byte load per lane, LZ lanes per row: a wave's load k covers tile rows
+    // RL k .. RL k + RL - 1 (RL = 64 / LZ), lane l writing row RL k + l / LZ, bytes
+    // 16 (l % LZ) .. +15 of it.
+    constexpr int V4 = NV / 4, RPP = NT / V4, NR = CH / RPP;
+    static_assert(NT % V4 == 0 && CH % RPP == 0 && (V4 == 16 || V4 == 32), "o row map");
+    constexpr int LZ = C::ZROW / 16, RL = 64 / LZ;
+    static_assert(!GATE || ((LZ == 8 || LZ == 16) && (CH / RL) % NW == 0), "z tile map");
     const TZ *zg = GATE ? (const TZ *)a.z + head * DV : nullptr;
-    auto load_z = [&](int64_t c0, int Lc, int tid) {
-        const int j = tid % V4;
+    auto load_z = [&](int64_t c0, int Lc, int lane, int wave) {
+        typedef __attribute__((address_space(1))) void gptr;
+        typedef __attribute__((address_space(3))) void lptr;
+        constexpr int NZI = CH / RL / NW;  // loads per wave
 #pragma unroll
-        for (int it = 0; it < NZ; ++it) {
-            const int r = it * RPP + tid / V4;
-            zr[it] = r < Lc ? Z4<TZ>::load(zg + (c0 + r) * a.ld_z + 4 * j) : Z4<TZ>::zero();
-        }
-        wr = *reinterpret_cast<const float4 *>(a.norm_w + 4 * j);
-    };
-    auto flush_o = [&](const float *Os, int64_t c0, int Lc, int tid) {
-#pragma unroll
-        for (int it = 0; it < CH / RPP; ++it) {
-            const int r = it * RPP + tid / V4, j = tid % V4;
-            float4 o = *reinterpret_cast<const float4 *>(Os + r * LDO + 4 * j);
-            if constexpr (GATE) {  // every lane takes part in the row sums
-                const float ss =
-                    lane_group_sum<V4>(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
-                o = gate4(o, rsqrtf(ss * (1.f / DV) + a.norm_eps), wr, Z4<TZ>::get(zr[it]));
-            }
+        for (int i = 0; i < NZI; ++i) {
+            const int grp = wave * NZI + i, r = RL * grp + lane / LZ;
             if (r < Lc)
-                *reinterpret_cast<float4 *>(ob + (c0 + r) * (int64_t)H * DV + 4 * j) = o;
+                __builtin_amdgcn_global_load_lds(
+                    (gptr *)(zg + (c0 + r) * a.ld_z + (lane % LZ) * (16 / (int)sizeof(TZ))),
+                    (lptr *)(smem + C::OFF_Z + grp * RL * C::ZROW), 16, 0, 0);
+        }
+    };
+    if constexpr (GATE) {
+        for (int i = tid0; i < NV; i += NT)
+            ((float *)(smem + C::OFF_W))[i] = a.norm_w[i];
+    }
+    auto flush_o = [&](const float *Os, int64_t c0, int Lc, int tid) {
+        const int j = tid % V4;
+        float4 ov[NR];
+#pragma unroll
+        for (int it = 0; it < NR; ++it)
+            ov[it] = *reinterpret_cast<const float4 *>(Os + (it * RPP + tid / V4) * LDO + 4 * j);
+        if constexpr (GATE) {
+            // row sums of squares over the V4 lanes of each row (every lane takes part), the
+            // NR rows' reductions independent of each other
+            float ss[NR];
+#pragma unroll
+            for (int it = 0; it < NR; ++it) {
+                const float4 o = ov[it];
+                ss[it] = group_sum<16>(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+                if constexpr (V4 == 32)  // rows of 32 lanes: add the other 16 (swizzle xor 16)
+                    ss[it] += __int_as_float(
+                        __builtin_amdgcn_ds_swizzle(__float_as_int(ss[it]), 0x401F));
+            }
+            const float4 w = *reinterpret_cast<const float4 *>(smem + C::OFF_W + 16 * j);
+#pragma unroll
+            for (int it = 0; it < NR; ++it) {
+                const int r = it * RPP + tid / V4;
+                const typename Z4<TZ>::raw z = *reinterpret_cast<const typename Z4<TZ>::raw *>(
+                    smem + C::OFF_Z + r * C::ZROW + 4 * j * (int)sizeof(TZ));
+                ov[it] = gate4(ov[it], rsqrtf(ss[it] * (1.f / DV) + a.norm_eps), w,
+                               Z4<TZ>::get(z));
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NR; ++it) {
+            const int r = it * RPP + tid / V4;
+            if (r < Lc)
+                *reinterpret_cast<float4 *>(ob + (c0 + r) * (int64_t)H * DV + 4 * j) = ov[it];
         }
     };
 
@@ -1094,6 +1131,11 @@ __global__ void __launch_bounds__(NW * 64)
         float *ea = graw + 2 * CH;  // a_r = e^Gamma_r
         float *ed = graw + 3 * CH;  // a_C / a_r
         float *Os = (float *)(smem + zo + C::OFF_O);
+
+        // the previous chunk's z tile (LDS-DMA, counted like the prefetch loads) lands
+        // before the barrier that precedes its flush
+        if constexpr (GATE)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // ---- A: registers -> LDS: q, k (L2, scale), v, raw gates, beta -----------------
 #pragma unroll
@@ -1412,6 +1454,10 @@ __global__ void __launch_bounds__(NW * 64)
 
         if (cs + CH < end)
             prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH));
+        if constexpr (GATE) {
+            if (write_o)
+                load_z(cs, L, lane, wave);
+        }
 
         // ---- F: state products for this wave's 16*NCB columns -------------------------
         //   X = V - diag(a) K h,  U = T diag(beta) X,  O = diag(a) Q h + P U,
@@ -1543,10 +1589,10 @@ __global__ void __launch_bounds__(NW * 64)
                 }
             }
         }
-        if constexpr (GATE) {
-            if (write_o)
-                load_z(cs, L, tid);
-        }
+        __syncthreads();
+    }
+    if constexpr (GATE) {  // the last chunk's z tile: every wave's LDS-DMA loads landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
     if (C::STAGE_O && write_o && start < end) {  // the last chunk's o (loop ends on a barrier)
@@ -1569,7 +1615,7 @@ __global__ void __launch_bounds__(NW * 64)
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
     auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE>;
@@ -1589,8 +1635,9 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 // per wave, per-channel gate, output gate fused). Input kind: 0 = f32 rows, 1 = bf16 rows,
 // 2 = fp16 activations of the front end. A workgroup covers NW * NCB * 16 dv columns of one
 // (stream, head). The default (widest) shapes that stage o also come with the output gate
-// fused into the o flush; the per-channel-gate instance at 128 columns does not stage o,
-// and gates o in a separate pass (gate_kernel).
+// fused into the o flush, where o and the z tile fit in LDS; the per-channel-gate instances
+// at 128 columns (o not staged) and fp32 at 64 columns (no room for the z tile) gate o in
+// a separate pass (gate_kernel).
 #define GDN_CHUNK_INSTANCES(X)                          \
     X(bf16, f16, 1, 128, 128, 8, 1, false, false)       \
     X(bf16, f16, 1, 128, 128, 4, 2, false, false)       \
@@ -1614,8 +1661,7 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
     X(f16, f16, 2, 64, 64, 4, 1, false, true)           \
     X(float, float, 0, 64, 64, 4, 1, false, true)       \
     X(bf16, f16, 1, 64, 64, 4, 1, true, true)           \
-    X(f16, f16, 2, 64, 64, 4, 1, true, true)            \
-    X(float, float, 0, 64, 64, 4, 1, true, true)
+    X(f16, f16, 2, 64, 64, 4, 1, true, true)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
 // with the output gate fused

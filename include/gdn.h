@@ -220,8 +220,9 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
  *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan)
  *   GDN_PROF_STATE  the carried conv window update (front end calls only)
  *   GDN_PROF_GATE   the output gate when it runs as its own pass (the per-key-channel gate
- *                   at dk = dv = 128; elsewhere it is fused into the o flush of the chunk
- *                   kernel or the decode kernel and nothing is recorded here)
+ *                   at dk = dv = 128 or with float32 inputs; elsewhere it is fused into the
+ *                   o flush of the chunk kernel or the decode kernel and nothing is
+ *                   recorded here)
  * gdn_profile_read waits for every recorded pair, writes the summed milliseconds and the
  * launch count of buckets 0..nbuckets-1, and forgets the records. Host pointers; events
  * are created once and reused. Enabling costs two event records per kernel.

@@ -1,9 +1,10 @@
 """Parity of the output gate (gated RMSNorm of o with z) with the oracle.
 
 The reference output is the oracle's o passed through the oracle's gated RMSNorm. Where the
-chunk kernel stages whole o rows in LDS the gate runs in its o flush; the per-key-channel
-instance at dk = dv = 128 runs it as its own pass (gate_kernel); the decode kernel applies
-it to the row it finishes. Every kind is covered below.
+chunk kernel stages whole o rows and a z tile in LDS the gate runs in its o flush; the
+per-key-channel instances at dk = dv = 128 and in fp32 run it as its own pass
+(gate_kernel); the decode kernel applies it to the row it finishes. Every kind is covered
+below.
 """
 import dataclasses
 
@@ -81,9 +82,11 @@ def test_gated_prefill_matches_oracle(name):
 
 
 def test_gate_pass_only_where_o_is_not_staged():
-    """The per-key-channel instance at 128 columns gates in a pass of its own; the others
-    record nothing in that profile bucket."""
+    """The per-key-channel instances at 128 columns and in fp32 gate in a pass of their
+    own; the others record nothing in that profile bucket."""
     for base, kw, want in ((5, dict(lengths=[200], H=2), 1),
+                           (1, dict(lengths=[200], H=2, gate="kda"), 1),
+                           (1, dict(lengths=[200], H=2), 0),
                            (2, dict(lengths=[200], H=2), 0)):
         spec = spec_small(base, out_gate=True, seed=22, **kw)
         inp = inputs.make(spec)
