@@ -39,8 +39,10 @@ hipEvent_t take()
         pool.pop_back();
         return e;
     }
+    // timing only: no system-scope fence (cache write-back) when the event is recorded,
+    // which would add its own cost to the bracketed kernel
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
         return nullptr;
     return e;
 }
