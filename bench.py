@@ -98,7 +98,7 @@ def cpu_baseline(spec, inp, budget_s: float) -> dict:
     def run(heads):
         r = oracle.prefill(inp["x"], inp["g"], inp["beta"], inp["h0"], H=H, dk=spec.dk,
                            dv=spec.dv, cu_seqlens=cu, conv_w=inp["conv_w"],
-                           conv_state=inp["conv_state"], heads=heads)
+                           conv_state=inp["conv_state"], heads=heads, Hqk=spec.qk_heads)
         if spec.out_gate:
             oracle.gated_rmsnorm(r["o"], inp["z"][:spec.N][:, heads], inp["norm_w"],
                                  spec.norm_eps)
@@ -143,6 +143,8 @@ def main() -> int:
                     help="time the decode step (64 streams, one token each) instead")
     ap.add_argument("--gate", action="store_true",
                     help="with the output gate (gated RMSNorm of o with z)")
+    ap.add_argument("--qk-heads", type=int, default=0,
+                    help="q/k heads shared by the value heads (0 = as many as value heads)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -155,19 +157,24 @@ def main() -> int:
     from gated_delta_rule_depthwise_amd.runner import Decode, Prefill
 
     import dataclasses
-    dev = "cuda"
-    if args.decode:
-        spec = inputs.decode_config(64, gate=args.decode)
+
+    def variant(spec):
         if args.gate:
             spec = dataclasses.replace(spec, out_gate=True, name=spec.name + "-gated")
+        if args.qk_heads:
+            spec = dataclasses.replace(spec, Hqk=args.qk_heads,
+                                       name=spec.name + "-qk%d" % args.qk_heads)
+        return spec
+
+    dev = "cuda"
+    if args.decode:
+        spec = variant(inputs.decode_config(64, gate=args.decode))
         inp = inputs.make(spec)
         first = Decode(inp, dev)
         per_copy = sum(t.numel() * t.element_size() for t in
                        (first.x, first.g, first.beta, first.o, first.h))
     else:
-        spec = inputs.config(args.config)
-        if args.gate:
-            spec = dataclasses.replace(spec, out_gate=True, name=spec.name + "-gated")
+        spec = variant(inputs.config(args.config))
         inp = inputs.make(spec)
         first = Prefill(inp, dev)
         per_copy = sum(t.numel() * t.element_size() for t in
@@ -247,6 +254,7 @@ def main() -> int:
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
                    "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
                    "front_end": spec.front_end, "output_gate": spec.out_gate,
+                   "qk_heads": spec.qk_heads,
                    "input_copies_rotated": copies},
         "roofline": {"bound": "hbm",
                      "kernel": kname,

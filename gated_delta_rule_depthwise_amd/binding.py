@@ -43,7 +43,7 @@ class gdn_params(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("conv_k", ctypes.c_int32),
                 ("ld_qkv", ctypes.c_int64), ("z", ctypes.c_void_p),
                 ("norm_w", ctypes.c_void_p), ("ld_z", ctypes.c_int64),
-                ("norm_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("norm_eps", ctypes.c_float), ("Hqk", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -106,17 +106,18 @@ def _p(x):
 
 
 def params(H, dk, dv, chunk=64, eps=1e-6, scale=None, dtype=GDN_BF16, conv_k=0, ld_qkv=None,
-           z=None, norm_w=None, ld_z=None, norm_eps=1e-6):
-    """A gdn_params struct (ld_qkv defaults to the packed row 2*H*dk + H*dv; ld_z to H*dv).
-    ``z`` and ``norm_w`` (device tensors or pointers) turn the output gate on."""
+           z=None, norm_w=None, ld_z=None, norm_eps=1e-6, Hqk=0):
+    """A gdn_params struct (ld_qkv defaults to the packed row 2*Hqk*dk + H*dv; ld_z to
+    H*dv). ``z`` and ``norm_w`` (device tensors or pointers) turn the output gate on;
+    ``Hqk`` (0 = H) is the q/k head count."""
     if scale is None:
         scale = dk ** -0.5
     if ld_qkv is None:
-        ld_qkv = 2 * H * dk + H * dv
+        ld_qkv = 2 * (Hqk or H) * dk + H * dv
     if ld_z is None:
         ld_z = H * dv
     return gdn_params(H, dk, dv, chunk, eps, scale, dtype, conv_k, ld_qkv, _p(z), _p(norm_w),
-                      ld_z, norm_eps, 0)
+                      ld_z, norm_eps, Hqk)
 
 
 def gdn_prefill(p, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream):

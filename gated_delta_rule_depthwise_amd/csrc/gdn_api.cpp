@@ -82,9 +82,11 @@ int elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+int32_t qk_heads(const gdn_params *p) { return p->Hqk ? p->Hqk : p->H; }
+
 int64_t conv_dim(const gdn_params *p)
 {
-    return 2 * (int64_t)p->H * p->dk + (int64_t)p->H * p->dv;
+    return 2 * (int64_t)qk_heads(p) * p->dk + (int64_t)p->H * p->dv;
 }
 
 // input kind of the chunk kernel: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
@@ -132,6 +134,8 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_ARG;
     if (p->H < 1 || p->dk < 1 || p->dv < 1 || p->H > 4096)
         return GDN_E_ARG;
+    if (p->Hqk < 0 || p->Hqk > p->H || (p->Hqk && p->H % p->Hqk))
+        return GDN_E_ARG;
     if (!(p->eps == p->eps) || !(p->scale == p->scale))
         return GDN_E_ARG;
     if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
@@ -144,7 +148,7 @@ int check_params(const gdn_params *p, int kda)
     if (sh.nv == 0)
         return GDN_E_UNSUPPORTED;
     const int64_t vec = 16 / elem_bytes(p->dtype);
-    if (p->ld_qkv < (int64_t)p->H * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
+    if (p->ld_qkv < (int64_t)qk_heads(p) * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
         p->ld_qkv % vec != 0)
         return GDN_E_ARG;
     if (p->z) {  // output gate
@@ -316,6 +320,7 @@ int run(const Call &c)
     ca.o = (float *)c.o;
     ca.st = c.st;
     ca.H = p->H;
+    ca.qk_group = p->H / qk_heads(p);
     ca.eps = p->eps;
     if (fused) {
         ca.z = p->z;
@@ -332,7 +337,7 @@ int run(const Call &c)
         fa.y = c.ws;
         fa.st = c.st;
         fa.N = c.N;
-        fa.H = p->H, fa.dk = p->dk, fa.dv = p->dv, fa.K = p->conv_k;
+        fa.H = p->H, fa.Hqk = qk_heads(p), fa.dk = p->dk, fa.dv = p->dv, fa.K = p->conv_k;
         fa.do_l2 = p->eps >= 0.f;
         fa.eps = p->eps;
         fa.scale = p->scale;
@@ -353,8 +358,8 @@ int run(const Call &c)
         const size_t es = elem_bytes(p->dtype);
         char *y = (char *)c.ws;
         ca.q = y;
-        ca.k = y + (size_t)p->H * p->dk * es;
-        ca.v = y + (size_t)2 * p->H * p->dk * es;
+        ca.k = y + (size_t)qk_heads(p) * p->dk * es;
+        ca.v = y + (size_t)2 * qk_heads(p) * p->dk * es;
         ca.ld = conv_dim(p);
         ca.do_l2 = 0;
         ca.scale = 1.f;
@@ -550,7 +555,7 @@ int decode(const gdn_params *p, int kda, const void *q, const void *k, const voi
     a.g = g, a.beta = beta, a.h_ptrs = h_ptrs;
     a.conv_state_ptrs = conv_state_ptrs, a.conv_w = conv_w;
     a.o = (float *)o;
-    a.B = B, a.H = p->H, a.dk = p->dk, a.dv = p->dv, a.K = p->conv_k;
+    a.B = B, a.H = p->H, a.Hqk = qk_heads(p), a.dk = p->dk, a.dv = p->dv, a.K = p->conv_k;
     a.do_l2 = p->eps >= 0.f;
     a.eps = p->eps;
     a.scale = p->scale;
@@ -558,9 +563,13 @@ int decode(const gdn_params *p, int kda, const void *q, const void *k, const voi
     a.ld_z = p->ld_z;
     a.norm_w = p->norm_w;
     a.norm_eps = p->norm_eps;
-    // one fused launch: front end, recurrence step and window update
+    // one fused launch: front end, recurrence step and window update (plus a pass for the
+    // q/k windows when q/k heads are shared)
     Stage st(GDN_PROF_RECUR, (hipStream_t)stream);
     if (gdn::launch_decode(p->dtype, kda, a, (hipStream_t)stream) != hipSuccess)
+        return GDN_E_HIP;
+    if (front && a.Hqk != a.H &&
+        gdn::launch_decode_qk_window(p->dtype, a, (hipStream_t)stream) != hipSuccess)
         return GDN_E_HIP;
     st.done();
     return GDN_OK;

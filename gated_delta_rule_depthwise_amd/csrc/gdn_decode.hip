@@ -77,8 +77,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
     __shared__ __align__(16) float sq[DK], sk[DK], sv[DV], sa[DK];
     __shared__ float4 red[P][CPR];
 
-    const int H = a.H;
+    const int H = a.H, Hqk = a.Hqk;
     const int b = blockIdx.x / H, head = blockIdx.x - b * H;
+    const int head_qk = head / (H / Hqk);  // the q/k head this value head reads
+    // q/k windows are advanced here only when no other workgroup reads them (Hqk == H);
+    // otherwise by decode_qk_window_kernel after the step
+    const bool own_qk = Hqk == H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int jc = tid % CPR, p = tid / CPR;
     float *hp = a.h_ptrs[b] + (int64_t)head * DK * DV + 4 * jc;
@@ -102,12 +106,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
         const int sec = c < DK ? 0 : c < 2 * DK ? 1 : 2;
         const int e = sec == 0 ? c : sec == 1 ? c - DK : c - 2 * DK;
         const T *src = (const T *)(sec == 0 ? a.q : sec == 1 ? a.k : a.v);
-        const int64_t col = (int64_t)head * (sec == 2 ? DV : DK) + e;
+        const int64_t col = sec == 2 ? (int64_t)head * DV + e : (int64_t)head_qk * DK + e;
         const T raw = src[(int64_t)b * a.ld + col];
         float x = to_float(raw);
         if constexpr (K > 0) {
             const int64_t ch =
-                (sec == 0 ? 0 : sec == 1 ? (int64_t)H * DK : 2 * (int64_t)H * DK) + col;
+                (sec == 0 ? 0 : sec == 1 ? (int64_t)Hqk * DK : 2 * (int64_t)Hqk * DK) + col;
             T *win = (T *)a.conv_state_ptrs[b] + ch * W;
             const float *w = a.conv_w + ch * K;
             float acc = w[K - 1] * x;
@@ -118,10 +122,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_kernel(const DecodeArgs a)
                 acc += w[i] * to_float(old[i]);
             }
             // the window keeps the last K-1 raw inputs, oldest first
+            if (sec == 2 || own_qk) {
 #pragma unroll
-            for (int i = 0; i + 1 < W; ++i)
-                win[i] = old[i + 1];
-            win[W - 1] = raw;
+                for (int i = 0; i + 1 < W; ++i)
+                    win[i] = old[i + 1];
+                win[W - 1] = raw;
+            }
             x = silu(acc);
         }
         (sec == 0 ? sq : sec == 1 ? sk : sv)[e] = x;
@@ -229,7 +235,50 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+// The q/k windows of a step whose q/k heads serve several value heads: every reader has
+// finished (the decode kernel ran before on the same stream). One thread per (stream,
+// q/k channel).
+template <typename T, int K>
+__global__ void __launch_bounds__(256) decode_qk_window_kernel(const DecodeArgs a)
+{
+    constexpr int W = K - 1;
+    const int nqk = 2 * a.Hqk * a.dk;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.B * nqk)
+        return;
+    const int b = (int)(idx / nqk), c = (int)(idx - (int64_t)b * nqk);
+    const int qk = a.Hqk * a.dk;
+    const T *src = c < qk ? (const T *)a.q + c : (const T *)a.k + (c - qk);
+    T *win = (T *)a.conv_state_ptrs[b] + (int64_t)c * W;
+    T old[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        old[i] = win[i];
+#pragma unroll
+    for (int i = 0; i + 1 < W; ++i)
+        win[i] = old[i + 1];
+    win[W - 1] = src[(int64_t)b * a.ld];
+}
+
+template <typename T>
+hipError_t launch_qk_window_t(const DecodeArgs &a, hipStream_t s)
+{
+    const unsigned g = (unsigned)(((int64_t)a.B * 2 * a.Hqk * a.dk + 255) / 256);
+    switch (a.K) {
+    case 2: hipLaunchKernelGGL((decode_qk_window_kernel<T, 2>), dim3(g), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_qk_window_kernel<T, 3>), dim3(g), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_qk_window_kernel<T, 4>), dim3(g), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_qk_window(int dtype, const DecodeArgs &a, hipStream_t s)
+{
+    return dtype ? launch_qk_window_t<bf16>(a, s) : launch_qk_window_t<float>(a, s);
+}
 
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s)
 {

@@ -16,15 +16,16 @@ struct Streams {
 
 // Fused chunk kernel: per (stream, head, dv slice), every chunk of the stream in order.
 struct ChunkArgs {
-    const void *q, *k, *v;  // row r of head h: q + r*ld + h*dk (k likewise, v + h*dv)
-    int64_t ld;
+    const void *q, *k, *v;  // row r, value head h: q + r*ld + (h/qk_group)*dk (k likewise),
+    int64_t ld;             // v + r*ld + h*dv
     const float *g;         // [N][H] or [N][H][dk]
     const float *beta;      // [N][H]
     float *h;               // single state [H][dk][dv] (when h_ptrs == nullptr)
     float *const *h_ptrs;   // per-stream states
     float *o;               // [N][H][dv]
     Streams st;
-    int32_t H;
+    int32_t H;              // value heads (the grid and the states)
+    int32_t qk_group;       // value heads per q/k head (H / Hqk)
     int32_t do_l2;          // normalise q and k rows on load
     float eps;
     float scale;            // multiplies q on load
@@ -93,7 +94,7 @@ struct FrontArgs {
     void *y;                // out: [N][cd] packed activations (fp16 for bf16 rows), stride cd
     Streams st;
     int64_t N;
-    int32_t H, dk, dv, K;
+    int32_t H, Hqk, dk, dv, K;  // cd = 2*Hqk*dk + H*dv
     int32_t do_l2;
     float eps, scale;
     int32_t tile_rows;      // tokens per workgroup tile: a multiple of 4, >= 32
@@ -110,7 +111,7 @@ struct DecodeArgs {
     void *const *conv_state_ptrs;    // per-stream [cd][K-1] (K > 0)
     const float *conv_w;             // [cd][K] (K > 0)
     float *o;                        // [B][H][dv]
-    int32_t B, H, dk, dv, K;
+    int32_t B, H, Hqk, dk, dv, K;    // value head h reads q/k head h / (H / Hqk)
     int32_t do_l2;
     float eps, scale;
     const void *z;                   // output gate (nullptr: off): row b at z + b*ld_z
@@ -134,6 +135,9 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
+// q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after
+// the step by a pass of its own
+hipError_t launch_decode_qk_window(int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
 // 1 if the (in_kind, dk, dv, kda, nv, waves, gate) instance exists.

@@ -340,11 +340,11 @@ template <typename T, typename TOUT, int K>
 __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
 {
     constexpr int W = K - 1;
-    const int cd = 2 * a.H * a.dk + a.H * a.dv;
+    const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
     const int cg = blockIdx.x * FRONT_THREADS + threadIdx.x;  // channel group
     const int c0 = cg * FRONT_CPT;                              // first packed channel
     const bool active = c0 < cd;
-    const int qk = a.H * a.dk;
+    const int qk = a.Hqk * a.dk;
     const int sec = !active ? 2 : (c0 < qk ? 0 : (c0 < 2 * qk ? 1 : 2));
     const T *src = sec == 0 ? (const T *)a.q + c0
                  : sec == 1 ? (const T *)a.k + (c0 - qk)
@@ -493,7 +493,7 @@ template <typename T, int K>
 __global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
 {
     constexpr int W = K - 1;
-    const int cd = 2 * a.H * a.dk + a.H * a.dv;
+    const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)a.st.B * cd)
         return;
@@ -504,7 +504,7 @@ __global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
     if (len <= 0)
         return;
     T *cs = a.conv_state_ptrs ? (T *)a.conv_state_ptrs[b] : (T *)a.conv_state;
-    const int qk = a.H * a.dk;
+    const int qk = a.Hqk * a.dk;
     const T *src = c < qk ? (const T *)a.q + c
                  : c < 2 * qk ? (const T *)a.k + (c - qk)
                               : (const T *)a.v + (c - 2 * qk);
@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
 template <typename T, typename TOUT, int K>
 hipError_t launch_front_tk(const FrontArgs &a, hipStream_t s)
 {
-    const int cd = 2 * a.H * a.dk + a.H * a.dv;
+    const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
     const int groups = cd / FRONT_CPT;
     if (a.tile_rows < FRONT_ROWS || a.tile_rows % 4)
         return hipErrorInvalidValue;
@@ -543,7 +543,7 @@ hipError_t launch_front_tk(const FrontArgs &a, hipStream_t s)
 template <typename T, int K>
 hipError_t launch_state_tk(const FrontArgs &a, hipStream_t s)
 {
-    const int cd = 2 * a.H * a.dk + a.H * a.dv;
+    const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
     const int64_t n = (int64_t)a.st.B * cd;
     hipLaunchKernelGGL((conv_state_kernel<T, K>), dim3((unsigned)((n + 255) / 256)), dim3(256),
                        0, s, a);
@@ -676,6 +676,7 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
 // fused chunk kernel
 
 constexpr int CH = 64;  // chunk length
+
 
 template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false>
 struct ChunkCfg {
@@ -969,8 +970,9 @@ __global__ void __launch_bounds__(NW * 64)
     const int64_t hoff = (int64_t)head * DK * DV;
     const int colw = slice * NV + wave0 * 16 * NCB;  // this wave's first dv column
 
-    const TIN *qg = (const TIN *)a.q + head * DK;
-    const TIN *kg = (const TIN *)a.k + head * DK;
+    const int head_qk = head / a.qk_group;  // the q/k head this value head reads
+    const TIN *qg = (const TIN *)a.q + head_qk * DK;
+    const TIN *kg = (const TIN *)a.k + head_qk * DK;
     const TIN *vg = (const TIN *)a.v + head * DV + slice * NV;
     float *ob = a.o + head * DV + slice * NV;  // this workgroup's o columns
     const int64_t ld = a.ld;
@@ -1586,7 +1588,13 @@ __global__ void __launch_bounds__(NW * 64)
                     for (int i = 0; i < 4; ++i)
                         u[I][i] *= dr[I][i];
             }
-            const frag vf0 = pack<T>(u[0], u[1]), vf1 = pack<T>(u[2], u[3]);
+            // U as an fp16 hi + lo pair here too: the state accumulates these products over
+            // the whole stream, and heavy-tailed states (max/RMS ~ 50) need U beyond fp16
+            // (a single fp16 U left err(h) at 3.3% on such a state; the pair: 1.8%, for
+            // 2-4% more time per chunk)
+            frag vf0, vf1, vl0, vl1;
+            pack_split<T>(u[0], u[1], vf0, vl0);
+            pack_split<T>(u[2], u[3], vf1, vl1);
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb) {
                 if constexpr (KDA) {
@@ -1594,14 +1602,19 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         hs[cb][mb][i] *= __expf(gcr[i]);
-                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kd, 0, 16 * mb, lane), vf0);
-                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kd, 32, 16 * mb, lane), vf1);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         hs[cb][mb][i] *= aC;
-                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Ks, 0, 16 * mb, lane), vf0);
-                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Ks, 32, 16 * mb, lane), vf1);
+                }
+                const T *Kt = KDA ? Kd : Ks;
+                const frag k0 = ld_frag_t_qk<DK>(Kt, 0, 16 * mb, lane);
+                const frag k1 = ld_frag_t_qk<DK>(Kt, 32, 16 * mb, lane);
+                mma(hs[cb][mb], k0, vf0);
+                mma(hs[cb][mb], k1, vf1);
+                if constexpr (SPLIT) {
+                    mma(hs[cb][mb], k0, vl0);
+                    mma(hs[cb][mb], k1, vl1);
                 }
             }
         }

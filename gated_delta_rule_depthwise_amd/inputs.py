@@ -7,8 +7,9 @@ rounded to bfloat16 by torch (round to nearest even).
 
 Layouts (all row-major, rows = tokens of every stream back to back):
 
-* ``x``          [alloc, 2*H*dk + H*dv]  packed ``[q | k | v]`` rows (raw conv input when
-  the front end is on, otherwise q, k, v themselves), dtype f32 or bf16.
+* ``x``          [alloc, 2*Hqk*dk + H*dv]  packed ``[q | k | v]`` rows (raw conv input
+  when the front end is on, otherwise q, k, v themselves), dtype f32 or bf16; Hqk = H
+  unless the spec sets fewer q/k heads.
 * ``g``          [alloc, H] (GDN, one log-gate per head) or [alloc, H, dk] (KDA), f32.
 * ``beta``       [alloc, H] f32, already through the sigmoid.
 * ``h0``         [B, H, dk, dv] f32 initial state per stream.
@@ -58,6 +59,7 @@ class Spec:
     eps: float = 1e-6
     out_gate: bool = False            # gated RMSNorm of o with z (z, norm_w drawn last)
     norm_eps: float = 1e-6
+    Hqk: int = 0                      # q/k heads (0 = H); value head h reads h // (H // Hqk)
 
     @property
     def B(self) -> int:
@@ -68,8 +70,12 @@ class Spec:
         return int(sum(self.lengths))
 
     @property
+    def qk_heads(self) -> int:
+        return self.Hqk or self.H
+
+    @property
     def cd(self) -> int:
-        return 2 * self.H * self.dk + self.H * self.dv
+        return 2 * self.qk_heads * self.dk + self.H * self.dv
 
     @property
     def alloc(self) -> int:

@@ -53,7 +53,7 @@ class Prefill:
             scale=spec.scale if scale is None else scale,
             dtype=B.GDN_BF16 if spec.dtype == "bf16" else B.GDN_F32,
             conv_k=spec.conv_k if spec.front_end else 0, ld_qkv=spec.cd,
-            z=self.z, norm_w=self.norm_w, norm_eps=spec.norm_eps)
+            z=self.z, norm_w=self.norm_w, norm_eps=spec.norm_eps, Hqk=spec.Hqk)
         kind = {"single": B.GDN_KIND_SINGLE, "batched": B.GDN_KIND_BATCHED,
                 "varlen": B.GDN_KIND_VARLEN}[mode]
         self.kind = kind
@@ -65,8 +65,8 @@ class Prefill:
         es = self.x.element_size()
         base = self.x.data_ptr()
         self.q_ptr = base
-        self.k_ptr = base + spec.H * spec.dk * es
-        self.v_ptr = base + 2 * spec.H * spec.dk * es
+        self.k_ptr = base + spec.qk_heads * spec.dk * es
+        self.v_ptr = base + 2 * spec.qk_heads * spec.dk * es
 
     def reset(self):
         """Restore the initial states (h, conv window)."""
@@ -129,8 +129,8 @@ class Decode:
         es = self.x.element_size()
         base = self.x.data_ptr()
         self.q_ptr = base
-        self.k_ptr = base + spec.H * spec.dk * es
-        self.v_ptr = base + 2 * spec.H * spec.dk * es
+        self.k_ptr = base + spec.qk_heads * spec.dk * es
+        self.v_ptr = base + 2 * spec.qk_heads * spec.dk * es
 
     def _params(self, ld, z=None, ld_z=None):
         sp = self.spec
@@ -138,7 +138,7 @@ class Decode:
                         dtype=B.GDN_BF16 if sp.dtype == "bf16" else B.GDN_F32,
                         conv_k=sp.conv_k if sp.front_end else 0, ld_qkv=ld,
                         z=self.z if z is None else z, norm_w=self.norm_w, ld_z=ld_z,
-                        norm_eps=sp.norm_eps)
+                        norm_eps=sp.norm_eps, Hqk=sp.Hqk)
 
     def reset(self):
         """Restore the initial states (h, conv window)."""
@@ -167,5 +167,5 @@ class Decode:
         # the output gate's z in the same prefill layout: stream b's row b*T + t
         zp = None if self.z is None else self.z.data_ptr() + t * sp.H * sp.dv * es
         p = self._params(T * sp.cd, zp, T * sp.H * sp.dv)
-        return self._call(p, base, base + sp.H * sp.dk * es, base + 2 * sp.H * sp.dk * es,
-                          g, beta, stream)
+        return self._call(p, base, base + sp.qk_heads * sp.dk * es,
+                          base + 2 * sp.qk_heads * sp.dk * es, g, beta, stream)

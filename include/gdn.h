@@ -65,7 +65,7 @@ extern "C" {
 #define GDN_KIND_VARLEN 2
 
 typedef struct gdn_params {
-    int32_t H;      /* heads (q, k and v share the head count)                            */
+    int32_t H;      /* value heads: g, beta, o and the states have H heads (see Hqk)      */
     int32_t dk;     /* key head dim: 64 or 128                                            */
     int32_t dv;     /* value head dim: 64 or 128                                          */
     int32_t chunk;  /* tokens per chunk: 64                                               */
@@ -85,7 +85,11 @@ typedef struct gdn_params {
     const float *norm_w;  /* DEVICE [dv] float weights shared by the heads, 16-byte aligned */
     int64_t ld_z;         /* row stride of z in elements (>= H*dv, 16-byte multiple)       */
     float norm_eps;       /* >= 0, finite                                                   */
-    int32_t reserved;     /* 0                                                              */
+    /* q/k heads (0 = H). With 0 < Hqk < H, H must be a multiple of Hqk and each q/k head
+     * serves H/Hqk consecutive value heads: value head h reads q/k head h / (H/Hqk). The
+     * packed rows are then [q (Hqk*dk) | k (Hqk*dk) | v (H*dv)], cd = 2*Hqk*dk + H*dv,
+     * and the conv channels of q/k head j are j*dk + c and Hqk*dk + j*dk + c.            */
+    int32_t Hqk;
 } gdn_params;
 
 /*
@@ -96,7 +100,8 @@ typedef struct gdn_params {
  *   q, k, v   row i of q is q + i*ld_qkv, head h at offset h*dk (k likewise, v at h*dv).
  *             With the front end on, these are the raw conv inputs of the packed row
  *             [q | k | v]: the conv channel of q element (h, c) is h*dk + c, of k element
- *             H*dk + h*dk + c, of v element 2*H*dk + h*dv + c (cd = 2*H*dk + H*dv).
+ *             H*dk + h*dk + c, of v element 2*H*dk + h*dv + c (cd = 2*H*dk + H*dv), with
+ *             Hqk in place of H for q and k when p->Hqk is set.
  *   g         [t][H] float log-gates (kda_prefill: [t][H][dk], one per key channel).
  *   beta      [t][H] float, used as given.
  *   h         [H][dk][dv] float state, in/out.

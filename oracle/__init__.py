@@ -177,8 +177,11 @@ def gated_rmsnorm(o, z, w, eps=1e-6):
 
 
 def prefill(x, g, beta, h0, *, H, dk, dv, cu_seqlens=None, conv_w=None, conv_state=None,
-            l2=True, eps=1e-6, scale=None, heads=None):
-    """The whole path over packed rows ``x = [q (H*dk) | k (H*dk) | v (H*dv)]``.
+            l2=True, eps=1e-6, scale=None, heads=None, Hqk=None):
+    """The whole path over packed rows ``x = [q (Hqk*dk) | k (Hqk*dk) | v (H*dv)]``.
+
+    Hqk (default H) q/k heads; value head h reads q/k head h // (H // Hqk) (each q/k head
+    serves H // Hqk consecutive value heads). g, beta, h0 and the outputs have H heads.
 
     x: [>=N, 2*H*dk + H*dv] (rows at or past cu_seqlens[-1] are never read);
     g: [>=N, H] or [>=N, H, dk]; beta: [>=N, H]; h0: [B, H, dk, dv].
@@ -186,17 +189,21 @@ def prefill(x, g, beta, h0, *, H, dk, dv, cu_seqlens=None, conv_w=None, conv_sta
     heads: optional list of heads to evaluate (each head is independent of the others;
     the conv is depthwise, so only that head's channels are read).
     Returns dict(o [N, Hs, dv], h [B, Hs, dk, dv], conv_state [B, Hs*(2dk+dv) channels in
-    q|k|v order, K-1] or None, channels) for the selected heads Hs.
+    q|k|v order, K-1] or None, channels) for the selected heads Hs (a q/k head shared by
+    several selected value heads appears once per value head).
     """
     cu = np.asarray([0, x.shape[0]] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
     N = int(cu[-1])
     B = cu.size - 1
     heads = list(range(H)) if heads is None else [int(hh) for hh in heads]
     Hs = len(heads)
+    Hqk = H if Hqk is None else int(Hqk)
+    assert 1 <= Hqk <= H and H % Hqk == 0
+    grp = H // Hqk
     cols = np.concatenate(
-        [np.arange(hh * dk, (hh + 1) * dk) for hh in heads]
-        + [H * dk + np.arange(hh * dk, (hh + 1) * dk) for hh in heads]
-        + [2 * H * dk + np.arange(hh * dv, (hh + 1) * dv) for hh in heads]).astype(np.int64)
+        [np.arange((hh // grp) * dk, (hh // grp + 1) * dk) for hh in heads]
+        + [Hqk * dk + np.arange((hh // grp) * dk, (hh // grp + 1) * dk) for hh in heads]
+        + [2 * Hqk * dk + np.arange(hh * dv, (hh + 1) * dv) for hh in heads]).astype(np.int64)
     if hasattr(x, "detach"):
         import torch
         xs = _f64(x[:N].index_select(1, torch.as_tensor(cols)))

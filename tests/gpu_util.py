@@ -46,7 +46,7 @@ def run_oracle(inp, heads=None, eps=None, scale=None, l2=None):
         inp["x"], inp["g"], inp["beta"], inp["h0"], H=spec.H, dk=spec.dk, dv=spec.dv,
         cu_seqlens=inp["cu_seqlens"].numpy(), conv_w=inp["conv_w"],
         conv_state=inp["conv_state"], l2=(eps >= 0) if l2 is None else l2, eps=max(eps, 0.0),
-        scale=spec.scale if scale is None else scale, heads=heads)
+        scale=spec.scale if scale is None else scale, heads=heads, Hqk=spec.qk_heads)
 
 
 def compare(call, ref, heads=None, tol=None, o_metric=None):

@@ -156,6 +156,19 @@ def test_output_gate_refusals():
                             None) == B.GDN_E_ARG, kw
 
 
+def test_shared_qk_head_refusals():
+    for H, Hqk in ((4, -1), (4, 5), (6, 4)):
+        p = B.params(H, 64, 64, dtype=B.GDN_F32, Hqk=Hqk, ld_qkv=2 * H * 64 + H * 64)
+        assert _single(p) == B.GDN_E_ARG, (H, Hqk)
+        assert B.gdn_decode(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 2,
+                            None) == B.GDN_E_ARG
+    # the packed row of 2 q/k heads and 4 value heads is 2*2*64 + 4*64 wide
+    p = B.params(4, 64, 64, dtype=B.GDN_F32, Hqk=2)
+    assert p.ld_qkv == 2 * 2 * 64 + 4 * 64
+    assert B.gdn_workspace_bytes(B.params(4, 64, 64, conv_k=4, Hqk=2), 1, 10,
+                                 B.GDN_KIND_VARLEN) == (10 * 512 * 2 + 255) // 256 * 256
+
+
 def test_params_struct_layout():
     """The ctypes struct matches include/gdn.h as a C compiler lays it out."""
     import subprocess

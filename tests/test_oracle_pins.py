@@ -228,6 +228,51 @@ def test_conv_split_equals_one_shot():
 
 
 # ---------------------------------------------------------------------------------------
+# shared q/k heads
+
+
+@pytest.mark.parametrize("front", [False, True])
+def test_shared_qk_heads_equal_repeated_heads(front):
+    """Hqk q/k heads serving H value heads (value head h reads q/k head h // (H/Hqk)) give
+    exactly the results of H heads whose q/k columns, conv taps and windows are the
+    q/k head's, repeated in place for each value head it serves."""
+    rng = np.random.default_rng(41)
+    T, H, Hqk, dk, dv, K = 9, 6, 2, 4, 3, 4
+    grp = H // Hqk
+    cd_s, cd_f = 2 * Hqk * dk + H * dv, 2 * H * dk + H * dv
+    x = rng.standard_normal((T, cd_s))
+    g = -np.logaddexp(0.0, rng.standard_normal((T, H)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))
+    h0 = 0.3 * rng.standard_normal((1, H, dk, dv))
+    # full layout: channel list of the shared layout for every channel of the full one
+    src = np.concatenate(
+        [np.arange((h // grp) * dk, (h // grp + 1) * dk) for h in range(H)]
+        + [Hqk * dk + np.arange((h // grp) * dk, (h // grp + 1) * dk) for h in range(H)]
+        + [2 * Hqk * dk + np.arange(h * dv, (h + 1) * dv) for h in range(H)])
+    assert src.size == cd_f
+    kw, kf = {}, {}
+    if front:
+        w = rng.standard_normal((cd_s, K))
+        st = rng.standard_normal((1, cd_s, K - 1))
+        kw = dict(conv_w=w, conv_state=st)
+        kf = dict(conv_w=w[src], conv_state=st[:, src])
+    shared = oracle.prefill(x, g, beta, h0, H=H, dk=dk, dv=dv, Hqk=Hqk, **kw)
+    full = oracle.prefill(x[:, src], g, beta, h0, H=H, dk=dk, dv=dv, **kf)
+    np.testing.assert_array_equal(shared["o"], full["o"])
+    np.testing.assert_array_equal(shared["h"], full["h"])
+    if front:
+        np.testing.assert_array_equal(shared["conv_state"], full["conv_state"])
+    # the grouping is seen: value heads that read q/k head h % Hqk instead differ
+    alt = np.concatenate(
+        [np.arange((h % Hqk) * dk, (h % Hqk + 1) * dk) for h in range(H)]
+        + [Hqk * dk + np.arange((h % Hqk) * dk, (h % Hqk + 1) * dk) for h in range(H)]
+        + [2 * Hqk * dk + np.arange(h * dv, (h + 1) * dv) for h in range(H)])
+    ka = dict(conv_w=kw["conv_w"][alt], conv_state=kw["conv_state"][:, alt]) if front else {}
+    other = oracle.prefill(x[:, alt], g, beta, h0, H=H, dk=dk, dv=dv, **ka)
+    assert np.abs(other["o"] - shared["o"]).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------------------
 # output gate (gated RMSNorm)
 
 
