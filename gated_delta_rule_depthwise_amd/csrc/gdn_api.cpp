@@ -113,8 +113,7 @@ Shape pick_shape(const gdn_params *p, int kda, int64_t BH)
         e = getenv("GDN_WAVES");
         fwaves = e ? atoi(e) : 0;
     }
-    // the output gate needs whole o rows per workgroup: the overrides do not apply
-    if (!p->z && fcols > 0 && p->dv % fcols == 0 &&
+    if (fcols > 0 && p->dv % fcols == 0 &&
         gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves, 0))
         return Shape{fcols, fwaves};
     // The widest instance: one workgroup per (stream, head) computes the chunk
@@ -151,8 +150,8 @@ int check_params(const gdn_params *p, int kda)
     if (p->ld_qkv < (int64_t)qk_heads(p) * p->dk || p->ld_qkv < (int64_t)p->H * p->dv ||
         p->ld_qkv % vec != 0)
         return GDN_E_ARG;
-    if (p->z) {  // output gate
-        if (sh.nv != p->dv)
+    if (p->z) {  // output gate (fused, or a separate pass over o rows of dv 64/128/256)
+        if (p->dv != 64 && p->dv != 128 && p->dv != 256)
             return GDN_E_UNSUPPORTED;
         if (!p->norm_w || !aligned16(p->z) || !aligned16(p->norm_w) ||
             p->ld_z < (int64_t)p->H * p->dv || p->ld_z % vec != 0 ||
@@ -539,7 +538,7 @@ int decode(const gdn_params *p, int kda, const void *q, const void *k, const voi
     int rc = check_params(p, kda);
     if (rc != GDN_OK)
         return rc;
-    if (p->dk != p->dv || (p->dk != 64 && p->dk != 128))
+    if (!((p->dk == 64 || p->dk == 128) && (p->dv == p->dk || p->dv == 2 * p->dk)))
         return GDN_E_UNSUPPORTED;
     if (B < 1 || (int64_t)B * p->H > (int64_t)INT32_MAX)
         return GDN_E_ARG;

@@ -232,6 +232,10 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s)
         return launch_dk<T, 128, 128, KDA>(a, s);
     if (a.dk == 64 && a.dv == 64)
         return launch_dk<T, 64, 64, KDA>(a, s);
+    if (a.dk == 128 && a.dv == 256)
+        return launch_dk<T, 128, 256, KDA>(a, s);
+    if (a.dk == 64 && a.dv == 128)
+        return launch_dk<T, 64, 128, KDA>(a, s);
     return hipErrorInvalidValue;
 }
 

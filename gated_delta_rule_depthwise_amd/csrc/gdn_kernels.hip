@@ -631,7 +631,8 @@ __device__ __forceinline__ float lane_group_sum(float x)
 }
 
 // Separate pass for instances that cannot stage whole o rows: rows [0, N) x H heads of o
-// gated in place. One 32- or 16-lane group per (row, head), 4 values per lane.
+// gated in place. One group of dv/4 lanes (16, 32 or a wave) per (row, head), 4 values
+// per lane.
 template <typename TZ, int DV>
 __global__ void __launch_bounds__(256) gate_kernel(const GateArgs a)
 {
@@ -666,6 +667,12 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
             hipLaunchKernelGGL((gate_kernel<bf16, 64>), dim3(g), dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL((gate_kernel<float, 64>), dim3(g), dim3(256), 0, s, a);
+    } else if (a.dv == 256) {
+        const unsigned g = (unsigned)((items + 3) / 4);
+        if (dtype)
+            hipLaunchKernelGGL((gate_kernel<bf16, 256>), dim3(g), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((gate_kernel<float, 256>), dim3(g), dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }
@@ -1666,7 +1673,8 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 // (stream, head). The default (widest) shapes that stage o also come with the output gate
 // fused into the o flush, where o and the z tile fit in LDS; the per-channel-gate instances
 // at 128 columns (o not staged) and fp32 at 64 columns (no room for the z tile) gate o in
-// a separate pass (gate_kernel).
+// a separate pass (gate_kernel), and so do the dk != dv shapes, whose value rows span two
+// workgroups (dv = 2 dk: two column slices of one (stream, head)).
 #define GDN_CHUNK_INSTANCES(X)                          \
     X(bf16, f16, 1, 128, 128, 8, 1, false, false)       \
     X(bf16, f16, 1, 128, 128, 4, 2, false, false)       \
@@ -1690,7 +1698,13 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
     X(f16, f16, 2, 64, 64, 4, 1, false, true)           \
     X(float, float, 0, 64, 64, 4, 1, false, true)       \
     X(bf16, f16, 1, 64, 64, 4, 1, true, true)           \
-    X(f16, f16, 2, 64, 64, 4, 1, true, true)
+    X(f16, f16, 2, 64, 64, 4, 1, true, true)              \
+    X(bf16, f16, 1, 128, 256, 8, 1, false, false)     \
+    X(f16, f16, 2, 128, 256, 8, 1, false, false)      \
+    X(bf16, f16, 1, 128, 256, 8, 1, true, false)      \
+    X(f16, f16, 2, 128, 256, 8, 1, true, false)       \
+    X(float, float, 0, 64, 128, 4, 1, false, false)   \
+    X(float, float, 0, 64, 128, 4, 1, true, false)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
 // with the output gate fused

@@ -66,8 +66,10 @@ extern "C" {
 
 typedef struct gdn_params {
     int32_t H;      /* value heads: g, beta, o and the states have H heads (see Hqk)      */
-    int32_t dk;     /* key head dim: 64 or 128                                            */
-    int32_t dv;     /* value head dim: 64 or 128                                          */
+    int32_t dk;     /* key head dim                                                       */
+    int32_t dv;     /* value head dim. Compiled (dk, dv): bf16 (64, 64), (128, 128),
+                       (128, 256); f32 (64, 64), (64, 128). dv != dk runs unsegmented and
+                       gates o (if asked) in a separate pass                              */
     int32_t chunk;  /* tokens per chunk: 64                                               */
     float eps;      /* L2 eps for q and k; eps < 0: q and k are used as given (no L2)     */
     float scale;    /* multiplies q after the optional L2 (normally 1/sqrt(dk))           */
@@ -193,8 +195,10 @@ int kda_prefill_varlen(const gdn_params *p, const void *q, const void *k, const 
  *             16-byte aligned, in/out. The B states must not overlap.
  *   conv_state_ptrs, conv_w  as for gdn_prefill_batched (NULL iff conv_k == 0).
  *   o         [B][H][dv] float32, out (16-byte aligned).
- * dk == dv, 64 or 128 (else GDN_E_UNSUPPORTED); B >= 1. No workspace. The step is one
- * kernel; with profiling enabled it is recorded in GDN_PROF_RECUR.
+ * (dk, dv) = (64, 64), (128, 128), (64, 128) or (128, 256), either dtype (else
+ * GDN_E_UNSUPPORTED); B >= 1. No workspace. The step is one kernel (plus a small pass that
+ * advances the q/k windows when Hqk < H); with profiling enabled it is recorded in
+ * GDN_PROF_RECUR.
  */
 int gdn_decode(const gdn_params *p, const void *q, const void *k, const void *v,
                const float *g, const float *beta, float *const *h_ptrs,

@@ -91,6 +91,8 @@ def test_refusals_before_launch():
     assert _single(p, q=FAKE + 2) == B.GDN_E_ARG             # misaligned rows
     assert _single(B.params(2, 64, 64, chunk=32)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 96, 96)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 64, 128)) == B.GDN_E_UNSUPPORTED     # bf16 has 128 x 256
+    assert _single(B.params(2, 128, 64, dtype=B.GDN_F32)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 64, 64, dtype=7)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 64, 64, conv_k=5)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 64, 64, ld_qkv=100)) == B.GDN_E_ARG    # ld < H*dk
