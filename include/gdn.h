@@ -37,6 +37,11 @@
  *     nothing is launched and no buffer changes (the pages refuse a bad token count before
  *     any launch). GDN_E_HIP reports a failed launch.
  *   - Not thread-safe per device for concurrent calls sharing one workspace.
+ *   - Graph capture: a call enqueues kernel launches only (no memset, copy, allocation or
+ *     host wait), so after one eager call of the same shape on the device (which does the
+ *     one-time kernel setup) it can be captured in a HIP graph and replayed; each replay
+ *     reads and advances the states as the captured call did. Profiling must be off while
+ *     capturing.
  */
 #ifndef GDN_H
 #define GDN_H
