@@ -196,3 +196,38 @@ def test_segmented_scan_matches_serial_scan(case):
           "o %.3g h %.3g" % (spec.name, S, *e_seg, *e_ser, d_o, d_h), flush=True)
     assert d_o <= tol and d_h <= tol
     assert d_o > 0, "the two scans should differ in rounding: is the state carried?"
+
+
+def test_refused_calls_leave_buffers_unchanged():
+    """A refused call (too many tokens for the workspace, a bad stride, an unsupported
+    chunk) launches nothing: the state, conv window and o keep their bytes."""
+    import ctypes
+    from gated_delta_rule_depthwise_amd import binding as B
+    from gated_delta_rule_depthwise_amd.runner import Prefill
+    spec = spec_small(2, lengths=[200], H=2, seed=61)
+    inp = inputs.make(spec)
+    call = Prefill(inp, "cuda", o_fill=SENTINEL)
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (call.o, call.h, call.conv_state)]
+    s = torch.cuda.current_stream().cuda_stream
+    p = call.params
+    bad_chunk = B.gdn_params.from_buffer_copy(p)
+    bad_chunk.chunk = 32
+    bad_ld = B.gdn_params.from_buffer_copy(p)
+    bad_ld.ld_qkv = p.ld_qkv + 1
+    # the front end's activations need this many bytes for N tokens
+    front = B.gdn_workspace_bytes(p, 1, spec.N, B.GDN_KIND_VARLEN)
+    cases = [(p, spec.N, front - 1, B.GDN_E_WORKSPACE),
+             (bad_chunk, spec.N, call.ws_bytes, B.GDN_E_UNSUPPORTED),
+             (bad_ld, spec.N, call.ws_bytes, B.GDN_E_ARG), (p, 0, call.ws_bytes, B.GDN_E_ARG)]
+    for prm, t, nbytes, want in cases:
+        rc = B.gdn_prefill(prm, call.q_ptr, call.k_ptr, call.v_ptr, call.g, call.beta, call.h,
+                           call.conv_state, call.conv_w, call.o, t, call.ws, nbytes, s)
+        assert rc == want, (rc, want)
+    rc = B.gdn_decode(bad_chunk, call.q_ptr, call.k_ptr, call.v_ptr, call.g, call.beta,
+                      call.h_ptrs, call.cs_ptrs, call.conv_w, call.o, 1, s)
+    assert rc == B.GDN_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    for a, b in zip((call.o, call.h, call.conv_state), before):
+        assert torch.equal(a, b)
+    assert ctypes.sizeof(p) == 72
