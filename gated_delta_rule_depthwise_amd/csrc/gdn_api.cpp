@@ -161,6 +161,10 @@ int check_params(const gdn_params *p, int kda)
     return GDN_OK;
 }
 
+// streams of a varlen call ranked by length (workspace, after the activations)
+constexpr int32_t kMaxOrderB = 1024;
+size_t order_bytes(int32_t B) { return B <= kMaxOrderB ? align_up((size_t)B * 4) : 0; }
+
 size_t front_bytes(const gdn_params *p, int64_t max_tokens)
 {
     if (p->conv_k == 0)
@@ -311,7 +315,15 @@ int run(const Call &c)
             sp = SegPlan{0, 0};
     }
 
+    // varlen calls with more workgroups than CUs: streams dispatch longest first, from a
+    // ranking kept in the workspace after the front end's activations
+    int32_t *order = nullptr;
+    if (c.st.cu && c.ws && c.st.B <= kMaxOrderB && grid > cu_count() &&
+        c.ws_bytes >= need + order_bytes(c.st.B))
+        order = (int32_t *)((char *)c.ws + need);
+
     ChunkArgs ca{};
+    ca.order = order;
     ca.g = c.g;
     ca.beta = c.beta;
     ca.h = c.h;
@@ -369,6 +381,8 @@ int run(const Call &c)
     }
     {
         Stage st(GDN_PROF_RECUR, c.stream);
+        if (order && gdn::launch_stream_order(c.st.cu, c.st.B, order, c.stream) != hipSuccess)
+            return GDN_E_HIP;
         if (!sp.S) {
             if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)grid, c.stream) != hipSuccess)
@@ -618,6 +632,8 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
     if (kind != GDN_KIND_VARLEN && p->dk == p->dv && sh.nv > 0 &&
         (int64_t)B * p->H * (p->dv / sh.nv) < cu_count() && max_tokens / B >= 3 * 64)
         seg = seg_bytes(p, B, kMaxSeg);
+    if (kind == GDN_KIND_VARLEN)
+        seg = order_bytes(B);
     return front_bytes(p, max_tokens) + seg;
 }
 

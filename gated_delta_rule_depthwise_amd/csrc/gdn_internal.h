@@ -39,6 +39,8 @@ struct ChunkArgs {
     int32_t nseg;           // S
     int64_t seg_len;        // tokens per segment, a multiple of the chunk
     float *seg_ws;
+    // varlen: the stream of workgroup slot i (streams ranked longest first), or nullptr
+    const int32_t *order;
     // output gate (fused instances): o <- o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
     const void *z;          // row r of head h: z + r*ld_z + h*dv (bf16, or float for f32)
     int64_t ld_z;
@@ -138,6 +140,8 @@ hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s)
 // q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after
 // the step by a pass of its own
 hipError_t launch_decode_qk_window(int dtype, const DecodeArgs &a, hipStream_t s);
+// order[i] = the stream of rank i by length, longest first (ties by index), B <= 1024
+hipError_t launch_stream_order(const int32_t *cu, int32_t B, int32_t *order, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
 // 1 if the (in_kind, dk, dv, kda, nv, waves, gate) instance exists.

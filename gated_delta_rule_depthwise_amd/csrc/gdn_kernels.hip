@@ -943,7 +943,8 @@ __global__ void __launch_bounds__(NW * 64)
     constexpr int NS = DV / NV;  // dv slices
     const int job = blockIdx.x / (BH * NS), jr = blockIdx.x - job * (BH * NS);
     const int slice = jr / BH, bh = jr - slice * BH;
-    const int b = bh / H, head = bh - b * H;
+    const int bi = bh / H, head = bh - bi * H;
+    const int b = a.order ? a.order[bi] : bi;  // varlen: longest streams dispatch first
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     float *state = (a.h_ptrs ? a.h_ptrs[b] : a.h);
@@ -1847,6 +1848,33 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
 // varlen chunk table: one block, streams handled CT_THREADS at a time
 
 constexpr int CT_THREADS = 256;
+
+// Streams ranked by length, longest first: with more workgroups than CUs, the longest
+// streams then start in the first round instead of waiting behind short ones (list
+// scheduling, longest first). One thread per stream counts the streams ahead of it.
+__global__ void __launch_bounds__(256) stream_order_kernel(const int32_t *cu, int32_t B,
+                                                           int32_t *order)
+{
+    __shared__ int32_t len[1024];
+    for (int i = threadIdx.x; i < B; i += 256)
+        len[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    for (int b = threadIdx.x; b < B; b += 256) {
+        const int32_t lb = len[b];
+        int rank = 0;
+        for (int j = 0; j < B; ++j)
+            rank += len[j] > lb || (len[j] == lb && j < b);
+        order[rank] = b;
+    }
+}
+
+hipError_t launch_stream_order(const int32_t *cu, int32_t B, int32_t *order, hipStream_t s)
+{
+    if (B < 1 || B > 1024)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_order_kernel, dim3(1), dim3(256), 0, s, cu, B, order);
+    return hipGetLastError();
+}
 
 __global__ void __launch_bounds__(CT_THREADS)
 chunk_table_kernel(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,

@@ -252,6 +252,11 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 /* Bytes of device workspace a call of `kind` with B streams and up to max_tokens rows in
  * total needs (0 if none). Returns 0 for invalid parameters.
  *
+ * For varlen calls (B <= 1024) it also holds B int32: the streams ranked by length, so that
+ * when a call has more (stream, head) workgroups than the device has CUs the longest
+ * streams are dispatched first (written by a small kernel on the call's stream; a
+ * workspace without room for it keeps the index order).
+ *
  * The workspace holds the front end's activations and, for single and batched calls with
  * fewer (stream, head) work units than the device has compute units, the states of the
  * segmented scan: each stream is cut into S segments of whole chunks; one launch runs

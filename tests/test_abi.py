@@ -56,7 +56,7 @@ def test_segment_plan():
     p = B.params(32, 128, 128, conv_k=4)           # one stream, 32 heads
     full = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
     front = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN)
-    assert front == 4096 * 3 * 32 * 128 * 2
+    assert front == 4096 * 3 * 32 * 128 * 2 + 256   # + the varlen stream ranking
     S = B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 4096, full)
     assert 3 <= S <= 12
     # the states: per slot [H][dk][dv] fp32, 3S-5 slots
@@ -168,7 +168,7 @@ def test_shared_qk_head_refusals():
     p = B.params(4, 64, 64, dtype=B.GDN_F32, Hqk=2)
     assert p.ld_qkv == 2 * 2 * 64 + 4 * 64
     assert B.gdn_workspace_bytes(B.params(4, 64, 64, conv_k=4, Hqk=2), 1, 10,
-                                 B.GDN_KIND_VARLEN) == (10 * 512 * 2 + 255) // 256 * 256
+                                 B.GDN_KIND_SINGLE) == (10 * 512 * 2 + 255) // 256 * 256
 
 
 def test_params_struct_layout():

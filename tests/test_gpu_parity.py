@@ -215,8 +215,8 @@ def test_refused_calls_leave_buffers_unchanged():
     bad_chunk.chunk = 32
     bad_ld = B.gdn_params.from_buffer_copy(p)
     bad_ld.ld_qkv = p.ld_qkv + 1
-    # the front end's activations need this many bytes for N tokens
-    front = B.gdn_workspace_bytes(p, 1, spec.N, B.GDN_KIND_VARLEN)
+    # the front end's activations alone need N * cd bf16 values
+    front = spec.N * spec.cd * 2
     cases = [(p, spec.N, front - 1, B.GDN_E_WORKSPACE),
              (bad_chunk, spec.N, call.ws_bytes, B.GDN_E_UNSUPPORTED),
              (bad_ld, spec.N, call.ws_bytes, B.GDN_E_ARG), (p, 0, call.ws_bytes, B.GDN_E_ARG)]
