@@ -1,5 +1,6 @@
 /*
- * gdn.h -- C ABI of libgdn: the chunked gated-delta-rule prefill (GDN and KDA) on MI355X.
+ * gdn.h -- C ABI of libgdn: the chunked gated-delta-rule prefill (GDN and KDA) on MI355X,
+ * its single-token decode step, and the gated RMSNorm of the output.
  *
  * The operation (pages "split_prefill.rs" -- prefill_gdn_full, prefill_gdn_full_batched,
  * prefill_gdn_full_batched_fla_varlen -- and "metrale_model_arch/glm5next_kda/prefill.rs"
@@ -16,7 +17,10 @@
  *        o_t = S_t q_t,
  *      evaluated chunk by chunk (cumulative log-gates, the beta-weighted WY/UT transform,
  *      then the inter-chunk scan that carries h). alpha_t is one scalar per head (GDN) or
- *      one value per key channel (KDA).
+ *      one value per key channel (KDA);
+ *   4. optional output gate (gdn_params.z): o <- o / sqrt(mean(o^2) + eps) * w * silu(z)
+ *      per token and head (page "split_prefill.rs", prefill_phase3).
+ *   gdn_decode / kda_decode run steps 1-4 for one new token per stream.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument except `p` is a DEVICE pointer; `p` is a host pointer.
