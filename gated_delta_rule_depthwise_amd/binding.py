@@ -29,7 +29,7 @@ GDN_KIND_VARLEN = 2
 EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",
            "kda_prefill_batched", "kda_prefill_varlen", "gdn_decode", "kda_decode",
            "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
-           "gdn_segments", "gdn_status_string")
+           "gdn_segments", "gdn_segment_plan", "gdn_status_string")
 GDN_PROF_FRONT = 0
 GDN_PROF_RECUR = 1
 GDN_PROF_STATE = 2
@@ -86,6 +86,8 @@ def load(path: str = SO):
         lib.gdn_workspace_bytes.restype = _sz
         lib.gdn_segments.argtypes = [_pp, _i32, _i32, _i64, _sz]
         lib.gdn_segments.restype = ctypes.c_int
+        lib.gdn_segment_plan.argtypes = [_pp, _i32, _i32, _i64, _sz, _vp, _vp]
+        lib.gdn_segment_plan.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
@@ -193,6 +195,15 @@ def gdn_workspace_bytes(p, B, max_tokens, kind):
 
 def gdn_segments(p, kind, B, t_per_stream, ws_bytes):
     return int(load().gdn_segments(ctypes.byref(p), kind, B, t_per_stream, ws_bytes))
+
+
+def gdn_segment_plan(p, kind, B, t_per_stream, ws_bytes):
+    """(S, tokens of segment 0, tokens of each inner segment); S = 0 when unsegmented."""
+    s0 = ctypes.c_int64(0)
+    s1 = ctypes.c_int64(0)
+    S = int(load().gdn_segment_plan(ctypes.byref(p), kind, B, t_per_stream, ws_bytes,
+                                    ctypes.byref(s0), ctypes.byref(s1)))
+    return S, s0.value, s1.value
 
 
 def gdn_status_string(status):

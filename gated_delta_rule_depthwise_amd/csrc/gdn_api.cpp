@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "gdn.h"
@@ -196,23 +197,105 @@ int cu_count()
 }
 
 struct SegPlan {
-    int S;            // 0: no segmentation
-    int64_t seg_len;  // tokens
+    int S;             // 0: no segmentation
+    int64_t seg0_len;  // tokens of segment 0
+    int64_t seg_len;   // tokens of each inner segment (the last segment takes the rest)
 };
 
-// Cost in chunk steps of a launch of `wgs` one-per-CU workgroups that each walk `chunks`.
-double waves_cost(int64_t wgs, int64_t chunks, int ncu)
+// Finishing time of `n` equal jobs of duration `d` dispatched in order onto the CUs, whose
+// free times are kept as (time, count) groups sorted by time (a launch's workgroups go to
+// the CUs as they free up, one per CU).
+struct CuPool {
+    std::vector<std::pair<double, int64_t>> free;  // (time, CUs), ascending
+    double end = 0.0;
+    explicit CuPool(int ncu) : free{{0.0, (int64_t)ncu}} {}
+    void run(int64_t n, double d)
+    {
+        while (n > 0) {
+            std::pair<double, int64_t> f = free.front();
+            free.erase(free.begin());
+            const int64_t m = n < f.second ? n : f.second;
+            n -= m;
+            if (m < f.second)
+                free.insert(free.begin(), {f.first, f.second - m});
+            const double t = f.first + d;
+            end = t > end ? t : end;
+            auto it = free.begin();
+            while (it != free.end() && it->first < t)
+                ++it;
+            if (it != free.end() && it->first == t)
+                it->second += m;
+            else
+                free.insert(it, {t, m});
+        }
+    }
+};
+
+// Relative cost of one chunk step by job kind, measured on the 4096-token front-end
+// stream (32 heads, d = 128, all CUs busy): a step that writes o 8.5 us, an end-state job
+// from h = 0 (no q rows, no o) 7.0 us, a transition job (from h = I, v = 0) 6.2 us; one
+// step of the chain of segment maps about 3 us, plus 3 us to start it.
+constexpr double kStepB = 0.82, kStepA = 0.73, kChainStep = 0.35, kChainBase = 0.35;
+
+// Estimated time, in chunk steps that write o, of the segmented scan of U work units per
+// job with segment lengths (in chunks) l0, l1 (segments 1..S-2) and the rest.
+double seg_cost(int S, int64_t l0, int64_t l1, int64_t last, int64_t U, int ncu)
 {
-    return (double)((wgs + ncu - 1) / ncu) * (double)chunks;
+    CuPool p1(ncu);  // pass 1 in dispatch order: segment 0, end states, transitions
+    p1.run(U, (double)l0);
+    p1.run((int64_t)(S - 2) * U, kStepB * (double)l1);
+    p1.run((int64_t)(S - 2) * U, kStepA * (double)l1);
+    CuPool p2(ncu);  // pass 2: segments 1..S-2, then the last one
+    p2.run((int64_t)(S - 2) * U, (double)l1);
+    p2.run(U, (double)last);
+    return p1.end + p2.end + kChainBase + kChainStep * (S - 2);
+}
+
+// The plan of one call: cached for the last shape asked (every call of a model layer asks
+// the same).
+SegPlan seg_search(int64_t nc, int64_t U, int ncu)
+{
+    static std::mutex mu;
+    static int64_t k_nc = -1, k_u = -1;
+    static int k_ncu = -1;
+    static SegPlan k_plan{0, 0, 0};
+    std::lock_guard<std::mutex> g(mu);
+    if (nc == k_nc && U == k_u && ncu == k_ncu)
+        return k_plan;
+    CuPool serial(ncu);
+    serial.run(U, (double)nc);
+    double best = 0.8 * serial.end;  // segment only for a clear gain
+    SegPlan plan{0, 0, 0};
+    for (int S = 3; S <= kMaxSeg && S <= nc; ++S) {
+        // inner segments from about nc / S to nc / (S - 2) chunks, segment 0 up to about
+        // twice as long; long streams are searched on a coarser grid (at most ~32 x 64
+        // candidates per S)
+        const int64_t lo = nc / S > 2 ? nc / S - 1 : 1;
+        const int64_t hi = (nc + S - 3) / (S - 2);
+        const int64_t st1 = (hi - lo) / 32 + 1;
+        for (int64_t l1 = lo; l1 <= hi; l1 += st1) {
+            const int64_t st0 = (2 * l1 + 2) / 64 + 1;
+            for (int64_t l0 = 1; l0 <= 2 * l1 + 2; l0 += st0) {
+                const int64_t last = nc - l0 - (S - 2) * l1;
+                if (last < 1)
+                    break;
+                const double c = seg_cost(S, l0, l1, last, U, ncu);
+                if (c < best)
+                    best = c, plan = SegPlan{S, l0 * 64, l1 * 64};
+            }
+        }
+    }
+    k_nc = nc, k_u = U, k_ncu = ncu, k_plan = plan;
+    return plan;
 }
 
 SegPlan seg_plan(const gdn_params *p, int32_t B, int64_t tps, int nslices, int ncu)
 {
-    SegPlan none{0, 0};
+    SegPlan none{0, 0, 0};
     if (p->dk != p->dv || p->chunk != 64 || tps < 1)
         return none;
     const int64_t nc = (tps + 63) / 64;
-    static int force = -1;  // GDN_SEG: 0 never segments, S >= 3 asks for S segments
+    static int force = -1;  // GDN_SEG: 0 never segments, S >= 3 asks for S equal segments
     if (force < 0) {
         const char *e = getenv("GDN_SEG");
         force = e ? atoi(e) : 0x7fffffff;
@@ -222,25 +305,9 @@ SegPlan seg_plan(const gdn_params *p, int32_t B, int64_t tps, int nslices, int n
     if (force >= 3 && force <= kMaxSeg && force != 0x7fffffff) {
         const int64_t L = (nc + force - 1) / force;
         const int Se = (int)((nc + L - 1) / L);
-        return Se >= 3 ? SegPlan{Se, L * 64} : none;
+        return Se >= 3 ? SegPlan{Se, L * 64, L * 64} : none;
     }
-    const int64_t U = (int64_t)B * p->H * nslices;
-    const double base = waves_cost(U, nc, ncu);
-    double best = 0.8 * base;  // segment only for a clear gain
-    SegPlan plan = none;
-    for (int S = 3; S <= kMaxSeg && S <= nc; ++S) {
-        const int64_t L = (nc + S - 1) / S;
-        const int Se = (int)((nc + L - 1) / L);
-        if (Se < 3)
-            continue;
-        // the chain of S-2 steps of (dk x dk) x (dk x 16) products costs about a
-        // quarter of a chunk step each
-        const double cost = waves_cost((2 * (int64_t)Se - 3) * U, L, ncu) +
-                            waves_cost((int64_t)(Se - 1) * U, L, ncu) + 0.25 * (Se - 2);
-        if (cost < best)
-            best = cost, plan = SegPlan{Se, L * 64};
-    }
-    return plan;
+    return seg_search(nc, (int64_t)B * p->H * nslices, ncu);
 }
 
 size_t seg_bytes(const gdn_params *p, int32_t B, int S)
@@ -307,12 +374,12 @@ int run(const Call &c)
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
     // segmented scan when it pays and the workspace has room for its states
-    SegPlan sp{0, 0};
+    SegPlan sp{0, 0, 0};
     if (!c.st.cu) {
         sp = seg_plan(p, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
         if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.st.B, sp.S) ||
                      grid * (2 * sp.S - 3) > (int64_t)INT32_MAX))
-            sp = SegPlan{0, 0};
+            sp = SegPlan{0, 0, 0};
     }
 
     // varlen calls with more workgroups than CUs: streams dispatch longest first, from a
@@ -389,6 +456,7 @@ int run(const Call &c)
                 return GDN_E_HIP;
         } else {
             ca.nseg = sp.S;
+            ca.seg0_len = sp.seg0_len;
             ca.seg_len = sp.seg_len;
             ca.seg_ws = (float *)((char *)c.ws + need);
             ca.pass = 1;
@@ -637,9 +705,13 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
     return front_bytes(p, max_tokens) + seg;
 }
 
-int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
-                 size_t ws_bytes)
+int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
+                     size_t ws_bytes, int64_t *seg0_tokens, int64_t *seg_tokens)
 {
+    if (seg0_tokens)
+        *seg0_tokens = 0;
+    if (seg_tokens)
+        *seg_tokens = 0;
     int rc0 = check_params(p, 0), rc1 = check_params(p, 1);
     if (rc0 != GDN_OK && rc1 != GDN_OK)
         return rc0;
@@ -651,9 +723,19 @@ int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_str
     const Shape sh = pick_shape(p, rc0 == GDN_OK ? 0 : 1, (int64_t)B * p->H);
     const SegPlan sp = seg_plan(p, B, t_per_stream, p->dv / sh.nv, cu_count());
     const size_t need = front_bytes(p, (int64_t)B * t_per_stream);
-    if (sp.S && ws_bytes >= need + seg_bytes(p, B, sp.S))
-        return sp.S;
-    return 0;
+    if (!sp.S || ws_bytes < need + seg_bytes(p, B, sp.S))
+        return 0;
+    if (seg0_tokens)
+        *seg0_tokens = sp.seg0_len;
+    if (seg_tokens)
+        *seg_tokens = sp.seg_len;
+    return sp.S;
+}
+
+int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
+                 size_t ws_bytes)
+{
+    return gdn_segment_plan(p, kind, B, t_per_stream, ws_bytes, nullptr, nullptr);
 }
 
 int gdn_profile_enable(int on)

@@ -34,10 +34,12 @@ struct ChunkArgs {
     // slot H(b, 1)); jobs 1..S-2 run segment j from h = 0 (end state to slot B(b, j)); jobs
     // S-1..2S-4 run segment j-(S-2) from h = I with v = 0 (end state, the segment's
     // transition, to slot A(b, j-(S-2))). pass 2: job j runs segment j+1 from slot H(b, j+1)
-    // (o written; the last segment's end state to the stream's state).
+    // (o written; the last segment's end state to the stream's state). Segment 0 holds
+    // seg0_len tokens, segments 1..S-2 seg_len each, segment S-1 the rest of the stream.
     int32_t pass;
     int32_t nseg;           // S
-    int64_t seg_len;        // tokens per segment, a multiple of the chunk
+    int64_t seg0_len;       // tokens of segment 0, a multiple of the chunk
+    int64_t seg_len;        // tokens of each inner segment, a multiple of the chunk
     float *seg_ws;
     // varlen: the stream of workgroup slot i (streams ranked longest first), or nullptr
     const int32_t *order;

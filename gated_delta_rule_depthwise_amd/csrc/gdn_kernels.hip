@@ -972,8 +972,9 @@ __global__ void __launch_bounds__(NW * 64)
                 hout = nullptr;
         }
         const int64_t s0 = start;
-        start = min(s0 + seg * a.seg_len, end);
-        end = min(start + a.seg_len, end);
+        start = min(s0 + (seg == 0 ? 0 : a.seg0_len + (seg - 1) * a.seg_len), end);
+        if (seg < S - 1)  // the last segment runs to the stream's end
+            end = min(start + (seg == 0 ? a.seg0_len : a.seg_len), end);
     }
     const int64_t hoff = (int64_t)head * DK * DV;
     const int colw = slice * NV + wave0 * 16 * NCB;  // this wave's first dv column

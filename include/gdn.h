@@ -282,6 +282,16 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
 int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
                  size_t ws_bytes);
 
+/* The same plan with its segment lengths: returns what gdn_segments returns and, for a
+ * segmented plan, writes the tokens of segment 0 to *seg0_tokens and of each of segments
+ * 1..S-2 to *seg_tokens (multiples of the chunk; segment S-1 takes the rest of each
+ * stream); both are set to 0 otherwise. Either pointer may be NULL. Segment 0 may be longer
+ * than the inner segments: the plan is the cheapest one under a list-schedule estimate of
+ * the two launches on the device's compute units, and segment 0 runs beside the inner
+ * segments' map jobs, which cost less per chunk than a chunk that writes o. */
+int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
+                     size_t ws_bytes, int64_t *seg0_tokens, int64_t *seg_tokens);
+
 /* Static description of a status code. */
 const char *gdn_status_string(int status);
 

@@ -78,6 +78,27 @@ def test_segment_plan():
     assert B.gdn_segments(p, 7, 1, 4096, full) == B.GDN_E_ARG
 
 
+@pytest.mark.parametrize("H,T", [(32, 4096), (32, 16384), (4, 4096), (2, 700), (16, 1000),
+                                 (32, 1 << 20)])
+def test_segment_plan_lengths(H, T):
+    """A segmented plan cuts each stream into whole chunks: segment 0 and the S-2 inner
+    segments leave at least one chunk for the last segment, and the plan agrees with
+    gdn_segments."""
+    p = B.params(H, 128, 128, conv_k=4)
+    ws = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_SINGLE)
+    S, l0, l1 = B.gdn_segment_plan(p, B.GDN_KIND_SINGLE, 1, T, ws)
+    assert S == B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, T, ws)
+    if S == 0:
+        assert l0 == 0 and l1 == 0
+        return
+    assert 3 <= S <= 12
+    assert l0 > 0 and l1 > 0 and l0 % 64 == 0 and l1 % 64 == 0
+    assert l0 + (S - 2) * l1 < T, "the last segment would be empty"
+    # no room for the states: unsegmented, lengths cleared
+    front = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_VARLEN)
+    assert B.gdn_segment_plan(p, B.GDN_KIND_SINGLE, 1, T, front) == (0, 0, 0)
+
+
 def _single(p, t=10, ws=None, ws_bytes=0, h=FAKE, g=FAKE, cs=None, cw=None, q=FAKE):
     return B.gdn_prefill(p, q, FAKE, FAKE, g, FAKE, h, cs, cw, FAKE, t, ws, ws_bytes, None)
 
