@@ -1256,8 +1256,11 @@ __global__ void __launch_bounds__(NW * 64)
         if constexpr (KDA) {
             // per channel, in place in Gk: each thread scans CH/PARTS rows of one channel,
             // then adds the totals of the parts above it
+            // The parts' totals go through the Ms tile, unused until the preparation.
             constexpr int PARTS = NT / DK, RP = CH / PARTS;
+            static_assert(PARTS * DK * 4 <= C::SZ_MS, "part totals");
             const int c = tid % DK, part = tid / DK;
+            float *tot = (float *)(smem + zo + C::OFF_M);
             float xs[RP];
             float run = 0.f;
 #pragma unroll
@@ -1265,19 +1268,15 @@ __global__ void __launch_bounds__(NW * 64)
                 run += Gk[(part * RP + j) * LDG + c];
                 xs[j] = run;
             }
-#pragma unroll
-            for (int j = 0; j < RP; ++j)
-                Gk[(part * RP + j) * LDG + c] = xs[j];
+            tot[part * DK + c] = run;
             __syncthreads();
             float add = 0.f;
-            for (int pp = 0; pp < part; ++pp)
-                add += Gk[(pp * RP + RP - 1) * LDG + c];
-            __syncthreads();
-            if (part > 0) {
 #pragma unroll
-                for (int j = 0; j < RP; ++j)
-                    Gk[(part * RP + j) * LDG + c] = xs[j] + add;
-            }
+            for (int pp = 0; pp < PARTS - 1; ++pp)
+                add += pp < part ? tot[pp * DK + c] : 0.f;
+#pragma unroll
+            for (int j = 0; j < RP; ++j)
+                Gk[(part * RP + j) * LDG + c] = xs[j] + add;
             __syncthreads();
         }
         const float gC = graw[CH - 1];  // graw holds Gamma (written in stage A)
@@ -1507,22 +1506,40 @@ __global__ void __launch_bounds__(NW * 64)
         __syncthreads();
         T *Kd = (T *)(smem + zo + C::OFF_M);  // per-channel gate: (K . e^(G_C - G)), over Ms
         if constexpr (KDA) {
-            // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1
-            for (int idx = tid; idx < CH * (DK / 4); idx += NT) {
-                const int r = idx / (DK / 4), c0 = (idx % (DK / 4)) * 4;
+            // Ks <- K . e^G, Qs <- Q . e^G, Kd <- K . e^(G_C - G): every factor is <= 1.
+            // A thread owns 4 channels of NI rows (the same channels in each, so G_C is read
+            // once); all its tile reads are issued before the exponentials, as 4-element
+            // vectors.
+            typedef T T4 __attribute__((ext_vector_type(4)));
+            constexpr int NI = CH * (DK / 4) / NT;
+            static_assert(NI * NT == CH * (DK / 4) && NT % (DK / 4) == 0, "rescale map");
+            const int c0 = (tid % (DK / 4)) * 4, r0 = tid / (DK / 4);
+            const f32x4 gcv = *reinterpret_cast<const f32x4 *>(Gk + (CH - 1) * LDG + c0);
+            T4 kv[NI], qv[NI];
+            f32x4 gv[NI];
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const int r = r0 + it * (NT / (DK / 4));
                 const int off = QK<T, DK>::at(r, c0 / 4);
-                T *kp = Ks + off;
-                T *qp = Qs + off;
-                T *dp = Kd + off;
+                kv[it] = *reinterpret_cast<const T4 *>(Ks + off);
+                qv[it] = *reinterpret_cast<const T4 *>(Qs + off);
+                gv[it] = *reinterpret_cast<const f32x4 *>(Gk + r * LDG + c0);
+            }
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const int r = r0 + it * (NT / (DK / 4));
+                const int off = QK<T, DK>::at(r, c0 / 4);
+                T4 kd, ke, qe;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float gg = Gk[r * LDG + c0 + i];
-                    const float gcc = Gk[(CH - 1) * LDG + c0 + i];
-                    const float kv = (float)kp[i], qv = (float)qp[i];
-                    dp[i] = (T)(kv * __expf(gcc - gg));
-                    kp[i] = (T)(kv * __expf(gg));
-                    qp[i] = (T)(qv * __expf(gg));
+                    const float e = __expf(gv[it][i]);
+                    kd[i] = (T)((float)kv[it][i] * __expf(gcv[i] - gv[it][i]));
+                    ke[i] = (T)((float)kv[it][i] * e);
+                    qe[i] = (T)((float)qv[it][i] * e);
                 }
+                *reinterpret_cast<T4 *>(Kd + off) = kd;
+                *reinterpret_cast<T4 *>(Ks + off) = ke;
+                *reinterpret_cast<T4 *>(Qs + off) = qe;
             }
             __syncthreads();
         }
