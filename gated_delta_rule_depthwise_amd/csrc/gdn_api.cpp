@@ -440,10 +440,12 @@ int run(const Call &c)
         ca.v = y + (size_t)2 * qk_heads(p) * p->dk * es;
         ca.ld = conv_dim(p);
         ca.do_l2 = 0;
+        ca.unit_keys = p->eps >= 0.f;  // the front end normalised q and k
         ca.scale = 1.f;
     } else {
         ca.q = c.q, ca.k = c.k, ca.v = c.v, ca.ld = p->ld_qkv;
         ca.do_l2 = p->eps >= 0.f;
+        ca.unit_keys = ca.do_l2;
         ca.scale = p->scale;
     }
     {

@@ -27,6 +27,7 @@ struct ChunkArgs {
     int32_t H;              // value heads (the grid and the states)
     int32_t qk_group;       // value heads per q/k head (H / Hqk)
     int32_t do_l2;          // normalise q and k rows on load
+    int32_t unit_keys;      // keys arrive normalised or are normalised on load (|k| <= 1)
     float eps;
     float scale;            // multiplies q on load
     // Segmented scan of long streams (see SegLayout). pass 0: each workgroup walks a whole

@@ -719,7 +719,10 @@ struct ChunkCfg {
     // Gamma[64], beta[64], a = e^Gamma [64], a_C / a [64]
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);
     static constexpr int LDO = NV + 16;  // o rows (fp32): 4 rows of a D-layout write hit 32 banks
-    static constexpr int OFF_O = OFF_G + 4 * CH * 4;
+    // + the running log decay bound of a transition job (one float, padded to 16 bytes;
+    // scalar gate without the fused output gate only)
+    static constexpr bool STOP = !KDA && !GATE;
+    static constexpr int OFF_O = OFF_G + 4 * CH * 4 + (STOP ? 16 : 0);
     // o is staged in LDS when it fits (not with the per-channel gate tile at 128 columns)
     static constexpr bool STAGE_O = OFF_O + CH * LDO * 4 <= 160 * 1024;
     // output gate: the z rows of a chunk (the caller's element type, as wide as T) and the
@@ -1164,7 +1167,22 @@ __global__ void __launch_bounds__(NW * 64)
         }
     };
 
-    for (int64_t cs = start; cs < end; cs += CH) {
+    // A transition job stops once its transition has underflowed. Token t multiplies it by
+    // (I - beta_t k_t k_t^T) alpha_t, of norm <= alpha_t when beta_t |k_t|^2 lies in [0, 2];
+    // a chunk by a factor of norm <= e^(Gamma_C). Once the running bound is below e^-110
+    // (under half the smallest fp32 subnormal) every entry is 0 in fp32 and stays 0 through
+    // the remaining chunks, so the job writes zeros and ends. The bound is read only after
+    // a chunk's barriers (never before the first chunk), by every wave alike.
+    // (not in the instances with the output gate fused, which have no registers to spare)
+    if (C::STOP && tid0 == 0)
+        ((float *)(smem + C::OFF_G))[4 * CH] = 0.f;
+    const bool may_stop = C::STOP && h_ident && a.unit_keys;
+    auto underflowed = [&]() {
+        return may_stop && __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                         __builtin_bit_cast(int, ((const float *)(
+                                                             smem + C::OFF_G))[4 * CH]))) < -110.f;
+    };
+    for (int64_t cs = start; cs < end && !(cs > start && underflowed()); cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
         // Thread coordinates and tile addresses are re-derived from opaque copies in every
         // chunk: otherwise the compiler hoists each per-lane LDS address out of the loop
@@ -1249,6 +1267,14 @@ __global__ void __launch_bounds__(NW * 64)
             bet[tid] = pb;
             ea[tid] = __expf(gam);
             ed[tid] = __expf(gl - gam);
+            if constexpr (C::STOP) {
+                // running log of a bound on the norm of the job's transition: each chunk
+                // adds Gamma_C, valid while every beta lies in [0, 1.9] (else +inf; 1.9
+                // leaves room for keys a rounding above unit length: beta |k|^2 < 2)
+                const bool bad = __ballot(!(pb >= 0.f && pb <= 1.9f)) != 0;
+                if (tid == 0)
+                    graw[4 * CH] += bad ? __builtin_inff() : gl;
+            }
         }
         __syncthreads();
 
@@ -1669,6 +1695,13 @@ __global__ void __launch_bounds__(NW * 64)
             }
         }
         __syncthreads();
+    }
+    if (underflowed()) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int mb = 0; mb < DK / 16; ++mb)
+                hs[cb][mb] = zero4();
     }
     if constexpr (GATE) {  // the last chunk's z tile: every wave's LDS-DMA loads landed
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

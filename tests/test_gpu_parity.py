@@ -231,3 +231,24 @@ def test_refused_calls_leave_buffers_unchanged():
     for a, b in zip((call.o, call.h, call.conv_state), before):
         assert torch.equal(a, b)
     assert ctypes.sizeof(p) == 72
+
+
+@pytest.mark.parametrize("case", ["gdn-front-T4096-H4", "gdn-bf16-T3000-H2"])
+def test_segmented_scan_fast_decay(case):
+    """Fast decay (log-gates -softplus(N(0,1))): each inner segment's transition underflows
+    within its first chunks, so the transition jobs stop early and write zeros. The call
+    still matches the oracle and the serial scan."""
+    from gated_delta_rule_depthwise_amd import binding as B
+    spec = (spec_small(2, lengths=[4096], H=4, seed=56) if case == "gdn-front-T4096-H4"
+            else spec_small(3, lengths=[3000], H=2, seed=57))
+    inp = inputs.make(spec)
+    seg = run_gpu(inp)
+    ser = run_gpu(inp, segmented=False)
+    assert B.gdn_segments(seg.params, seg.kind, spec.B, spec.N, seg.ws_bytes) >= 3
+    ref = run_oracle(inp)
+    e_seg = compare(seg, ref)
+    compare(ser, ref)
+    assert rel_err(seg.o[:spec.N].cpu().numpy(), ser.o[:spec.N].cpu().numpy()) <= 2e-2
+    assert rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy()) <= 2e-2
+    print("%s seg err(o)=%.3g err(h)=%.3g" % (spec.name, *e_seg), flush=True)
+
