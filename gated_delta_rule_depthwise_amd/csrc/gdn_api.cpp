@@ -314,7 +314,7 @@ size_t seg_bytes(const gdn_params *p, int32_t B, int S)
 {
     if (S < 3)
         return 0;
-    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S};
+    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S, p->H};
     return align_up((size_t)lay.total() * sizeof(float));
 }
 
@@ -467,7 +467,7 @@ int run(const Call &c)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
             cb.seg_ws = ca.seg_ws;
-            cb.lay = gdn::SegLayout{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S};
+            cb.lay = gdn::SegLayout{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
             cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;

@@ -63,10 +63,11 @@ struct GateArgs {
 };
 
 // Slots of the segmented scan, each one [H][dk][dv] fp32 (dk == dv): H(b, s), s = 1..S-1;
-// B(b, s) and A(b, s), s = 1..S-2.
+// B(b, s) and A(b, s), s = 1..S-2; then one flag per (b, s, head), 1.0 when the transition
+// job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0.
 struct SegLayout {
     int64_t slot;  // floats per slot
-    int32_t B, S;
+    int32_t B, S, H;
     __host__ __device__ int64_t h(int b, int s) const
     {
         return ((int64_t)b * (S - 1) + s - 1) * slot;
@@ -79,7 +80,14 @@ struct SegLayout {
     {
         return ((int64_t)B * (2 * S - 3) + (int64_t)b * (S - 2) + s - 1) * slot;
     }
-    __host__ __device__ int64_t total() const { return (int64_t)B * (3 * S - 5) * slot; }
+    __host__ __device__ int64_t zero_flag(int b, int s, int head) const
+    {
+        return (int64_t)B * (3 * S - 5) * slot + ((int64_t)b * S + s) * H + head;
+    }
+    __host__ __device__ int64_t total() const
+    {
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H;
+    }
 };
 
 // h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).

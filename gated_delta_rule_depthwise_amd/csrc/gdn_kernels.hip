@@ -955,8 +955,9 @@ __global__ void __launch_bounds__(NW * 64)
     const float *hin = state;  // nullptr: start from 0
     float *hout = state;       // nullptr: the end state is not needed
     bool h_ident = false, v_zero = false, write_o = true;
+    float *zflag = nullptr;  // transition jobs: whether their transition was found zero
     if (a.pass != 0) {
-        const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg};
+        const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg, H};
         const int S = a.nseg;
         int seg;
         if (a.pass == 1) {
@@ -968,6 +969,8 @@ __global__ void __launch_bounds__(NW * 64)
             }
             hout = a.seg_ws + (job == 0 ? lay.h(b, 1) : job <= S - 2 ? lay.bs(b, seg)
                                                                        : lay.as(b, seg));
+            if (h_ident)
+                zflag = a.seg_ws + lay.zero_flag(b, seg, head);
         } else {
             seg = job + 1;
             hin = a.seg_ws + lay.h(b, seg);
@@ -1696,13 +1699,16 @@ __global__ void __launch_bounds__(NW * 64)
         }
         __syncthreads();
     }
-    if (underflowed()) {
+    const bool zero_transition = underflowed();
+    if (zero_transition) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb)
                 hs[cb][mb] = zero4();
     }
+    if (zflag && tid0 == 0)  // every transition job writes its flag (the workspace is reused)
+        *zflag = zero_transition ? 1.f : 0.f;
     if constexpr (GATE) {  // the last chunk's z tile: every wave's LDS-DMA loads landed
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -1841,19 +1847,25 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     for (int idx = tid; idx < DK * 16; idx += NWV * 64)
         hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
 
+    // A step whose transition job found A(b, s) zero is h(b, s+1) = B(b, s): no A to load, no
+    // product, and no wait for h(b, s) (the flag is the same for the whole workgroup).
+    auto zero_at = [&](int s) { return a.seg_ws[a.lay.zero_flag(b, s, head)] != 0.f; };
     // A blocks and B rows of the next two steps (ring of 2), so a step's loads have two
     // steps' time to arrive
     f32x4 av[2][RBW][NRB], bv[2][RBW];
     auto load = [&](int s, int slot) {
         const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk]
         const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
+        const bool za = zero_at(s);
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int rb = wave + NWV * j;
             if (rb < NRB) {
+                if (!za) {
 #pragma unroll
-                for (int kb = 0; kb < NRB; ++kb)
-                    av[slot][j][kb] = blk_a(A, DK, rb, kb, lane);
+                    for (int kb = 0; kb < NRB; ++kb)
+                        av[slot][j][kb] = blk_a(A, DK, rb, kb, lane);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     bv[slot][j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
@@ -1861,12 +1873,13 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
         }
     };
     auto step = [&](int s, int slot) {
+        const bool zs = zero_at(s);
         f32x4 acc[RBW];
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int rb = wave + NWV * j;
             acc[j] = bv[slot][j];
-            if (rb < NRB) {
+            if (rb < NRB && !zs) {
 #pragma unroll
                 for (int kb = 0; kb < NRB; ++kb) {
                     const float *hc = &hsm[16 * kb + 4 * g4][c16];
@@ -1876,7 +1889,8 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
         }
         if (s + 2 <= S - 2)
             load(s + 2, slot);
-        __syncthreads();  // every wave has read h(b, s)
+        if (!zs)
+            __syncthreads();  // every wave has read h(b, s)
         float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
@@ -1890,7 +1904,10 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
                 }
             }
         }
-        __syncthreads();
+        // the next step reads h(b, s+1) from every wave's rows unless its transition is zero
+        // (each wave writes the same rows in every step, so a zero step needs no wait)
+        if (s + 1 <= S - 2 && !zero_at(s + 1))
+            __syncthreads();
     };
     load(1, 0);
     if (S - 2 >= 2)
