@@ -1846,17 +1846,21 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     const float *h1 = a.seg_ws + a.lay.h(b, 1) + hoff;
     for (int idx = tid; idx < DK * 16; idx += NWV * 64)
         hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
+    // the zero-transition flags of every step, read once (visible after the first barrier)
+    __shared__ float zf[32];
+    if (tid < S - 2 && tid < 32)
+        zf[tid] = a.seg_ws[a.lay.zero_flag(b, tid + 1, head)];
 
     // A step whose transition job found A(b, s) zero is h(b, s+1) = B(b, s): no A to load, no
     // product, and no wait for h(b, s) (the flag is the same for the whole workgroup).
-    auto zero_at = [&](int s) { return a.seg_ws[a.lay.zero_flag(b, s, head)] != 0.f; };
+    auto zero_at = [&](int s) { return zf[s - 1] != 0.f; };
     // A blocks and B rows of the next two steps (ring of 2), so a step's loads have two
     // steps' time to arrive
     f32x4 av[2][RBW][NRB], bv[2][RBW];
-    auto load = [&](int s, int slot) {
+    auto load = [&](int s, int slot, bool flags_known) {
         const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk]
         const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
-        const bool za = zero_at(s);
+        const bool za = flags_known && zero_at(s);
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int rb = wave + NWV * j;
@@ -1888,7 +1892,7 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
             }
         }
         if (s + 2 <= S - 2)
-            load(s + 2, slot);
+            load(s + 2, slot, true);
         if (!zs)
             __syncthreads();  // every wave has read h(b, s)
         float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
@@ -1909,10 +1913,11 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
         if (s + 1 <= S - 2 && !zero_at(s + 1))
             __syncthreads();
     };
-    load(1, 0);
+    // the first two steps' blocks are requested before the flags are visible (A included)
+    load(1, 0, false);
     if (S - 2 >= 2)
-        load(2, 1);
-    __syncthreads();
+        load(2, 1, false);
+    __syncthreads();  // h(b, 1) and the flags
     // the ring slot is a compile-time index: steps go in pairs
     for (int s = 1; s <= S - 2; s += 2) {
         step(s, 0);
