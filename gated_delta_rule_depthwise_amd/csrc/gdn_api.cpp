@@ -253,20 +253,22 @@ double seg_cost(int S, int64_t l0, int64_t l1, int64_t last, int64_t U, int ncu)
 
 // The plan of one call: cached for the last shape asked (every call of a model layer asks
 // the same).
-SegPlan seg_search(int64_t nc, int64_t U, int ncu)
+// With warm starts possible (max_s > 0), S is at most max_s: a call in warm mode runs segment
+// 0 and S - 1 warm jobs per (stream, head) in one launch, which then fits one round.
+SegPlan seg_search(int64_t nc, int64_t U, int ncu, int max_s)
 {
     static std::mutex mu;
     static int64_t k_nc = -1, k_u = -1;
-    static int k_ncu = -1;
+    static int k_ncu = -1, k_max = -1;
     static SegPlan k_plan{0, 0, 0};
     std::lock_guard<std::mutex> g(mu);
-    if (nc == k_nc && U == k_u && ncu == k_ncu)
+    if (nc == k_nc && U == k_u && ncu == k_ncu && max_s == k_max)
         return k_plan;
     CuPool serial(ncu);
     serial.run(U, (double)nc);
     double best = 0.8 * serial.end;  // segment only for a clear gain
     SegPlan plan{0, 0, 0};
-    for (int S = 3; S <= kMaxSeg && S <= nc; ++S) {
+    for (int S = 3; S <= kMaxSeg && S <= nc && (max_s == 0 || S <= max_s); ++S) {
         // inner segments from about nc / S to nc / (S - 2) chunks, segment 0 up to about
         // twice as long; long streams are searched on a coarser grid (at most ~32 x 64
         // candidates per S)
@@ -285,11 +287,15 @@ SegPlan seg_search(int64_t nc, int64_t U, int ncu)
             }
         }
     }
-    k_nc = nc, k_u = U, k_ncu = ncu, k_plan = plan;
+    k_nc = nc, k_u = U, k_ncu = ncu, k_max = max_s, k_plan = plan;
     return plan;
 }
 
-SegPlan seg_plan(const gdn_params *p, int32_t B, int64_t tps, int nslices, int ncu)
+// Warm starts apply to calls whose keys have unit length or less (L2 in the call or in the
+// front end) and without the fused output gate; the scalar gate is checked at launch.
+bool warm_capable(const gdn_params *p) { return p->eps >= 0.f && !p->z; }
+
+SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslices, int ncu)
 {
     SegPlan none{0, 0, 0};
     if (p->dk != p->dv || p->chunk != 64 || tps < 1)
@@ -307,7 +313,9 @@ SegPlan seg_plan(const gdn_params *p, int32_t B, int64_t tps, int nslices, int n
         const int Se = (int)((nc + L - 1) / L);
         return Se >= 3 ? SegPlan{Se, L * 64, L * 64} : none;
     }
-    return seg_search(nc, (int64_t)B * p->H * nslices, ncu);
+    const int64_t U = (int64_t)B * p->H * nslices;
+    const int max_s = !kda && warm_capable(p) && ncu / U >= 3 ? (int)(ncu / U) : 0;
+    return seg_search(nc, U, ncu, max_s);
 }
 
 size_t seg_bytes(const gdn_params *p, int32_t B, int S)
@@ -376,7 +384,7 @@ int run(const Call &c)
     // segmented scan when it pays and the workspace has room for its states
     SegPlan sp{0, 0, 0};
     if (!c.st.cu) {
-        sp = seg_plan(p, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
+        sp = seg_plan(p, c.kda, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
         if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.st.B, sp.S) ||
                      grid * (2 * sp.S - 3) > (int64_t)INT32_MAX))
             sp = SegPlan{0, 0, 0};
@@ -461,13 +469,28 @@ int run(const Call &c)
             ca.seg0_len = sp.seg0_len;
             ca.seg_len = sp.seg_len;
             ca.seg_ws = (float *)((char *)c.ws + need);
+            const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
+            // warm starts: the plan of each (stream, head) from its gates, before pass 1
+            ca.warm = !c.kda && warm_capable(p) && sp.S <= 32;
+            if (ca.warm) {
+                gdn::WarmArgs wa{};
+                wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
+                wa.nseg = sp.S, wa.seg0_len = sp.seg0_len, wa.seg_len = sp.seg_len;
+                wa.seg_ws = ca.seg_ws, wa.lay = lay;
+                if (gdn::launch_warm_plan(wa, c.stream) != hipSuccess)
+                    return GDN_E_HIP;
+            }
             ca.pass = 1;
+            const int64_t jobs1 = ca.warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
+            if (grid * jobs1 > (int64_t)INT32_MAX)
+                return GDN_E_ARG;
             if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
-                                  (int)(grid * (2 * sp.S - 3)), c.stream) != hipSuccess)
+                                  (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
             cb.seg_ws = ca.seg_ws;
-            cb.lay = gdn::SegLayout{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
+            cb.lay = lay;
+            cb.warm = ca.warm;
             cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;
@@ -723,7 +746,8 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
     if (kind == GDN_KIND_VARLEN)
         return 0;
     const Shape sh = pick_shape(p, rc0 == GDN_OK ? 0 : 1, (int64_t)B * p->H);
-    const SegPlan sp = seg_plan(p, B, t_per_stream, p->dv / sh.nv, cu_count());
+    const SegPlan sp = seg_plan(p, rc0 == GDN_OK ? 0 : 1, B, t_per_stream, p->dv / sh.nv,
+                                cu_count());
     const size_t need = front_bytes(p, (int64_t)B * t_per_stream);
     if (!sp.S || ws_bytes < need + seg_bytes(p, B, sp.S))
         return 0;

@@ -39,6 +39,10 @@ struct ChunkArgs {
     // seg0_len tokens, segments 1..S-2 seg_len each, segment S-1 the rest of the stream.
     int32_t pass;
     int32_t nseg;           // S
+    // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
+    // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
+    // the map jobs, the chain and pass 2 then return at once
+    int32_t warm;
     int64_t seg0_len;       // tokens of segment 0, a multiple of the chunk
     int64_t seg_len;        // tokens of each inner segment, a multiple of the chunk
     float *seg_ws;
@@ -64,7 +68,9 @@ struct GateArgs {
 
 // Slots of the segmented scan, each one [H][dk][dv] fp32 (dk == dv): H(b, s), s = 1..S-1;
 // B(b, s) and A(b, s), s = 1..S-2; then one flag per (b, s, head), 1.0 when the transition
-// job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0.
+// job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0; then the
+// warm-start plan: per (b, head) the mode (1.0: every segment starts warm, no chain) and
+// per (b, s, head) the chunks of warm-up before segment s.
 struct SegLayout {
     int64_t slot;  // floats per slot
     int32_t B, S, H;
@@ -84,9 +90,18 @@ struct SegLayout {
     {
         return (int64_t)B * (3 * S - 5) * slot + ((int64_t)b * S + s) * H + head;
     }
+    __host__ __device__ int64_t warm_mode(int b, int head) const
+    {
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H + (int64_t)b * H + head;
+    }
+    __host__ __device__ int64_t warm_chunks(int b, int s, int head) const
+    {
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H + (int64_t)B * H +
+               ((int64_t)b * S + s) * H + head;
+    }
     __host__ __device__ int64_t total() const
     {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H;
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * (2 * S + 1) * H;
     }
 };
 
@@ -95,6 +110,22 @@ struct CombineArgs {
     float *seg_ws;
     SegLayout lay;
     int32_t H, dk, dv;
+    int32_t warm;           // (stream, head) pairs in warm mode have no chain
+};
+
+// Warm-start plan of a segmented call: per (stream, head), each chunk's total log-gate and
+// whether its betas lie in [0, 1.9]; per segment boundary the fewest chunks before it whose
+// log-gates sum below -110; warm mode when every boundary has such a window inside the
+// previous segment.
+struct WarmArgs {
+    const float *g;         // [N][H]
+    const float *beta;      // [N][H]
+    Streams st;
+    int32_t H;
+    int32_t nseg;
+    int64_t seg0_len, seg_len;
+    float *seg_ws;
+    SegLayout lay;
 };
 
 // Front end: conv + SiLU (+ L2 and scale of q, k) over every channel of the packed rows.
@@ -147,6 +178,7 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 // the output gate as its own pass (dtype: element type of z, GDN_F32 or GDN_BF16)
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 // q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after
 // the step by a pass of its own

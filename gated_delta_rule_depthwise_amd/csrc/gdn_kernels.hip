@@ -956,22 +956,40 @@ __global__ void __launch_bounds__(NW * 64)
     float *hout = state;       // nullptr: the end state is not needed
     bool h_ident = false, v_zero = false, write_o = true;
     float *zflag = nullptr;  // transition jobs: whether their transition was found zero
+    int64_t warm_rows = 0;   // warm jobs: rows run from h = 0 before the segment, without o
     if (a.pass != 0) {
         const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg, H};
         const int S = a.nseg;
+        // warm mode of this (stream, head): uniform over the workgroup; the jobs it makes
+        // redundant return before touching LDS or a barrier
+        const bool warm = a.warm && a.seg_ws[lay.warm_mode(b, head)] != 0.f;
         int seg;
         if (a.pass == 1) {
-            seg = job <= S - 2 ? job : job - (S - 2);
-            if (job > 0) {
+            if (job >= 2 * S - 3) {  // warm job of segment job - (2S - 4)
+                if (!warm)
+                    return;
+                seg = job - (2 * S - 4);
                 hin = nullptr;
-                write_o = false;
-                h_ident = v_zero = job > S - 2;
+                if (seg < S - 1)
+                    hout = nullptr;
+                warm_rows = (int64_t)a.seg_ws[lay.warm_chunks(b, seg, head)] * CH;
+            } else {
+                if (warm && job > 0)
+                    return;
+                seg = job <= S - 2 ? job : job - (S - 2);
+                if (job > 0) {
+                    hin = nullptr;
+                    write_o = false;
+                    h_ident = v_zero = job > S - 2;
+                }
+                hout = a.seg_ws + (job == 0 ? lay.h(b, 1) : job <= S - 2 ? lay.bs(b, seg)
+                                                                           : lay.as(b, seg));
+                if (h_ident)
+                    zflag = a.seg_ws + lay.zero_flag(b, seg, head);
             }
-            hout = a.seg_ws + (job == 0 ? lay.h(b, 1) : job <= S - 2 ? lay.bs(b, seg)
-                                                                       : lay.as(b, seg));
-            if (h_ident)
-                zflag = a.seg_ws + lay.zero_flag(b, seg, head);
         } else {
+            if (warm)
+                return;
             seg = job + 1;
             hin = a.seg_ws + lay.h(b, seg);
             if (seg < S - 1)
@@ -982,6 +1000,10 @@ __global__ void __launch_bounds__(NW * 64)
         if (seg < S - 1)  // the last segment runs to the stream's end
             end = min(start + (seg == 0 ? a.seg0_len : a.seg_len), end);
     }
+    // o is written from row o_start on (never by map jobs); a warm job starts warm_rows
+    // earlier, from h = 0, with chunks that compute no o
+    const int64_t o_start = write_o ? start : INT64_MAX;
+    start -= warm_rows;
     const int64_t hoff = (int64_t)head * DK * DV;
     const int colw = slice * NV + wave0 * 16 * NCB;  // this wave's first dv column
 
@@ -1047,9 +1069,10 @@ __global__ void __launch_bounds__(NW * 64)
     const float *b_src = a.beta + (int64_t)(tid0 & (CH - 1)) * H + head;
     auto prefetch = [&](int64_t c0, int Lc) {
         const int64_t roff = c0 * ld;
+        const bool with_q = c0 >= o_start;  // q rows only feed o
 #pragma unroll
         for (int it = 0; it < NQK; ++it)
-            pq[it] = qk_row[it] < Lc && (qk_isk[it] || write_o)
+            pq[it] = qk_row[it] < Lc && (qk_isk[it] || with_q)
                          ? load_stream16(qk_src[it] + roff)
                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -1187,6 +1210,7 @@ __global__ void __launch_bounds__(NW * 64)
     };
     for (int64_t cs = start; cs < end && !(cs > start && underflowed()); cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
+        write_o = cs >= o_start;  // this chunk computes o
         // Thread coordinates and tile addresses are re-derived from opaque copies in every
         // chunk: otherwise the compiler hoists each per-lane LDS address out of the loop
         // and holds a register for every one of them across all stages.
@@ -1326,7 +1350,7 @@ __global__ void __launch_bounds__(NW * 64)
         // chunk's rows are requested at the start of the state stage. (Issued together
         // right after the loads above, they would hold every wave while the CU's
         // vector-memory path drains.)
-        if (C::STAGE_O && write_o && cs > start)
+        if (C::STAGE_O && cs - CH >= o_start && cs > start)
             flush_o(Os, cs - CH, CH, tid);  // only the last chunk of a stream is partial
 
         // Two waves share a SIMD and the older one wins every issue slot: without help the
@@ -1713,7 +1737,8 @@ __global__ void __launch_bounds__(NW * 64)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    if (C::STAGE_O && write_o && start < end) {  // the last chunk's o (loop ends on a barrier)
+    if (C::STAGE_O && end > o_start && start < end) {  // the last chunk's o (the loop ends
+                                                          // on a barrier)
         const int64_t last = start + (end - start - 1) / CH * CH;
         flush_o((const float *)(smem + C::OFF_O), last, (int)(end - last), tid0);
     }
@@ -1837,6 +1862,8 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     const int BH = a.lay.B * a.H;
     const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
     const int b = bh / a.H, head = bh - b * a.H;
+    if (a.warm && a.seg_ws[a.lay.warm_mode(b, head)] != 0.f)
+        return;  // every segment of this (stream, head) starts warm: no chain
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -1924,6 +1951,89 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
         if (s + 1 <= S - 2)
             step(s + 1, 1);
     }
+}
+
+// One workgroup per (stream, head); see WarmArgs. Chunks are those of the stream's own grid
+// (the segment boundaries fall on it).
+constexpr int WARM_MAX_CHUNKS = 2048;
+__global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
+{
+    __shared__ float gsum[WARM_MAX_CHUNKS];
+    __shared__ int ok[32];
+    const int b = blockIdx.x / a.H, head = blockIdx.x - b * a.H;
+    const int tid = threadIdx.x;
+    int64_t start, end;
+    stream_bounds(a.st, b, start, end);
+    const int64_t nc = (end - start + CH - 1) / CH;
+    const int S = a.nseg;
+    if (nc <= WARM_MAX_CHUNKS) {
+        // a wave sums a chunk, lane l reading its row l; each wave takes 4 chunks at a time
+        // (chunks base + wave + 4u), their loads issued together
+        const int lane = tid & 63, wv = tid >> 6;
+        for (int64_t base = 0; base < nc; base += 16) {
+            float gv[4];
+            bool bd[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = base + wv + 4 * u, r = start + c * CH + lane;
+                const bool in = c < nc && r < end;
+                gv[u] = in ? a.g[r * a.H + head] : 0.f;
+                const float bt = in ? a.beta[r * a.H + head] : 0.f;
+                bd[u] = in && !(bt >= 0.f && bt <= 1.9f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = base + wv + 4 * u;
+                const float sum = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gv[u])),
+                                                     63));
+                const bool bad = __ballot(bd[u]) != 0;
+                if (c < nc && lane == 0)
+                    gsum[c] = bad ? __builtin_inff() : sum;  // +inf: no bound through it
+            }
+        }
+    }
+    __syncthreads();
+    // boundary s (segment s's first chunk cs): the fewest chunks w before it, inside
+    // segment s - 1, whose total log-gate is below -110
+    if (tid < 32) {
+        int w_ok = 1;
+        if (tid >= 1 && tid <= S - 1) {
+            const int s = tid;
+            const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
+            const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
+            int w = 0;
+            w_ok = 0;
+            if (nc <= WARM_MAX_CHUNKS && cs <= nc) {
+                float acc = 0.f;
+                for (int64_t c = cs - 1; c >= cp; --c) {
+                    acc += gsum[c];
+                    ++w;
+                    if (acc < -110.f) {
+                        w_ok = 1;
+                        break;
+                    }
+                }
+            }
+            a.seg_ws[a.lay.warm_chunks(b, s, head)] = w_ok ? (float)w : 0.f;
+        }
+        ok[tid] = w_ok;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int all = 1;
+        for (int s = 1; s <= S - 1 && s < 32; ++s)
+            all &= ok[s];
+        a.seg_ws[a.lay.warm_mode(b, head)] = (all && S - 1 < 32) ? 1.f : 0.f;
+    }
+}
+
+hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
+{
+    if (a.nseg < 3 || a.nseg > 32 || a.seg0_len % CH || a.seg_len % CH)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(warm_plan_kernel, dim3((unsigned)(a.st.B * a.H)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s)

@@ -274,7 +274,8 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
 
 /* Segments per stream (S >= 3, or 0 for an unsegmented scan) that a single (kind
- * GDN_KIND_SINGLE, B = 1) or batched (GDN_KIND_BATCHED) call with these parameters,
+ * GDN_KIND_SINGLE, B = 1) or batched (GDN_KIND_BATCHED) GDN call (a KDA call when only the
+ * per-key-channel gate is compiled for these parameters) with these parameters,
  * t_per_stream tokens per stream and ws_bytes of workspace would use on the current device;
  * always 0 for GDN_KIND_VARLEN. Negative status for invalid arguments. Host only; enqueues
  * nothing. The environment variable GDN_SEG (read once) overrides the choice: 0 never

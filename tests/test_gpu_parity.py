@@ -252,3 +252,21 @@ def test_segmented_scan_fast_decay(case):
     assert rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy()) <= 2e-2
     print("%s seg err(o)=%.3g err(h)=%.3g" % (spec.name, *e_seg), flush=True)
 
+
+def test_segmented_scan_mixed_warm_and_chain():
+    """Heads 0-1 decay slowly (their segments start from the chain of segment maps), heads
+    2-3 fast (their segments start warm, from h = 0 a few chunks early): one call holds both
+    modes, and every head matches the oracle and the serial scan."""
+    import dataclasses
+    fast = spec_small(2, lengths=[4096], H=4, seed=58)
+    slow = dataclasses.replace(fast, gate_dist="slow")
+    inp = inputs.make(fast)
+    inp["g"][:, :2] = inputs.make(slow)["g"][:, :2]
+    seg = run_gpu(inp)
+    ser = run_gpu(inp, segmented=False)
+    ref = run_oracle(inp)
+    compare(seg, ref)
+    compare(ser, ref)
+    assert rel_err(seg.o[:fast.N].cpu().numpy(), ser.o[:fast.N].cpu().numpy()) <= 2e-2
+    assert rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy()) <= 2e-2
+
