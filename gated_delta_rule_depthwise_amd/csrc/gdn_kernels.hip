@@ -1953,84 +1953,66 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     }
 }
 
-// One workgroup per (stream, head); see WarmArgs. Chunks are those of the stream's own grid
-// (the segment boundaries fall on it).
-constexpr int WARM_MAX_CHUNKS = 2048;
+// One workgroup per (stream, head); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
+// it walks back from the boundary over the previous segment's chunks, four at a time (lane l
+// reading row l of each), until their log-gates sum below -110.
 __global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
 {
-    __shared__ float gsum[WARM_MAX_CHUNKS];
     __shared__ int ok[32];
     const int b = blockIdx.x / a.H, head = blockIdx.x - b * a.H;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
-    const int64_t nc = (end - start + CH - 1) / CH;
     const int S = a.nseg;
-    if (nc <= WARM_MAX_CHUNKS) {
-        // a wave sums a chunk, lane l reading its row l; each wave takes 4 chunks at a time
-        // (chunks base + wave + 4u), their loads issued together
-        const int lane = tid & 63, wv = tid >> 6;
-        for (int64_t base = 0; base < nc; base += 16) {
-            float gv[4];
-            bool bd[4];
+    if (tid < 32)
+        ok[tid] = 1;
+    __syncthreads();
+    for (int s = wv + 1; s <= S - 1; s += 4) {  // uniform per wave
+        const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
+        const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
+        float acc = 0.f;
+        int w = 0, done = 0;  // done: 1 found, -1 not possible
+        for (int64_t c0 = cs - 1; c0 >= cp && !done; c0 -= 4) {
+            float gv[4], bv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int64_t c = base + wv + 4 * u, r = start + c * CH + lane;
-                const bool in = c < nc && r < end;
+                const int64_t r = start + (c0 - u) * CH + lane;
+                const bool in = c0 - u >= cp && r < end;
                 gv[u] = in ? a.g[r * a.H + head] : 0.f;
-                const float bt = in ? a.beta[r * a.H + head] : 0.f;
-                bd[u] = in && !(bt >= 0.f && bt <= 1.9f);
+                bv[u] = in ? a.beta[r * a.H + head] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int64_t c = base + wv + 4 * u;
                 const float sum = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gv[u])),
                                                      63));
-                const bool bad = __ballot(bd[u]) != 0;
-                if (c < nc && lane == 0)
-                    gsum[c] = bad ? __builtin_inff() : sum;  // +inf: no bound through it
-            }
-        }
-    }
-    __syncthreads();
-    // boundary s (segment s's first chunk cs): the fewest chunks w before it, inside
-    // segment s - 1, whose total log-gate is below -110
-    if (tid < 32) {
-        int w_ok = 1;
-        if (tid >= 1 && tid <= S - 1) {
-            const int s = tid;
-            const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
-            const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
-            int w = 0;
-            w_ok = 0;
-            if (nc <= WARM_MAX_CHUNKS && cs <= nc) {
-                float acc = 0.f;
-                for (int64_t c = cs - 1; c >= cp; --c) {
-                    acc += gsum[c];
-                    ++w;
-                    if (acc < -110.f) {
-                        w_ok = 1;
-                        break;
+                const bool bad = __ballot(!(bv[u] >= 0.f && bv[u] <= 1.9f)) != 0;
+                if (!done && c0 - u >= cp) {
+                    if (bad) {
+                        done = -1;
+                    } else {
+                        acc += sum;
+                        ++w;
+                        if (acc < -110.f)
+                            done = 1;
                     }
                 }
             }
-            a.seg_ws[a.lay.warm_chunks(b, s, head)] = w_ok ? (float)w : 0.f;
         }
-        ok[tid] = w_ok;
+        if (lane == 0) {
+            a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
+            if (done != 1)
+                ok[0] = 0;
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        int all = 1;
-        for (int s = 1; s <= S - 1 && s < 32; ++s)
-            all &= ok[s];
-        a.seg_ws[a.lay.warm_mode(b, head)] = (all && S - 1 < 32) ? 1.f : 0.f;
-    }
+    if (tid == 0)
+        a.seg_ws[a.lay.warm_mode(b, head)] = ok[0] ? 1.f : 0.f;
 }
 
 hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
 {
-    if (a.nseg < 3 || a.nseg > 32 || a.seg0_len % CH || a.seg_len % CH)
+    if (a.nseg < 3 || a.seg0_len % CH || a.seg_len % CH)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(warm_plan_kernel, dim3((unsigned)(a.st.B * a.H)), dim3(256), 0, s, a);
     return hipGetLastError();
