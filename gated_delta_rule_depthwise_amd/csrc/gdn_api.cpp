@@ -292,8 +292,8 @@ SegPlan seg_search(int64_t nc, int64_t U, int ncu, int max_s)
 }
 
 // Warm starts apply to calls whose keys have unit length or less (L2 in the call or in the
-// front end) and without the fused output gate; the scalar gate is checked at launch.
-bool warm_capable(const gdn_params *p) { return p->eps >= 0.f && !p->z; }
+// front end); the scalar gate is checked at launch.
+bool warm_capable(const gdn_params *p) { return p->eps >= 0.f; }
 
 SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslices, int ncu)
 {
