@@ -238,8 +238,10 @@ def main() -> int:
     if args.decode:
         kname = "decode_kernel (front end + one recurrence step + window update, fused)"
     elif dom == "recur" and segs:
-        kname = ("recur: chunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
-                 "(segmented scan, %d segments)" % segs)
+        kname = ("recur: %schunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
+                 "(segmented scan, %d segments%s)"
+                 % ("" if spec.gate == "kda" else "warm_plan_kernel + ", segs,
+                    "" if spec.gate == "kda" else "; warm starts where the gates allow"))
     else:
         kname = dom
 
