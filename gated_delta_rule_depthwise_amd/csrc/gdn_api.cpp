@@ -414,8 +414,23 @@ int run(const Call &c)
         ca.norm_w = p->norm_w;
         ca.norm_eps = p->norm_eps;
     }
+    // warm starts (segmented calls): the plan of each (stream, head) from its gates, run by
+    // extra workgroups of the front launch when there is one, else by a launch of its own
+    // at the start of the scan
+    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
+    gdn::WarmArgs wa{};
+    ca.warm = sp.S && !c.kda && warm_capable(p);
+    if (ca.warm) {
+        wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
+        wa.nseg = sp.S, wa.seg0_len = sp.seg0_len, wa.seg_len = sp.seg_len;
+        wa.seg_ws = (float *)((char *)c.ws + need), wa.lay = lay;
+    }
     FrontArgs fa{};
     if (front) {
+        if (ca.warm) {
+            fa.warm = wa;
+            fa.warm_groups = c.st.B * p->H;
+        }
         fa.q = c.q, fa.k = c.k, fa.v = c.v, fa.ld = p->ld_qkv;
         fa.conv_w = c.conv_w;
         fa.conv_state = c.conv_state;
@@ -469,14 +484,7 @@ int run(const Call &c)
             ca.seg0_len = sp.seg0_len;
             ca.seg_len = sp.seg_len;
             ca.seg_ws = (float *)((char *)c.ws + need);
-            const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
-            // warm starts: the plan of each (stream, head) from its gates, before pass 1
-            ca.warm = !c.kda && warm_capable(p) && sp.S <= 32;
-            if (ca.warm) {
-                gdn::WarmArgs wa{};
-                wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
-                wa.nseg = sp.S, wa.seg0_len = sp.seg0_len, wa.seg_len = sp.seg_len;
-                wa.seg_ws = ca.seg_ws, wa.lay = lay;
+            if (ca.warm && !front) {
                 if (gdn::launch_warm_plan(wa, c.stream) != hipSuccess)
                     return GDN_E_HIP;
             }

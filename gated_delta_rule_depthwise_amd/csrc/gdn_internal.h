@@ -113,6 +113,7 @@ struct CombineArgs {
     int32_t warm;           // (stream, head) pairs in warm mode have no chain
 };
 
+
 // Warm-start plan of a segmented call: per (stream, head), each chunk's total log-gate and
 // whether its betas lie in [0, 1.9]; per segment boundary the fewest chunks before it whose
 // log-gates sum below -110; warm mode when every boundary has such a window inside the
@@ -142,6 +143,10 @@ struct FrontArgs {
     int32_t do_l2;
     float eps, scale;
     int32_t tile_rows;      // tokens per workgroup tile: a multiple of 4, >= 32
+    // warm-start plan run by extra workgroups of the same launch (it reads only gates and
+    // betas), when warm_groups > 0: one per (stream, head)
+    WarmArgs warm;
+    int32_t warm_groups;
 };
 
 // One decode step: a single token per stream through the front end (optional), L2 and the

@@ -336,9 +336,81 @@ __device__ __forceinline__ int find_stream(const Streams &s, int64_t t)
     return lo;
 }
 
+constexpr int CH = 64;  // chunk length
+
+// One workgroup per (stream, head); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
+// it walks back from the boundary over the previous segment's chunks, four at a time (lane l
+// reading row l of each), until their log-gates sum below -110.
+__device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
+{
+    __shared__ int ok[32];
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int64_t start, end;
+    stream_bounds(a.st, b, start, end);
+    const int S = a.nseg;
+    if (tid < 32)
+        ok[tid] = 1;
+    __syncthreads();
+    for (int s = wv + 1; s <= S - 1; s += 4) {  // uniform per wave
+        const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
+        const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
+        float acc = 0.f;
+        int w = 0, done = 0;  // done: 1 found, -1 not possible
+        for (int64_t c0 = cs - 1; c0 >= cp && !done; c0 -= 4) {
+            float gv[4], bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t r = start + (c0 - u) * CH + lane;
+                const bool in = c0 - u >= cp && r < end;
+                gv[u] = in ? a.g[r * a.H + head] : 0.f;
+                bv[u] = in ? a.beta[r * a.H + head] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float sum = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gv[u])),
+                                                     63));
+                const bool bad = __ballot(!(bv[u] >= 0.f && bv[u] <= 1.9f)) != 0;
+                if (!done && c0 - u >= cp) {
+                    if (bad) {
+                        done = -1;
+                    } else {
+                        acc += sum;
+                        ++w;
+                        if (acc < -110.f)
+                            done = 1;
+                    }
+                }
+            }
+        }
+        if (lane == 0) {
+            a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
+            if (done != 1)
+                ok[0] = 0;
+        }
+    }
+    __syncthreads();
+    if (tid == 0)
+        a.seg_ws[a.lay.warm_mode(b, head)] = ok[0] ? 1.f : 0.f;
+}
+
+__global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
+{
+    warm_plan_block(a, blockIdx.x);
+}
+
 template <typename T, typename TOUT, int K>
 __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
 {
+    static_assert(FRONT_THREADS == 256, "the warm-start plan runs on 256 threads");
+    if (blockIdx.y >= (a.N + a.tile_rows - 1) / a.tile_rows) {  // extra rows: warm plan
+        const int64_t i = (int64_t)(blockIdx.y - (a.N + a.tile_rows - 1) / a.tile_rows) *
+                              gridDim.x + blockIdx.x;
+        if (i < a.warm_groups)
+            warm_plan_block(a.warm, (int)i);
+        return;
+    }
     constexpr int W = K - 1;
     const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
     const int cg = blockIdx.x * FRONT_THREADS + threadIdx.x;  // channel group
@@ -534,8 +606,9 @@ hipError_t launch_front_tk(const FrontArgs &a, hipStream_t s)
     const int groups = cd / FRONT_CPT;
     if (a.tile_rows < FRONT_ROWS || a.tile_rows % 4)
         return hipErrorInvalidValue;
-    dim3 grid((groups + FRONT_THREADS - 1) / FRONT_THREADS,
-              (unsigned)((a.N + a.tile_rows - 1) / a.tile_rows));
+    const unsigned gx = (unsigned)((groups + FRONT_THREADS - 1) / FRONT_THREADS);
+    dim3 grid(gx, (unsigned)((a.N + a.tile_rows - 1) / a.tile_rows +
+                             (a.warm_groups + gx - 1) / gx));
     hipLaunchKernelGGL((front_kernel<T, TOUT, K>), grid, dim3(FRONT_THREADS), 0, s, a);
     return hipGetLastError();
 }
@@ -681,8 +754,6 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
 
 // ------------------------------------------------------------------------------------
 // fused chunk kernel
-
-constexpr int CH = 64;  // chunk length
 
 
 template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false>
@@ -1951,63 +2022,6 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
         if (s + 1 <= S - 2)
             step(s + 1, 1);
     }
-}
-
-// One workgroup per (stream, head); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
-// it walks back from the boundary over the previous segment's chunks, four at a time (lane l
-// reading row l of each), until their log-gates sum below -110.
-__global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
-{
-    __shared__ int ok[32];
-    const int b = blockIdx.x / a.H, head = blockIdx.x - b * a.H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int64_t start, end;
-    stream_bounds(a.st, b, start, end);
-    const int S = a.nseg;
-    if (tid < 32)
-        ok[tid] = 1;
-    __syncthreads();
-    for (int s = wv + 1; s <= S - 1; s += 4) {  // uniform per wave
-        const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
-        const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
-        float acc = 0.f;
-        int w = 0, done = 0;  // done: 1 found, -1 not possible
-        for (int64_t c0 = cs - 1; c0 >= cp && !done; c0 -= 4) {
-            float gv[4], bv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t r = start + (c0 - u) * CH + lane;
-                const bool in = c0 - u >= cp && r < end;
-                gv[u] = in ? a.g[r * a.H + head] : 0.f;
-                bv[u] = in ? a.beta[r * a.H + head] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float sum = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gv[u])),
-                                                     63));
-                const bool bad = __ballot(!(bv[u] >= 0.f && bv[u] <= 1.9f)) != 0;
-                if (!done && c0 - u >= cp) {
-                    if (bad) {
-                        done = -1;
-                    } else {
-                        acc += sum;
-                        ++w;
-                        if (acc < -110.f)
-                            done = 1;
-                    }
-                }
-            }
-        }
-        if (lane == 0) {
-            a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
-            if (done != 1)
-                ok[0] = 0;
-        }
-    }
-    __syncthreads();
-    if (tid == 0)
-        a.seg_ws[a.lay.warm_mode(b, head)] = ok[0] ? 1.f : 0.f;
 }
 
 hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
