@@ -270,7 +270,17 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
  * 1..S-1 from their start states. (The pages' chunked scan carries h serially across a
  * stream's chunks; the recurrence is affine in h, so the segment maps compose exactly up
  * to rounding.) A call whose ws_bytes covers the front end but not the segment states runs
- * unsegmented. */
+ * unsegmented.
+ *
+ * Two shortcuts of the segmented scan depend on the gates, decided on the device: with the
+ * scalar gate and keys of unit length or less (eps >= 0), every token multiplies a segment's
+ * transition by a factor of norm at most exp(g_t) while beta_t lies in [0, 1.9], so once a
+ * running sum of log-gates is below -110 the transition is zero in fp32. A transition job
+ * then stops and writes zeros, and the chain copies that step's end state. And when every
+ * segment boundary of a (stream, head) has such a window of chunks inside the previous
+ * segment, each segment starts from a zero state that many chunks early ("warm start"),
+ * all in the first launch, with no chain: the results are those of the chain up to fp32
+ * rounding. Slowly decaying heads take the chain; one call may hold both. */
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
 
 /* Segments per stream (S >= 3, or 0 for an unsegmented scan) that a single (kind
