@@ -465,6 +465,11 @@ int run(const Call &c)
         ca.do_l2 = 0;
         ca.unit_keys = p->eps >= 0.f;  // the front end normalised q and k
         ca.scale = 1.f;
+        // the new carried windows: extra workgroups of the scan's first launch (after the
+        // front end, the only reader of the old windows)
+        ca.window = fa;
+        ca.window_dtype = p->dtype == GDN_BF16;
+        ca.window_items = (int64_t)c.st.B * conv_dim(p);
     } else {
         ca.q = c.q, ca.k = c.k, ca.v = c.v, ca.ld = p->ld_qkv;
         ca.do_l2 = p->eps >= 0.f;
@@ -503,6 +508,7 @@ int run(const Call &c)
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;
             ca.pass = 2;
+            ca.window_items = 0;  // the windows went out with pass 1
             if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
                 return GDN_E_HIP;
@@ -520,12 +526,6 @@ int run(const Call &c)
         ga.eps = p->norm_eps;
         Stage st(GDN_PROF_GATE, c.stream);
         if (gdn::launch_gate(p->dtype, ga, c.stream) != hipSuccess)
-            return GDN_E_HIP;
-        st.done();
-    }
-    if (front) {
-        Stage st(GDN_PROF_STATE, c.stream);
-        if (gdn::launch_conv_state(p->dtype, fa, c.stream) != hipSuccess)
             return GDN_E_HIP;
         st.done();
     }

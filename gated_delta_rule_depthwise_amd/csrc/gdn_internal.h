@@ -14,46 +14,6 @@ struct Streams {
     int32_t B;
 };
 
-// Fused chunk kernel: per (stream, head, dv slice), every chunk of the stream in order.
-struct ChunkArgs {
-    const void *q, *k, *v;  // row r, value head h: q + r*ld + (h/qk_group)*dk (k likewise),
-    int64_t ld;             // v + r*ld + h*dv
-    const float *g;         // [N][H] or [N][H][dk]
-    const float *beta;      // [N][H]
-    float *h;               // single state [H][dk][dv] (when h_ptrs == nullptr)
-    float *const *h_ptrs;   // per-stream states
-    float *o;               // [N][H][dv]
-    Streams st;
-    int32_t H;              // value heads (the grid and the states)
-    int32_t qk_group;       // value heads per q/k head (H / Hqk)
-    int32_t do_l2;          // normalise q and k rows on load
-    int32_t unit_keys;      // keys arrive normalised or are normalised on load (|k| <= 1)
-    float eps;
-    float scale;            // multiplies q on load
-    // Segmented scan of long streams (see SegLayout). pass 0: each workgroup walks a whole
-    // stream. pass 1: job 0 runs segment 0 from the stream's state (o written, end state to
-    // slot H(b, 1)); jobs 1..S-2 run segment j from h = 0 (end state to slot B(b, j)); jobs
-    // S-1..2S-4 run segment j-(S-2) from h = I with v = 0 (end state, the segment's
-    // transition, to slot A(b, j-(S-2))). pass 2: job j runs segment j+1 from slot H(b, j+1)
-    // (o written; the last segment's end state to the stream's state). Segment 0 holds
-    // seg0_len tokens, segments 1..S-2 seg_len each, segment S-1 the rest of the stream.
-    int32_t pass;
-    int32_t nseg;           // S
-    // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
-    // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
-    // the map jobs, the chain and pass 2 then return at once
-    int32_t warm;
-    int64_t seg0_len;       // tokens of segment 0, a multiple of the chunk
-    int64_t seg_len;        // tokens of each inner segment, a multiple of the chunk
-    float *seg_ws;
-    // varlen: the stream of workgroup slot i (streams ranked longest first), or nullptr
-    const int32_t *order;
-    // output gate (fused instances): o <- o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
-    const void *z;          // row r of head h: z + r*ld_z + h*dv (bf16, or float for f32)
-    int64_t ld_z;
-    const float *norm_w;    // [dv]
-    float norm_eps;
-};
 
 // The output gate as a separate pass over rows [0, N) of o, all heads.
 struct GateArgs {
@@ -147,6 +107,53 @@ struct FrontArgs {
     // betas), when warm_groups > 0: one per (stream, head)
     WarmArgs warm;
     int32_t warm_groups;
+};
+
+// Fused chunk kernel: per (stream, head, dv slice), every chunk of the stream in order.
+struct ChunkArgs {
+    const void *q, *k, *v;  // row r, value head h: q + r*ld + (h/qk_group)*dk (k likewise),
+    int64_t ld;             // v + r*ld + h*dv
+    const float *g;         // [N][H] or [N][H][dk]
+    const float *beta;      // [N][H]
+    float *h;               // single state [H][dk][dv] (when h_ptrs == nullptr)
+    float *const *h_ptrs;   // per-stream states
+    float *o;               // [N][H][dv]
+    Streams st;
+    int32_t H;              // value heads (the grid and the states)
+    int32_t qk_group;       // value heads per q/k head (H / Hqk)
+    int32_t do_l2;          // normalise q and k rows on load
+    int32_t unit_keys;      // keys arrive normalised or are normalised on load (|k| <= 1)
+    float eps;
+    float scale;            // multiplies q on load
+    // Segmented scan of long streams (see SegLayout). pass 0: each workgroup walks a whole
+    // stream. pass 1: job 0 runs segment 0 from the stream's state (o written, end state to
+    // slot H(b, 1)); jobs 1..S-2 run segment j from h = 0 (end state to slot B(b, j)); jobs
+    // S-1..2S-4 run segment j-(S-2) from h = I with v = 0 (end state, the segment's
+    // transition, to slot A(b, j-(S-2))). pass 2: job j runs segment j+1 from slot H(b, j+1)
+    // (o written; the last segment's end state to the stream's state). Segment 0 holds
+    // seg0_len tokens, segments 1..S-2 seg_len each, segment S-1 the rest of the stream.
+    int32_t pass;
+    int32_t nseg;           // S
+    // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
+    // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
+    // the map jobs, the chain and pass 2 then return at once
+    int32_t warm;
+    // set by the launch: workgroups [0, job_groups) are jobs; the rest update the front
+    // end's carried windows (window_items = streams x channels, 0 when there is none)
+    int32_t job_groups;
+    int64_t window_items;
+    int32_t window_dtype;   // 1: bf16 rows, 0: fp32
+    FrontArgs window;
+    int64_t seg0_len;       // tokens of segment 0, a multiple of the chunk
+    int64_t seg_len;        // tokens of each inner segment, a multiple of the chunk
+    float *seg_ws;
+    // varlen: the stream of workgroup slot i (streams ranked longest first), or nullptr
+    const int32_t *order;
+    // output gate (fused instances): o <- o / sqrt(mean(o^2) + norm_eps) * norm_w * silu(z)
+    const void *z;          // row r of head h: z + r*ld_z + h*dv (bf16, or float for f32)
+    int64_t ld_z;
+    const float *norm_w;    // [dv]
+    float norm_eps;
 };
 
 // One decode step: a single token per stream through the front end (optional), L2 and the

@@ -561,12 +561,13 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
 
 // New carried window of every stream: the last K-1 entries of [old window | rows].
 // Runs after front_kernel (which reads the old windows), one thread per (stream, channel).
+// New carried window of every stream: the last K-1 entries of [old window | rows], one
+// item per (stream, channel); after every reader of the old window.
 template <typename T, int K>
-__global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
+__device__ __forceinline__ void conv_window_update(const FrontArgs &a, int64_t idx)
 {
     constexpr int W = K - 1;
     const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)a.st.B * cd)
         return;
     const int b = (int)(idx / cd), c = (int)(idx - (int64_t)b * cd);
@@ -597,6 +598,31 @@ __global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
 #pragma unroll
     for (int j = 0; j < W; ++j)
         cs[(int64_t)c * W + j] = nw[j];
+}
+
+template <typename T, int K>
+__global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
+{
+    conv_window_update<T, K>(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// The window update for item idx (stream-major channels) of a call of element type dtype
+// (1: bf16, 0: fp32) and a.K taps, for launches that carry it in extra workgroups.
+__device__ __forceinline__ void conv_window_item(const FrontArgs &a, int dtype, int64_t idx)
+{
+    if (dtype) {
+        switch (a.K) {
+        case 2: conv_window_update<bf16, 2>(a, idx); break;
+        case 3: conv_window_update<bf16, 3>(a, idx); break;
+        case 4: conv_window_update<bf16, 4>(a, idx); break;
+        }
+    } else {
+        switch (a.K) {
+        case 2: conv_window_update<float, 2>(a, idx); break;
+        case 3: conv_window_update<float, 3>(a, idx); break;
+        case 4: conv_window_update<float, 4>(a, idx); break;
+        }
+    }
 }
 
 template <typename T, typename TOUT, int K>
@@ -1012,6 +1038,11 @@ __global__ void __launch_bounds__(NW * 64)
     const int tid0 = threadIdx.x, lane0 = tid0 & 63;
     const int wave0 = __builtin_amdgcn_readfirstlane(tid0 >> 6);
 
+    if (blockIdx.x >= a.job_groups) {  // extra workgroups: the front end's new windows
+        conv_window_item(a.window, a.window_dtype,
+                         (int64_t)(blockIdx.x - a.job_groups) * NT + tid0);
+        return;
+    }
     const int H = a.H;
     const int BH = a.st.B * H;
     constexpr int NS = DV / NV;  // dv slices
@@ -1841,7 +1872,12 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
             return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), C::BYTES, s, a);
+    ChunkArgs ar = a;
+    ar.job_groups = grid;
+    const int64_t extra = (a.window_items + NW * 64 - 1) / (NW * 64);
+    if ((int64_t)grid + extra > (int64_t)INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(grid + extra)), dim3(NW * 64), C::BYTES, s, ar);
     return hipGetLastError();
 }
 

@@ -234,9 +234,13 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
  * front end and recurrence (page "metrale_model_arch/glm5next_kda/prefill.rs",
  * profile::start / profile::end with KDA_FRONT, KDA_RECUR, KDA_BACK). While enabled, every
  * call records a hipEvent pair around each of its kernels on the call's stream:
- *   GDN_PROF_FRONT  conv + SiLU + L2 kernel (front end calls only)
- *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan)
- *   GDN_PROF_STATE  the carried conv window update (front end calls only)
+ *   GDN_PROF_FRONT  conv + SiLU + L2 kernel (front end calls only; for segmented calls
+ *                   with the scalar gate it also holds the warm-start plan)
+ *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan; the
+ *                   carried conv windows are updated by extra workgroups of its first
+ *                   launch, after the front end)
+ *   GDN_PROF_STATE  unused by prefill calls (the windows go out with the scan); kept so
+ *                   that bucket numbers stay fixed
  *   GDN_PROF_GATE   the output gate when it runs as its own pass (the per-key-channel gate
  *                   at dk = dv = 128 or with float32 inputs; elsewhere it is fused into the
  *                   o flush of the chunk kernel or the decode kernel and nothing is

@@ -30,15 +30,15 @@ def timed(call):
 
 @pytest.mark.parametrize("case", ["segmented-front", "varlen", "gated-pass"])
 def test_prefill_stage_timers(case):
-    if case == "segmented-front":   # front, chunk pass 1, chain, chunk pass 2, window
+    if case == "segmented-front":   # front (+ warm plan), chunk passes and chain (+ windows)
         spec = spec_small(2, lengths=[2048], H=4, seed=61)
-        stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR, B.GDN_PROF_STATE}
+        stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR}
     elif case == "varlen":          # stream ranking + chunk kernel, no front end
         spec = spec_small(4, lengths=[1, 300, 64, 129], H=2, seed=62)
         stages = {B.GDN_PROF_RECUR}
     else:                           # output gate in its own pass (per-channel gate, d=128)
         spec = spec_small(5, lengths=[200], H=2, out_gate=True, seed=63)
-        stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR, B.GDN_PROF_GATE, B.GDN_PROF_STATE}
+        stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR, B.GDN_PROF_GATE}
     inp = inputs.make(spec)
     ref = Prefill(inp, "cuda")
     assert ref() == 0
