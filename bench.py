@@ -71,7 +71,8 @@ def algorithmic_bytes(spec) -> dict:
     if spec.front_end:
         # front: raw rows in, activations out (same element size), taps, windows read
         out["front"] = 2 * N * cd * es + cd * spec.conv_k * 4 + B * cd * (spec.conv_k - 1) * es
-        out["state"] = 2 * B * cd * (spec.conv_k - 1) * es
+        # the new windows (last raw rows read, windows rewritten) go out with the scan
+        out["recur"] += 2 * B * cd * (spec.conv_k - 1) * es
     return out
 
 
@@ -238,12 +239,17 @@ def main() -> int:
     if args.decode:
         kname = "decode_kernel (front end + one recurrence step + window update, fused)"
     elif dom == "recur" and segs:
+        warm = spec.gate != "kda"
         kname = ("recur: %schunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
                  "(segmented scan, %d segments%s)"
-                 % ("" if spec.gate == "kda" else "warm_plan_kernel + ", segs,
-                    "" if spec.gate == "kda" else "; warm starts where the gates allow"))
+                 % ("warm_plan_kernel + " if warm and not spec.front_end else "", segs,
+                    "; warm starts where the gates allow" if warm else ""))
+        if warm and spec.front_end:
+            kname += "; the warm-start plan runs with the front kernel"
     else:
         kname = dom
+    if not args.decode and dom == "recur" and spec.front_end:
+        kname += "; the new conv windows go out with the scan's first launch"
 
     ms_per_step = elapsed * 1e3 / args.steps
     line = {

@@ -180,7 +180,6 @@ struct DecodeArgs {
 // launch error.
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
 // new carried conv windows; must run after every kernel that reads the old ones
-hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s);
 // in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end;
 // nv: dv columns per workgroup (the grid is B * H * dv / nv workgroups); waves: waves per
 // workgroup, 0 = the first compiled instance of that width; gate: the instance with the

@@ -600,12 +600,6 @@ __device__ __forceinline__ void conv_window_update(const FrontArgs &a, int64_t i
         cs[(int64_t)c * W + j] = nw[j];
 }
 
-template <typename T, int K>
-__global__ void __launch_bounds__(256) conv_state_kernel(const FrontArgs a)
-{
-    conv_window_update<T, K>(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
-}
-
 // The window update for item idx (stream-major channels) of a call of element type dtype
 // (1: bf16, 0: fp32) and a.K taps, for launches that carry it in extra workgroups.
 __device__ __forceinline__ void conv_window_item(const FrontArgs &a, int dtype, int64_t idx)
@@ -639,31 +633,6 @@ hipError_t launch_front_tk(const FrontArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename T, int K>
-hipError_t launch_state_tk(const FrontArgs &a, hipStream_t s)
-{
-    const int cd = 2 * a.Hqk * a.dk + a.H * a.dv;
-    const int64_t n = (int64_t)a.st.B * cd;
-    hipLaunchKernelGGL((conv_state_kernel<T, K>), dim3((unsigned)((n + 255) / 256)), dim3(256),
-                       0, s, a);
-    return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_state_t(const FrontArgs &a, hipStream_t s)
-{
-    switch (a.K) {
-    case 2: return launch_state_tk<T, 2>(a, s);
-    case 3: return launch_state_tk<T, 3>(a, s);
-    case 4: return launch_state_tk<T, 4>(a, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_conv_state(int dtype, const FrontArgs &a, hipStream_t s)
-{
-    return dtype ? launch_state_t<bf16>(a, s) : launch_state_t<float>(a, s);
-}
 
 template <typename T, typename TOUT>
 hipError_t launch_front_t(const FrontArgs &a, hipStream_t s)
