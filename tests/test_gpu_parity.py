@@ -233,18 +233,21 @@ def test_refused_calls_leave_buffers_unchanged():
     assert ctypes.sizeof(p) == 72
 
 
-@pytest.mark.parametrize("case", ["gdn-front-T4096-H4", "gdn-bf16-T3000-H2"])
+@pytest.mark.parametrize("case", ["gdn-front-T4096-H4", "gdn-bf16-T3000-H2",
+                                  "batched-2x2048-H2"])
 def test_segmented_scan_fast_decay(case):
     """Fast decay (log-gates -softplus(N(0,1))): each inner segment's transition underflows
     within its first chunks, so the transition jobs stop early and write zeros. The call
     still matches the oracle and the serial scan."""
     from gated_delta_rule_depthwise_amd import binding as B
-    spec = (spec_small(2, lengths=[4096], H=4, seed=56) if case == "gdn-front-T4096-H4"
-            else spec_small(3, lengths=[3000], H=2, seed=57))
+    spec = {"gdn-front-T4096-H4": lambda: spec_small(2, lengths=[4096], H=4, seed=56),
+            "gdn-bf16-T3000-H2": lambda: spec_small(3, lengths=[3000], H=2, seed=57),
+            "batched-2x2048-H2": lambda: spec_small(3, lengths=[2048, 2048], H=2, seed=59),
+            }[case]()
     inp = inputs.make(spec)
     seg = run_gpu(inp)
     ser = run_gpu(inp, segmented=False)
-    assert B.gdn_segments(seg.params, seg.kind, spec.B, spec.N, seg.ws_bytes) >= 3
+    assert B.gdn_segments(seg.params, seg.kind, spec.B, spec.N // spec.B, seg.ws_bytes) >= 3
     ref = run_oracle(inp)
     e_seg = compare(seg, ref)
     compare(ser, ref)
