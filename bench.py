@@ -151,7 +151,7 @@ def main() -> int:
     args = ap.parse_args()
     args.profile_every = max(1, args.profile_every)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
