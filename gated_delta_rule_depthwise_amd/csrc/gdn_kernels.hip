@@ -343,14 +343,14 @@ constexpr int CH = 64;  // chunk length
 // reading row l of each), until their log-gates sum below -110.
 __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
 {
-    __shared__ int ok[32];
+    __shared__ int all_ok;  // cleared by a wave that finds a boundary without a window
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     const int S = a.nseg;
-    if (tid < 32)
-        ok[tid] = 1;
+    if (tid == 0)
+        all_ok = 1;
     __syncthreads();
     for (int s = wv + 1; s <= S - 1; s += 4) {  // uniform per wave
         const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
@@ -387,12 +387,12 @@ __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
         if (lane == 0) {
             a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
             if (done != 1)
-                ok[0] = 0;
+                all_ok = 0;
         }
     }
     __syncthreads();
     if (tid == 0)
-        a.seg_ws[a.lay.warm_mode(b, head)] = ok[0] ? 1.f : 0.f;
+        a.seg_ws[a.lay.warm_mode(b, head)] = all_ok ? 1.f : 0.f;
 }
 
 __global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
@@ -559,8 +559,6 @@ __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
     }
 }
 
-// New carried window of every stream: the last K-1 entries of [old window | rows].
-// Runs after front_kernel (which reads the old windows), one thread per (stream, channel).
 // New carried window of every stream: the last K-1 entries of [old window | rows], one
 // item per (stream, channel); after every reader of the old window.
 template <typename T, int K>
