@@ -133,12 +133,13 @@ def cpu_baseline(spec, inp, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--profile-every", type=int, default=4,
-                    help="record the stage events on every n-th timed step (1 = all)")
+    ap.add_argument("--profile-every", type=int, default=0,
+                    help="record the stage events on every n-th timed step (1 = all; "
+                         "0 = about 5 of the timed steps)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -149,7 +150,8 @@ def main() -> int:
     ap.add_argument("--qk-heads", type=int, default=0,
                     help="q/k heads shared by the value heads (0 = as many as value heads)")
     args = ap.parse_args()
-    args.profile_every = max(1, args.profile_every)
+    if args.profile_every <= 0:
+        args.profile_every = max(1, args.steps // 5)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
