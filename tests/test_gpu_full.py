@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gated_delta_rule_depthwise_amd import inputs
-from tests.gpu_util import compare, rel_err, run_gpu, run_oracle
+from tests.gpu_util import compare, rel_err, run_gpu, run_oracle, spec_small
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,20 @@ def test_config5_kda_one_shot_and_4_calls():
     assert rel_err(h[:, sel].numpy(), ref["h"]) < 2e-2
     assert rel_err(o4.numpy(), one.o[:16384].cpu().numpy()) < 2e-2
     assert torch.equal(cs, one.conv_state.cpu())
+
+
+def test_long_stream_64bit_indices():
+    """One stream of 196608 tokens through the front end, C2's shapes otherwise: the raw
+    rows and the activations hold 2.4 G elements (4.8 GB) and o 3.2 GB, so row offsets
+    and element indices pass 2^31 and every address the kernels form must be 64-bit. The
+    oracle recomputes heads 0 and 31; the new conv windows are checked on every channel."""
+    T = 196608
+    spec = spec_small(2, lengths=[T])
+    assert T * spec.cd > 2 ** 31
+    inp = inputs.make(spec)
+    call = run_gpu(inp)
+    ref = run_oracle(inp, heads=[0, 31])
+    e_o, e_h = compare(call, ref, heads=[0, 31])
+    print("%s: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
+    want = inp["x"][T - 3:T].t().contiguous()
+    assert torch.equal(call.conv_state[0].cpu(), want)
