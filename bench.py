@@ -222,7 +222,7 @@ def main() -> int:
     # segment maps + pass 2, timed together as one stage
     segs = 0
     if not args.decode and first.kind != B.GDN_KIND_VARLEN:
-        segs = B.gdn_segments(first.params, first.kind, spec.B, spec.N // spec.B,
+        segs = B.gdn_segments(first.params, first.plan_kind, spec.B, spec.N // spec.B,
                               first.ws_bytes)
     names = {B.GDN_PROF_FRONT: "front", B.GDN_PROF_RECUR: "recur", B.GDN_PROF_STATE: "state",
              B.GDN_PROF_GATE: "gate"}

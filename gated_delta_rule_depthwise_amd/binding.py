@@ -24,6 +24,7 @@ GDN_BF16 = 1
 GDN_KIND_SINGLE = 0
 GDN_KIND_BATCHED = 1
 GDN_KIND_VARLEN = 2
+GDN_PLAN_KDA = 0x100  # or-ed into the kind of gdn_segments / gdn_segment_plan
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",

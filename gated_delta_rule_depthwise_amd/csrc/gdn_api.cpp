@@ -745,17 +745,18 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
         *seg0_tokens = 0;
     if (seg_tokens)
         *seg_tokens = 0;
-    int rc0 = check_params(p, 0), rc1 = check_params(p, 1);
-    if (rc0 != GDN_OK && rc1 != GDN_OK)
-        return rc0;
+    const int kda = (kind & GDN_PLAN_KDA) ? 1 : 0;
+    kind &= ~GDN_PLAN_KDA;
+    const int rc = check_params(p, kda);
+    if (rc != GDN_OK)
+        return rc;
     if (B < 1 || t_per_stream < 1 || kind < GDN_KIND_SINGLE || kind > GDN_KIND_VARLEN ||
         (kind == GDN_KIND_SINGLE && B != 1))
         return GDN_E_ARG;
     if (kind == GDN_KIND_VARLEN)
         return 0;
-    const Shape sh = pick_shape(p, rc0 == GDN_OK ? 0 : 1, (int64_t)B * p->H);
-    const SegPlan sp = seg_plan(p, rc0 == GDN_OK ? 0 : 1, B, t_per_stream, p->dv / sh.nv,
-                                cu_count());
+    const Shape sh = pick_shape(p, kda, (int64_t)B * p->H);
+    const SegPlan sp = seg_plan(p, kda, B, t_per_stream, p->dv / sh.nv, cu_count());
     const size_t need = front_bytes(p, (int64_t)B * t_per_stream);
     if (!sp.S || ws_bytes < need + seg_bytes(p, B, sp.S))
         return 0;

@@ -57,6 +57,8 @@ class Prefill:
         kind = {"single": B.GDN_KIND_SINGLE, "batched": B.GDN_KIND_BATCHED,
                 "varlen": B.GDN_KIND_VARLEN}[mode]
         self.kind = kind
+        # the kind to ask gdn_segments / gdn_segment_plan with: the plan of this call's gate
+        self.plan_kind = kind | (B.GDN_PLAN_KDA if spec.gate == "kda" else 0)
         # segmented=False sizes the workspace for the front end only, which makes a single
         # or batched call run its scan unsegmented
         self.ws_bytes = B.gdn_workspace_bytes(

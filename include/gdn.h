@@ -72,6 +72,9 @@ extern "C" {
 #define GDN_KIND_SINGLE 0
 #define GDN_KIND_BATCHED 1
 #define GDN_KIND_VARLEN 2
+/* OR-ed into the kind of gdn_segments / gdn_segment_plan: the plan of a KDA call (per-key-
+ * channel gate) instead of a GDN call (scalar gate); the two plans differ */
+#define GDN_PLAN_KDA 0x100
 
 typedef struct gdn_params {
     int32_t H;      /* value heads: g, beta, o and the states have H heads (see Hqk)      */
@@ -288,11 +291,11 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
 
 /* Segments per stream (S >= 3, or 0 for an unsegmented scan) that a single (kind
- * GDN_KIND_SINGLE, B = 1) or batched (GDN_KIND_BATCHED) GDN call (a KDA call when only the
- * per-key-channel gate is compiled for these parameters) with these parameters,
- * t_per_stream tokens per stream and ws_bytes of workspace would use on the current device;
- * always 0 for GDN_KIND_VARLEN. Negative status for invalid arguments. Host only; enqueues
- * nothing. The environment variable GDN_SEG (read once) overrides the choice: 0 never
+ * GDN_KIND_SINGLE, B = 1) or batched (GDN_KIND_BATCHED) GDN call (KDA call with
+ * GDN_PLAN_KDA or-ed into kind) with these parameters, t_per_stream tokens per stream and
+ * ws_bytes of workspace would use on the current device; always 0 for GDN_KIND_VARLEN.
+ * Negative status for invalid arguments, or GDN_E_UNSUPPORTED when that call is not
+ * compiled for these parameters. Host only; enqueues nothing. The environment variable GDN_SEG (read once) overrides the choice: 0 never
  * segments, 3..12 asks for that many segments. */
 int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
                  size_t ws_bytes);

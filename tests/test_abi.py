@@ -69,7 +69,16 @@ def test_segment_plan():
     assert B.gdn_segments(pb, B.GDN_KIND_BATCHED, 8, 2048, 1 << 40) == 0
     pk = B.params(32, 128, 128, conv_k=4)          # long KDA stream
     wk = B.gdn_workspace_bytes(pk, 1, 16384, B.GDN_KIND_SINGLE)
-    assert B.gdn_segments(pk, B.GDN_KIND_SINGLE, 1, 16384, wk) >= 3
+    kda = B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA
+    assert B.gdn_segments(pk, kda, 1, 16384, wk) >= 3
+    # A GDN call with unit keys may start every segment warm, so its plan keeps segment 0
+    # and the warm jobs of all (stream, head) pairs in one round: S <= CUs / (streams *
+    # heads) = 8. A KDA call always chains its segments and has no such cap: on 256 CUs
+    # its plan is 9 segments of 40, 27 x 7 and 27 chunks.
+    S_g, _, _ = B.gdn_segment_plan(pk, B.GDN_KIND_SINGLE, 1, 16384, wk)
+    assert 3 <= S_g <= 8
+    assert B.gdn_segment_plan(pk, kda, 1, 16384, wk) == (9, 40 * 64, 27 * 64)
+    assert B.gdn_segments(pk, B.GDN_KIND_VARLEN | B.GDN_PLAN_KDA, 1, 16384, wk) == 0
     # no compiled instance: the status of the refused call
     pr = B.params(4, 64, 128, dtype=B.GDN_BF16)
     assert B.gdn_segments(pr, B.GDN_KIND_SINGLE, 1, 4096, 1 << 40) == B.GDN_E_UNSUPPORTED
@@ -78,16 +87,17 @@ def test_segment_plan():
     assert B.gdn_segments(p, 7, 1, 4096, full) == B.GDN_E_ARG
 
 
+@pytest.mark.parametrize("kda", [0, B.GDN_PLAN_KDA])
 @pytest.mark.parametrize("H,T", [(32, 4096), (32, 16384), (4, 4096), (2, 700), (16, 1000),
                                  (32, 1 << 20)])
-def test_segment_plan_lengths(H, T):
+def test_segment_plan_lengths(H, T, kda):
     """A segmented plan cuts each stream into whole chunks: segment 0 and the S-2 inner
     segments leave at least one chunk for the last segment, and the plan agrees with
     gdn_segments."""
     p = B.params(H, 128, 128, conv_k=4)
     ws = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_SINGLE)
-    S, l0, l1 = B.gdn_segment_plan(p, B.GDN_KIND_SINGLE, 1, T, ws)
-    assert S == B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, T, ws)
+    S, l0, l1 = B.gdn_segment_plan(p, B.GDN_KIND_SINGLE | kda, 1, T, ws)
+    assert S == B.gdn_segments(p, B.GDN_KIND_SINGLE | kda, 1, T, ws)
     if S == 0:
         assert l0 == 0 and l1 == 0
         return
@@ -96,7 +106,7 @@ def test_segment_plan_lengths(H, T):
     assert l0 + (S - 2) * l1 < T, "the last segment would be empty"
     # no room for the states: unsegmented, lengths cleared
     front = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_VARLEN)
-    assert B.gdn_segment_plan(p, B.GDN_KIND_SINGLE, 1, T, front) == (0, 0, 0)
+    assert B.gdn_segment_plan(p, B.GDN_KIND_SINGLE | kda, 1, T, front) == (0, 0, 0)
 
 
 def _single(p, t=10, ws=None, ws_bytes=0, h=FAKE, g=FAKE, cs=None, cw=None, q=FAKE):

@@ -106,7 +106,7 @@ def test_gated_segmented_scan():
     spec = spec_small(2, lengths=[4096], H=4, out_gate=True, gate_dist="slow", seed=23)
     inp = inputs.make(spec)
     call = run_gpu(inp)
-    assert B.gdn_segments(call.params, call.kind, 1, 4096, call.ws_bytes) >= 3
+    assert B.gdn_segments(call.params, call.plan_kind, 1, 4096, call.ws_bytes) >= 3
     ref = gated(inp, run_oracle(inp))
     compare(call, ref, o_metric=ref["o_metric"])
 

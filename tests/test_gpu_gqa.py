@@ -40,7 +40,7 @@ def test_shared_qk_segmented_scan():
     spec = spec_small(2, lengths=[4096], H=4, Hqk=2, gate_dist="slow", seed=32)
     inp = inputs.make(spec)
     call = run_gpu(inp)
-    assert B.gdn_segments(call.params, call.kind, 1, 4096, call.ws_bytes) >= 3
+    assert B.gdn_segments(call.params, call.plan_kind, 1, 4096, call.ws_bytes) >= 3
     compare(call, run_oracle(inp))
 
 

@@ -183,9 +183,9 @@ def test_segmented_scan_matches_serial_scan(case):
     seg = run_gpu(inp)
     ser = run_gpu(inp, segmented=False)
     tps = spec.N // spec.B
-    S = B.gdn_segments(seg.params, seg.kind, spec.B, tps, seg.ws_bytes)
+    S = B.gdn_segments(seg.params, seg.plan_kind, spec.B, tps, seg.ws_bytes)
     assert S >= 3, "expected a segmented plan"
-    assert B.gdn_segments(ser.params, ser.kind, spec.B, tps, ser.ws_bytes) == 0
+    assert B.gdn_segments(ser.params, ser.plan_kind, spec.B, tps, ser.ws_bytes) == 0
     ref = run_oracle(inp)
     e_seg = compare(seg, ref)
     e_ser = compare(ser, ref)
@@ -247,7 +247,7 @@ def test_segmented_scan_fast_decay(case):
     inp = inputs.make(spec)
     seg = run_gpu(inp)
     ser = run_gpu(inp, segmented=False)
-    assert B.gdn_segments(seg.params, seg.kind, spec.B, spec.N // spec.B, seg.ws_bytes) >= 3
+    assert B.gdn_segments(seg.params, seg.plan_kind, spec.B, spec.N // spec.B, seg.ws_bytes) >= 3
     ref = run_oracle(inp)
     e_seg = compare(seg, ref)
     compare(ser, ref)

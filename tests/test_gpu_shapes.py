@@ -35,7 +35,7 @@ def test_wide_values_match_oracle(name):
         inp = inputs.refill_tails(inp, float("nan"))
     call = run_gpu(inp)
     if call.kind != B.GDN_KIND_VARLEN:
-        assert B.gdn_segments(call.params, call.kind, spec.B, spec.N // spec.B,
+        assert B.gdn_segments(call.params, call.plan_kind, spec.B, spec.N // spec.B,
                               call.ws_bytes) == 0
     compare(call, run_oracle(inp))
 
