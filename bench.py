@@ -265,7 +265,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in; fp32 arithmetic; fp32 o" if args.decode else
+        "dtype": ("%s in; fp32 arithmetic; fp32 o" % spec.dtype) if args.decode else
+                 "f32 in; fp32 MFMA and VALU; fp32 o" if spec.dtype == "f32" else
                  "bf16 in; fp16 MFMA operands, fp32 accumulate/VALU; fp32 o",
         "data": "synthetic (seeded; distributions of the workload description)",
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
