@@ -1,8 +1,8 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
 
-The whole call runs on every head; the fp64 oracle recomputes a sample of heads (each head
-is independent, so its outputs are computable one head at a time) and the errors are taken
-over those heads. conv windows and untouched o rows are checked on every channel/row.
+The whole call runs on every head and the fp64 oracle recomputes every head, so each error
+is taken over the whole o tensor and every final state (the 196608-token stream samples
+two heads). conv windows and untouched o rows are checked on every channel/row.
 """
 import numpy as np
 import pytest
@@ -13,10 +13,7 @@ from tests.gpu_util import compare, rel_err, run_gpu, run_oracle, spec_small
 
 pytestmark = pytest.mark.gpu
 
-HEADS = [0, 13, 31]
-
-
-def _full(i, heads=HEADS, fill=0.0):
+def _full(i, heads=None, fill=0.0):
     spec = inputs.config(i, pad_fill=fill)
     inp = inputs.make(spec)
     call = run_gpu(inp)
@@ -39,7 +36,7 @@ def test_config3_batched_8x2048():
 
 @pytest.mark.parametrize("fill", [float("nan"), 1e30])
 def test_config4_varlen_tails(fill):
-    _full(4, heads=[0, 31], fill=fill)
+    _full(4, fill=fill)
 
 
 def test_config5_kda_one_shot_and_4_calls():
@@ -48,8 +45,8 @@ def test_config5_kda_one_shot_and_4_calls():
     spec = inputs.config(5)
     inp = inputs.make(spec)
     one = run_gpu(inp)
-    ref = run_oracle(inp, heads=[0, 31])
-    e_o, e_h = compare(one, ref, heads=[0, 31])
+    ref = run_oracle(inp)
+    e_o, e_h = compare(one, ref)
     print("%s one-shot: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
     import dataclasses
     h, cs = inp["h0"], inp["conv_state"]
@@ -67,9 +64,8 @@ def test_config5_kda_one_shot_and_4_calls():
         parts.append(c.o[:4096].cpu())
         h, cs = c.h.cpu(), c.conv_state.cpu()
     o4 = torch.cat(parts)
-    sel = [0, 31]
-    assert rel_err(o4[:, sel].numpy(), ref["o"]) < 2e-2
-    assert rel_err(h[:, sel].numpy(), ref["h"]) < 2e-2
+    assert rel_err(o4.numpy(), ref["o"]) < 2e-2
+    assert rel_err(h.numpy(), ref["h"]) < 2e-2
     assert rel_err(o4.numpy(), one.o[:16384].cpu().numpy()) < 2e-2
     assert torch.equal(cs, one.conv_state.cpu())
 
@@ -89,3 +85,18 @@ def test_long_stream_64bit_indices():
     print("%s: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
     want = inp["x"][T - 3:T].t().contiguous()
     assert torch.equal(call.conv_state[0].cpu(), want)
+
+
+@pytest.mark.xfail(strict=True, reason="fp16 storage of the front end's activations: the "
+                   "error floor of that one rounding exceeds 2e-2 on this seed")
+def test_config2_other_seed_activation_rounding_floor():
+    """A known gap, pinned. The default prefill workload drawn with seed 102 instead of 2:
+    over all heads the call's err(o) is 0.029. The fp64 oracle fed the same activations
+    rounded once to fp16 (and nothing else) gives 0.0285, so the floor comes from storing
+    the front end's output as fp16, not from the scan's arithmetic. The test fails until
+    v and k cross from the front end to the scan with more precision than fp16."""
+    import dataclasses
+    spec = dataclasses.replace(inputs.config(2), seed=102)
+    inp = inputs.make(spec)
+    call = run_gpu(inp)
+    compare(call, run_oracle(inp))
