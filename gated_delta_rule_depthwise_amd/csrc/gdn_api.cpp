@@ -90,37 +90,39 @@ int64_t conv_dim(const gdn_params *p)
     return 2 * (int64_t)qk_heads(p) * p->dk + (int64_t)p->H * p->dv;
 }
 
-// input kind of the chunk kernel: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations
-int in_kind(const gdn_params *p)
+// The front end runs inside the chunk kernel's load stage (conv + SiLU + L2 in fp32 on
+// the raw rows, no activation buffer) for bf16 rows with 4 taps, the scalar gate, one q/k
+// head per value head, dk == dv, no output gate and row strides below 2^24 elements (the
+// kernel forms a chunk's row offsets in 32 bits); other front-end calls run it as a
+// kernel of its own that hands the chunk kernel packed activations.
+bool fused_front(const gdn_params *p, int kda)
+{
+    return p->conv_k == 4 && p->dtype == GDN_BF16 && !kda && !p->z &&
+           qk_heads(p) == p->H && p->dk == p->dv && p->ld_qkv < (1 << 24) &&
+           gdn::chunk_instance_exists(3, p->dk, p->dv, 0, p->dv, 0, 0);
+}
+
+// input kind of the chunk kernel: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations of
+// the front kernel, 3 = bf16 raw rows with the front end fused
+int in_kind(const gdn_params *p, int kda)
 {
     if (p->dtype != GDN_BF16)
         return 0;
-    return p->conv_k > 0 ? 2 : 1;
+    if (p->conv_k == 0)
+        return 1;
+    return fused_front(p, kda) ? 3 : 2;
 }
 
-// Workgroup shape: dv columns per workgroup and waves per workgroup (the widest compiled
-// instance). GDN_COLS / GDN_WAVES force a compiled shape.
+// Workgroup shape: dv columns per workgroup and waves per workgroup: the widest compiled
+// instance, so that one workgroup per (stream, head) computes the chunk preparation once
+// for all its columns and 8-wave instances hide latency with two waves per SIMD.
 struct Shape {
     int nv, waves;
 };
 
-Shape pick_shape(const gdn_params *p, int kda, int64_t BH)
+Shape pick_shape(const gdn_params *p, int kda)
 {
-    const int ik = in_kind(p);
-    static int fcols = -1, fwaves = -1;
-    if (fcols < 0) {
-        const char *e = getenv("GDN_COLS");
-        fcols = e ? atoi(e) : 0;
-        e = getenv("GDN_WAVES");
-        fwaves = e ? atoi(e) : 0;
-    }
-    if (fcols > 0 && p->dv % fcols == 0 &&
-        gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, fcols, fwaves, 0))
-        return Shape{fcols, fwaves};
-    // The widest instance: one workgroup per (stream, head) computes the chunk
-    // preparation once for all its columns, and 8-wave instances hide latency with two
-    // waves per SIMD.
-    (void)BH;
+    const int ik = in_kind(p, kda);
     for (int nv : {128, 64}) {
         if (p->dv % nv == 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0, 0))
             return Shape{nv, 0};
@@ -144,7 +146,7 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_UNSUPPORTED;
     if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
         return GDN_E_UNSUPPORTED;
-    const Shape sh = pick_shape(p, kda, 1);
+    const Shape sh = pick_shape(p, kda);
     if (sh.nv == 0)
         return GDN_E_UNSUPPORTED;
     const int64_t vec = 16 / elem_bytes(p->dtype);
@@ -166,11 +168,21 @@ int check_params(const gdn_params *p, int kda)
 constexpr int32_t kMaxOrderB = 1024;
 size_t order_bytes(int32_t B) { return B <= kMaxOrderB ? align_up((size_t)B * 4) : 0; }
 
-size_t front_bytes(const gdn_params *p, int64_t max_tokens)
+// the front kernel's activations (front-end calls that do not fuse it)
+size_t front_bytes(const gdn_params *p, int kda, int64_t max_tokens)
 {
-    if (p->conv_k == 0)
+    if (p->conv_k == 0 || fused_front(p, kda))
         return 0;
     return align_up((size_t)max_tokens * (size_t)conv_dim(p) * elem_bytes(p->dtype));
+}
+
+// segmented calls with the front end fused: the new windows of the streams whose last
+// segment runs in the first launch (warm mode), staged until the combine kernel copies them
+size_t win_bytes(const gdn_params *p, int kda, int32_t B)
+{
+    if (!fused_front(p, kda))
+        return 0;
+    return align_up((size_t)B * (size_t)conv_dim(p) * (p->conv_k - 1) * 2);
 }
 
 // ---- segmented scan of long streams -----------------------------------------------------
@@ -301,29 +313,17 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
     if (p->dk != p->dv || p->chunk != 64 || tps < 1)
         return none;
     const int64_t nc = (tps + 63) / 64;
-    static int force = -1;  // GDN_SEG: 0 never segments, S >= 3 asks for S equal segments
-    if (force < 0) {
-        const char *e = getenv("GDN_SEG");
-        force = e ? atoi(e) : 0x7fffffff;
-    }
-    if (force == 0)
-        return none;
-    if (force >= 3 && force <= kMaxSeg && force != 0x7fffffff) {
-        const int64_t L = (nc + force - 1) / force;
-        const int Se = (int)((nc + L - 1) / L);
-        return Se >= 3 ? SegPlan{Se, L * 64, L * 64} : none;
-    }
     const int64_t U = (int64_t)B * p->H * nslices;
     const int max_s = !kda && warm_capable(p) && ncu / U >= 3 ? (int)(ncu / U) : 0;
     return seg_search(nc, U, ncu, max_s);
 }
 
-size_t seg_bytes(const gdn_params *p, int32_t B, int S)
+size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S)
 {
     if (S < 3)
         return 0;
     const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S, p->H};
-    return align_up((size_t)lay.total() * sizeof(float));
+    return align_up((size_t)lay.total() * sizeof(float)) + win_bytes(p, kda, B);
 }
 
 struct Call {
@@ -361,33 +361,33 @@ int run(const Call &c)
         return GDN_E_ARG;
     if (c.N < 1 || c.N > (int64_t)INT32_MAX)
         return GDN_E_ARG;
-    const size_t need = front_bytes(p, c.N);
+    const bool fused_fe = front && fused_front(p, c.kda);
+    const size_t need = front_bytes(p, c.kda, c.N);
     if (c.ws_bytes < need || (need && !c.ws))
         return GDN_E_WORKSPACE;
     if (need && !aligned16(c.ws))
         return GDN_E_ARG;
 
     const int64_t BH = (int64_t)c.st.B * p->H;
-    const Shape sh = pick_shape(p, c.kda, BH);
+    const Shape sh = pick_shape(p, c.kda);
+    const int ik = in_kind(p, c.kda);
     // the output gate rides in the o flush where the instance stages o, else its own pass
-    // (GDN_GATE_PASS=1, read once, forces the pass)
-    static const bool force_pass = [] {
-        const char *e = getenv("GDN_GATE_PASS");
-        return e && atoi(e) != 0;
-    }();
-    const int fused = p->z && !force_pass &&
-                      gdn::chunk_instance_exists(in_kind(p), p->dk, p->dv, c.kda, sh.nv,
-                                                 sh.waves, 1);
+    const int fused = p->z && gdn::chunk_instance_exists(ik, p->dk, p->dv, c.kda, sh.nv,
+                                                         sh.waves, 1);
     const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
-    // segmented scan when it pays and the workspace has room for its states
+    // segmented scan when it pays, the workspace has room for its states and the job
+    // counts of its launches fit a grid
     SegPlan sp{0, 0, 0};
+    bool warm = false;
     if (!c.st.cu) {
         sp = seg_plan(p, c.kda, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
-        if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.st.B, sp.S) ||
-                     grid * (2 * sp.S - 3) > (int64_t)INT32_MAX))
-            sp = SegPlan{0, 0, 0};
+        warm = sp.S && !c.kda && warm_capable(p);
+        const int64_t jobs1 = warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
+        if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.kda, c.st.B, sp.S) ||
+                     grid * jobs1 > (int64_t)INT32_MAX))
+            sp = SegPlan{0, 0, 0}, warm = false;
     }
 
     // varlen calls with more workgroups than CUs: streams dispatch longest first, from a
@@ -418,15 +418,30 @@ int run(const Call &c)
     // extra workgroups of the front launch when there is one, else by a launch of its own
     // at the start of the scan
     const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
+    float *seg_ws = sp.S ? (float *)((char *)c.ws + need) : nullptr;
+    void *win_ws = sp.S && fused_fe
+                       ? (char *)seg_ws + align_up((size_t)lay.total() * sizeof(float))
+                       : nullptr;
     gdn::WarmArgs wa{};
-    ca.warm = sp.S && !c.kda && warm_capable(p);
+    ca.warm = warm;
     if (ca.warm) {
         wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
         wa.nseg = sp.S, wa.seg0_len = sp.seg0_len, wa.seg_len = sp.seg_len;
-        wa.seg_ws = (float *)((char *)c.ws + need), wa.lay = lay;
+        wa.seg_ws = seg_ws, wa.lay = lay;
     }
     FrontArgs fa{};
-    if (front) {
+    if (fused_fe) {
+        // conv + SiLU + L2 in the chunk kernel's load stage, straight from the raw rows
+        ca.q = c.q, ca.k = c.k, ca.v = c.v, ca.ld = p->ld_qkv;
+        ca.do_l2 = p->eps >= 0.f;
+        ca.unit_keys = ca.do_l2;
+        ca.scale = p->scale;
+        ca.conv_w = c.conv_w;
+        ca.conv_state = c.conv_state;
+        ca.conv_state_ptrs = c.conv_state_ptrs;
+        ca.win_ws = win_ws;
+        ca.cd = (int32_t)conv_dim(p);
+    } else if (front) {
         if (ca.warm) {
             fa.warm = wa;
             fa.warm_groups = c.st.B * p->H;
@@ -481,23 +496,21 @@ int run(const Call &c)
         if (order && gdn::launch_stream_order(c.st.cu, c.st.B, order, c.stream) != hipSuccess)
             return GDN_E_HIP;
         if (!sp.S) {
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)grid, c.stream) != hipSuccess)
                 return GDN_E_HIP;
         } else {
             ca.nseg = sp.S;
             ca.seg0_len = sp.seg0_len;
             ca.seg_len = sp.seg_len;
-            ca.seg_ws = (float *)((char *)c.ws + need);
-            if (ca.warm && !front) {
+            ca.seg_ws = seg_ws;
+            if (ca.warm && !(front && !fused_fe)) {
                 if (gdn::launch_warm_plan(wa, c.stream) != hipSuccess)
                     return GDN_E_HIP;
             }
             ca.pass = 1;
             const int64_t jobs1 = ca.warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
-            if (grid * jobs1 > (int64_t)INT32_MAX)
-                return GDN_E_ARG;
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
@@ -505,11 +518,15 @@ int run(const Call &c)
             cb.lay = lay;
             cb.warm = ca.warm;
             cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
+            cb.h = c.h, cb.h_ptrs = c.h_ptrs;
+            cb.win_ws = win_ws;
+            cb.conv_state = c.conv_state, cb.conv_state_ptrs = c.conv_state_ptrs;
+            cb.cd = (int32_t)conv_dim(p);
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;
             ca.pass = 2;
             ca.window_items = 0;  // the windows went out with pass 1
-            if (gdn::launch_chunk(in_kind(p), p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
                 return GDN_E_HIP;
         }
@@ -720,22 +737,22 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
 
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind)
 {
-    if (check_params(p, 0) != GDN_OK && check_params(p, 1) != GDN_OK)
+    const int kda = (kind & GDN_PLAN_KDA) ? 1 : 0;
+    kind &= ~GDN_PLAN_KDA;
+    if (check_params(p, kda) != GDN_OK)
         return 0;
     if (B < 1 || max_tokens < 1 || kind < GDN_KIND_SINGLE || kind > GDN_KIND_VARLEN)
         return 0;
     // room for any segment plan a call of up to max_tokens can make: only calls with fewer
     // (stream, head, slice) workgroups than CUs ever segment
     size_t seg = 0;
-    Shape sh = pick_shape(p, 0, 1);
-    if (sh.nv == 0)
-        sh = pick_shape(p, 1, 1);
+    const Shape sh = pick_shape(p, kda);
     if (kind != GDN_KIND_VARLEN && p->dk == p->dv && sh.nv > 0 &&
         (int64_t)B * p->H * (p->dv / sh.nv) < cu_count() && max_tokens / B >= 3 * 64)
-        seg = seg_bytes(p, B, kMaxSeg);
+        seg = seg_bytes(p, kda, B, kMaxSeg);
     if (kind == GDN_KIND_VARLEN)
         seg = order_bytes(B);
-    return front_bytes(p, max_tokens) + seg;
+    return front_bytes(p, kda, max_tokens) + seg;
 }
 
 int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
@@ -755,10 +772,10 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
         return GDN_E_ARG;
     if (kind == GDN_KIND_VARLEN)
         return 0;
-    const Shape sh = pick_shape(p, kda, (int64_t)B * p->H);
+    const Shape sh = pick_shape(p, kda);
     const SegPlan sp = seg_plan(p, kda, B, t_per_stream, p->dv / sh.nv, cu_count());
-    const size_t need = front_bytes(p, (int64_t)B * t_per_stream);
-    if (!sp.S || ws_bytes < need + seg_bytes(p, B, sp.S))
+    const size_t need = front_bytes(p, kda, (int64_t)B * t_per_stream);
+    if (!sp.S || ws_bytes < need + seg_bytes(p, kda, B, sp.S))
         return 0;
     if (seg0_tokens)
         *seg0_tokens = sp.seg0_len;

@@ -66,11 +66,23 @@ struct SegLayout {
 };
 
 // h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).
+// (Stream, head) pairs in warm mode have no chain: their last segment ran in the first
+// launch, beside the job that read the stream's initial state, so it left its end state in
+// slot H(b, S-1) (and, with the front end fused, the new conv windows in win_ws); this
+// kernel, the first to run after that launch, copies them to the caller's buffers.
 struct CombineArgs {
     float *seg_ws;
     SegLayout lay;
     int32_t H, dk, dv;
-    int32_t warm;           // (stream, head) pairs in warm mode have no chain
+    int32_t warm;
+    float *h;                       // single stream state (h_ptrs == nullptr)
+    float *const *h_ptrs;
+    // fused front end in warm mode: the new windows of every stream, [B][cd][3] bf16, to
+    // copy to the caller's windows (nullptr: nothing to copy)
+    const void *win_ws;
+    void *conv_state;
+    void *const *conv_state_ptrs;
+    int32_t cd;
 };
 
 
@@ -154,6 +166,16 @@ struct ChunkArgs {
     int64_t ld_z;
     const float *norm_w;    // [dv]
     float norm_eps;
+    // Front end fused into the load stage (q, k, v are the raw bf16 conv inputs; 4 taps;
+    // one q/k head per value head): the conv taps, the carried windows (read by the job
+    // holding a stream's first chunk) and where the job that ends a stream puts the new
+    // windows: the caller's windows, or in warm mode win_ws, from where the combine kernel
+    // copies them once the first launch (which read the old ones) is done.
+    const float *conv_w;            // [cd][4]
+    void *conv_state;               // [cd][3] of the single stream (conv_state_ptrs == nullptr)
+    void *const *conv_state_ptrs;   // per stream
+    void *win_ws;                   // [B][cd][3] bf16 (segmented calls)
+    int32_t cd;                     // channels of a packed row
 };
 
 // One decode step: a single token per stream through the front end (optional), L2 and the

@@ -1,22 +1,29 @@
 // gdn_kernels.hip -- gfx950 (CDNA4) kernels of the chunked gated-delta-rule prefill.
 //
-// Two kernels carry the path (pages "metrale_model_arch/glm5next_kda/prefill.rs" --
-// the launch sequence conv_prefill, l2, fill, split_widen, chunk_prepare, chunk_scan of
-// prefill_with_pad_fill -- and "split_prefill.rs" -- the batched and varlen entry points):
+// Pages "metrale_model_arch/glm5next_kda/prefill.rs" (the launch sequence conv_prefill, l2,
+// fill, split_widen, chunk_prepare, chunk_scan of prefill_with_pad_fill) and
+// "split_prefill.rs" (the batched and varlen entry points):
 //
-//  * front_kernel: causal depthwise conv1d + SiLU over every channel of the packed
-//    [q | k | v] rows, then L2 of each q and k head vector and the q scale, written once as
-//    packed activations. Parallel over (channel group, token tile). A small follow-up
-//    kernel advances the carried conv windows once every tile has read the old ones.
-//    Replaces conv_prefill + l2 + split_widen.
 //  * chunk_kernel: one workgroup per (stream, head, dv slice) walks the stream's chunks in
-//    order. Per chunk it builds the cumulative log-gates, K K^T and Q K^T on MFMA, the
-//    unit-lower-triangular inverse T = (I + M)^-1 by 16x16 block substitution, the WY/UT
-//    factors W = T diag(beta) (K . a) and U~ = T diag(beta) V, and then the state
-//    products U = U~ - W h, O = (Q . a) h + P U, h <- a_C h + (K . a_C/a)^T U with h held
-//    in MFMA accumulator registers across chunks. Replaces chunk_prepare + chunk_scan and
-//    the separate q/k/v widen buffers; tail rows of a partial chunk are zeroed by select on
-//    load, never read.
+//    order (or, for few long streams, one segment of them; see combine_kernel). Per chunk:
+//    the load stage brings the chunk's rows into LDS tiles -- with the front end fused
+//    (bf16 raw rows), the causal depthwise conv + SiLU, the L2 of q and k and the q scale
+//    run here in fp32 on raw rows that arrived by LDS-DMA one chunk ahead; otherwise the
+//    rows (or the front kernel's activations) are L2-normalised on load. Then the
+//    cumulative log-gates, M = strict_tril(diag(beta) K K^T . decay) and P = tril(Q K^T .
+//    decay) on MFMA, the inverse of each 16x16 diagonal block of (I + M), and the state
+//    products U = T diag(beta)(V - diag(a) K h) by block forward substitution, O =
+//    diag(a) Q h + P U and h <- a_C h + K^T diag(a_C / a) U, with h held in MFMA
+//    accumulators across chunks. Tail rows of a partial chunk are zeroed by select, never
+//    read. Replaces chunk_prepare + chunk_scan and the q/k/v widen buffers.
+//  * front_kernel: the front end as a kernel of its own, for the calls the chunk kernel
+//    does not fuse it into (float32 rows, the per-key-channel gate, shared q/k heads,
+//    dv != dk, 2 or 3 taps, the output gate): conv + SiLU, L2 and q scale written once as
+//    packed activations (fp32 for float32 rows, fp16 for bf16 rows). The carried windows
+//    are then advanced by extra workgroups of the first chunk-kernel launch.
+//  * combine_kernel: the chain of segment maps of the segmented scan, and the hand-over of
+//    warm-started streams' final states and windows.
+//  * decode lives in gdn_decode.hip.
 //
 // MFMA fragment convention (v_mfma_f32_16x16x32_f16, and 8 x v_mfma_f32_16x16x4_f32 for
 // float inputs): lane l = 16*g + c holds, for a 32-wide contraction block starting at k0,
@@ -104,7 +111,25 @@ __device__ __forceinline__ void store_stream16(void *p, float4 v)
     __builtin_nontemporal_store(w, (nt_f4 *)p);
 }
 
-// Sum over aligned groups of N lanes, N in {4, 8, 16}; every lane of a group gets the same// Sum over aligned groups of N lanes, N in {4, 8, 16}; every lane of a group gets the same
+// LDS-DMA of 16 bytes per lane: global p -> LDS byte address lds + 16 * lane (lds uniform
+// over the wave). Issued as inline asm: for the builtin the compiler assumes that every
+// later LDS read may read the transfer's destination and waits for all loads in flight
+// before each one, which stalls a whole stage on a prefetch meant for the next chunk. The
+// callers wait for their transfers themselves (vmcnt(0), then a barrier) before reading
+// the destination, and do not touch it while transfers are in flight.
+__device__ __forceinline__ void dma16(const void *p, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(p), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Sum over aligned groups of N lanes, N in {4, 8, 16}; every lane of a group gets the same
 // bits (each step adds the same two partial sums in both lanes).
 template <int N>
 __device__ __forceinline__ float group_sum(float x)
@@ -749,7 +774,8 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
 // fused chunk kernel
 
 
-template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false>
+template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false,
+          bool FRONT = false>
 struct ChunkCfg {
     static constexpr int NV = 16 * NW * NCB;  // dv columns per workgroup (16*NCB per wave)
     // fp16 operands: T = (I+M)^-1 and P are applied as fp16 hi + lo pairs, and the
@@ -772,29 +798,57 @@ struct ChunkCfg {
     static constexpr int SZ_P = CH * LDT * (int)sizeof(T);
     static constexpr int SZ_F = CH * LDF * 4;
     static constexpr int SZ_MS = SZ_F > SZ_Q ? SZ_F : SZ_Q;  // the KDA gated K^T tile reuses it
+    // Front end fused into the load stage (bf16 raw rows; conv + SiLU + L2 per chunk):
+    // q and k are stored as fp16 hi + lo tiles, and v is never a tile: the raw v rows of
+    // the chunk, with the KC - 1 rows before it, sit in a raw region from which each lane
+    // convolves the values of its own D-layout rows in fp32. The raw q|k rows of the next
+    // chunk land by LDS-DMA on the two Q tiles and the inversion scratch, which are dead
+    // from the end of the preparation until the next load stage, and the raw v rows on
+    // their own region.
+    static constexpr int KC = 4;                 // conv taps of the fused front end
+    static constexpr int RR = CH + KC - 1;       // raw rows per chunk
+    static constexpr int SZ_QF = 2 * SZ_Q;       // Q hi, Q lo
+    static constexpr int LDX = 20;               // row stride of the 16x16 inversion scratch
+    static constexpr int SZ_X = 4 * 16 * LDX * 4;
+    static constexpr int RQK = 2 * DK * 2;       // bytes per raw [q | k] row
+    static constexpr int VS = NV * 2 / 16;       // 16-byte pieces of a raw v row
+    // one slot of padding per raw v row: the u16 reads of D-layout rows 4 apart then fall
+    // in different halves of the banks
+    static constexpr int RVB = (VS + 1) * 16;
+    static constexpr int SZ_RV = RR * RVB;
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + SZ_Q;
-    static constexpr int OFF_V = OFF_K + SZ_Q;
-    static constexpr int OFF_P = OFF_V + SZ_V;                    // P (hi)
+    static constexpr int OFF_QL = SZ_Q;               // Q lo (fused front end)
+    static constexpr int OFF_X = FRONT ? SZ_QF : 0;  // inversion scratch (fused front end)
+    static constexpr int OFF_K = FRONT ? SZ_QF + SZ_X : OFF_Q + SZ_Q;
+    static constexpr int OFF_KL = OFF_K + SZ_Q;      // K lo (fused front end)
+    static constexpr int OFF_V = OFF_KL + (FRONT ? SZ_Q : 0);    // V tile, or the raw v rows
+    static constexpr int OFF_P = OFF_V + (FRONT ? SZ_RV : SZ_V);  // P (hi)
     static constexpr int OFF_PL = OFF_P + SZ_P;                   // P (lo)
     static constexpr int OFF_MT = OFF_PL + (SPLIT ? SZ_P : 0);    // M_IJ (J<I), T_II
     static constexpr int OFF_M = OFF_MT + SZ_P;                   // diagonal blocks of M, fp32
-    static constexpr int OFF_GK = OFF_M + SZ_MS;  // per-channel cumulative log-gates
+    static constexpr int OFF_GK = OFF_M + (FRONT ? 0 : SZ_MS);  // per-channel cumulative log-gates
     // Gamma[64], beta[64], a = e^Gamma [64], a_C / a [64]
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);
-    static constexpr int LDO = NV + 16;  // o rows (fp32): 4 rows of a D-layout write hit 32 banks
+    // o rows (fp32). Fused front end: rows 4 apart (the lane groups of a D-layout write)
+    // 16 banks apart
+    static constexpr int LDO = NV + (FRONT ? 4 : 16);
     // + the running log decay bound of a transition job (one float, padded to 16 bytes;
     // scalar gate without the fused output gate only)
     static constexpr bool STOP = !KDA && !GATE;
     static constexpr int OFF_O = OFF_G + 4 * CH * 4 + (STOP ? 16 : 0);
     // o is staged in LDS when it fits (not with the per-channel gate tile at 128 columns)
     static constexpr bool STAGE_O = OFF_O + CH * LDO * 4 <= 160 * 1024;
+    // fused front end: the q and k conv taps of this head, [2][KC][DK] float
+    static constexpr int OFF_CW = OFF_O + (STAGE_O ? CH * LDO * 4 : 0);
     // output gate: the z rows of a chunk (the caller's element type, as wide as T) and the
     // norm weights of the NV columns
-    static constexpr int OFF_Z = OFF_O + (STAGE_O ? CH * LDO * 4 : 0);
+    static constexpr int OFF_Z = OFF_CW + (FRONT ? 2 * KC * DK * 4 : 0);
     static constexpr int ZROW = NV * (int)sizeof(T);
     static constexpr int OFF_W = OFF_Z + (GATE ? CH * ZROW : 0);
     static constexpr int BYTES = OFF_W + (GATE ? NV * 4 : 0);
+    static_assert(!FRONT || RR * RQK <= SZ_QF + SZ_X, "raw q|k rows fit over Q and the scratch");
+    static_assert(!FRONT || (SPLIT && !KDA && !GATE && NCB == 1 && STAGE_O && NV == DV),
+                  "fused front end: fp16 operands, scalar gate, one column block per wave");
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -975,13 +1029,15 @@ __device__ __forceinline__ int block_task(int wave, int j)
     }
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE>
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE,
+          bool FRONT>
 __global__ void __launch_bounds__(NW * 64)
     __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE>;
+    static_assert(!FRONT || std::is_same<TIN, bf16>::value, "fused front end: bf16 raw rows");
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
     // the output gate normalises whole o rows, which the staged o holds
     static_assert(!GATE || (C::STAGE_O && C::NV == DV), "output gate needs staged o rows");
     // z comes in the caller's element type (bf16 also when the operands are fp16)
@@ -1019,7 +1075,10 @@ __global__ void __launch_bounds__(NW * 64)
     const int b = a.order ? a.order[bi] : bi;  // varlen: longest streams dispatch first
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
+    const int64_t sbeg = start;  // the stream's first row
     float *state = (a.h_ptrs ? a.h_ptrs[b] : a.h);
+    bool last_seg = true;    // this job's rows end the stream (fused front end: it writes the
+    bool win_staged = false; // new windows, to the warm-mode staging area if win_staged)
     // segmented scan: this job's rows, where its state comes from and goes to
     const float *hin = state;  // nullptr: start from 0
     float *hout = state;       // nullptr: the end state is not needed
@@ -1039,9 +1098,13 @@ __global__ void __launch_bounds__(NW * 64)
                     return;
                 seg = job - (2 * S - 4);
                 hin = nullptr;
-                if (seg < S - 1)
-                    hout = nullptr;
+                // The last segment's end state is the stream's final state. Job 0 of this
+                // launch reads the stream's initial state from the same buffer and nothing
+                // orders the two workgroups, so it goes to slot H(b, S-1) (unused in warm
+                // mode), and the combine kernel, the next launch, copies it over.
+                hout = seg < S - 1 ? nullptr : a.seg_ws + lay.h(b, S - 1);
                 warm_rows = (int64_t)a.seg_ws[lay.warm_chunks(b, seg, head)] * CH;
+                win_staged = true;
             } else {
                 if (warm && job > 0)
                     return;
@@ -1068,6 +1131,7 @@ __global__ void __launch_bounds__(NW * 64)
         start = min(s0 + (seg == 0 ? 0 : a.seg0_len + (seg - 1) * a.seg_len), end);
         if (seg < S - 1)  // the last segment runs to the stream's end
             end = min(start + (seg == 0 ? a.seg0_len : a.seg_len), end);
+        last_seg = seg == S - 1;
     }
     // o is written from row o_start on (never by map jobs); a warm job starts warm_rows
     // earlier, from h = 0, with chunks that compute no o
@@ -1134,21 +1198,95 @@ __global__ void __launch_bounds__(NW * 64)
         gk_row[it] = wave0 * GRW + lane0 / GPR + it * NW * GRW;
         gk_src[it] = a.g + ((int64_t)gk_row[it] * H + head) * DK + (lane0 % GPR) * 4;
     }
-    const float *g_src = a.g + (int64_t)(tid0 & (CH - 1)) * H + head;
-    const float *b_src = a.beta + (int64_t)(tid0 & (CH - 1)) * H + head;
+    const int gb_off = (tid0 & (CH - 1)) * H;  // this lane's row of the gates and betas
+    // Fused front end: the raw rows of the chunk at c0 (Lc rows) and the KC - 1 rows before
+    // it go straight into LDS by LDS-DMA, one 16-byte piece per lane (a wave instruction
+    // fills 1 KiB): raw row rho of a region holds stream row c0 - (KC - 1) + rho, as
+    // [q | k] (RQK bytes) or v (RVB bytes, the last 16 of them padding). Rows before the
+    // stream's first row (the carried window, at the first chunk) are stored before the
+    // loop; rows at or past the chunk's end are never read and never used.
+    constexpr int KC = C::KC;
+    const int qk_heads = H / a.qk_group;
+    // The raw rows used are [max(stream start, c0 - (KC - 1)), c0 + Lc): raw row indices
+    // [rlo, rhi) of the chunk. Addresses are a uniform row base plus a 32-bit lane offset
+    // (the host keeps RR row strides within 32 bits for these calls).
+    auto prefetch_raw = [&](int64_t c0, int Lc, bool with_q, int lane, int wave) {
+        const int rlo = (int)max((int64_t)0, sbeg - (c0 - (KC - 1)));
+        const int rhi = Lc + KC - 1;
+        const int ldi = (int)ld;
+        const TIN *qb = qg + (c0 - (KC - 1)) * ld, *kb = kg + (c0 - (KC - 1)) * ld;
+        constexpr int QS = C::RQK / 16, NQI = (C::RR * QS + 63) / 64;
+#pragma unroll
+        for (int i = 0; i < (NQI + NW - 1) / NW; ++i) {
+            const int n = wave + NW * i;
+            const int slot = 64 * n + lane, rho = slot / QS, pc = slot % QS;
+            const bool isk = pc >= QS / 2;
+            if (n < NQI && rho >= rlo && rho < rhi && (isk || with_q))
+                dma16((isk ? kb : qb) + (rho * ldi + (pc % (QS / 2)) * 8),
+                      lds_addr(smem + C::OFF_Q + 1024 * n));
+        }
+        if (!v_zero) {
+            const TIN *vb = vg + (c0 - (KC - 1)) * ld;
+            constexpr int VSL = C::VS + 1, NVI = (C::RR * VSL + 63) / 64;
+#pragma unroll
+            for (int i = 0; i < (NVI + NW - 1) / NW; ++i) {
+                const int n = wave + NW * i;
+                const int slot = 64 * n + lane, rho = slot / VSL, pc = slot - rho * VSL;
+                if (n < NVI && pc < C::VS && rho >= rlo && rho < rhi)
+                    dma16(vb + (rho * ldi + pc * 8), lds_addr(smem + C::OFF_V + 1024 * n));
+            }
+        }
+    };
+    // conv channel of q/k element c (tensor 0: q, 1: k) and of v column c of this workgroup
+    auto qk_channel = [&](int tensor, int c) {
+        return (tensor ? qk_heads * DK : 0) + head_qk * DK + c;
+    };
+    auto v_channel = [&](int c) { return 2 * qk_heads * DK + head * DV + slice * NV + c; };
+    float wv[FRONT ? KC : 1];  // this lane's v column taps (fused front end)
+    if constexpr (FRONT) {
+        // q and k taps of this head into LDS, [tensor][tap][channel]
+        for (int idx = tid0; idx < 2 * KC * DK; idx += NT) {
+            const int t = idx / (KC * DK), rem = idx - t * KC * DK, j = rem / DK;
+            ((float *)(smem + C::OFF_CW))[idx] =
+                a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * KC + j];
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+            wv[j] = a.conv_w[(int64_t)v_channel(16 * wave0 + (lane0 & 15)) * KC + j];
+        // the stream's first chunk: raw rows 0 .. KC-2 are the carried window
+        if (start == sbeg && start < end) {
+            const TIN *cw = (const TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
+                                                            : a.conv_state);
+            constexpr int W = KC - 1;
+            for (int idx = tid0; idx < (2 * DK + NV) * W; idx += NT) {
+                const int ch = idx / W, j = idx - ch * W;
+                if (ch < 2 * DK)
+                    *(TIN *)(smem + C::OFF_Q + j * C::RQK + ch * 2) =
+                        cw[(int64_t)qk_channel(ch >= DK, ch % DK) * W + j];
+                else
+                    *(TIN *)(smem + C::OFF_V + j * C::RVB + (ch - 2 * DK) * 2) =
+                        cw[(int64_t)v_channel(ch - 2 * DK) * W + j];
+            }
+        }
+    }
     auto prefetch = [&](int64_t c0, int Lc) {
         const int64_t roff = c0 * ld;
         const bool with_q = c0 >= o_start;  // q rows only feed o
+        if constexpr (FRONT) {
+            prefetch_raw(c0, Lc, with_q, threadIdx.x & 63,
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+        } else {
 #pragma unroll
-        for (int it = 0; it < NQK; ++it)
-            pq[it] = qk_row[it] < Lc && (qk_isk[it] || with_q)
-                         ? load_stream16(qk_src[it] + roff)
-                         : make_uint4(0, 0, 0, 0);
+            for (int it = 0; it < NQK; ++it)
+                pq[it] = qk_row[it] < Lc && (qk_isk[it] || with_q)
+                             ? load_stream16(qk_src[it] + roff)
+                             : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int it = 0; it < NVV; ++it)
-            pv[it] = v_row[it] < Lc && !v_zero
-                         ? load_stream16(v_src[it] + roff)
-                         : make_uint4(0, 0, 0, 0);
+            for (int it = 0; it < NVV; ++it)
+                pv[it] = v_row[it] < Lc && !v_zero
+                             ? load_stream16(v_src[it] + roff)
+                             : make_uint4(0, 0, 0, 0);
+        }
         if constexpr (KDA) {
 #pragma unroll
             for (int it = 0; it < NGK; ++it)
@@ -1156,10 +1294,14 @@ __global__ void __launch_bounds__(NW * 64)
                               ? load_stream16(gk_src[it] + c0 * H * DK)
                               : make_uint4(0, 0, 0, 0);
         }
-        if (tid0 < CH) {
+        if (threadIdx.x < CH) {
+            // opaque per call: a 64-bit per-lane address held across the chunk loop would
+            // be spilled, and its reload waits for every load in flight
+            int go = gb_off;
+            asm volatile("" : "+v"(go));
             if constexpr (!KDA)
-                pg = tid0 < Lc ? g_src[c0 * H] : 0.f;
-            pb = tid0 < Lc ? b_src[c0 * H] : 0.f;
+                pg = (int)threadIdx.x < Lc ? (a.g + (c0 * H + head))[go] : 0.f;
+            pb = (int)threadIdx.x < Lc ? (a.beta + (c0 * H + head))[go] : 0.f;
         }
     };
     if (start < end)
@@ -1235,9 +1377,12 @@ __global__ void __launch_bounds__(NW * 64)
 
     // X = V - diag(a) K h and O = diag(a) Q h for column block cb of this wave (the
     // per-channel gate's tiles carry e^G already)
+    // Fused front end: V is the conv + SiLU of the raw v rows (Vs is then the raw region),
+    // computed here in fp32 for this lane's D-layout rows 16 I + 4 g + i and column; rows
+    // at or past the chunk's end (Lc rows) are 0. Q h takes q's fp16 hi part.
     auto kh_qh = [&](int cb, f32x4 (&x)[4], f32x4 (&o)[4], const float (&ar)[4][4],
-                     const T *Ks, const T *Qs, const T *Vs, int wave, int lane, int g4,
-                     int c16) {
+                     const T *Ks, const void *Qs, const void *Vs, int wave, int lane, int g4,
+                     int c16, int Lc) {
         const int vc = 16 * (wave * NCB + cb);  // this block's columns within Vs
         frag hf[DK / 32];
 #pragma unroll
@@ -1250,13 +1395,35 @@ __global__ void __launch_bounds__(NW * 64)
             for (int kb = 0; kb < DK / 32; ++kb) {
                 mma(kh, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), hf[kb]);
                 if (write_o)
-                    mma(qh, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), hf[kb]);
+                    mma(qh, ld_frag_qk<DK>((const T *)Qs, 16 * I, 32 * kb, lane), hf[kb]);
+            }
+            float v[4];
+            if constexpr (FRONT) {
+                // raw rows 16 I + 4 g .. + KC + 2 of this column (raw row = chunk row + KC - 1)
+                const unsigned char *rv = (const unsigned char *)Vs + (vc + c16) * 2 +
+                                          (16 * I + 4 * g4) * C::RVB;
+                float xr[KC + 3];
+#pragma unroll
+                for (int u = 0; u < KC + 3; ++u)
+                    xr[u] = __uint_as_float((uint32_t)*(const unsigned short *)(rv + u * C::RVB)
+                                            << 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int j = 0; j < KC; ++j)
+                        acc += wv[j] * xr[i + j];
+                    v[i] = 16 * I + 4 * g4 + i < Lc && !v_zero ? silu(acc) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (float)((const T *)Vs)[(16 * I + 4 * g4 + i) * LDV + vc + c16];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float v = (float)Vs[(16 * I + 4 * g4 + i) * LDV + vc + c16];
                 const float arr = KDA ? 1.f : ar[I][i];
-                x[I][i] = v - arr * kh[i];
+                x[I][i] = v[i] - arr * kh[i];
                 o[I][i] = arr * qh[i];
             }
         }
@@ -1301,12 +1468,110 @@ __global__ void __launch_bounds__(NW * 64)
         float *ea = graw + 2 * CH;  // a_r = e^Gamma_r
         float *ed = graw + 3 * CH;  // a_C / a_r
         float *Os = (float *)(smem + zo + C::OFF_O);
+        T *Kl = (T *)(smem + zo + C::OFF_KL);      // fused front end: K lo
+        T *Ql = (T *)(smem + zo + C::OFF_QL);      // fused front end: Q lo
+        float *Xs = (float *)(smem + zo + C::OFF_X);  // fused front end: inversion scratch
 
         // the previous chunk's z tile (LDS-DMA, counted like the prefetch loads) lands
         // before the barrier that precedes its flush
         if constexpr (GATE)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+        if constexpr (FRONT) {
+            // ---- A (fused front end): raw rows -> conv + SiLU -> L2, scale -> tiles -------
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS-DMA rows
+            __syncthreads();  // every wave's rows, and the window rows of a first chunk
+            // Lane group gi of LQ lanes takes 8 channels each of one tensor (q or k) for rows
+            // 4 rg .. 4 rg + 3, so a row's L2 sum is a sum over the group (DPP).
+            constexpr int LQ = DK / 8, GPW = 64 / LQ;
+            static_assert(NW * GPW / 2 * 4 == CH, "conv row map");
+            const int gi = lane / LQ, cg = lane % LQ, tsr = gi & 1;
+            const int rg = wave * (GPW / 2) + (gi >> 1);
+            const unsigned char *rq = smem + zo + C::OFF_Q + tsr * DK * 2 + cg * 16;
+            const float *wt = (const float *)(smem + zo + C::OFF_CW) + tsr * KC * DK + 8 * cg;
+            float y[4][8];
+            {
+                float w[KC][8];
+#pragma unroll
+                for (int j = 0; j < KC; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(wt + j * DK + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            w[j][4 * h + e] = t4[e];
+                    }
+                uint4 raw[KC + 3];
+#pragma unroll
+                for (int u = 0; u < KC + 3; ++u)
+                    raw[u] = *reinterpret_cast<const uint4 *>(rq + (4 * rg + u) * C::RQK);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                    for (int j = 0; j < KC; ++j) {
+                        float xv[8];
+                        unpack((const bf16 *)nullptr, raw[i + j], xv);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[e] += w[j][e] * xv[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        y[i][e] = silu(acc[e]);
+                }
+            }
+            // L2 of each row over the head, the q scale; rows at or past the end are 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = tsr ? 1.f : a.scale;
+                if (a.do_l2) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        ss += y[i][e] * y[i][e];
+                    m *= rsqrtf(group_sum<LQ>(ss) + a.eps);
+                }
+                const bool live = 4 * rg + i < L;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    y[i][e] = live ? y[i][e] * m : 0.f;
+            }
+            // the stream's last chunk: the new windows are its raw rows L .. L + KC - 2 (the
+            // last KC - 1 entries of [old window | rows]), read before the tiles cover them
+            if (last_seg && cs + CH >= end) {
+                TIN *wo = win_staged ? (TIN *)a.win_ws + (int64_t)b * a.cd * (KC - 1)
+                                     : (TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
+                                                                 : a.conv_state);
+                constexpr int W = KC - 1;
+                for (int idx = tid; idx < (2 * DK + NV) * W; idx += NT) {
+                    const int ch = idx / W, j = idx - ch * W;
+                    if (ch < 2 * DK)
+                        wo[(int64_t)qk_channel(ch >= DK, ch % DK) * W + j] =
+                            *(const TIN *)(smem + zo + C::OFF_Q + (L + j) * C::RQK + ch * 2);
+                    else
+                        wo[(int64_t)v_channel(ch - 2 * DK) * W + j] = *(const TIN *)(
+                            smem + zo + C::OFF_V + (L + j) * C::RVB + (ch - 2 * DK) * 2);
+                }
+            }
+            __syncthreads();  // the raw q|k rows are read before the Q tile covers them
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rg + i;
+                if (tsr == 1 || write_o) {  // q only feeds o
+                    T *dh = tsr ? Ks : Qs, *dl = tsr ? Kl : Ql;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        f16x4 hi4, lo4;
+                        split4(f32x4{y[i][4 * h], y[i][4 * h + 1], y[i][4 * h + 2],
+                                     y[i][4 * h + 3]},
+                               hi4, lo4);
+                        *reinterpret_cast<f16x4 *>(dh + QK<T, DK>::at(r, 2 * cg + h)) = hi4;
+                        *reinterpret_cast<f16x4 *>(dl + QK<T, DK>::at(r, 2 * cg + h)) = lo4;
+                    }
+                }
+            }
+        } else {
         // ---- A: registers -> LDS: q, k (L2, scale), v, raw gates, beta -----------------
 #pragma unroll
         for (int it = 0; it < NQK; ++it) {
@@ -1354,6 +1619,7 @@ __global__ void __launch_bounds__(NW * 64)
                 const int r = wave * GRW + lane / GPR + it * NW * GRW;
                 *reinterpret_cast<uint4 *>(Gk + r * LDG + (lane % GPR) * 4) = pgk[it];
             }
+        }
         }
         if (tid < CH) {  // wave 0: Gamma = inclusive prefix sum of the log-gates, and decays
             const float gam = wave_scan(pg);
@@ -1445,7 +1711,7 @@ __global__ void __launch_bounds__(NW * 64)
         }
         f32x4 xe[EARLY ? 4 : 1], oe[EARLY ? 4 : 1];
         if constexpr (EARLY)
-            kh_qh(0, xe, oe, ar, Ks, Qs, Vs, wave, lane, g4, c16);
+            kh_qh(0, xe, oe, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
 
         // ---- C: M = strict_tril(diag(beta) K K^T . decay), P = tril(Q K^T . decay) ------
         // The 10 lower 16x16 blocks (I, J), numbered row by row. Waves 0-3 each take one
@@ -1470,8 +1736,18 @@ __global__ void __launch_bounds__(NW * 64)
                     const frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
                     if (do_m)
                         mma(am, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), fb);
-                    if (do_p)
-                        mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
+                    if (do_p) {
+                        if constexpr (FRONT) {
+                            // Q K^T with q and k as fp16 hi + lo pairs (the lo x lo term is
+                            // below fp32 rounding)
+                            const frag qh8 = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
+                            mma(ap, qh8, fb);
+                            mma(ap, qh8, ld_frag_qk<DK>(Kl, 16 * J, 32 * kb, lane));
+                            mma(ap, ld_frag_qk<DK>(Ql, 16 * I, 32 * kb, lane), fb);
+                        } else {
+                            mma(ap, ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane), fb);
+                        }
+                    }
                 }
             } else if (I != J) {
                 // off-diagonal block: reference row b = 16I (first row of block I), so
@@ -1592,12 +1868,14 @@ __global__ void __launch_bounds__(NW * 64)
                 // operands go through this block's own corner of Ms (no other wave touches
                 // it).
                 const int base = 16 * I;
-                float *scr = Ms + base * LDF + base;
+                // this block's corner of Ms, or (fused front end) its own scratch block
+                float *scr = FRONT ? Xs + base * C::LDX : Ms + base * LDF + base;
+                constexpr int lds = FRONT ? C::LDX : LDF;
                 auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        scr[(4 * g4 + i) * LDF + c16] = d[i];
-                    return blk_a(Ms, LDF, I, I, lane);
+                        scr[(4 * g4 + i) * lds + c16] = d[i];
+                    return blk_a(scr, lds, 0, 0, lane);
                 };
                 f32x4 nb;  // N, D layout
 #pragma unroll
@@ -1685,7 +1963,7 @@ __global__ void __launch_bounds__(NW * 64)
                 for (int I = 0; I < 4; ++I)
                     x[I] = xe[I], o[I] = oe[I];
             } else {
-                kh_qh(cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16);
+                kh_qh(cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
             }
             if (NW == 8 && wave >= 4 && cb == NCB - 1)
                 __builtin_amdgcn_s_setprio(0);
@@ -1788,6 +2066,10 @@ __global__ void __launch_bounds__(NW * 64)
                     mma(hs[cb][mb], k0, vl0);
                     mma(hs[cb][mb], k1, vl1);
                 }
+                if constexpr (FRONT) {  // k as an fp16 hi + lo pair as well
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 0, 16 * mb, lane), vf0);
+                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 32, 16 * mb, lane), vf1);
+                }
             }
         }
         __syncthreads();
@@ -1824,13 +2106,14 @@ __global__ void __launch_bounds__(NW * 64)
     }
 }
 
-template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE>
+template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE,
+          bool FRONT>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
-    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE>;
+    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
     static bool attr_set = false;  // per instance; same value on every device
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -1849,53 +2132,56 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 }
 
 // Instances: (input element, operand type, input kind, dk, dv, waves, column blocks of 16
-// per wave, per-channel gate, output gate fused). Input kind: 0 = f32 rows, 1 = bf16 rows,
-// 2 = fp16 activations of the front end. A workgroup covers NW * NCB * 16 dv columns of one
+// per wave, per-channel gate, output gate fused, front end fused). Input kind: 0 = f32
+// rows, 1 = bf16 rows, 2 = fp16 activations of the front kernel, 3 = bf16 raw rows with the
+// conv front end fused into the load stage. A workgroup covers NW * NCB * 16 dv columns of one
 // (stream, head). The default (widest) shapes that stage o also come with the output gate
 // fused into the o flush, where o and the z tile fit in LDS; the per-channel-gate instances
 // at 128 columns (o not staged) and fp32 at 64 columns (no room for the z tile) gate o in
 // a separate pass (gate_kernel), and so do the dk != dv shapes, whose value rows span two
 // workgroups (dv = 2 dk: two column slices of one (stream, head)).
 #define GDN_CHUNK_INSTANCES(X)                          \
-    X(bf16, f16, 1, 128, 128, 8, 1, false, false)       \
-    X(bf16, f16, 1, 128, 128, 4, 2, false, false)       \
-    X(bf16, f16, 1, 128, 128, 4, 1, false, false)       \
-    X(f16, f16, 2, 128, 128, 8, 1, false, false)        \
-    X(f16, f16, 2, 128, 128, 4, 2, false, false)        \
-    X(f16, f16, 2, 128, 128, 4, 1, false, false)        \
-    X(bf16, f16, 1, 64, 64, 4, 1, false, false)         \
-    X(f16, f16, 2, 64, 64, 4, 1, false, false)          \
-    X(float, float, 0, 64, 64, 4, 1, false, false)      \
-    X(bf16, f16, 1, 128, 128, 8, 1, true, false)        \
-    X(bf16, f16, 1, 128, 128, 4, 1, true, false)        \
-    X(f16, f16, 2, 128, 128, 8, 1, true, false)         \
-    X(f16, f16, 2, 128, 128, 4, 1, true, false)         \
-    X(bf16, f16, 1, 64, 64, 4, 1, true, false)          \
-    X(f16, f16, 2, 64, 64, 4, 1, true, false)           \
-    X(float, float, 0, 64, 64, 4, 1, true, false)       \
-    X(bf16, f16, 1, 128, 128, 8, 1, false, true)        \
-    X(f16, f16, 2, 128, 128, 8, 1, false, true)         \
-    X(bf16, f16, 1, 64, 64, 4, 1, false, true)          \
-    X(f16, f16, 2, 64, 64, 4, 1, false, true)           \
-    X(float, float, 0, 64, 64, 4, 1, false, true)       \
-    X(bf16, f16, 1, 64, 64, 4, 1, true, true)           \
-    X(f16, f16, 2, 64, 64, 4, 1, true, true)              \
-    X(bf16, f16, 1, 128, 256, 8, 1, false, false)     \
-    X(f16, f16, 2, 128, 256, 8, 1, false, false)      \
-    X(bf16, f16, 1, 128, 256, 8, 1, true, false)      \
-    X(f16, f16, 2, 128, 256, 8, 1, true, false)       \
-    X(float, float, 0, 64, 128, 4, 1, false, false)   \
-    X(float, float, 0, 64, 128, 4, 1, true, false)
+    X(bf16, f16, 1, 128, 128, 8, 1, false, false, false) \
+    X(bf16, f16, 1, 128, 128, 4, 2, false, false, false) \
+    X(bf16, f16, 1, 128, 128, 4, 1, false, false, false) \
+    X(f16, f16, 2, 128, 128, 8, 1, false, false, false) \
+    X(f16, f16, 2, 128, 128, 4, 2, false, false, false) \
+    X(f16, f16, 2, 128, 128, 4, 1, false, false, false) \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, false, false) \
+    X(f16, f16, 2, 64, 64, 4, 1, false, false, false) \
+    X(float, float, 0, 64, 64, 4, 1, false, false, false) \
+    X(bf16, f16, 1, 128, 128, 8, 1, true, false, false) \
+    X(bf16, f16, 1, 128, 128, 4, 1, true, false, false) \
+    X(f16, f16, 2, 128, 128, 8, 1, true, false, false) \
+    X(f16, f16, 2, 128, 128, 4, 1, true, false, false) \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, false, false) \
+    X(f16, f16, 2, 64, 64, 4, 1, true, false, false) \
+    X(float, float, 0, 64, 64, 4, 1, true, false, false) \
+    X(bf16, f16, 1, 128, 128, 8, 1, false, true, false) \
+    X(f16, f16, 2, 128, 128, 8, 1, false, true, false) \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, true, false) \
+    X(f16, f16, 2, 64, 64, 4, 1, false, true, false) \
+    X(float, float, 0, 64, 64, 4, 1, false, true, false) \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, true, false) \
+    X(f16, f16, 2, 64, 64, 4, 1, true, true, false) \
+    X(bf16, f16, 1, 128, 256, 8, 1, false, false, false) \
+    X(f16, f16, 2, 128, 256, 8, 1, false, false, false) \
+    X(bf16, f16, 1, 128, 256, 8, 1, true, false, false) \
+    X(f16, f16, 2, 128, 256, 8, 1, true, false, false) \
+    X(float, float, 0, 64, 128, 4, 1, false, false, false) \
+    X(float, float, 0, 64, 128, 4, 1, true, false, false) \
+    X(bf16, f16, 3, 128, 128, 8, 1, false, false, true)   \
+    X(bf16, f16, 3, 64, 64, 4, 1, false, false, true)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
 // with the output gate fused
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
                         const ChunkArgs &a, int grid, hipStream_t s)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G)                                          \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F)                                       \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
         (waves == 0 || waves == NW) && !gate == !G)                                    \
-        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD, G>(a, grid, s);
+        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD, G, F>(a, grid, s);
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return hipErrorInvalidValue;
@@ -1903,7 +2189,7 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 
 int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G)                                          \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F)                                       \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
         (waves == 0 || waves == NW) && !gate == !G)                                    \
         return 1;
@@ -1936,8 +2222,32 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     const int BH = a.lay.B * a.H;
     const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
     const int b = bh / a.H, head = bh - b * a.H;
-    if (a.warm && a.seg_ws[a.lay.warm_mode(b, head)] != 0.f)
-        return;  // every segment of this (stream, head) starts warm: no chain
+    if (a.warm && a.seg_ws[a.lay.warm_mode(b, head)] != 0.f) {
+        // every segment of this (stream, head) started warm in the first launch: no chain.
+        // Its last segment left the final state in slot H(b, S-1) (and, with the front end
+        // fused, the new windows in win_ws) because the job that read the initial state and
+        // the old windows ran in that same launch; copy this workgroup's share over.
+        const int64_t hoff = (int64_t)head * DK * DK;
+        const float *src = a.seg_ws + a.lay.h(b, a.lay.S - 1) + hoff;
+        float *dst = (a.h_ptrs ? a.h_ptrs[b] : a.h) + hoff;
+        for (int idx = threadIdx.x; idx < DK * 16; idx += NWV * 64) {
+            const int64_t e = (int64_t)(idx >> 4) * DK + 16 * cbk + (idx & 15);
+            dst[e] = src[e];
+        }
+        if (a.win_ws) {  // bf16 windows [cd][3]; this head's q, k and v channels
+            const int nch = 2 * DK + DK, per = (nch * 3 + DK / 16 - 1) / (DK / 16);
+            const uint16_t *ws = (const uint16_t *)a.win_ws + (int64_t)b * a.cd * 3;
+            uint16_t *cw = (uint16_t *)(a.conv_state_ptrs ? a.conv_state_ptrs[b] : a.conv_state);
+            for (int e = cbk * per + (int)threadIdx.x; e < min((cbk + 1) * per, nch * 3);
+                 e += NWV * 64) {
+                const int ch = e / 3, j = e - 3 * ch;
+                const int gc = ch < 2 * DK ? (ch >= DK ? a.H * DK : 0) + head * DK + ch % DK
+                                           : 2 * a.H * DK + head * DK + ch - 2 * DK;
+                cw[(int64_t)gc * 3 + j] = ws[(int64_t)gc * 3 + j];
+            }
+        }
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, c16 = lane & 15;

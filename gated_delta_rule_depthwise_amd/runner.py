@@ -62,7 +62,8 @@ class Prefill:
         # segmented=False sizes the workspace for the front end only, which makes a single
         # or batched call run its scan unsegmented
         self.ws_bytes = B.gdn_workspace_bytes(
-            self.params, spec.B, spec.N, kind if segmented else B.GDN_KIND_VARLEN)
+            self.params, spec.B, spec.N,
+            (kind if segmented else B.GDN_KIND_VARLEN) | (self.plan_kind & B.GDN_PLAN_KDA))
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
         es = self.x.element_size()
         base = self.x.data_ptr()

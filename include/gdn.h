@@ -36,7 +36,14 @@
  *     GDN_BF16); o, g, beta, h and conv_w are float32. (o is float32 for bf16 inputs too:
  *     rounding o itself to bf16 already costs about 2e-2 of max|error|/RMS on these
  *     heavy-tailed outputs.) The dense products run on MFMA with fp32 accumulation, with
- *     fp16 operands for bf16 inputs and fp32 operands for float32 inputs.
+ *     fp16 operands for bf16 inputs (hi + lo pairs where a single fp16 rounding would
+ *     show in o or h) and fp32 operands for float32 inputs.
+ *   - Front end: with bf16 rows, 4 taps, the scalar gate (gdn_*), one q/k head per value
+ *     head, dk == dv, no output gate and ld_qkv < 2^24, the conv + SiLU + L2 run inside
+ *     the scan's load stage in fp32 straight from the raw rows (no activation buffer; q
+ *     and k enter the products as fp16 hi + lo pairs, v in fp32). Every other front-end call runs the
+ *     front end as a kernel of its own that hands the scan fp16 (bf16 rows) or fp32
+ *     activations through the workspace.
  *   - Errors: every check below runs on the host before anything is enqueued; on error
  *     nothing is launched and no buffer changes (the pages refuse a bad token count before
  *     any launch). GDN_E_HIP reports a failed launch.
@@ -72,8 +79,9 @@ extern "C" {
 #define GDN_KIND_SINGLE 0
 #define GDN_KIND_BATCHED 1
 #define GDN_KIND_VARLEN 2
-/* OR-ed into the kind of gdn_segments / gdn_segment_plan: the plan of a KDA call (per-key-
- * channel gate) instead of a GDN call (scalar gate); the two plans differ */
+/* OR-ed into the kind of gdn_segments / gdn_segment_plan / gdn_workspace_bytes: the plan
+ * and workspace of a KDA call (per-key-channel gate) instead of a GDN call (scalar gate);
+ * the two differ */
 #define GDN_PLAN_KDA 0x100
 
 typedef struct gdn_params {
@@ -261,7 +269,9 @@ int gdn_profile_enable(int on);
 int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
 
 /* Bytes of device workspace a call of `kind` with B streams and up to max_tokens rows in
- * total needs (0 if none). Returns 0 for invalid parameters.
+ * total needs (0 if none). Returns 0 for invalid parameters. The size is that of a GDN
+ * call (scalar gate); or GDN_PLAN_KDA into kind for a KDA call, whose front end (when
+ * conv_k > 0) always needs room for its activations.
  *
  * For varlen calls (B <= 1024) it also holds B int32: the streams ranked by length, so that
  * when a call has more (stream, head) workgroups than the device has CUs the longest
@@ -295,8 +305,7 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
  * GDN_PLAN_KDA or-ed into kind) with these parameters, t_per_stream tokens per stream and
  * ws_bytes of workspace would use on the current device; always 0 for GDN_KIND_VARLEN.
  * Negative status for invalid arguments, or GDN_E_UNSUPPORTED when that call is not
- * compiled for these parameters. Host only; enqueues nothing. The environment variable GDN_SEG (read once) overrides the choice: 0 never
- * segments, 3..12 asks for that many segments. */
+ * compiled for these parameters. Host only; enqueues nothing. */
 int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
                  size_t ws_bytes);
 

@@ -41,8 +41,18 @@ def test_status_strings():
 def test_workspace_bytes():
     p = B.params(32, 128, 128, conv_k=4)
     cd = 3 * 32 * 128
-    ws = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
+    # the per-key-channel gate runs its front end as a kernel of its own: activations
+    ws = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA)
     assert ws >= 4096 * cd * 2 and ws % 256 == 0
+    # the scalar gate fuses the front end into the scan: no activation buffer, only the
+    # segment states and the staged windows of a segmented call
+    wg = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
+    assert 0 < wg < 4096 * cd * 2 and wg % 256 == 0
+    assert B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN) == 256  # stream ranking
+    assert B.gdn_workspace_bytes(p, 1, 10, B.GDN_KIND_SINGLE) == 0
+    # float32 rows: the front kernel and its fp32 activations
+    pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)
+    assert B.gdn_workspace_bytes(pf, 1, 10, B.GDN_KIND_VARLEN) == 10 * 3 * 32 * 64 * 4 + 256
     assert B.gdn_workspace_bytes(B.params(32, 128, 128), 8, 16384, B.GDN_KIND_BATCHED) == 0
     assert B.gdn_workspace_bytes(p, 0, 4096, B.GDN_KIND_SINGLE) == 0
     assert B.gdn_workspace_bytes(p, 1, 0, B.GDN_KIND_SINGLE) == 0
@@ -54,9 +64,11 @@ def test_segment_plan():
     has room for the segment states; a workspace without that room, varlen calls and calls
     that already fill the device run unsegmented."""
     p = B.params(32, 128, 128, conv_k=4)           # one stream, 32 heads
+    kd = B.GDN_PLAN_KDA
     full = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
     front = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN)
-    assert front == 4096 * 3 * 32 * 128 * 2 + 256   # + the varlen stream ranking
+    assert front == 256                              # the varlen stream ranking only
+    assert B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN | kd) == 4096 * 3 * 32 * 128 * 2 + 256
     S = B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 4096, full)
     assert 3 <= S <= 12
     # the states: per slot [H][dk][dv] fp32, 3S-5 slots
@@ -68,9 +80,12 @@ def test_segment_plan():
     assert B.gdn_workspace_bytes(pb, 8, 16384, B.GDN_KIND_BATCHED) == 0
     assert B.gdn_segments(pb, B.GDN_KIND_BATCHED, 8, 2048, 1 << 40) == 0
     pk = B.params(32, 128, 128, conv_k=4)          # long KDA stream
-    wk = B.gdn_workspace_bytes(pk, 1, 16384, B.GDN_KIND_SINGLE)
     kda = B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA
+    wk = B.gdn_workspace_bytes(pk, 1, 16384, kda)
     assert B.gdn_segments(pk, kda, 1, 16384, wk) >= 3
+    # a workspace sized for the scalar gate has no room for KDA's activations
+    assert B.gdn_segments(pk, kda, 1, 16384,
+                          B.gdn_workspace_bytes(pk, 1, 16384, B.GDN_KIND_SINGLE)) == 0
     # A GDN call with unit keys may start every segment warm, so its plan keeps segment 0
     # and the warm jobs of all (stream, head) pairs in one round: S <= CUs / (streams *
     # heads) = 8. A KDA call always chains its segments and has no such cap: on 256 CUs
@@ -95,7 +110,7 @@ def test_segment_plan_lengths(H, T, kda):
     segments leave at least one chunk for the last segment, and the plan agrees with
     gdn_segments."""
     p = B.params(H, 128, 128, conv_k=4)
-    ws = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_SINGLE)
+    ws = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_SINGLE | kda)
     S, l0, l1 = B.gdn_segment_plan(p, B.GDN_KIND_SINGLE | kda, 1, T, ws)
     assert S == B.gdn_segments(p, B.GDN_KIND_SINGLE | kda, 1, T, ws)
     if S == 0:
@@ -105,7 +120,7 @@ def test_segment_plan_lengths(H, T, kda):
     assert l0 > 0 and l1 > 0 and l0 % 64 == 0 and l1 % 64 == 0
     assert l0 + (S - 2) * l1 < T, "the last segment would be empty"
     # no room for the states: unsegmented, lengths cleared
-    front = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_VARLEN)
+    front = B.gdn_workspace_bytes(p, 1, T, B.GDN_KIND_VARLEN | kda)
     assert B.gdn_segment_plan(p, B.GDN_KIND_SINGLE | kda, 1, T, front) == (0, 0, 0)
 
 
@@ -131,8 +146,9 @@ def test_refusals_before_launch():
     assert _single(B.params(0, 64, 64)) == B.GDN_E_ARG
     nan = B.params(2, 64, 64, scale=float("nan"))
     assert _single(nan) == B.GDN_E_ARG
-    # front end: conv pointers required, and a workspace large enough for t tokens
-    pf = B.params(2, 64, 64, conv_k=4)
+    # front end: conv pointers required, and (front kernel: float32 rows) a workspace large
+    # enough for t tokens
+    pf = B.params(2, 64, 64, conv_k=4, dtype=B.GDN_F32)
     assert _single(pf) == B.GDN_E_ARG
     need = B.gdn_workspace_bytes(pf, 1, 10, B.GDN_KIND_SINGLE)
     assert _single(pf, cs=FAKE, cw=FAKE, ws=FAKE, ws_bytes=need - 1) == B.GDN_E_WORKSPACE

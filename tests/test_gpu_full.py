@@ -87,16 +87,18 @@ def test_long_stream_64bit_indices():
     assert torch.equal(call.conv_state[0].cpu(), want)
 
 
-@pytest.mark.xfail(strict=True, reason="fp16 storage of the front end's activations: the "
-                   "error floor of that one rounding exceeds 2e-2 on this seed")
-def test_config2_other_seed_activation_rounding_floor():
-    """A known gap, pinned. The default prefill workload drawn with seed 102 instead of 2:
-    over all heads the call's err(o) is 0.029. The fp64 oracle fed the same activations
-    rounded once to fp16 (and nothing else) gives 0.0285, so the floor comes from storing
-    the front end's output as fp16, not from the scan's arithmetic. The test fails until
-    v and k cross from the front end to the scan with more precision than fp16."""
+@pytest.mark.parametrize("seed", range(100, 108))
+def test_config2_seed_sweep(seed):
+    """The default prefill workload (T=4096 through the front end, H=32, d=128) redrawn with
+    seeds 100..107: every head's o and every final state within 2e-2 of the oracle, the
+    conv windows bitwise. On these seeds an fp16 hand-over of the front end's activations
+    alone exceeds the bar (seed 102: err(o) 0.029; seeds 101, 104: err(h) 0.021, 0.024),
+    so they check that k and v reach the scan's products with more than fp16 precision."""
     import dataclasses
-    spec = dataclasses.replace(inputs.config(2), seed=102)
+    spec = dataclasses.replace(inputs.config(2), seed=seed)
     inp = inputs.make(spec)
     call = run_gpu(inp)
-    compare(call, run_oracle(inp))
+    e_o, e_h = compare(call, run_oracle(inp))
+    print("seed %d: err(o)=%.3g err(h)=%.3g" % (seed, e_o, e_h), flush=True)
+    want = inp["x"][4093:4096].t().contiguous()
+    assert torch.equal(call.conv_state[0].cpu(), want)
