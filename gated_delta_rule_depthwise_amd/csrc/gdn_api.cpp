@@ -90,27 +90,27 @@ int64_t conv_dim(const gdn_params *p)
     return 2 * (int64_t)qk_heads(p) * p->dk + (int64_t)p->H * p->dv;
 }
 
-// The front end runs inside the chunk kernel's load stage (conv + SiLU + L2 in fp32 on
-// the raw rows, no activation buffer) for bf16 rows with 4 taps, the scalar gate, one q/k
-// head per value head, dk == dv, no output gate and row strides below 2^24 elements (the
-// kernel forms a chunk's row offsets in 32 bits); other front-end calls run it as a
-// kernel of its own that hands the chunk kernel packed activations.
+// With bf16 rows the front end runs inside the chunk kernel's load stage (conv + SiLU +
+// L2 in fp32 on the raw rows, no activation buffer); the kernel forms a chunk's row
+// offsets in 32 bits, so it needs row strides below 2^24 elements. With float32 rows it
+// runs as a kernel of its own that hands the chunk kernel fp32 activations.
 bool fused_front(const gdn_params *p, int kda)
 {
-    return p->conv_k == 4 && p->dtype == GDN_BF16 && !kda && !p->z &&
-           qk_heads(p) == p->H && p->dk == p->dv && p->ld_qkv < (1 << 24) &&
-           gdn::chunk_instance_exists(3, p->dk, p->dv, 0, p->dv, 0, 0);
+    if (p->conv_k < 2 || p->conv_k > 4 || p->dtype != GDN_BF16 || p->ld_qkv >= (1 << 24))
+        return false;
+    for (int nv : {128, 64})
+        if (p->dv % nv == 0 && gdn::chunk_instance_exists(3, p->dk, p->dv, kda, nv, 0, 0))
+            return true;
+    return false;
 }
 
-// input kind of the chunk kernel: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations of
-// the front kernel, 3 = bf16 raw rows with the front end fused
+// input kind of the chunk kernel: 0 = f32 rows (or the front kernel's fp32 activations),
+// 1 = bf16 rows, 3 = bf16 raw rows with the front end fused
 int in_kind(const gdn_params *p, int kda)
 {
     if (p->dtype != GDN_BF16)
         return 0;
-    if (p->conv_k == 0)
-        return 1;
-    return fused_front(p, kda) ? 3 : 2;
+    return p->conv_k == 0 ? 1 : 3;
 }
 
 // Workgroup shape: dv columns per workgroup and waves per workgroup: the widest compiled
@@ -146,6 +146,8 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_UNSUPPORTED;
     if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
         return GDN_E_UNSUPPORTED;
+    if (p->conv_k != 0 && p->dtype == GDN_BF16 && !fused_front(p, kda))
+        return GDN_E_UNSUPPORTED;
     const Shape sh = pick_shape(p, kda);
     if (sh.nv == 0)
         return GDN_E_UNSUPPORTED;
@@ -168,21 +170,31 @@ int check_params(const gdn_params *p, int kda)
 constexpr int32_t kMaxOrderB = 1024;
 size_t order_bytes(int32_t B) { return B <= kMaxOrderB ? align_up((size_t)B * 4) : 0; }
 
-// the front kernel's activations (front-end calls that do not fuse it)
-size_t front_bytes(const gdn_params *p, int kda, int64_t max_tokens)
+// A fused front end whose windows are read by several workgroups (q/k heads shared by
+// value heads, or value heads split into column slices) stages the new windows and copies
+// them once every reader is done.
+bool win_shared(const gdn_params *p, int kda)
 {
-    if (p->conv_k == 0 || fused_front(p, kda))
-        return 0;
-    return align_up((size_t)max_tokens * (size_t)conv_dim(p) * elem_bytes(p->dtype));
+    return qk_heads(p) < p->H || pick_shape(p, kda).nv < p->dv;
 }
 
-// segmented calls with the front end fused: the new windows of the streams whose last
-// segment runs in the first launch (warm mode), staged until the combine kernel copies them
+// staged windows of a fused front end: [B][cd][conv_k-1] bf16
 size_t win_bytes(const gdn_params *p, int kda, int32_t B)
 {
-    if (!fused_front(p, kda))
+    if (p->conv_k == 0 || !fused_front(p, kda))
         return 0;
     return align_up((size_t)B * (size_t)conv_dim(p) * (p->conv_k - 1) * 2);
+}
+
+// at the start of the workspace: the front kernel's activations (float32 rows), or the
+// staged windows of a fused front end with shared windows
+size_t front_bytes(const gdn_params *p, int kda, int64_t max_tokens, int32_t B)
+{
+    if (p->conv_k == 0)
+        return 0;
+    if (fused_front(p, kda))
+        return win_shared(p, kda) ? win_bytes(p, kda, B) : 0;
+    return align_up((size_t)max_tokens * (size_t)conv_dim(p) * elem_bytes(p->dtype));
 }
 
 // ---- segmented scan of long streams -----------------------------------------------------
@@ -318,12 +330,15 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
     return seg_search(nc, U, ncu, max_s);
 }
 
+// the segment states, and for a fused front end without shared windows the windows that
+// warm-started streams stage for the combine kernel
 size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S)
 {
     if (S < 3)
         return 0;
     const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S, p->H};
-    return align_up((size_t)lay.total() * sizeof(float)) + win_bytes(p, kda, B);
+    return align_up((size_t)lay.total() * sizeof(float)) +
+           (win_shared(p, kda) ? 0 : win_bytes(p, kda, B));
 }
 
 struct Call {
@@ -362,7 +377,8 @@ int run(const Call &c)
     if (c.N < 1 || c.N > (int64_t)INT32_MAX)
         return GDN_E_ARG;
     const bool fused_fe = front && fused_front(p, c.kda);
-    const size_t need = front_bytes(p, c.kda, c.N);
+    const bool shared = fused_fe && win_shared(p, c.kda);
+    const size_t need = front_bytes(p, c.kda, c.N, c.st.B);
     if (c.ws_bytes < need || (need && !c.ws))
         return GDN_E_WORKSPACE;
     if (need && !aligned16(c.ws))
@@ -419,7 +435,8 @@ int run(const Call &c)
     // at the start of the scan
     const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, c.st.B, sp.S, p->H};
     float *seg_ws = sp.S ? (float *)((char *)c.ws + need) : nullptr;
-    void *win_ws = sp.S && fused_fe
+    void *win_ws = shared ? c.ws
+                   : sp.S && fused_fe
                        ? (char *)seg_ws + align_up((size_t)lay.total() * sizeof(float))
                        : nullptr;
     gdn::WarmArgs wa{};
@@ -441,6 +458,8 @@ int run(const Call &c)
         ca.conv_state_ptrs = c.conv_state_ptrs;
         ca.win_ws = win_ws;
         ca.cd = (int32_t)conv_dim(p);
+        ca.conv_k = p->conv_k;
+        ca.win_shared = shared;
     } else if (front) {
         if (ca.warm) {
             fa.warm = wa;
@@ -519,15 +538,25 @@ int run(const Call &c)
             cb.warm = ca.warm;
             cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
             cb.h = c.h, cb.h_ptrs = c.h_ptrs;
-            cb.win_ws = win_ws;
+            cb.win_ws = shared ? nullptr : win_ws;  // shared windows: the copy below
             cb.conv_state = c.conv_state, cb.conv_state_ptrs = c.conv_state_ptrs;
             cb.cd = (int32_t)conv_dim(p);
+            cb.Hqk = qk_heads(p);
+            cb.conv_k = p->conv_k;
             if (gdn::launch_combine(cb, c.stream) != hipSuccess)
                 return GDN_E_HIP;
             ca.pass = 2;
             ca.window_items = 0;  // the windows went out with pass 1
             if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
                                   (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
+                return GDN_E_HIP;
+        }
+        if (shared) {  // every workgroup that read the old windows is done
+            gdn::WindowCopyArgs wc{};
+            wc.win_ws = win_ws;
+            wc.conv_state = c.conv_state, wc.conv_state_ptrs = c.conv_state_ptrs;
+            wc.st = c.st, wc.cd = (int32_t)conv_dim(p), wc.W = p->conv_k - 1;
+            if (gdn::launch_window_copy(wc, c.stream) != hipSuccess)
                 return GDN_E_HIP;
         }
         st.done();
@@ -752,7 +781,7 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
         seg = seg_bytes(p, kda, B, kMaxSeg);
     if (kind == GDN_KIND_VARLEN)
         seg = order_bytes(B);
-    return front_bytes(p, kda, max_tokens) + seg;
+    return front_bytes(p, kda, max_tokens, B) + seg;
 }
 
 int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
@@ -774,7 +803,7 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
         return 0;
     const Shape sh = pick_shape(p, kda);
     const SegPlan sp = seg_plan(p, kda, B, t_per_stream, p->dv / sh.nv, cu_count());
-    const size_t need = front_bytes(p, kda, (int64_t)B * t_per_stream);
+    const size_t need = front_bytes(p, kda, (int64_t)B * t_per_stream, B);
     if (!sp.S || ws_bytes < need + seg_bytes(p, kda, B, sp.S))
         return 0;
     if (seg0_tokens)

@@ -77,12 +77,24 @@ struct CombineArgs {
     int32_t warm;
     float *h;                       // single stream state (h_ptrs == nullptr)
     float *const *h_ptrs;
-    // fused front end in warm mode: the new windows of every stream, [B][cd][3] bf16, to
-    // copy to the caller's windows (nullptr: nothing to copy)
+    // fused front end in warm mode: the new windows of every stream, [B][cd][conv_k-1]
+    // bf16, to copy to the caller's windows (nullptr: nothing to copy here)
     const void *win_ws;
     void *conv_state;
     void *const *conv_state_ptrs;
     int32_t cd;
+    int32_t Hqk;     // q/k heads
+    int32_t conv_k;
+};
+
+// The staged windows [B][cd][W] (bf16) of a fused front-end call copied to the caller's;
+// a zero-length stream wrote none and keeps its window.
+struct WindowCopyArgs {
+    const void *win_ws;
+    void *conv_state;
+    void *const *conv_state_ptrs;
+    Streams st;
+    int32_t cd, W;
 };
 
 
@@ -166,16 +178,20 @@ struct ChunkArgs {
     int64_t ld_z;
     const float *norm_w;    // [dv]
     float norm_eps;
-    // Front end fused into the load stage (q, k, v are the raw bf16 conv inputs; 4 taps;
-    // one q/k head per value head): the conv taps, the carried windows (read by the job
-    // holding a stream's first chunk) and where the job that ends a stream puts the new
-    // windows: the caller's windows, or in warm mode win_ws, from where the combine kernel
-    // copies them once the first launch (which read the old ones) is done.
-    const float *conv_w;            // [cd][4]
-    void *conv_state;               // [cd][3] of the single stream (conv_state_ptrs == nullptr)
+    // Front end fused into the load stage (q, k, v are the raw bf16 conv inputs, conv_k
+    // taps): the conv taps, the carried windows (read by the job holding a stream's first
+    // chunk) and where the job that ends a stream puts the new windows: the caller's
+    // windows, or win_ws when a later kernel must copy them there -- in warm mode (the
+    // combine kernel, after the launch that read the old windows) and when several
+    // workgroups read one window (win_shared: q/k heads shared by value heads, or dv
+    // slices; window_copy_kernel at the end of the call).
+    const float *conv_w;            // [cd][conv_k]
+    void *conv_state;               // [cd][conv_k-1] of the single stream (conv_state_ptrs == nullptr)
     void *const *conv_state_ptrs;   // per stream
-    void *win_ws;                   // [B][cd][3] bf16 (segmented calls)
+    void *win_ws;                   // [B][cd][conv_k-1] bf16
     int32_t cd;                     // channels of a packed row
+    int32_t conv_k;
+    int32_t win_shared;
 };
 
 // One decode step: a single token per stream through the front end (optional), L2 and the
@@ -211,6 +227,7 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 // the output gate as its own pass (dtype: element type of z, GDN_F32 or GDN_BF16)
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s);
 hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 // q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after

@@ -668,10 +668,10 @@ hipError_t launch_front_t(const FrontArgs &a, hipStream_t s)
     }
 }
 
-// bf16 raw rows give fp16 activations (the chunk kernel's operand type); f32 gives f32
+// float32 rows (bf16 rows run the front end inside the chunk kernel)
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s)
 {
-    return dtype ? launch_front_t<bf16, f16>(a, s) : launch_front_t<float, float>(a, s);
+    return dtype ? hipErrorInvalidValue : launch_front_t<float, float>(a, s);
 }
 
 // ------------------------------------------------------------------------------------
@@ -799,15 +799,24 @@ struct ChunkCfg {
     static constexpr int SZ_F = CH * LDF * 4;
     static constexpr int SZ_MS = SZ_F > SZ_Q ? SZ_F : SZ_Q;  // the KDA gated K^T tile reuses it
     // Front end fused into the load stage (bf16 raw rows; conv + SiLU + L2 per chunk):
-    // q and k are stored as fp16 hi + lo tiles, and v is never a tile: the raw v rows of
-    // the chunk, with the KC - 1 rows before it, sit in a raw region from which each lane
-    // convolves the values of its own D-layout rows in fp32. The raw q|k rows of the next
-    // chunk land by LDS-DMA on the two Q tiles and the inversion scratch, which are dead
-    // from the end of the preparation until the next load stage, and the raw v rows on
-    // their own region.
+    // k is stored as fp16 hi + lo tiles and, with the scalar gate, q too; v is never a
+    // tile: the raw v rows of the chunk, with the KC - 1 rows before it, sit in a raw
+    // region from which each lane convolves the values of its own D-layout rows in fp32.
+    // The raw q|k rows of the next chunk land by LDS-DMA on tiles that are dead from the
+    // end of the chunk's last read of q and k until the next load stage (scalar gate: the
+    // two Q tiles and the inversion scratch, read up to the preparation; per-key-channel
+    // gate: the Q and K tiles, whose products with h are taken right after the gates'
+    // rescale), and the raw v rows on their own region.
+    // The per-key-channel gate keeps k as an fp16 hi + lo pair in every fp16 instance: the
+    // rescaled operands (the gate factors of M and P, K e^G, K e^(G_C - G)) are formed from
+    // k in about fp32, and K e^(G_C - G), which builds the state, is itself a hi + lo pair
+    // (the lo half over the K lo tile once the rescale has read it).
+    static constexpr bool KLO = FRONT || (KDA && SPLIT);  // K lo tile
+    static constexpr bool QLO = FRONT && !KDA;            // Q lo tile
+    static constexpr bool XSCR = FRONT && !KDA;           // separate inversion scratch
     static constexpr int KC = 4;                 // conv taps of the fused front end
     static constexpr int RR = CH + KC - 1;       // raw rows per chunk
-    static constexpr int SZ_QF = 2 * SZ_Q;       // Q hi, Q lo
+    static constexpr int SZ_QF = QLO ? 2 * SZ_Q : SZ_Q;  // Q (hi, lo)
     static constexpr int LDX = 20;               // row stride of the 16x16 inversion scratch
     static constexpr int SZ_X = 4 * 16 * LDX * 4;
     static constexpr int RQK = 2 * DK * 2;       // bytes per raw [q | k] row
@@ -817,16 +826,17 @@ struct ChunkCfg {
     static constexpr int RVB = (VS + 1) * 16;
     static constexpr int SZ_RV = RR * RVB;
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_QL = SZ_Q;               // Q lo (fused front end)
-    static constexpr int OFF_X = FRONT ? SZ_QF : 0;  // inversion scratch (fused front end)
-    static constexpr int OFF_K = FRONT ? SZ_QF + SZ_X : OFF_Q + SZ_Q;
-    static constexpr int OFF_KL = OFF_K + SZ_Q;      // K lo (fused front end)
-    static constexpr int OFF_V = OFF_KL + (FRONT ? SZ_Q : 0);    // V tile, or the raw v rows
+    static constexpr int OFF_QL = SZ_Q;               // Q lo
+    static constexpr int OFF_X = SZ_QF;               // inversion scratch (scalar-gate fusion)
+    static constexpr int OFF_K = SZ_QF + (XSCR ? SZ_X : 0);
+    static constexpr int OFF_KL = OFF_K + SZ_Q;      // K lo
+    static constexpr int OFF_V = OFF_KL + (KLO ? SZ_Q : 0);      // V tile, or the raw v rows
     static constexpr int OFF_P = OFF_V + (FRONT ? SZ_RV : SZ_V);  // P (hi)
     static constexpr int OFF_PL = OFF_P + SZ_P;                   // P (lo)
     static constexpr int OFF_MT = OFF_PL + (SPLIT ? SZ_P : 0);    // M_IJ (J<I), T_II
-    static constexpr int OFF_M = OFF_MT + SZ_P;                   // diagonal blocks of M, fp32
-    static constexpr int OFF_GK = OFF_M + (FRONT ? 0 : SZ_MS);  // per-channel cumulative log-gates
+    // diagonal blocks of M, fp32; per-key-channel gate: K e^(G_C - G) (hi) after the rescale
+    static constexpr int OFF_M = OFF_MT + SZ_P;
+    static constexpr int OFF_GK = OFF_M + (XSCR ? 0 : SZ_MS);  // per-channel cumulative log-gates
     // Gamma[64], beta[64], a = e^Gamma [64], a_C / a [64]
     static constexpr int OFF_G = OFF_GK + (KDA ? CH * LDG * 4 : 0);
     // o rows (fp32). Fused front end: rows 4 apart (the lane groups of a D-layout write)
@@ -846,9 +856,10 @@ struct ChunkCfg {
     static constexpr int ZROW = NV * (int)sizeof(T);
     static constexpr int OFF_W = OFF_Z + (GATE ? CH * ZROW : 0);
     static constexpr int BYTES = OFF_W + (GATE ? NV * 4 : 0);
-    static_assert(!FRONT || RR * RQK <= SZ_QF + SZ_X, "raw q|k rows fit over Q and the scratch");
-    static_assert(!FRONT || (SPLIT && !KDA && !GATE && NCB == 1 && STAGE_O && NV == DV),
-                  "fused front end: fp16 operands, scalar gate, one column block per wave");
+    // the raw q|k rows land on the dead tiles at the start of the layout
+    static_assert(!FRONT || RR * RQK <= (KDA ? OFF_KL : OFF_K), "raw q|k rows fit");
+    static_assert(!FRONT || (SPLIT && !GATE && NCB == 1 && (STAGE_O || KDA)),
+                  "fused front end: fp16 operands, one column block per wave, no output gate");
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -1178,7 +1189,7 @@ __global__ void __launch_bounds__(NW * 64)
     // uniform offset) and the chunk row each 16-byte piece belongs to.
     const TIN *qk_src[NQK];
     const TIN *v_src[NVV];
-    const float *gk_src[NGK];
+    int gk_off[NGK];
     int qk_row[NQK], v_row[NVV], gk_row[NGK];
     bool qk_isk[NQK];
 #pragma unroll
@@ -1196,7 +1207,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
     for (int it = 0; it < NGK; ++it) {
         gk_row[it] = wave0 * GRW + lane0 / GPR + it * NW * GRW;
-        gk_src[it] = a.g + ((int64_t)gk_row[it] * H + head) * DK + (lane0 % GPR) * 4;
+        gk_off[it] = (gk_row[it] * H + head) * DK + (lane0 % GPR) * 4;
     }
     const int gb_off = (tid0 & (CH - 1)) * H;  // this lane's row of the gates and betas
     // Fused front end: the raw rows of the chunk at c0 (Lc rows) and the KC - 1 rows before
@@ -1242,30 +1253,38 @@ __global__ void __launch_bounds__(NW * 64)
         return (tensor ? qk_heads * DK : 0) + head_qk * DK + c;
     };
     auto v_channel = [&](int c) { return 2 * qk_heads * DK + head * DV + slice * NV + c; };
+    // With K = conv_k < KC taps the conv runs as KC taps, the first KC - K of them zero,
+    // and the window keeps the last K - 1 raw inputs.
+    const int Kt = FRONT ? a.conv_k : KC, Wn = Kt - 1, tap0 = KC - Kt;
     float wv[FRONT ? KC : 1];  // this lane's v column taps (fused front end)
     if constexpr (FRONT) {
         // q and k taps of this head into LDS, [tensor][tap][channel]
         for (int idx = tid0; idx < 2 * KC * DK; idx += NT) {
             const int t = idx / (KC * DK), rem = idx - t * KC * DK, j = rem / DK;
             ((float *)(smem + C::OFF_CW))[idx] =
-                a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * KC + j];
+                j < tap0 ? 0.f
+                         : a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * Kt + j - tap0];
         }
 #pragma unroll
         for (int j = 0; j < KC; ++j)
-            wv[j] = a.conv_w[(int64_t)v_channel(16 * wave0 + (lane0 & 15)) * KC + j];
-        // the stream's first chunk: raw rows 0 .. KC-2 are the carried window
+            wv[j] = j < tap0 ? 0.f
+                             : a.conv_w[(int64_t)v_channel(16 * wave0 + (lane0 & 15)) * Kt +
+                                        j - tap0];
+        // the stream's first chunk: raw rows 0 .. KC-2 are the carried window, after zeros
+        // in the rows a shorter window does not reach (multiplied by zero taps; never read
+        // from stale LDS)
         if (start == sbeg && start < end) {
             const TIN *cw = (const TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
                                                             : a.conv_state);
             constexpr int W = KC - 1;
             for (int idx = tid0; idx < (2 * DK + NV) * W; idx += NT) {
-                const int ch = idx / W, j = idx - ch * W;
+                const int ch = idx / W, j = idx - ch * W, e = j - (W - Wn);
                 if (ch < 2 * DK)
                     *(TIN *)(smem + C::OFF_Q + j * C::RQK + ch * 2) =
-                        cw[(int64_t)qk_channel(ch >= DK, ch % DK) * W + j];
+                        e < 0 ? (TIN)0.f : cw[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + e];
                 else
                     *(TIN *)(smem + C::OFF_V + j * C::RVB + (ch - 2 * DK) * 2) =
-                        cw[(int64_t)v_channel(ch - 2 * DK) * W + j];
+                        e < 0 ? (TIN)0.f : cw[(int64_t)v_channel(ch - 2 * DK) * Wn + e];
             }
         }
     }
@@ -1288,11 +1307,13 @@ __global__ void __launch_bounds__(NW * 64)
                              : make_uint4(0, 0, 0, 0);
         }
         if constexpr (KDA) {
+            const float *gbase = a.g + c0 * H * DK;
 #pragma unroll
-            for (int it = 0; it < NGK; ++it)
-                pgk[it] = gk_row[it] < Lc
-                              ? load_stream16(gk_src[it] + c0 * H * DK)
-                              : make_uint4(0, 0, 0, 0);
+            for (int it = 0; it < NGK; ++it) {
+                int go = gk_off[it];  // opaque per call, as for the scalar gates below
+                asm volatile("" : "+v"(go));
+                pgk[it] = gk_row[it] < Lc ? load_stream16(gbase + go) : make_uint4(0, 0, 0, 0);
+            }
         }
         if (threadIdx.x < CH) {
             // opaque per call: a 64-bit per-lane address held across the chunk loop would
@@ -1537,21 +1558,23 @@ __global__ void __launch_bounds__(NW * 64)
                 for (int e = 0; e < 8; ++e)
                     y[i][e] = live ? y[i][e] * m : 0.f;
             }
-            // the stream's last chunk: the new windows are its raw rows L .. L + KC - 2 (the
-            // last KC - 1 entries of [old window | rows]), read before the tiles cover them
+            // the stream's last chunk: the new windows are its raw rows L + KC - 1 - Wn ..
+            // L + KC - 2 (the last Wn entries of [old window | rows]), read before the tiles
+            // cover them
             if (last_seg && cs + CH >= end) {
-                TIN *wo = win_staged ? (TIN *)a.win_ws + (int64_t)b * a.cd * (KC - 1)
-                                     : (TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
-                                                                 : a.conv_state);
-                constexpr int W = KC - 1;
-                for (int idx = tid; idx < (2 * DK + NV) * W; idx += NT) {
-                    const int ch = idx / W, j = idx - ch * W;
+                TIN *wo = win_staged || a.win_shared
+                              ? (TIN *)a.win_ws + (int64_t)b * a.cd * Wn
+                              : (TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
+                                                          : a.conv_state);
+                const int r0 = L + KC - 1 - Wn;
+                for (int idx = tid; idx < (2 * DK + NV) * Wn; idx += NT) {
+                    const int ch = idx / Wn, j = idx - ch * Wn;
                     if (ch < 2 * DK)
-                        wo[(int64_t)qk_channel(ch >= DK, ch % DK) * W + j] =
-                            *(const TIN *)(smem + zo + C::OFF_Q + (L + j) * C::RQK + ch * 2);
+                        wo[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + j] =
+                            *(const TIN *)(smem + zo + C::OFF_Q + (r0 + j) * C::RQK + ch * 2);
                     else
-                        wo[(int64_t)v_channel(ch - 2 * DK) * W + j] = *(const TIN *)(
-                            smem + zo + C::OFF_V + (L + j) * C::RVB + (ch - 2 * DK) * 2);
+                        wo[(int64_t)v_channel(ch - 2 * DK) * Wn + j] = *(const TIN *)(
+                            smem + zo + C::OFF_V + (r0 + j) * C::RVB + (ch - 2 * DK) * 2);
                 }
             }
             __syncthreads();  // the raw q|k rows are read before the Q tile covers them
@@ -1567,7 +1590,8 @@ __global__ void __launch_bounds__(NW * 64)
                                      y[i][4 * h + 3]},
                                hi4, lo4);
                         *reinterpret_cast<f16x4 *>(dh + QK<T, DK>::at(r, 2 * cg + h)) = hi4;
-                        *reinterpret_cast<f16x4 *>(dl + QK<T, DK>::at(r, 2 * cg + h)) = lo4;
+                        if (tsr == 1 || C::QLO)
+                            *reinterpret_cast<f16x4 *>(dl + QK<T, DK>::at(r, 2 * cg + h)) = lo4;
                     }
                 }
             }
@@ -1603,7 +1627,15 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
             for (int h = 0; h < VEC / 4; ++h) {  // 4-element chunks of the Q/K layout
                 const float y[4] = {x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
-                store_vec4(dst + QK<T, DK>::at(r, c0 / 4 + h), y);
+                if constexpr (C::KLO && SPLIT) {
+                    f16x4 hi4, lo4;
+                    split4(f32x4{y[0], y[1], y[2], y[3]}, hi4, lo4);
+                    *reinterpret_cast<f16x4 *>(dst + QK<T, DK>::at(r, c0 / 4 + h)) = hi4;
+                    if (isk)
+                        *reinterpret_cast<f16x4 *>(Kl + QK<T, DK>::at(r, c0 / 4 + h)) = lo4;
+                } else {
+                    store_vec4(dst + QK<T, DK>::at(r, c0 / 4 + h), y);
+                }
             }
         }
 #pragma unroll
@@ -1613,13 +1645,13 @@ __global__ void __launch_bounds__(NW * 64)
             unpack((const TIN *)nullptr, pv[it], x);
             store_vec(Vs + r * LDV + (lane % LPV) * VEC, x);
         }
+        }
         if constexpr (KDA) {
 #pragma unroll
             for (int it = 0; it < NGK; ++it) {
                 const int r = wave * GRW + lane / GPR + it * NW * GRW;
                 *reinterpret_cast<uint4 *>(Gk + r * LDG + (lane % GPR) * 4) = pgk[it];
             }
-        }
         }
         if (tid < CH) {  // wave 0: Gamma = inclusive prefix sum of the log-gates, and decays
             const float gam = wave_scan(pg);
@@ -1760,6 +1792,18 @@ __global__ void __launch_bounds__(NW * 64)
                     frag fk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
                     frag fq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
                     frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
+                    // k in about fp32 (hi + lo) before the factors are applied
+                    float kI[8], kJ[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        kI[i] = (float)fk[i], kJ[i] = (float)fb[i];
+                    if constexpr (C::KLO) {
+                        const frag fkl = ld_frag_qk<DK>(Kl, 16 * I, 32 * kb, lane);
+                        const frag fbl = ld_frag_qk<DK>(Kl, 16 * J, 32 * kb, lane);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            kI[i] += (float)fkl[i], kJ[i] += (float)fbl[i];
+                    }
                     const int c0 = 32 * kb + 4 * g4;
                     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gb + c0);
                     const f32x4 b1 = *reinterpret_cast<const f32x4 *>(gb + c0 + 16);
@@ -1770,12 +1814,12 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float ea = __expf(r0[i] - b0[i]), ea1 = __expf(r1[i] - b1[i]);
-                        fk[i] = (T)((float)fk[i] * ea);
-                        fk[4 + i] = (T)((float)fk[4 + i] * ea1);
+                        fk[i] = (T)(kI[i] * ea);
+                        fk[4 + i] = (T)(kI[4 + i] * ea1);
                         fq[i] = (T)((float)fq[i] * ea);
                         fq[4 + i] = (T)((float)fq[4 + i] * ea1);
-                        fb[i] = (T)((float)fb[i] * __expf(b0[i] - s0[i]));
-                        fb[4 + i] = (T)((float)fb[4 + i] * __expf(b1[i] - s1[i]));
+                        fb[i] = (T)(kJ[i] * __expf(b0[i] - s0[i]));
+                        fb[4 + i] = (T)(kJ[4 + i] * __expf(b1[i] - s1[i]));
                     }
                     if (do_m)
                         mma(am, fk, fb);
@@ -1794,6 +1838,9 @@ __global__ void __launch_bounds__(NW * 64)
                     for (int kb = 0; kb < DK / 32; ++kb) {
                         const frag xk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
                         const frag xq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
+                        frag xkl{};
+                        if constexpr (C::KLO)
+                            xkl = ld_frag_qk<DK>(Kl, 16 * I, 32 * kb, lane);
                         const int c0 = 32 * kb + 4 * g4;
                         bf16x8 kh_, kl_, qh_, ql_, bh, bl;
 #pragma unroll
@@ -1801,8 +1848,9 @@ __global__ void __launch_bounds__(NW * 64)
                             const int ch = c0 + (i < 4 ? i : 12 + i);
                             const float d = grs[ch] - gm[ch];
                             const float ea = __expf(fminf(d, 80.f));
-                            const float kv = (float)xk[i] * ea, qv = (float)xq[i] * ea;
-                            const float bv = (float)xk[i] * __expf(fminf(-d, 80.f));
+                            const float kx = (float)xk[i] + (C::KLO ? (float)xkl[i] : 0.f);
+                            const float kv = kx * ea, qv = (float)xq[i] * ea;
+                            const float bv = kx * __expf(fminf(-d, 80.f));
                             kh_[i] = (bf16)kv;
                             kl_[i] = (bf16)(kv - (float)kh_[i]);
                             qh_[i] = (bf16)qv;
@@ -1869,8 +1917,8 @@ __global__ void __launch_bounds__(NW * 64)
                 // it).
                 const int base = 16 * I;
                 // this block's corner of Ms, or (fused front end) its own scratch block
-                float *scr = FRONT ? Xs + base * C::LDX : Ms + base * LDF + base;
-                constexpr int lds = FRONT ? C::LDX : LDF;
+                float *scr = C::XSCR ? Xs + base * C::LDX : Ms + base * LDF + base;
+                constexpr int lds = C::XSCR ? C::LDX : LDF;
                 auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -1914,14 +1962,17 @@ __global__ void __launch_bounds__(NW * 64)
             constexpr int NI = CH * (DK / 4) / NT;
             static_assert(NI * NT == CH * (DK / 4) && NT % (DK / 4) == 0, "rescale map");
             const int c0 = (tid % (DK / 4)) * 4, r0 = tid / (DK / 4);
+            // (k = hi + lo; the K lo tile then takes the lo half of K e^(G_C - G))
             const f32x4 gcv = *reinterpret_cast<const f32x4 *>(Gk + (CH - 1) * LDG + c0);
-            T4 kv[NI], qv[NI];
+            T4 kv[NI], klv[NI], qv[NI];
             f32x4 gv[NI];
 #pragma unroll
             for (int it = 0; it < NI; ++it) {
                 const int r = r0 + it * (NT / (DK / 4));
                 const int off = QK<T, DK>::at(r, c0 / 4);
                 kv[it] = *reinterpret_cast<const T4 *>(Ks + off);
+                if constexpr (C::KLO)
+                    klv[it] = *reinterpret_cast<const T4 *>(Kl + off);
                 qv[it] = *reinterpret_cast<const T4 *>(Qs + off);
                 gv[it] = *reinterpret_cast<const f32x4 *>(Gk + r * LDG + c0);
             }
@@ -1929,21 +1980,35 @@ __global__ void __launch_bounds__(NW * 64)
             for (int it = 0; it < NI; ++it) {
                 const int r = r0 + it * (NT / (DK / 4));
                 const int off = QK<T, DK>::at(r, c0 / 4);
-                T4 kd, ke, qe;
+                T4 kd, kdl, ke, qe;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float e = __expf(gv[it][i]);
-                    kd[i] = (T)((float)kv[it][i] * __expf(gcv[i] - gv[it][i]));
-                    ke[i] = (T)((float)kv[it][i] * e);
+                    const float kx = (float)kv[it][i] + (C::KLO ? (float)klv[it][i] : 0.f);
+                    const float d = kx * __expf(gcv[i] - gv[it][i]);
+                    kd[i] = (T)d;
+                    kdl[i] = (T)(d - (float)kd[i]);
+                    ke[i] = (T)(kx * e);
                     qe[i] = (T)((float)qv[it][i] * e);
                 }
                 *reinterpret_cast<T4 *>(Kd + off) = kd;
+                if constexpr (C::KLO)
+                    *reinterpret_cast<T4 *>(Kl + off) = kdl;
                 *reinterpret_cast<T4 *>(Ks + off) = ke;
                 *reinterpret_cast<T4 *>(Qs + off) = qe;
             }
             __syncthreads();
         }
 
+        // Per-key-channel gate with the front end fused: K h, Q h and the v conv run here,
+        // on the rescaled tiles, so that Q, K and the raw v rows are dead before the next
+        // chunk's raw rows land on them
+        constexpr bool LATE = FRONT && KDA;
+        f32x4 xl[LATE ? 4 : 1], ol[LATE ? 4 : 1];
+        if constexpr (LATE) {
+            kh_qh(0, xl, ol, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
+            __syncthreads();
+        }
         if (cs + CH < end)
             prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH));
         if constexpr (GATE) {
@@ -1962,6 +2027,10 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
                     x[I] = xe[I], o[I] = oe[I];
+            } else if constexpr (LATE) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    x[I] = xl[I], o[I] = ol[I];
             } else {
                 kh_qh(cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
             }
@@ -2066,7 +2135,7 @@ __global__ void __launch_bounds__(NW * 64)
                     mma(hs[cb][mb], k0, vl0);
                     mma(hs[cb][mb], k1, vl1);
                 }
-                if constexpr (FRONT) {  // k as an fp16 hi + lo pair as well
+                if constexpr (C::KLO) {  // the k operand as an fp16 hi + lo pair as well
                     mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 0, 16 * mb, lane), vf0);
                     mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 32, 16 * mb, lane), vf1);
                 }
@@ -2144,34 +2213,26 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
     X(bf16, f16, 1, 128, 128, 8, 1, false, false, false) \
     X(bf16, f16, 1, 128, 128, 4, 2, false, false, false) \
     X(bf16, f16, 1, 128, 128, 4, 1, false, false, false) \
-    X(f16, f16, 2, 128, 128, 8, 1, false, false, false) \
-    X(f16, f16, 2, 128, 128, 4, 2, false, false, false) \
-    X(f16, f16, 2, 128, 128, 4, 1, false, false, false) \
     X(bf16, f16, 1, 64, 64, 4, 1, false, false, false) \
-    X(f16, f16, 2, 64, 64, 4, 1, false, false, false) \
     X(float, float, 0, 64, 64, 4, 1, false, false, false) \
     X(bf16, f16, 1, 128, 128, 8, 1, true, false, false) \
     X(bf16, f16, 1, 128, 128, 4, 1, true, false, false) \
-    X(f16, f16, 2, 128, 128, 8, 1, true, false, false) \
-    X(f16, f16, 2, 128, 128, 4, 1, true, false, false) \
     X(bf16, f16, 1, 64, 64, 4, 1, true, false, false) \
-    X(f16, f16, 2, 64, 64, 4, 1, true, false, false) \
     X(float, float, 0, 64, 64, 4, 1, true, false, false) \
     X(bf16, f16, 1, 128, 128, 8, 1, false, true, false) \
-    X(f16, f16, 2, 128, 128, 8, 1, false, true, false) \
     X(bf16, f16, 1, 64, 64, 4, 1, false, true, false) \
-    X(f16, f16, 2, 64, 64, 4, 1, false, true, false) \
     X(float, float, 0, 64, 64, 4, 1, false, true, false) \
     X(bf16, f16, 1, 64, 64, 4, 1, true, true, false) \
-    X(f16, f16, 2, 64, 64, 4, 1, true, true, false) \
     X(bf16, f16, 1, 128, 256, 8, 1, false, false, false) \
-    X(f16, f16, 2, 128, 256, 8, 1, false, false, false) \
     X(bf16, f16, 1, 128, 256, 8, 1, true, false, false) \
-    X(f16, f16, 2, 128, 256, 8, 1, true, false, false) \
     X(float, float, 0, 64, 128, 4, 1, false, false, false) \
     X(float, float, 0, 64, 128, 4, 1, true, false, false) \
-    X(bf16, f16, 3, 128, 128, 8, 1, false, false, true)   \
-    X(bf16, f16, 3, 64, 64, 4, 1, false, false, true)
+    X(bf16, f16, 3, 128, 128, 8, 1, false, false, true) \
+    X(bf16, f16, 3, 64, 64, 4, 1, false, false, true) \
+    X(bf16, f16, 3, 128, 128, 8, 1, true, false, true) \
+    X(bf16, f16, 3, 64, 64, 4, 1, true, false, true) \
+    X(bf16, f16, 3, 128, 256, 8, 1, false, false, true) \
+    X(bf16, f16, 3, 128, 256, 8, 1, true, false, true)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
 // with the output gate fused
@@ -2234,16 +2295,17 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
             const int64_t e = (int64_t)(idx >> 4) * DK + 16 * cbk + (idx & 15);
             dst[e] = src[e];
         }
-        if (a.win_ws) {  // bf16 windows [cd][3]; this head's q, k and v channels
-            const int nch = 2 * DK + DK, per = (nch * 3 + DK / 16 - 1) / (DK / 16);
-            const uint16_t *ws = (const uint16_t *)a.win_ws + (int64_t)b * a.cd * 3;
+        if (a.win_ws) {  // bf16 windows [cd][W]; this head's q, k and v channels
+            const int W = a.conv_k - 1, hq = head / (a.H / a.Hqk);
+            const int nch = 2 * DK + DK, per = (nch * W + DK / 16 - 1) / (DK / 16);
+            const uint16_t *ws = (const uint16_t *)a.win_ws + (int64_t)b * a.cd * W;
             uint16_t *cw = (uint16_t *)(a.conv_state_ptrs ? a.conv_state_ptrs[b] : a.conv_state);
-            for (int e = cbk * per + (int)threadIdx.x; e < min((cbk + 1) * per, nch * 3);
+            for (int e = cbk * per + (int)threadIdx.x; e < min((cbk + 1) * per, nch * W);
                  e += NWV * 64) {
-                const int ch = e / 3, j = e - 3 * ch;
-                const int gc = ch < 2 * DK ? (ch >= DK ? a.H * DK : 0) + head * DK + ch % DK
-                                           : 2 * a.H * DK + head * DK + ch - 2 * DK;
-                cw[(int64_t)gc * 3 + j] = ws[(int64_t)gc * 3 + j];
+                const int ch = e / W, j = e - W * ch;
+                const int gc = ch < 2 * DK ? (ch >= DK ? a.Hqk * DK : 0) + hq * DK + ch % DK
+                                           : 2 * a.Hqk * DK + head * DK + ch - 2 * DK;
+                cw[(int64_t)gc * W + j] = ws[(int64_t)gc * W + j];
             }
         }
         return;
@@ -2342,6 +2404,33 @@ hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
     if (a.nseg < 3 || a.seg0_len % CH || a.seg_len % CH)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(warm_plan_kernel, dim3((unsigned)(a.st.B * a.H)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// One thread per (stream, window entry): the staged windows to the caller's.
+__global__ void __launch_bounds__(256) window_copy_kernel(const WindowCopyArgs a)
+{
+    const int64_t per = (int64_t)a.cd * a.W;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.st.B * per)
+        return;
+    const int b = (int)(i / per);
+    const int64_t e = i - (int64_t)b * per;
+    int64_t sb, eb;
+    stream_bounds(a.st, b, sb, eb);
+    if (eb <= sb)
+        return;
+    uint16_t *cw = (uint16_t *)(a.conv_state_ptrs ? a.conv_state_ptrs[b] : a.conv_state);
+    cw[e] = ((const uint16_t *)a.win_ws)[i];
+}
+
+hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s)
+{
+    const int64_t n = (int64_t)a.st.B * a.cd * a.W;
+    if (n < 1 || (n + 255) / 256 > (int64_t)INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(window_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 

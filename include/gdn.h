@@ -38,10 +38,10 @@
  *     heavy-tailed outputs.) The dense products run on MFMA with fp32 accumulation, with
  *     fp16 operands for bf16 inputs (hi + lo pairs where a single fp16 rounding would
  *     show in o or h) and fp32 operands for float32 inputs.
- *   - Front end: with bf16 rows, 4 taps, the scalar gate (gdn_*), one q/k head per value
- *     head, dk == dv, no output gate and ld_qkv < 2^24, the conv + SiLU + L2 run inside
- *     the scan's load stage in fp32 straight from the raw rows (no activation buffer; q
- *     and k enter the products as fp16 hi + lo pairs, v in fp32). Every other front-end call runs the
+ *   - Front end: with bf16 rows, 4 taps, one q/k head per value head, dk == dv, no output
+ *     gate and ld_qkv < 2^24, the conv + SiLU + L2 run inside the scan's load stage in
+ *     fp32 straight from the raw rows (no activation buffer; k, and with the scalar gate
+ *     q, enter the products as fp16 hi + lo pairs, v in fp32). Every other front-end call runs the
  *     front end as a kernel of its own that hands the scan fp16 (bf16 rows) or fp32
  *     activations through the workspace.
  *   - Errors: every check below runs on the host before anything is enqueued; on error
@@ -245,11 +245,12 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
  * front end and recurrence (page "metrale_model_arch/glm5next_kda/prefill.rs",
  * profile::start / profile::end with KDA_FRONT, KDA_RECUR, KDA_BACK). While enabled, every
  * call records a hipEvent pair around each of its kernels on the call's stream:
- *   GDN_PROF_FRONT  conv + SiLU + L2 kernel (front end calls only; for segmented calls
- *                   with the scalar gate it also holds the warm-start plan)
- *   GDN_PROF_RECUR  the fused chunk kernel (WY/UT preparation + inter-chunk scan; the
- *                   carried conv windows are updated by extra workgroups of its first
- *                   launch, after the front end)
+ *   GDN_PROF_FRONT  the front kernel (conv + SiLU + L2) of float32 front-end calls; for
+ *                   segmented calls with the scalar gate it also holds the warm-start plan.
+ *                   bf16 front-end calls run the front end inside the chunk kernel.
+ *   GDN_PROF_RECUR  the fused chunk kernel (front end for bf16 rows, WY/UT preparation,
+ *                   inter-chunk scan), the warm-start plan when it has no front kernel to
+ *                   ride in, the chain of segment maps and the window copies
  *   GDN_PROF_STATE  unused by prefill calls (the windows go out with the scan); kept so
  *                   that bucket numbers stay fixed
  *   GDN_PROF_GATE   the output gate when it runs as its own pass (the per-key-channel gate

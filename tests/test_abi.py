@@ -41,15 +41,22 @@ def test_status_strings():
 def test_workspace_bytes():
     p = B.params(32, 128, 128, conv_k=4)
     cd = 3 * 32 * 128
-    # the per-key-channel gate runs its front end as a kernel of its own: activations
-    ws = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA)
-    assert ws >= 4096 * cd * 2 and ws % 256 == 0
-    # the scalar gate fuses the front end into the scan: no activation buffer, only the
-    # segment states and the staged windows of a segmented call
-    wg = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
-    assert 0 < wg < 4096 * cd * 2 and wg % 256 == 0
-    assert B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN) == 256  # stream ranking
-    assert B.gdn_workspace_bytes(p, 1, 10, B.GDN_KIND_SINGLE) == 0
+    # bf16 rows: the front end is fused into the scan, for either gate, so there is no
+    # activation buffer, only the segment states and the staged windows of a segmented call
+    for kd in (0, B.GDN_PLAN_KDA):
+        wg = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE | kd)
+        assert 0 < wg < 4096 * cd * 2 and wg % 256 == 0
+        assert B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN | kd) == 256  # ranking
+        assert B.gdn_workspace_bytes(p, 1, 10, B.GDN_KIND_SINGLE | kd) == 0
+    # shared q/k heads: several workgroups read a window, so the new windows are staged,
+    # [B][cd][conv_k - 1] bf16, even for a short call
+    pq = B.params(32, 128, 128, conv_k=3, Hqk=16)
+    cdq = 2 * 16 * 128 + 32 * 128
+    assert B.gdn_workspace_bytes(pq, 2, 10, B.GDN_KIND_BATCHED | B.GDN_PLAN_KDA) == 2 * cdq * 2 * 2
+    # float32 rows: the front kernel and its fp32 activations
+    pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)
+    ws = B.gdn_workspace_bytes(pf, 1, 4096, B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA)
+    assert ws >= 4096 * 3 * 32 * 64 * 4 and ws % 256 == 0
     # float32 rows: the front kernel and its fp32 activations
     pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)
     assert B.gdn_workspace_bytes(pf, 1, 10, B.GDN_KIND_VARLEN) == 10 * 3 * 32 * 64 * 4 + 256
@@ -68,7 +75,8 @@ def test_segment_plan():
     full = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_SINGLE)
     front = B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN)
     assert front == 256                              # the varlen stream ranking only
-    assert B.gdn_workspace_bytes(p, 1, 4096, B.GDN_KIND_VARLEN | kd) == 4096 * 3 * 32 * 128 * 2 + 256
+    pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)   # float32 rows: front kernel
+    assert B.gdn_workspace_bytes(pf, 1, 4096, B.GDN_KIND_VARLEN | kd) == 4096 * 3 * 32 * 64 * 4 + 256
     S = B.gdn_segments(p, B.GDN_KIND_SINGLE, 1, 4096, full)
     assert 3 <= S <= 12
     # the states: per slot [H][dk][dv] fp32, 3S-5 slots
@@ -83,9 +91,6 @@ def test_segment_plan():
     kda = B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA
     wk = B.gdn_workspace_bytes(pk, 1, 16384, kda)
     assert B.gdn_segments(pk, kda, 1, 16384, wk) >= 3
-    # a workspace sized for the scalar gate has no room for KDA's activations
-    assert B.gdn_segments(pk, kda, 1, 16384,
-                          B.gdn_workspace_bytes(pk, 1, 16384, B.GDN_KIND_SINGLE)) == 0
     # A GDN call with unit keys may start every segment warm, so its plan keeps segment 0
     # and the warm jobs of all (stream, head) pairs in one round: S <= CUs / (streams *
     # heads) = 8. A KDA call always chains its segments and has no such cap: on 256 CUs
@@ -214,8 +219,9 @@ def test_shared_qk_head_refusals():
     # the packed row of 2 q/k heads and 4 value heads is 2*2*64 + 4*64 wide
     p = B.params(4, 64, 64, dtype=B.GDN_F32, Hqk=2)
     assert p.ld_qkv == 2 * 2 * 64 + 4 * 64
+    # (a fused front end with shared q/k heads stages its new windows: 512 channels x 3)
     assert B.gdn_workspace_bytes(B.params(4, 64, 64, conv_k=4, Hqk=2), 1, 10,
-                                 B.GDN_KIND_SINGLE) == (10 * 512 * 2 + 255) // 256 * 256
+                                 B.GDN_KIND_SINGLE) == (512 * 3 * 2 + 255) // 256 * 256
 
 
 def test_params_struct_layout():

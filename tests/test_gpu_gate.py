@@ -82,12 +82,15 @@ def test_gated_prefill_matches_oracle(name):
 
 
 def test_gate_pass_only_where_o_is_not_staged():
-    """The per-key-channel instances at 128 columns and in fp32 gate in a pass of their
-    own; the others record nothing in that profile bucket."""
+    """The per-key-channel instances at 128 columns and in fp32, and every call whose front
+    end runs inside the scan (its tiles leave no room for a z tile), gate in a pass of
+    their own; the others gate in the o flush and record nothing in that profile bucket."""
     for base, kw, want in ((5, dict(lengths=[200], H=2), 1),
+                           (5, dict(lengths=[200], H=2, front_end=False), 1),
                            (1, dict(lengths=[200], H=2, gate="kda"), 1),
                            (1, dict(lengths=[200], H=2), 0),
-                           (2, dict(lengths=[200], H=2), 0)):
+                           (3, dict(lengths=[200], H=2), 0),
+                           (2, dict(lengths=[200], H=2), 1)):
         spec = spec_small(base, out_gate=True, seed=22, **kw)
         inp = inputs.make(spec)
         B.gdn_profile_read()
@@ -97,7 +100,7 @@ def test_gate_pass_only_where_o_is_not_staged():
         rc, _, launches = B.gdn_profile_read()
         assert rc == 0 and launches[B.GDN_PROF_GATE] == want
         ref = gated(inp, run_oracle(inp))
-    compare(call, ref, o_metric=ref["o_metric"])
+        compare(call, ref, o_metric=ref["o_metric"])
 
 
 def test_gated_segmented_scan():

@@ -204,7 +204,9 @@ def test_refused_calls_leave_buffers_unchanged():
     import ctypes
     from gated_delta_rule_depthwise_amd import binding as B
     from gated_delta_rule_depthwise_amd.runner import Prefill
-    spec = spec_small(2, lengths=[200], H=2, seed=61)
+    # (float32 rows: the front end runs as a kernel of its own and needs its activations in
+    # the workspace)
+    spec = spec_small(2, lengths=[200], H=2, dk=64, dv=64, dtype="f32", seed=61)
     inp = inputs.make(spec)
     call = Prefill(inp, "cuda", o_fill=SENTINEL)
     torch.cuda.synchronize()
@@ -215,8 +217,8 @@ def test_refused_calls_leave_buffers_unchanged():
     bad_chunk.chunk = 32
     bad_ld = B.gdn_params.from_buffer_copy(p)
     bad_ld.ld_qkv = p.ld_qkv + 1
-    # the front end's activations alone need N * cd bf16 values
-    front = spec.N * spec.cd * 2
+    # the front end's activations alone need N * cd float values
+    front = spec.N * spec.cd * 4
     cases = [(p, spec.N, front - 1, B.GDN_E_WORKSPACE),
              (bad_chunk, spec.N, call.ws_bytes, B.GDN_E_UNSUPPORTED),
              (bad_ld, spec.N, call.ws_bytes, B.GDN_E_ARG), (p, 0, call.ws_bytes, B.GDN_E_ARG)]

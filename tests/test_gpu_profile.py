@@ -28,17 +28,20 @@ def timed(call):
     return ms, launches, wall_ms
 
 
-@pytest.mark.parametrize("case", ["segmented-front", "varlen", "gated-pass"])
+@pytest.mark.parametrize("case", ["segmented-front", "f32-front", "varlen", "gated-pass"])
 def test_prefill_stage_timers(case):
-    if case == "segmented-front":   # front (+ warm plan), chunk passes and chain (+ windows)
+    if case == "segmented-front":   # bf16 rows: warm plan, chunk passes (front end fused), chain
         spec = spec_small(2, lengths=[2048], H=4, seed=61)
+        stages = {B.GDN_PROF_RECUR}
+    elif case == "f32-front":       # float32 rows: the front kernel, then the chunk kernel
+        spec = spec_small(2, lengths=[300], H=2, dk=64, dv=64, dtype="f32", seed=64)
         stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR}
     elif case == "varlen":          # stream ranking + chunk kernel, no front end
         spec = spec_small(4, lengths=[1, 300, 64, 129], H=2, seed=62)
         stages = {B.GDN_PROF_RECUR}
     else:                           # output gate in its own pass (per-channel gate, d=128)
         spec = spec_small(5, lengths=[200], H=2, out_gate=True, seed=63)
-        stages = {B.GDN_PROF_FRONT, B.GDN_PROF_RECUR, B.GDN_PROF_GATE}
+        stages = {B.GDN_PROF_RECUR, B.GDN_PROF_GATE}
     inp = inputs.make(spec)
     ref = Prefill(inp, "cuda")
     assert ref() == 0
