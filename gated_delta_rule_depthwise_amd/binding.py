@@ -27,7 +27,8 @@ GDN_KIND_VARLEN = 2
 GDN_PLAN_KDA = 0x100  # or-ed into the kind of gdn_segments / gdn_segment_plan
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_prefill", "kda_prefill", "gdn_prefill_batched", "gdn_prefill_varlen",
+EXPORTS = ("gdn_prefill", "gdn_prefill_noalloc", "gdn_noalloc_scratch_bytes", "kda_prefill",
+           "gdn_prefill_batched", "gdn_prefill_varlen",
            "kda_prefill_batched", "kda_prefill_varlen", "gdn_decode", "kda_decode",
            "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
            "gdn_segments", "gdn_segment_plan", "gdn_status_string")
@@ -68,6 +69,10 @@ def load(path: str = SO):
         single = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
         lib.gdn_prefill.argtypes = single
         lib.kda_prefill.argtypes = single
+        lib.gdn_prefill_noalloc.argtypes = single[:11] + [_vp]
+        lib.gdn_prefill_noalloc.restype = ctypes.c_int
+        lib.gdn_noalloc_scratch_bytes.argtypes = []
+        lib.gdn_noalloc_scratch_bytes.restype = _sz
         batched = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _sz, _vp]
         varlen = [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _vp,
                   _sz, _vp]
@@ -126,6 +131,15 @@ def params(H, dk, dv, chunk=64, eps=1e-6, scale=None, dtype=GDN_BF16, conv_k=0, 
 def gdn_prefill(p, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream):
     return load().gdn_prefill(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h),
                               _p(conv_state), _p(conv_w), _p(o), t, _p(ws), ws_bytes, stream)
+
+
+def gdn_prefill_noalloc(p, q, k, v, g, beta, h, conv_state, conv_w, o, t, stream):
+    return load().gdn_prefill_noalloc(ctypes.byref(p), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                      _p(h), _p(conv_state), _p(conv_w), _p(o), t, stream)
+
+
+def gdn_noalloc_scratch_bytes():
+    return int(load().gdn_noalloc_scratch_bytes())
 
 
 def kda_prefill(p, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws, ws_bytes, stream):

@@ -595,7 +595,59 @@ int single(const gdn_params *p, int kda, const void *q, const void *k, const voi
 
 }  // namespace
 
+// ---- the allocation-free single-stream call: its workspace is a file-scope device array,
+// one per device, whose device address is looked up once per device --------------------
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];  // device address of `scratch` on each device
+
+// The address of `scratch` on the current device. In host code the array's name stands in
+// for it but is not a device address, so only this pointer is ever handed to a kernel.
+int scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GDN_E_HIP;
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return GDN_E_HIP;
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return GDN_OK;
+}
+}  // namespace
+
 extern "C" {
+
+int gdn_prefill_noalloc(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *h, void *conv_state,
+                        const float *conv_w, void *o, int64_t t, void *stream)
+{
+    int rc = check_params(p, 0);
+    if (rc != GDN_OK)
+        return rc;
+    if (t < 1)
+        return GDN_E_ARG;
+    // the part of the workspace a call cannot run without must fit the array; segment
+    // states that do not fit make the scan run unsegmented
+    if (front_bytes(p, 0, t, 1) > GDN_NOALLOC_SCRATCH_BYTES)
+        return GDN_E_WORKSPACE;
+    void *ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc != GDN_OK)
+        return rc;
+    return single(p, 0, q, k, v, g, beta, h, conv_state, conv_w, o, t, ws,
+                  GDN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t gdn_noalloc_scratch_bytes(void) { return GDN_NOALLOC_SCRATCH_BYTES; }
 
 int gdn_prefill(const gdn_params *p, const void *q, const void *k, const void *v,
                 const float *g, const float *beta, float *h, void *conv_state,

@@ -149,6 +149,29 @@ int kda_prefill(const gdn_params *p, const void *q, const void *k, const void *v
                 void *stream);
 
 /*
+ * gdn_prefill without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine): its workspace is a device array of gdn_noalloc_scratch_bytes() (64 MiB) that
+ * the library holds on every GPU it runs on until the process ends. Its device address is
+ * looked up on the first call on each device, which must be the current device and the
+ * device of `stream`.
+ *   - Arguments, layouts and results are those of gdn_prefill.
+ *   - GDN_E_WORKSPACE when the workspace the call cannot run without (float32 rows with
+ *     the front end: t * cd floats of activations) exceeds the array; segment states
+ *     that do not fit make the scan run unsegmented, with the same results up to rounding.
+ *   - GDN_E_HIP if the array's address cannot be looked up.
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap on one GPU (two
+ *     streams, or host threads) race and give undefined results. Nothing in the array has
+ *     to start at zero; every call writes what it later reads.
+ */
+int gdn_prefill_noalloc(const gdn_params *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, float *h, void *conv_state,
+                        const float *conv_w, void *o, int64_t t, void *stream);
+/* Size in bytes of the device array behind gdn_prefill_noalloc. */
+size_t gdn_noalloc_scratch_bytes(void);
+
+/*
  * B streams of equal length t_per_stream lying back to back: stream b owns rows
  * [b*t_per_stream, (b+1)*t_per_stream) of q/k/v/g/beta/o (page "split_prefill.rs",
  * prefill_gdn_full_batched: one h-state pointer per stream, streams of equal length).

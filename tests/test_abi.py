@@ -242,3 +242,18 @@ def test_params_struct_layout():
                                               check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(B.gdn_params) == 72
     assert out[1:] == [getattr(B.gdn_params, f).offset for f in fields]
+
+
+def test_noalloc_refusals_before_launch():
+    """gdn_prefill_noalloc checks its arguments before it touches the device, and refuses a
+    call whose activations (float32 rows with the front end) would not fit its array."""
+    p = B.params(2, 64, 64, dtype=B.GDN_F32)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE]
+    assert B.gdn_prefill_noalloc(p, *args, 0, None) == B.GDN_E_ARG
+    assert B.gdn_prefill_noalloc(B.params(2, 64, 64, chunk=32), *args, 10, None) == B.GDN_E_UNSUPPORTED
+    cap = B.gdn_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)    # 6144 fp32 activations per row
+    t = cap // (3 * 32 * 64 * 4) + 1
+    assert B.gdn_prefill_noalloc(pf, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, t,
+                                 None) == B.GDN_E_WORKSPACE
