@@ -12,9 +12,12 @@ starts; several input copies are rotated so that a step never finds its inputs i
 token each (front end, one recurrence step on each stream's 2 MiB state, window update);
 the value is decoded tokens/s.
 
-Extra fields: ``roofline`` (the dominant kernel's algorithmic bytes per launch over its
-average duration, from hipEvents the library records on the call's stream during the timed
-steps) and ``cpu_baseline`` (the fp64 oracle on a bounded sample, on this host's cores).
+Extra fields: ``roofline`` (the call's algorithmic bytes -- every input read once, o written
+once in the input dtype, the states read and written once -- over the call's duration from
+hipEvents the library records on the call's stream during the timed steps, against the HBM
+peak; the same ratio over the wall-clock step; the call's algorithmic MFMA work against the
+dense fp16 peak; per-stage times) and ``cpu_baseline`` (the fp64 oracle on a bounded
+sample, on this host's cores).
 """
 from __future__ import annotations
 
@@ -29,7 +32,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 (vector and MFMA)
 METRIC = "prefill tokens/s per GDN/KDA layer (H=32, d=128) + % of MFMA/HBM roofline"
 DECODE_METRIC = ("decode tokens/s per GDN/KDA layer (one token per stream, H=32, d=128) "
                  "+ % of HBM roofline")
@@ -53,27 +58,35 @@ def gate_fused(spec) -> bool:
     return not (spec.gate == "kda" and (spec.dk == 128 or spec.dtype == "f32"))
 
 
-def algorithmic_bytes(spec) -> dict:
-    """Bytes each kernel must move per launch (inputs read once, outputs written once)."""
+def algorithmic_bytes(spec) -> int:
+    """Bytes a call must move at least: the q/k/v (or raw) rows read once, the gates and
+    betas read once, o written once in the input dtype, every state read and written once,
+    the conv taps and windows (read and written) once, and with the output gate z and its
+    weights read once. With bf16 rows, H=32 and d=128 this is 34,132 bytes per token on the
+    4096-token single stream."""
     N, H, dk, dv, B = spec.N, spec.H, spec.dk, spec.dv, spec.B
     es = 2 if spec.dtype == "bf16" else 4
-    cd = spec.cd
-    g_bytes = N * H * (dk if spec.gate == "kda" else 1) * 4
-    state = 2 * B * H * dk * dv * 4  # h read + written
-    chunk = N * cd * es + g_bytes + N * H * 4 + N * H * dv * 4 + state
-    out = {"recur": chunk}
-    if spec.out_gate:
-        zw = N * H * dv * es + dv * 4  # z and the norm weights
-        if gate_fused(spec):
-            out["recur"] += zw
-        else:  # o read back and rewritten
-            out["gate"] = zw + 2 * N * H * dv * 4
+    n = N * spec.cd * es                                         # q|k|v or raw rows
+    n += N * H * (dk if spec.gate == "kda" else 1) * 4           # log-gates
+    n += N * H * 4                                               # beta
+    n += N * H * dv * es                                         # o (input dtype)
+    n += 2 * B * H * dk * dv * 4                                 # h in and out
     if spec.front_end:
-        # front: raw rows in, activations out (same element size), taps, windows read
-        out["front"] = 2 * N * cd * es + cd * spec.conv_k * 4 + B * cd * (spec.conv_k - 1) * es
-        # the new windows (last raw rows read, windows rewritten) go out with the scan
-        out["recur"] += 2 * B * cd * (spec.conv_k - 1) * es
-    return out
+        n += spec.cd * spec.conv_k * 4 + 2 * B * spec.cd * (spec.conv_k - 1) * es
+    if spec.out_gate:
+        n += N * H * dv * es + dv * 4                            # z and the norm weights
+    return n
+
+
+def algorithmic_flops(spec) -> int:
+    """MFMA work of the chunked algorithm per call: per token and head the strict-lower
+    K K^T, the triangular solve, the triangular T K and T V, Q K^T and P U over the chunk,
+    and the three state products W h, Q h and K^T U: 2 H [(C-1)/2 dk + C^2/6 + 4 (C+1)/2 d
+    + 3 dk dv] per token (4.512 MFLOP at H=32, d=128, C=64)."""
+    C, d = spec.chunk, spec.dv
+    per_tok = 2 * spec.H * ((C - 1) / 2 * spec.dk + C * C / 6 + 4 * (C + 1) / 2 * d +
+                            3 * spec.dk * spec.dv)
+    return int(spec.N * per_tok)
 
 
 def decode_bytes(spec) -> dict:
@@ -218,8 +231,6 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
 
-    # the chunk scan: one chunk_kernel launch, or (segmented scan) pass 1 + the chain of
-    # segment maps + pass 2, timed together as one stage
     segs = 0
     if not args.decode and first.kind != B.GDN_KIND_VARLEN:
         segs = B.gdn_segments(first.params, first.plan_kind, spec.B, spec.N // spec.B,
@@ -228,32 +239,42 @@ def main() -> int:
              B.GDN_PROF_GATE: "gate"}
     avg_ms = {names[i]: ms[i] / launches[i] for i in names if launches[i]}
     launches_of = {names[i]: launches[i] for i in names if launches[i]}
-    dom = max(avg_ms, key=avg_ms.get)
-    alg = decode_bytes(spec) if args.decode else algorithmic_bytes(spec)
-    achieved = alg[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    call_ms = sum(avg_ms.values())  # every kernel of a call, one event pair per stage
+    ms_per_step = elapsed * 1e3 / args.steps
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        ent = tr.get(spec.name, {}).get(dom)
+        ent = tr.get(spec.name, {}).get("call")
         if ent and ent.get("kernel_hash") == kernel_hash("decode" if args.decode else
                                                          "prefill"):
             traffic = ent["bytes_per_launch"]
     if args.decode:
-        kname = "decode_kernel (front end + one recurrence step + window update, fused)"
-    elif dom == "recur" and segs:
-        warm = spec.gate != "kda"
-        kname = ("recur: %schunk_kernel pass 1 + combine_kernel + chunk_kernel pass 2 "
-                 "(segmented scan, %d segments%s)"
-                 % ("warm_plan_kernel + " if warm and not spec.front_end else "", segs,
-                    "; warm starts where the gates allow" if warm else ""))
-        if warm and spec.front_end:
-            kname += "; the warm-start plan runs with the front kernel"
+        alg = decode_bytes(spec)["recur"]
+        flops = 0
+        kname = ("the whole call: decode_kernel (front end + one recurrence step + window "
+                 "update, fused)")
     else:
-        kname = dom
-    if not args.decode and dom == "recur" and spec.front_end:
-        kname += "; the new conv windows go out with the scan's first launch"
+        alg = algorithmic_bytes(spec)
+        flops = algorithmic_flops(spec)
+        parts = []
+        if "front" in avg_ms:
+            parts.append("front_kernel (float32 rows)")
+        if spec.front_end and spec.dtype == "bf16":
+            parts.append("chunk_kernel with the front end fused")
+        else:
+            parts.append("chunk_kernel")
+        if segs:
+            warm = spec.gate != "kda"
+            parts.append("segmented scan of %d segments: %spass 1 + combine_kernel + pass 2%s"
+                         % (segs, "warm_plan_kernel + " if warm else "",
+                            "; warm starts where the gates allow" if warm else ""))
+        if "gate" in avg_ms:
+            parts.append("gate_kernel")
+        kname = "the whole call: " + "; ".join(parts)
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    fp32 = spec.dtype == "f32"
+    mfma_peak = FP32_PEAK_TFLOPS if fp32 else MFMA_PEAK_TFLOPS
 
-    ms_per_step = elapsed * 1e3 / args.steps
     line = {
         "metric": DECODE_METRIC if args.decode else METRIC,
         "value": spec.N / (ms_per_step * 1e-3),
@@ -266,8 +287,9 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("%s in; fp32 arithmetic; fp32 o" % spec.dtype) if args.decode else
-                 "f32 in; fp32 MFMA and VALU; fp32 o" if spec.dtype == "f32" else
-                 "bf16 in; fp16 MFMA operands, fp32 accumulate/VALU; fp32 o",
+                 "f32 in; fp32 MFMA and VALU; fp32 o" if fp32 else
+                 "bf16 in; fp16 MFMA operands (hi + lo pairs where a single rounding would "
+                 "show), fp32 accumulate and VALU; fp32 o",
         "data": "synthetic (seeded; distributions of the workload description)",
         "config": {"workload": spec.name, "tokens": spec.N, "streams": spec.B, "H": spec.H,
                    "dk": spec.dk, "dv": spec.dv, "chunk": spec.chunk, "gate": spec.gate,
@@ -278,9 +300,15 @@ def main() -> int:
                      "kernel": kname,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": alg[dom],
-                     "avg_launch_ms": avg_ms[dom], "timed_launches": launches_of[dom]},
-        "stage_ms_per_step": avg_ms,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_ms": call_ms,
+                     "timed_launches": max(launches_of.values()),
+                     "frac_wall": alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mfma": {"algorithmic_flops_per_launch": flops,
+                              "achieved_tflops": flops / (call_ms * 1e-3) / 1e12,
+                              "peak_tflops": mfma_peak,
+                              "frac": flops / (call_ms * 1e-3) / 1e12 / mfma_peak},
+                     "stage_ms": avg_ms},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_budget)

@@ -699,6 +699,8 @@ struct Z4<float> {
     __device__ static float4 get(const raw &u) { return u; }
 };
 
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+
 __device__ __forceinline__ float silu(float z)
 {
     return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
@@ -819,7 +821,13 @@ struct ChunkCfg {
     static constexpr int SZ_QF = QLO ? 2 * SZ_Q : SZ_Q;  // Q (hi, lo)
     static constexpr int LDX = 20;               // row stride of the 16x16 inversion scratch
     static constexpr int SZ_X = 4 * 16 * LDX * 4;
-    static constexpr int RQK = 2 * DK * 2;       // bytes per raw [q | k] row
+    static constexpr int RQ = DK * 2;            // bytes per raw q (or k) row
+    static constexpr int RQK = 2 * RQ;           // bytes per raw q and k row
+    // raw q rows [RR][DK], then raw k rows [RR][DK] (bf16), from OFF_Q
+    __host__ __device__ static constexpr int raw_qk(int tensor, int row)
+    {
+        return (tensor * RR + row) * RQ;
+    }
     static constexpr int VS = NV * 2 / 16;       // 16-byte pieces of a raw v row
     // one slot of padding per raw v row: the u16 reads of D-layout rows 4 apart then fall
     // in different halves of the banks
@@ -1221,22 +1229,27 @@ __global__ void __launch_bounds__(NW * 64)
     // The raw rows used are [max(stream start, c0 - (KC - 1)), c0 + Lc): raw row indices
     // [rlo, rhi) of the chunk. Addresses are a uniform row base plus a 32-bit lane offset
     // (the host keeps RR row strides within 32 bits for these calls).
-    auto prefetch_raw = [&](int64_t c0, int Lc, bool with_q, int lane, int wave) {
+    // part 0: the v rows; part 1: the q|k rows
+    auto prefetch_raw = [&](int64_t c0, int Lc, bool with_q, int lane, int wave, int part) {
         const int rlo = (int)max((int64_t)0, sbeg - (c0 - (KC - 1)));
         const int rhi = Lc + KC - 1;
         const int ldi = (int)ld;
         const TIN *qb = qg + (c0 - (KC - 1)) * ld, *kb = kg + (c0 - (KC - 1)) * ld;
-        constexpr int QS = C::RQK / 16, NQI = (C::RR * QS + 63) / 64;
+        // one tensor per wave instruction (a uniform row base, 32-bit lane offsets): q rows
+        // fill instructions [0, NQI), k rows [NQI, 2 NQI); lanes past the last raw row are
+        // masked, so a tensor's last instruction writes nothing beyond its rows
+        constexpr int QS = C::RQ / 16, NQI = (C::RR * QS + 63) / 64;
+        if (part == 1) {
 #pragma unroll
-        for (int i = 0; i < (NQI + NW - 1) / NW; ++i) {
-            const int n = wave + NW * i;
-            const int slot = 64 * n + lane, rho = slot / QS, pc = slot % QS;
-            const bool isk = pc >= QS / 2;
-            if (n < NQI && rho >= rlo && rho < rhi && (isk || with_q))
-                dma16((isk ? kb : qb) + (rho * ldi + (pc % (QS / 2)) * 8),
-                      lds_addr(smem + C::OFF_Q + 1024 * n));
-        }
-        if (!v_zero) {
+            for (int i = 0; i < (2 * NQI + NW - 1) / NW; ++i) {
+                const int n = wave + NW * i;
+                const int t = n >= NQI, m = n - t * NQI;
+                const int slot = 64 * m + lane, rho = slot / QS, pc = slot % QS;
+                if (n < 2 * NQI && rho >= rlo && rho < rhi && (t || with_q))
+                    dma16((t ? kb : qb) + (rho * ldi + pc * 8),
+                          lds_addr(smem + C::OFF_Q + C::raw_qk(t, 0) + 1024 * m));
+            }
+        } else if (!v_zero) {
             const TIN *vb = vg + (c0 - (KC - 1)) * ld;
             constexpr int VSL = C::VS + 1, NVI = (C::RR * VSL + 63) / 64;
 #pragma unroll
@@ -1258,12 +1271,14 @@ __global__ void __launch_bounds__(NW * 64)
     const int Kt = FRONT ? a.conv_k : KC, Wn = Kt - 1, tap0 = KC - Kt;
     float wv[FRONT ? KC : 1];  // this lane's v column taps (fused front end)
     if constexpr (FRONT) {
-        // q and k taps of this head into LDS, [tensor][tap][channel]
+        // q and k taps of this head into LDS, [tensor][tap][channel], times -log2(e): the
+        // conv then gives -z log2(e), the argument of the exp2 in the SiLU (see stage A)
         for (int idx = tid0; idx < 2 * KC * DK; idx += NT) {
             const int t = idx / (KC * DK), rem = idx - t * KC * DK, j = rem / DK;
             ((float *)(smem + C::OFF_CW))[idx] =
                 j < tap0 ? 0.f
-                         : a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * Kt + j - tap0];
+                         : a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * Kt + j - tap0] *
+                               -kLog2e;
         }
 #pragma unroll
         for (int j = 0; j < KC; ++j)
@@ -1280,7 +1295,7 @@ __global__ void __launch_bounds__(NW * 64)
             for (int idx = tid0; idx < (2 * DK + NV) * W; idx += NT) {
                 const int ch = idx / W, j = idx - ch * W, e = j - (W - Wn);
                 if (ch < 2 * DK)
-                    *(TIN *)(smem + C::OFF_Q + j * C::RQK + ch * 2) =
+                    *(TIN *)(smem + C::OFF_Q + C::raw_qk(ch >= DK, j) + (ch % DK) * 2) =
                         e < 0 ? (TIN)0.f : cw[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + e];
                 else
                     *(TIN *)(smem + C::OFF_V + j * C::RVB + (ch - 2 * DK) * 2) =
@@ -1292,8 +1307,10 @@ __global__ void __launch_bounds__(NW * 64)
         const int64_t roff = c0 * ld;
         const bool with_q = c0 >= o_start;  // q rows only feed o
         if constexpr (FRONT) {
-            prefetch_raw(c0, Lc, with_q, threadIdx.x & 63,
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+            const int lane = threadIdx.x & 63;
+            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            prefetch_raw(c0, Lc, with_q, lane, wave, 1);
+            prefetch_raw(c0, Lc, with_q, lane, wave, 0);
         } else {
 #pragma unroll
             for (int it = 0; it < NQK; ++it)
@@ -1508,7 +1525,7 @@ __global__ void __launch_bounds__(NW * 64)
             static_assert(NW * GPW / 2 * 4 == CH, "conv row map");
             const int gi = lane / LQ, cg = lane % LQ, tsr = gi & 1;
             const int rg = wave * (GPW / 2) + (gi >> 1);
-            const unsigned char *rq = smem + zo + C::OFF_Q + tsr * DK * 2 + cg * 16;
+            const unsigned char *rq = smem + zo + C::OFF_Q + C::raw_qk(tsr, 0) + cg * 16;
             const float *wt = (const float *)(smem + zo + C::OFF_CW) + tsr * KC * DK + 8 * cg;
             float y[4][8];
             {
@@ -1525,7 +1542,7 @@ __global__ void __launch_bounds__(NW * 64)
                 uint4 raw[KC + 3];
 #pragma unroll
                 for (int u = 0; u < KC + 3; ++u)
-                    raw[u] = *reinterpret_cast<const uint4 *>(rq + (4 * rg + u) * C::RQK);
+                    raw[u] = *reinterpret_cast<const uint4 *>(rq + (4 * rg + u) * C::RQ);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -1537,21 +1554,28 @@ __global__ void __launch_bounds__(NW * 64)
                         for (int e = 0; e < 8; ++e)
                             acc[e] += w[j][e] * xv[e];
                     }
+                    // acc = -z log2(e): e^-z = exp2(acc), and acc / (1 + e^-z) is
+                    // -log2(e) SiLU(z); the factor is taken out below
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        y[i][e] = silu(acc[e]);
+                        y[i][e] = acc[e] *
+                                  __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(acc[e]));
                 }
             }
-            // L2 of each row over the head, the q scale; rows at or past the end are 0
+            // L2 of each row over the head, the q scale; rows at or past the end are 0. The
+            // rows hold -log2(e) SiLU(z): y / sqrt(|y|^2 + eps) of the SiLU rows is
+            // -y' / sqrt(|y'|^2 + eps log2(e)^2) of these, and without L2 they are rescaled
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float m = tsr ? 1.f : a.scale;
+                float m = tsr ? -1.f : -a.scale;
                 if (a.do_l2) {
                     float ss = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         ss += y[i][e] * y[i][e];
-                    m *= rsqrtf(group_sum<LQ>(ss) + a.eps);
+                    m *= rsqrtf(group_sum<LQ>(ss) + a.eps * (kLog2e * kLog2e));
+                } else {
+                    m *= kLn2;
                 }
                 const bool live = 4 * rg + i < L;
 #pragma unroll
@@ -1571,7 +1595,8 @@ __global__ void __launch_bounds__(NW * 64)
                     const int ch = idx / Wn, j = idx - ch * Wn;
                     if (ch < 2 * DK)
                         wo[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + j] =
-                            *(const TIN *)(smem + zo + C::OFF_Q + (r0 + j) * C::RQK + ch * 2);
+                            *(const TIN *)(smem + zo + C::OFF_Q + C::raw_qk(ch >= DK, r0 + j) +
+                                           (ch % DK) * 2);
                     else
                         wo[(int64_t)v_channel(ch - 2 * DK) * Wn + j] = *(const TIN *)(
                             smem + zo + C::OFF_V + (r0 + j) * C::RVB + (ch - 2 * DK) * 2);
@@ -1583,15 +1608,28 @@ __global__ void __launch_bounds__(NW * 64)
                 const int r = 4 * rg + i;
                 if (tsr == 1 || write_o) {  // q only feeds o
                     T *dh = tsr ? Ks : Qs, *dl = tsr ? Kl : Ql;
+                    // the 4-element chunks 2 cg and 2 cg + 1 of row r sit side by side in
+                    // the permuted layout (the permutation flips the low 2 bits of the chunk
+                    // index), in swapped order when it flips bit 0: one 16-byte store each
+                    f16x4 hi4[2], lo4[2];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        f16x4 hi4, lo4;
+                    for (int h = 0; h < 2; ++h)
                         split4(f32x4{y[i][4 * h], y[i][4 * h + 1], y[i][4 * h + 2],
                                      y[i][4 * h + 3]},
-                               hi4, lo4);
-                        *reinterpret_cast<f16x4 *>(dh + QK<T, DK>::at(r, 2 * cg + h)) = hi4;
-                        if (tsr == 1 || C::QLO)
-                            *reinterpret_cast<f16x4 *>(dl + QK<T, DK>::at(r, 2 * cg + h)) = lo4;
+                               hi4[h], lo4[h]);
+                    const int sw = (r >> 2) & 1;
+                    const int off = QK<T, DK>::at(r, 2 * cg) - 4 * sw;
+                    const f16x8 hv = sw ? __builtin_shufflevector(hi4[1], hi4[0], 0, 1, 2, 3,
+                                                                  4, 5, 6, 7)
+                                        : __builtin_shufflevector(hi4[0], hi4[1], 0, 1, 2, 3,
+                                                                  4, 5, 6, 7);
+                    *reinterpret_cast<f16x8 *>(dh + off) = hv;
+                    if (tsr == 1 || C::QLO) {
+                        const f16x8 lv = sw ? __builtin_shufflevector(lo4[1], lo4[0], 0, 1, 2,
+                                                                      3, 4, 5, 6, 7)
+                                            : __builtin_shufflevector(lo4[0], lo4[1], 0, 1, 2,
+                                                                      3, 4, 5, 6, 7);
+                        *reinterpret_cast<f16x8 *>(dl + off) = lv;
                     }
                 }
             }
