@@ -115,3 +115,43 @@ def test_config5_seed_sweep(seed):
     call = run_gpu(inp)
     e_o, e_h = compare(call, run_oracle(inp))
     print("seed %d: err(o)=%.3g err(h)=%.3g" % (seed, e_o, e_h), flush=True)
+
+
+def test_kda_batched_8x2048():
+    """The per-key-channel gate on the batched workload's shapes: 8 streams x 2048 tokens,
+    H=32, d=128, bf16 q/k/v with L2 in the call, per-stream states through h_ptrs, the
+    log-gate tensor [N, H, dk] = -softplus(N(0,1)); every head against the oracle."""
+    import dataclasses
+    spec = dataclasses.replace(inputs.config(3), gate="kda",
+                               name="kda-batched-B8xT2048-H32-d128-bf16")
+    inp = inputs.make(spec)
+    call = run_gpu(inp)
+    e_o, e_h = compare(call, run_oracle(inp))
+    print("%s: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
+
+
+@pytest.mark.parametrize("fill", [float("nan"), 1e30])
+def test_kda_varlen_tails(fill):
+    """The per-key-channel gate on the varlen workload's 16 streams (lengths 1, 63, 64, 65
+    among them, 67117 tokens) with NaN and 1e30 in every per-token array past the last
+    token: every head and every stream's state against the oracle, o rows past the end
+    untouched."""
+    import dataclasses
+    spec = dataclasses.replace(inputs.config(4, pad_fill=fill), gate="kda",
+                               name="kda-varlen-B16-H32-d128-bf16")
+    inp = inputs.make(spec)
+    call = run_gpu(inp)
+    e_o, e_h = compare(call, run_oracle(inp))
+    print("%s tails %g: err(o)=%.3g err(h)=%.3g" % (spec.name, fill, e_o, e_h), flush=True)
+
+
+def test_kda_varlen_front_end():
+    """KDA varlen through the fused front end: the varlen workload's lengths with the conv
+    front end and per-stream windows (each stream its own carried window)."""
+    import dataclasses
+    spec = dataclasses.replace(inputs.config(4, pad_fill=float("nan")), gate="kda",
+                               front_end=True, name="kda-varlen-front-B16-H32-d128-bf16")
+    inp = inputs.make(spec)
+    call = run_gpu(inp)
+    e_o, e_h = compare(call, run_oracle(inp))
+    print("%s: err(o)=%.3g err(h)=%.3g" % (spec.name, e_o, e_h), flush=True)
