@@ -70,12 +70,16 @@ int gdn_oracle_conv_silu(int64_t T, int32_t C, int32_t K, const double *x,
     if (T < 0 || C <= 0 || K < 1 || !x || !w || !y)
         return ORACLE_EARG;
     const int32_t W = K - 1;
+    int failed = 0; /* set (never cleared) by any thread whose buffer could not be had */
 #pragma omp parallel for schedule(static)
     for (int32_t c = 0; c < C; ++c) {
         /* extended sequence for this channel: xe[0..W-1] = window, xe[W+t] = x[t] */
         double *xe = (double *)malloc(sizeof(double) * (size_t)(T + W + 1));
-        if (!xe)
+        if (!xe) {
+#pragma omp atomic write
+            failed = 1;
             continue;
+        }
         for (int32_t j = 0; j < W; ++j)
             xe[j] = st ? st[(int64_t)c * W + j] : 0.0;
         for (int64_t t = 0; t < T; ++t)
@@ -91,7 +95,7 @@ int gdn_oracle_conv_silu(int64_t T, int32_t C, int32_t K, const double *x,
                 st_out[(int64_t)c * W + j] = xe[T + j];
         free(xe);
     }
-    return ORACLE_OK;
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
 /* q <- scale * q / sqrt(|q|^2 + eps) over n entries */
@@ -131,7 +135,7 @@ int gdn_oracle_recurrence(int32_t B, const int64_t *cu, int32_t H, int32_t dk,
     for (int32_t b = 0; b < B; ++b)
         if (cu[b + 1] < cu[b])
             return ORACLE_EARG;
-    int err = ORACLE_OK;
+    int failed = 0; /* set (never cleared) by any thread whose buffers could not be had */
     const int64_t units = (int64_t)B * H;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t u = 0; u < units; ++u) {
@@ -141,7 +145,8 @@ int gdn_oracle_recurrence(int32_t B, const int64_t *cu, int32_t H, int32_t dk,
         double *kn = (double *)malloc(sizeof(double) * dk);
         double *e = (double *)malloc(sizeof(double) * dv);
         if (!qn || !kn || !e) {
-            err = ORACLE_ENOMEM;
+#pragma omp atomic write
+            failed = 1;
             free(qn), free(kn), free(e);
             continue;
         }
@@ -188,7 +193,7 @@ int gdn_oracle_recurrence(int32_t B, const int64_t *cu, int32_t H, int32_t dk,
         }
         free(qn), free(kn), free(e);
     }
-    return err;
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
 /* Threads the OpenMP runtime will use for the loops above (for reporting). */

@@ -420,3 +420,21 @@ def test_prefill_front_end_composition():
         ob, hb = oracle.recurrence(q, k, v, g[s], beta[s], h0[b:b + 1])
         np.testing.assert_array_equal(ob, r["o"][s])
         np.testing.assert_array_equal(hb[0], r["h"][b])
+
+
+def test_oracle_reports_allocation_failure():
+    """A channel buffer the oracle cannot allocate makes the call fail (ORACLE_ENOMEM = -2)
+    instead of skipping the channel: a stream of 2^58 tokens asks for 2^61 bytes per
+    channel, which malloc refuses before anything is read or written."""
+    import ctypes
+    lib = oracle._load()
+    dp = ctypes.POINTER(ctypes.c_double)
+    x = np.zeros(8)
+    w = np.zeros(4)
+    y = np.zeros(8)
+    rc = lib.gdn_oracle_conv_silu(2 ** 58, 1, 4, x.ctypes.data_as(dp), w.ctypes.data_as(dp),
+                                  None, y.ctypes.data_as(dp), None)
+    assert rc == -2
+    # and a call that can allocate still succeeds
+    assert lib.gdn_oracle_conv_silu(2, 1, 4, x.ctypes.data_as(dp), w.ctypes.data_as(dp),
+                                    None, y.ctypes.data_as(dp), None) == 0
