@@ -31,7 +31,9 @@ EXPORTS = ("gdn_prefill", "gdn_prefill_noalloc", "gdn_noalloc_scratch_bytes", "k
            "gdn_prefill_batched", "gdn_prefill_varlen",
            "kda_prefill_batched", "kda_prefill_varlen", "gdn_decode", "kda_decode",
            "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
-           "gdn_segments", "gdn_segment_plan", "gdn_status_string")
+           "gdn_segments", "gdn_segment_plan", "gdn_status_string", "gdn_debug_validate")
+GDN_BAD_CU_START, GDN_BAD_CU_ORDER, GDN_BAD_CU_TOTAL, GDN_BAD_CU_MAXLEN = 1, 2, 4, 8
+GDN_BAD_KDA_GATE = 16
 GDN_PROF_FRONT = 0
 GDN_PROF_RECUR = 1
 GDN_PROF_STATE = 2
@@ -94,6 +96,8 @@ def load(path: str = SO):
         lib.gdn_segments.restype = ctypes.c_int
         lib.gdn_segment_plan.argtypes = [_pp, _i32, _i32, _i64, _sz, _vp, _vp]
         lib.gdn_segment_plan.restype = ctypes.c_int
+        lib.gdn_debug_validate.argtypes = [_vp]
+        lib.gdn_debug_validate.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
@@ -223,3 +227,9 @@ def gdn_segment_plan(p, kind, B, t_per_stream, ws_bytes):
 
 def gdn_status_string(status):
     return load().gdn_status_string(status).decode()
+
+
+def gdn_debug_validate(status):
+    """Turn the device-side input checks on (status: a device int32 tensor or pointer) or
+    off (None)."""
+    return load().gdn_debug_validate(_p(status))

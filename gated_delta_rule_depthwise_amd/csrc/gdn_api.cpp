@@ -75,6 +75,9 @@ struct Stage {
     }
 };
 
+// debug validation status word (device), or nullptr: see gdn_debug_validate
+std::atomic<int32_t *> debug_status{nullptr};
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -354,6 +357,7 @@ struct Call {
     void *o;
     Streams st;
     int64_t N;
+    int32_t max_seqlen;  // varlen: the caller's bound on a stream's length
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
@@ -413,7 +417,25 @@ int run(const Call &c)
         c.ws_bytes >= need + order_bytes(c.st.B))
         order = (int32_t *)((char *)c.ws + need);
 
+    // debug validation of the device-side inputs, before every other kernel of the call
+    int32_t *dbg = debug_status.load();
+    if (dbg) {
+        gdn::ValidateArgs va{};
+        va.cu = c.st.cu;
+        va.B = c.st.B;
+        va.total = c.N;
+        va.max_seqlen = c.max_seqlen;
+        va.status = dbg;
+        if (c.kda) {
+            va.g = c.g;
+            va.ng = c.N * p->H * p->dk;
+        }
+        if (gdn::launch_validate(va, c.stream) != hipSuccess)
+            return GDN_E_HIP;
+    }
+
     ChunkArgs ca{};
+    ca.dbg = dbg;
     ca.order = order;
     ca.g = c.g;
     ca.beta = c.beta;
@@ -440,6 +462,7 @@ int run(const Call &c)
                        ? (char *)seg_ws + align_up((size_t)lay.total() * sizeof(float))
                        : nullptr;
     gdn::WarmArgs wa{};
+    wa.dbg = dbg;
     ca.warm = warm;
     if (ca.warm) {
         wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
@@ -447,6 +470,7 @@ int run(const Call &c)
         wa.seg_ws = seg_ws, wa.lay = lay;
     }
     FrontArgs fa{};
+    fa.dbg = dbg;
     if (fused_fe) {
         // conv + SiLU + L2 in the chunk kernel's load stage, straight from the raw rows
         ca.q = c.q, ca.k = c.k, ca.v = c.v, ca.ld = p->ld_qkv;
@@ -533,6 +557,7 @@ int run(const Call &c)
                                   (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
+            cb.dbg = dbg;
             cb.seg_ws = ca.seg_ws;
             cb.lay = lay;
             cb.warm = ca.warm;
@@ -553,6 +578,7 @@ int run(const Call &c)
         }
         if (shared) {  // every workgroup that read the old windows is done
             gdn::WindowCopyArgs wc{};
+            wc.dbg = dbg;
             wc.win_ws = win_ws;
             wc.conv_state = c.conv_state, wc.conv_state_ptrs = c.conv_state_ptrs;
             wc.st = c.st, wc.cd = (int32_t)conv_dim(p), wc.W = p->conv_k - 1;
@@ -563,6 +589,7 @@ int run(const Call &c)
     }
     if (p->z && !fused) {
         gdn::GateArgs ga{};
+        ga.dbg = dbg;
         ga.o = (float *)c.o;
         ga.z = p->z;
         ga.ld_z = p->ld_z;
@@ -698,6 +725,7 @@ int varlen(const gdn_params *p, int kda, const void *q, const void *k, const voi
     c.h_ptrs = h_ptrs, c.conv_state_ptrs = conv_state_ptrs, c.conv_w = conv_w, c.o = o;
     c.st = Streams{cu_seqlens, 0, B};
     c.N = total_tokens, c.ws = ws, c.ws_bytes = ws_bytes, c.stream = (hipStream_t)stream;
+    c.max_seqlen = max_seqlen;
     return run(c);
 }
 }  // namespace
@@ -869,6 +897,12 @@ int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_str
                  size_t ws_bytes)
 {
     return gdn_segment_plan(p, kind, B, t_per_stream, ws_bytes, nullptr, nullptr);
+}
+
+int gdn_debug_validate(int32_t *status)
+{
+    debug_status.store(status);
+    return GDN_OK;
 }
 
 int gdn_profile_enable(int on)

@@ -17,6 +17,7 @@ struct Streams {
 
 // The output gate as a separate pass over rows [0, N) of o, all heads.
 struct GateArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     float *o;               // [N][H][dv], in/out
     const void *z;
     int64_t ld_z;
@@ -71,6 +72,7 @@ struct SegLayout {
 // slot H(b, S-1) (and, with the front end fused, the new conv windows in win_ws); this
 // kernel, the first to run after that launch, copies them to the caller's buffers.
 struct CombineArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     float *seg_ws;
     SegLayout lay;
     int32_t H, dk, dv;
@@ -90,6 +92,7 @@ struct CombineArgs {
 // The staged windows [B][cd][W] (bf16) of a fused front-end call copied to the caller's;
 // a zero-length stream wrote none and keeps its window.
 struct WindowCopyArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     const void *win_ws;
     void *conv_state;
     void *const *conv_state_ptrs;
@@ -103,6 +106,7 @@ struct WindowCopyArgs {
 // log-gates sum below -110; warm mode when every boundary has such a window inside the
 // previous segment.
 struct WarmArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     const float *g;         // [N][H]
     const float *beta;      // [N][H]
     Streams st;
@@ -115,6 +119,7 @@ struct WarmArgs {
 
 // Front end: conv + SiLU (+ L2 and scale of q, k) over every channel of the packed rows.
 struct FrontArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     const void *q, *k, *v;  // raw rows, as in ChunkArgs
     int64_t ld;
     const float *conv_w;    // [cd][K]
@@ -135,6 +140,7 @@ struct FrontArgs {
 
 // Fused chunk kernel: per (stream, head, dv slice), every chunk of the stream in order.
 struct ChunkArgs {
+    const int32_t *dbg;     // debug validation status (device), or nullptr
     const void *q, *k, *v;  // row r, value head h: q + r*ld + (h/qk_group)*dk (k likewise),
     int64_t ld;             // v + r*ld + h*dv
     const float *g;         // [N][H] or [N][H][dk]
@@ -214,8 +220,29 @@ struct DecodeArgs {
     float norm_eps;
 };
 
+// Debug validation of a call's device-side inputs: cu_seqlens (when cu is set) and the
+// per-key-channel log-gates (when g is set, ng values of the real rows); violations OR
+// GDN_BAD_* bits into *status, and every kernel of the call then returns at once.
+struct ValidateArgs {
+    const int32_t *cu;
+    int32_t B;
+    int64_t total;
+    int32_t max_seqlen;
+    const float *g;
+    int64_t ng;
+    int32_t *status;
+};
+
+// A kernel of a call checked by the debug validation returns at once when a violation was
+// found (the check ran before it on the call's stream).
+__device__ __forceinline__ bool debug_stop(const int32_t *dbg)
+{
+    return dbg && *(volatile const int32_t *)dbg != 0;
+}
+
 // Launchers (defined in gdn_kernels.hip and gdn_decode.hip). Return hipSuccess or the
 // launch error.
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
 // new carried conv windows; must run after every kernel that reads the old ones
 // in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end;

@@ -35,6 +35,7 @@
 
 #include <type_traits>
 
+#include "gdn.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -422,12 +423,16 @@ __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
 
 __global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
 {
+    if (debug_stop(a.dbg))
+        return;
     warm_plan_block(a, blockIdx.x);
 }
 
 template <typename T, typename TOUT, int K>
 __global__ void __launch_bounds__(FRONT_THREADS) front_kernel(const FrontArgs a)
 {
+    if (debug_stop(a.dbg))
+        return;
     static_assert(FRONT_THREADS == 256, "the warm-start plan runs on 256 threads");
     if (blockIdx.y >= (a.N + a.tile_rows - 1) / a.tile_rows) {  // extra rows: warm plan
         const int64_t i = (int64_t)(blockIdx.y - (a.N + a.tile_rows - 1) / a.tile_rows) *
@@ -729,6 +734,8 @@ __device__ __forceinline__ float lane_group_sum(float x)
 template <typename TZ, int DV>
 __global__ void __launch_bounds__(256) gate_kernel(const GateArgs a)
 {
+    if (debug_stop(a.dbg))
+        return;
     constexpr int LPI = DV / 4, IPB = 256 / LPI;  // lanes per item, items per block
     const int64_t item = (int64_t)blockIdx.x * IPB + threadIdx.x / LPI;
     const int j = threadIdx.x % LPI;
@@ -1076,6 +1083,8 @@ __global__ void __launch_bounds__(NW * 64)
     static_assert(!KDA || NGK * NW * GRW == CH, "gate load map");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (debug_stop(a.dbg))
+        return;
 
     const int tid0 = threadIdx.x, lane0 = tid0 & 63;
     const int wave0 = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -2313,6 +2322,8 @@ int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int wave
 template <int DK, int NWV>
 __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
 {
+    if (debug_stop(a.dbg))
+        return;
     constexpr int NRB = DK / 16, RBW = (NRB + NWV - 1) / NWV;  // row blocks, per wave
     __shared__ float hsm[DK][20];  // 20 floats: rows 4 apart 16 banks apart
     // Workgroups go to the 8 XCDs round-robin by index: with the column block as the slow
@@ -2445,9 +2456,54 @@ hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Debug validation (see ValidateArgs): grid-stride over the B + 1 entries of cu_seqlens
+// and the ng log-gates; one atomic OR per wave that found something.
+__global__ void __launch_bounds__(256) validate_kernel(const ValidateArgs a)
+{
+    uint32_t bad = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (a.cu) {
+        for (int64_t b = i0; b <= a.B; b += stride) {
+            const int32_t c = a.cu[b];
+            if (b == 0 && c != 0)
+                bad |= GDN_BAD_CU_START;
+            if (b == a.B && (int64_t)c != a.total)
+                bad |= GDN_BAD_CU_TOTAL;
+            if (b < a.B) {
+                const int32_t d = a.cu[b + 1];
+                if (d < c)
+                    bad |= GDN_BAD_CU_ORDER;
+                else if (d - c > a.max_seqlen)
+                    bad |= GDN_BAD_CU_MAXLEN;
+            }
+        }
+    }
+    if (a.g) {
+        for (int64_t e = i0; e < a.ng; e += stride)
+            if (!(a.g[e] <= 0.f))  // a NaN is no decay either
+                bad |= GDN_BAD_KDA_GATE;
+    }
+    for (int m = 32; m >= 1; m >>= 1)
+        bad |= (uint32_t)__shfl_xor((int)bad, m);
+    if ((threadIdx.x & 63) == 0 && bad)
+        atomicOr(a.status, (int32_t)bad);
+}
+
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t s)
+{
+    const int64_t n = max((int64_t)a.B + 1, a.ng);
+    const int64_t blocks = min((n + 255) / 256, (int64_t)4096);
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)max(blocks, (int64_t)1)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
 // One thread per (stream, window entry): the staged windows to the caller's.
 __global__ void __launch_bounds__(256) window_copy_kernel(const WindowCopyArgs a)
 {
+    if (debug_stop(a.dbg))
+        return;
     const int64_t per = (int64_t)a.cd * a.W;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)a.st.B * per)

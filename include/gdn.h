@@ -193,8 +193,9 @@ int gdn_prefill_batched(const gdn_params *p, const void *q, const void *k, const
  * cu_seqlens[b+1]). Chunks restart at every stream start.
  *   cu_seqlens   device int32 [B+1], cu_seqlens[0] == 0, non-decreasing,
  *                cu_seqlens[B] == total_tokens. A zero-length stream is a no-op (its state
- *                is left as it was). Violations are not detected (the host does not read
- *                device memory) and give undefined results.
+ *                is left as it was). The host does not read device memory, so violations
+ *                give undefined results unless gdn_debug_validate is on (it then detects
+ *                them on the device and the call touches nothing).
  *   total_tokens host copy of cu_seqlens[B] (>= 1).
  *   max_seqlen   host upper bound of the longest stream (1 <= max_seqlen <= total_tokens).
  *   ws           >= gdn_workspace_bytes(p, B, total_tokens, GDN_KIND_VARLEN).
@@ -342,6 +343,25 @@ int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_str
  * segments' map jobs, which cost less per chunk than a chunk that writes o. */
 int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_stream,
                      size_t ws_bytes, int64_t *seg0_tokens, int64_t *seg_tokens);
+
+/*
+ * Debug validation of what the host cannot see without a synchronisation: the device-side
+ * cu_seqlens of varlen calls and the log-gates of per-key-channel calls (which must be a
+ * decay). Off by default. With `status` a DEVICE pointer to an int32, every later prefill
+ * call (any entry point, any stream) first launches a check on its stream; each violation
+ * ORs one of the bits below into *status, and then every other kernel of that call returns
+ * without reading or writing anything, so a malformed cu_seqlens cannot make the call
+ * access memory outside its buffers (h, o and the windows keep their bytes). The caller
+ * clears *status, makes its calls, and reads *status after synchronising the stream. NULL
+ * turns the checks off. The setting is process-wide; it costs one small launch per call
+ * (plus one read of the log-gates for per-key-channel calls). Returns GDN_OK.
+ */
+#define GDN_BAD_CU_START 1   /* cu_seqlens[0] != 0                                   */
+#define GDN_BAD_CU_ORDER 2   /* cu_seqlens decreases somewhere                         */
+#define GDN_BAD_CU_TOTAL 4   /* cu_seqlens[B] != total_tokens                          */
+#define GDN_BAD_CU_MAXLEN 8  /* a stream longer than max_seqlen                        */
+#define GDN_BAD_KDA_GATE 16  /* a per-key-channel log-gate above 0 or NaN, in a real row */
+int gdn_debug_validate(int32_t *status);
 
 /* Static description of a status code. */
 const char *gdn_status_string(int status);
