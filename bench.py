@@ -264,10 +264,9 @@ def main() -> int:
         else:
             parts.append("chunk_kernel")
         if segs:
-            warm = spec.gate != "kda"
-            parts.append("segmented scan of %d segments: %spass 1 + combine_kernel + pass 2%s"
-                         % (segs, "warm_plan_kernel + " if warm else "",
-                            "; warm starts where the gates allow" if warm else ""))
+            parts.append("segmented scan of %d segments: %swarm_plan_kernel + pass 1 + "
+                         "combine_kernel + pass 2; warm starts where the gates allow"
+                         % (segs, "gate_max_kernel + " if spec.gate == "kda" else ""))
         if "gate" in avg_ms:
             parts.append("gate_kernel")
         kname = "the whole call: " + "; ".join(parts)

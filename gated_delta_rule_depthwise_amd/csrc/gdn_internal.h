@@ -104,7 +104,8 @@ struct WindowCopyArgs {
 // Warm-start plan of a segmented call: per (stream, head), each chunk's total log-gate and
 // whether its betas lie in [0, 1.9]; per segment boundary the fewest chunks before it whose
 // log-gates sum below -110; warm mode when every boundary has such a window inside the
-// previous segment.
+// previous segment. With the per-key-channel gate, g holds each token's largest channel
+// log-gate (the norm of a token's transition is at most its largest channel decay).
 struct WarmArgs {
     const int32_t *dbg;     // debug validation status (device), or nullptr
     const float *g;         // [N][H]
@@ -256,6 +257,16 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s);
 hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s);
+// Largest per-key-channel log-gate of each (token, head): out[t][h] = max_c g[t][h][c] over
+// n = N * H pairs; the warm-start plan of the per-channel gate runs on it.
+struct GateMaxArgs {
+    const int32_t *dbg;  // debug validation status (device), or nullptr
+    const float *g;      // [N][H][dk]
+    float *out;          // [N][H]
+    int64_t n;
+    int32_t dk;
+};
+hipError_t launch_gate_max(const GateMaxArgs &a, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 // q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after
 // the step by a pass of its own

@@ -118,11 +118,13 @@ __device__ __forceinline__ void store_stream16(void *p, float4 v)
 // before each one, which stalls a whole stage on a prefetch meant for the next chunk. The
 // callers wait for their transfers themselves (vmcnt(0), then a barrier) before reading
 // the destination, and do not touch it while transfers are in flight.
-__device__ __forceinline__ void dma16(const void *p, uint32_t lds)
+// The global address is a uniform base (an SGPR pair) plus a 32-bit byte offset per lane,
+// so a transfer costs the wave no vector address arithmetic.
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(p), "s"(lds)
+                 : "v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -705,6 +707,7 @@ struct Z4<float> {
 };
 
 constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+constexpr float kExpCap = 80.f * kLog2e;  // largest exponent of a decay factor, log2 units
 
 __device__ __forceinline__ float silu(float z)
 {
@@ -835,11 +838,16 @@ struct ChunkCfg {
     {
         return (tensor * RR + row) * RQ;
     }
-    static constexpr int VS = NV * 2 / 16;       // 16-byte pieces of a raw v row
-    // one slot of padding per raw v row: the u16 reads of D-layout rows 4 apart then fall
-    // in different halves of the banks
-    static constexpr int RVB = (VS + 1) * 16;
-    static constexpr int SZ_RV = RR * RVB;
+    // raw v rows in blocks of 4 (one LDS-DMA instruction each), 32 bytes of padding after
+    // each block: the u16 reads of D-layout rows 4 apart (one block apart) then fall 8
+    // banks apart
+    static constexpr int RVR = NV * 2;            // bytes per raw v row
+    static constexpr int RVBLK = 4 * RVR + 32;    // bytes per block of 4 rows
+    __host__ __device__ static constexpr int raw_v(int row)
+    {
+        return (row >> 2) * RVBLK + (row & 3) * RVR;
+    }
+    static constexpr int SZ_RV = (RR + 3) / 4 * RVBLK;
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_QL = SZ_Q;               // Q lo
     static constexpr int OFF_X = SZ_QF;               // inversion scratch (scalar-gate fusion)
@@ -1229,8 +1237,9 @@ __global__ void __launch_bounds__(NW * 64)
     const int gb_off = (tid0 & (CH - 1)) * H;  // this lane's row of the gates and betas
     // Fused front end: the raw rows of the chunk at c0 (Lc rows) and the KC - 1 rows before
     // it go straight into LDS by LDS-DMA, one 16-byte piece per lane (a wave instruction
-    // fills 1 KiB): raw row rho of a region holds stream row c0 - (KC - 1) + rho, as
-    // [q | k] (RQK bytes) or v (RVB bytes, the last 16 of them padding). Rows before the
+    // fills up to 1 KiB): raw row rho of a region holds stream row c0 - (KC - 1) + rho: the
+    // q rows, then the k rows (RQ bytes each), and the v rows in padded blocks of 4 (raw_v).
+    // Rows before the
     // stream's first row (the carried window, at the first chunk) are stored before the
     // loop; rows at or past the chunk's end are never read and never used.
     constexpr int KC = C::KC;
@@ -1239,34 +1248,44 @@ __global__ void __launch_bounds__(NW * 64)
     // [rlo, rhi) of the chunk. Addresses are a uniform row base plus a 32-bit lane offset
     // (the host keeps RR row strides within 32 bits for these calls).
     // part 0: the v rows; part 1: the q|k rows
-    auto prefetch_raw = [&](int64_t c0, int Lc, bool with_q, int lane, int wave, int part) {
+    // A q|k instruction covers RPQ whole raw rows (1 KiB), a v instruction 4 rows (RVR
+    // bytes each: 1 KiB at 128 columns, the upper half of the lanes idle at 64). Each lane's
+    // byte offset from the instruction's first row is the same in every instruction.
+    constexpr int LPQ = DK / 8, RPQ = 64 / LPQ, NQI = (C::RR + RPQ - 1) / RPQ;
+    constexpr int LPVR = NV / 8, NVI = (C::RR + 3) / 4;
+    const int64_t ldb = ld * (int64_t)sizeof(TIN);
+    // this wave's instruction slots [i0, i1) of a part (the whole part by default)
+    auto prefetch_raw = [&](int64_t c0, int Lc, bool with_q, int lane, int wave, int part,
+                            int i0 = 0, int i1 = 1 << 20) {
         const int rlo = (int)max((int64_t)0, sbeg - (c0 - (KC - 1)));
         const int rhi = Lc + KC - 1;
-        const int ldi = (int)ld;
-        const TIN *qb = qg + (c0 - (KC - 1)) * ld, *kb = kg + (c0 - (KC - 1)) * ld;
-        // one tensor per wave instruction (a uniform row base, 32-bit lane offsets): q rows
-        // fill instructions [0, NQI), k rows [NQI, 2 NQI); lanes past the last raw row are
-        // masked, so a tensor's last instruction writes nothing beyond its rows
-        constexpr int QS = C::RQ / 16, NQI = (C::RR * QS + 63) / 64;
+        const bool full = rlo == 0 && rhi == C::RR;  // every raw row of the region
+        const int64_t r0 = c0 - (KC - 1);
         if (part == 1) {
+            const int lr = lane / LPQ;
+            const uint32_t off = (uint32_t)(lr * ldb) + (uint32_t)(lane % LPQ) * 16u;
+            // instructions [0, NQI) fill the q rows, [NQI, 2 NQI) the k rows
 #pragma unroll
             for (int i = 0; i < (2 * NQI + NW - 1) / NW; ++i) {
                 const int n = wave + NW * i;
                 const int t = n >= NQI, m = n - t * NQI;
-                const int slot = 64 * m + lane, rho = slot / QS, pc = slot % QS;
-                if (n < 2 * NQI && rho >= rlo && rho < rhi && (t || with_q))
-                    dma16((t ? kb : qb) + (rho * ldi + pc * 8),
+                const int row = RPQ * m + lr;
+                const bool ok = full ? row < C::RR : row >= rlo && row < rhi;
+                if (i >= i0 && i < i1 && n < 2 * NQI && (t || with_q) && ok)
+                    dma16((const char *)(t ? kg : qg) + (r0 + RPQ * m) * ldb, off,
                           lds_addr(smem + C::OFF_Q + C::raw_qk(t, 0) + 1024 * m));
             }
         } else if (!v_zero) {
-            const TIN *vb = vg + (c0 - (KC - 1)) * ld;
-            constexpr int VSL = C::VS + 1, NVI = (C::RR * VSL + 63) / 64;
+            const int lr = lane / LPVR;
+            const uint32_t off = (uint32_t)(lr * ldb) + (uint32_t)(lane % LPVR) * 16u;
 #pragma unroll
             for (int i = 0; i < (NVI + NW - 1) / NW; ++i) {
                 const int n = wave + NW * i;
-                const int slot = 64 * n + lane, rho = slot / VSL, pc = slot - rho * VSL;
-                if (n < NVI && pc < C::VS && rho >= rlo && rho < rhi)
-                    dma16(vb + (rho * ldi + pc * 8), lds_addr(smem + C::OFF_V + 1024 * n));
+                const int row = 4 * n + lr;
+                const bool ok = full ? row < C::RR : row >= rlo && row < rhi;
+                if (i >= i0 && i < i1 && n < NVI && lane < 4 * LPVR && ok)
+                    dma16((const char *)vg + (r0 + 4 * n) * ldb, off,
+                          lds_addr(smem + C::OFF_V + C::RVBLK * n));
             }
         }
     };
@@ -1307,19 +1326,41 @@ __global__ void __launch_bounds__(NW * 64)
                     *(TIN *)(smem + C::OFF_Q + C::raw_qk(ch >= DK, j) + (ch % DK) * 2) =
                         e < 0 ? (TIN)0.f : cw[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + e];
                 else
-                    *(TIN *)(smem + C::OFF_V + j * C::RVB + (ch - 2 * DK) * 2) =
+                    *(TIN *)(smem + C::OFF_V + C::raw_v(j) + (ch - 2 * DK) * 2) =
                         e < 0 ? (TIN)0.f : cw[(int64_t)v_channel(ch - 2 * DK) * Wn + e];
             }
         }
     }
-    auto prefetch = [&](int64_t c0, int Lc) {
+    // The raw rows of the next chunk go out in three groups spread over the state stage
+    // (group 0 at its start, 1 before P U, 2 before the state update): every workgroup
+    // runs the same steps at about the same time, and the rows of a whole chunk requested
+    // at once by every CU exceed what HBM delivers in that time, which would stall each
+    // wave on its own requests.
+    constexpr int SQ = (2 * NQI + NW - 1) / NW, SV = (NVI + NW - 1) / NW;
+    auto prefetch_group = [&](int64_t c0, int Lc, int grp) {
+        const bool with_q = c0 >= o_start;
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (grp == 0)
+            prefetch_raw(c0, Lc, with_q, lane, wave, 1, 0, (SQ + 1) / 2);
+        if (grp == 1) {
+            prefetch_raw(c0, Lc, with_q, lane, wave, 1, (SQ + 1) / 2, SQ);
+            prefetch_raw(c0, Lc, with_q, lane, wave, 0, 0, (SV + 1) / 2);
+        }
+        if (grp == 2)
+            prefetch_raw(c0, Lc, with_q, lane, wave, 0, (SV + 1) / 2, SV);
+    };
+    // rows = false: the gates only (the fused front end's rows then go by prefetch_group)
+    auto prefetch = [&](int64_t c0, int Lc, bool rows = true) {
         const int64_t roff = c0 * ld;
         const bool with_q = c0 >= o_start;  // q rows only feed o
         if constexpr (FRONT) {
-            const int lane = threadIdx.x & 63;
-            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            prefetch_raw(c0, Lc, with_q, lane, wave, 1);
-            prefetch_raw(c0, Lc, with_q, lane, wave, 0);
+            if (rows) {
+                const int lane = threadIdx.x & 63;
+                const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                prefetch_raw(c0, Lc, with_q, lane, wave, 1);
+                prefetch_raw(c0, Lc, with_q, lane, wave, 0);
+            }
         } else {
 #pragma unroll
             for (int it = 0; it < NQK; ++it)
@@ -1446,14 +1487,15 @@ __global__ void __launch_bounds__(NW * 64)
             }
             float v[4];
             if constexpr (FRONT) {
-                // raw rows 16 I + 4 g .. + KC + 2 of this column (raw row = chunk row + KC - 1)
+                // raw rows 16 I + 4 g .. + KC + 2 of this column (raw row = chunk row + KC - 1):
+                // block 4 I + g of the raw region and the next one
                 const unsigned char *rv = (const unsigned char *)Vs + (vc + c16) * 2 +
-                                          (16 * I + 4 * g4) * C::RVB;
+                                          (4 * I + g4) * C::RVBLK;
                 float xr[KC + 3];
 #pragma unroll
                 for (int u = 0; u < KC + 3; ++u)
-                    xr[u] = __uint_as_float((uint32_t)*(const unsigned short *)(rv + u * C::RVB)
-                                            << 16);
+                    xr[u] = __uint_as_float(
+                        (uint32_t)*(const unsigned short *)(rv + C::raw_v(u)) << 16);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float acc = 0.f;
@@ -1608,7 +1650,7 @@ __global__ void __launch_bounds__(NW * 64)
                                            (ch % DK) * 2);
                     else
                         wo[(int64_t)v_channel(ch - 2 * DK) * Wn + j] = *(const TIN *)(
-                            smem + zo + C::OFF_V + (r0 + j) * C::RVB + (ch - 2 * DK) * 2);
+                            smem + zo + C::OFF_V + C::raw_v(r0 + j) + (ch - 2 * DK) * 2);
                 }
             }
             __syncthreads();  // the raw q|k rows are read before the Q tile covers them
@@ -1721,8 +1763,9 @@ __global__ void __launch_bounds__(NW * 64)
 
         // ---- B: cumulative log-gate; lane r of every wave holds Gamma_r -----------------
         if constexpr (KDA) {
-            // per channel, in place in Gk: each thread scans CH/PARTS rows of one channel,
-            // then adds the totals of the parts above it
+            // per channel, in place in Gk, in log2 units (Gamma log2(e), for the exp2 of every
+            // decay factor): each thread scans CH/PARTS rows of one channel, then adds the
+            // totals of the parts above it
             // The parts' totals go through the Ms tile, unused until the preparation.
             constexpr int PARTS = NT / DK, RP = CH / PARTS;
             static_assert(PARTS * DK * 4 <= C::SZ_MS, "part totals");
@@ -1732,7 +1775,7 @@ __global__ void __launch_bounds__(NW * 64)
             float run = 0.f;
 #pragma unroll
             for (int j = 0; j < RP; ++j) {
-                run += Gk[(part * RP + j) * LDG + c];
+                run += Gk[(part * RP + j) * LDG + c] * kLog2e;
                 xs[j] = run;
             }
             tot[part * DK + c] = run;
@@ -1860,13 +1903,14 @@ __global__ void __launch_bounds__(NW * 64)
                     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(gs_ + c0 + 16);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float ea = __expf(r0[i] - b0[i]), ea1 = __expf(r1[i] - b1[i]);
+                        const float ea = __builtin_amdgcn_exp2f(r0[i] - b0[i]),
+                                    ea1 = __builtin_amdgcn_exp2f(r1[i] - b1[i]);
                         fk[i] = (T)(kI[i] * ea);
                         fk[4 + i] = (T)(kI[4 + i] * ea1);
                         fq[i] = (T)((float)fq[i] * ea);
                         fq[4 + i] = (T)((float)fq[4 + i] * ea1);
-                        fb[i] = (T)(kJ[i] * __expf(b0[i] - s0[i]));
-                        fb[4 + i] = (T)(kJ[4 + i] * __expf(b1[i] - s1[i]));
+                        fb[i] = (T)(kJ[i] * __builtin_amdgcn_exp2f(b0[i] - s0[i]));
+                        fb[4 + i] = (T)(kJ[4 + i] * __builtin_amdgcn_exp2f(b1[i] - s1[i]));
                     }
                     if (do_m)
                         mma(am, fk, fb);
@@ -1875,7 +1919,8 @@ __global__ void __launch_bounds__(NW * 64)
                 }
             } else {
                 // diagonal block: mid-block reference m = 16I + 8, so each factor spans at
-                // most 8 tokens of decay (exponents clamped at 80); the gated operands can
+                // most 8 tokens of decay (exponents clamped at 80, 80 log2(e) in the log2
+                // units of Gk); the gated operands can
                 // exceed the fp16 range, so they go in fp32 range: fp32 MFMA for fp32 tiles,
                 // bf16 hi + lo pairs (about 16 mantissa bits) for fp16 tiles
                 const float *gm = Gk + (16 * I + 8) * LDG;
@@ -1894,10 +1939,10 @@ __global__ void __launch_bounds__(NW * 64)
                         for (int i = 0; i < 8; ++i) {
                             const int ch = c0 + (i < 4 ? i : 12 + i);
                             const float d = grs[ch] - gm[ch];
-                            const float ea = __expf(fminf(d, 80.f));
+                            const float ea = __builtin_amdgcn_exp2f(fminf(d, kExpCap));
                             const float kx = (float)xk[i] + (C::KLO ? (float)xkl[i] : 0.f);
                             const float kv = kx * ea, qv = (float)xq[i] * ea;
-                            const float bv = kx * __expf(fminf(-d, 80.f));
+                            const float bv = kx * __builtin_amdgcn_exp2f(fminf(-d, kExpCap));
                             kh_[i] = (bf16)kv;
                             kl_[i] = (bf16)(kv - (float)kh_[i]);
                             qh_[i] = (bf16)qv;
@@ -1921,8 +1966,8 @@ __global__ void __launch_bounds__(NW * 64)
                     for (int j4 = 0; j4 < DK / 4; ++j4) {
                         const int ch = 4 * j4 + g4;
                         const float d = grs[ch] - gm[ch];
-                        const float ea = __expf(fminf(d, 80.f));
-                        const float bv = (float)kr[ch] * __expf(fminf(-d, 80.f));
+                        const float ea = __builtin_amdgcn_exp2f(fminf(d, kExpCap));
+                        const float bv = (float)kr[ch] * __builtin_amdgcn_exp2f(fminf(-d, kExpCap));
                         am = __builtin_amdgcn_mfma_f32_16x16x4f32((float)kr[ch] * ea, bv, am, 0,
                                                                   0, 0);
                         ap = __builtin_amdgcn_mfma_f32_16x16x4f32((float)qr[ch] * ea, bv, ap, 0,
@@ -2008,9 +2053,19 @@ __global__ void __launch_bounds__(NW * 64)
             typedef T T4 __attribute__((ext_vector_type(4)));
             constexpr int NI = CH * (DK / 4) / NT;
             static_assert(NI * NT == CH * (DK / 4) && NT % (DK / 4) == 0, "rescale map");
+            static_assert(DK <= 2 * CH, "e^(G_C) fits over a and a_C / a");
             const int c0 = (tid % (DK / 4)) * 4, r0 = tid / (DK / 4);
             // (k = hi + lo; the K lo tile then takes the lo half of K e^(G_C - G))
             const f32x4 gcv = *reinterpret_cast<const f32x4 *>(Gk + (CH - 1) * LDG + c0);
+            // e^(G_C) per channel, for the state update, over a and a_C / a (which the
+            // per-channel gate does not use)
+            if (r0 == 0) {
+                f32x4 e;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    e[i] = __builtin_amdgcn_exp2f(gcv[i]);
+                *reinterpret_cast<f32x4 *>(ea + c0) = e;
+            }
             T4 kv[NI], klv[NI], qv[NI];
             f32x4 gv[NI];
 #pragma unroll
@@ -2030,9 +2085,9 @@ __global__ void __launch_bounds__(NW * 64)
                 T4 kd, kdl, ke, qe;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = __expf(gv[it][i]);
+                    const float e = __builtin_amdgcn_exp2f(gv[it][i]);
                     const float kx = (float)kv[it][i] + (C::KLO ? (float)klv[it][i] : 0.f);
-                    const float d = kx * __expf(gcv[i] - gv[it][i]);
+                    const float d = kx * __builtin_amdgcn_exp2f(gcv[i] - gv[it][i]);
                     kd[i] = (T)d;
                     kdl[i] = (T)(d - (float)kd[i]);
                     ke[i] = (T)(kx * e);
@@ -2056,8 +2111,12 @@ __global__ void __launch_bounds__(NW * 64)
             kh_qh(0, xl, ol, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
             __syncthreads();
         }
-        if (cs + CH < end)
-            prefetch(cs + CH, (int)min((int64_t)CH, end - cs - CH));
+        const bool pf = cs + CH < end;  // the next chunk's rows and gates
+        const int pfL = (int)min((int64_t)CH, end - cs - CH);
+        if (pf)
+            prefetch(cs + CH, pfL, false);
+        if (FRONT && pf)
+            prefetch_group(cs + CH, pfL, 0);
         if constexpr (GATE) {
             if (write_o)
                 load_z(cs, L, lane, wave);
@@ -2108,6 +2167,8 @@ __global__ void __launch_bounds__(NW * 64)
                 if constexpr (SPLIT)
                     split4(u[I], uhs[I], uls[I]);
             }
+            if (FRONT && pf)
+                prefetch_group(cs + CH, pfL, 1);
             // O += P U with P and U as hi + lo pairs
             if (write_o) {
                 frag uh[2], ul[2];
@@ -2145,6 +2206,8 @@ __global__ void __launch_bounds__(NW * 64)
                     }
                 }
             }
+            if (FRONT && pf)
+                prefetch_group(cs + CH, pfL, 2);
             // h <- a_C h + K^T (diag(a_C / a) U); per-channel gate:
             // h <- diag(e^G_C) h + (K . e^(G_C - G))^T U
             if constexpr (!KDA) {
@@ -2164,10 +2227,10 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb) {
                 if constexpr (KDA) {
-                    const float *gcr = Gk + (CH - 1) * LDG + 16 * mb + 4 * g4;
+                    const f32x4 ec = *reinterpret_cast<const f32x4 *>(ea + 16 * mb + 4 * g4);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        hs[cb][mb][i] *= __expf(gcr[i]);
+                        hs[cb][mb][i] *= ec[i];
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -2540,6 +2603,38 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
         hipLaunchKernelGGL((combine_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Channel maximum of the per-key-channel log-gates: 8 lanes per (token, head), each
+// taking every eighth 4-channel group of the row, then a maximum over the 8.
+__global__ void __launch_bounds__(256) gate_max_kernel(const GateMaxArgs a)
+{
+    if (debug_stop(a.dbg))
+        return;
+    const int64_t pair = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int l = threadIdx.x & 7;
+    if (pair >= a.n)  // whole groups of 8 lanes leave together
+        return;
+    const float *row = a.g + pair * a.dk;
+    float m = -__builtin_inff();
+    for (int c = 4 * l; c < a.dk; c += 32) {
+        const uint4 u = load_stream16(row + c);
+        m = fmaxf(m, fmaxf(fmaxf(__uint_as_float(u.x), __uint_as_float(u.y)),
+                           fmaxf(__uint_as_float(u.z), __uint_as_float(u.w))));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    if (l == 0)
+        a.out[pair] = m;
+}
+
+hipError_t launch_gate_max(const GateMaxArgs &a, hipStream_t s)
+{
+    if (a.n < 1 || a.dk < 4 || a.dk % 4 || (a.n + 31) / 32 > (int64_t)INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gate_max_kernel, dim3((unsigned)((a.n + 31) / 32)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

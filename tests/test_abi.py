@@ -91,13 +91,19 @@ def test_segment_plan():
     kda = B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA
     wk = B.gdn_workspace_bytes(pk, 1, 16384, kda)
     assert B.gdn_segments(pk, kda, 1, 16384, wk) >= 3
-    # A GDN call with unit keys may start every segment warm, so its plan keeps segment 0
-    # and the warm jobs of all (stream, head) pairs in one round: S <= CUs / (streams *
-    # heads) = 8. A KDA call always chains its segments and has no such cap: on 256 CUs
-    # its plan is 9 segments of 40, 27 x 7 and 27 chunks.
+    # A call with unit keys (L2 in the call) may start every segment warm, so its plan
+    # keeps segment 0 and the warm jobs of all (stream, head) pairs in one round: S <= CUs
+    # / (streams * heads) = 8 on 256 CUs. Without L2 the segments always chain, with no such
+    # cap: the KDA plan is then 9 segments of 40, 27 x 7 and 27 chunks.
     S_g, _, _ = B.gdn_segment_plan(pk, B.GDN_KIND_SINGLE, 1, 16384, wk)
     assert 3 <= S_g <= 8
-    assert B.gdn_segment_plan(pk, kda, 1, 16384, wk) == (9, 40 * 64, 27 * 64)
+    assert B.gdn_segment_plan(pk, kda, 1, 16384, wk) == (8, 39 * 64, 31 * 64)
+    pn = B.params(32, 128, 128, conv_k=4, eps=-1.0)
+    wn = B.gdn_workspace_bytes(pn, 1, 16384, kda)
+    assert B.gdn_segment_plan(pn, kda, 1, 16384, wn) == (9, 40 * 64, 27 * 64)
+    # the warm-start plan of a KDA call reads each token's largest channel log-gate: N * H
+    # floats more than the same call without L2 (whose segments never start warm)
+    assert wk - wn == 16384 * 32 * 4
     assert B.gdn_segments(pk, B.GDN_KIND_VARLEN | B.GDN_PLAN_KDA, 1, 16384, wk) == 0
     # no compiled instance: the status of the refused call
     pr = B.params(4, 64, 128, dtype=B.GDN_BF16)

@@ -258,20 +258,40 @@ def test_segmented_scan_fast_decay(case):
     print("%s seg err(o)=%.3g err(h)=%.3g" % (spec.name, *e_seg), flush=True)
 
 
-def test_segmented_scan_mixed_warm_and_chain():
+def warm_flags(call, S):
+    """The warm-mode flag of each head of a single-stream segmented call: a float the
+    library's warm-start plan leaves in the workspace's segment area (after 3S - 5 state
+    slots and S x H transition flags), 1.0 where the head's segments start warm."""
+    spec = call.spec
+    slot = spec.H * spec.dk * spec.dv
+    base = (3 * S - 5) * slot + S * spec.H
+    f = call.ws[:(base + spec.H) * 4].view(torch.float32)
+    return [float(x) for x in f[base:base + spec.H].cpu()]
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_segmented_scan_mixed_warm_and_chain(gate):
     """Heads 0-1 decay slowly (their segments start from the chain of segment maps), heads
     2-3 fast (their segments start warm, from h = 0 a few chunks early): one call holds both
-    modes, and every head matches the oracle and the serial scan."""
+    modes, and every head matches the oracle and the serial scan. The per-key-channel gate
+    bounds a token's decay by its largest channel log-gate; its log-gates are scaled by 4 so
+    that the warm windows fit in segments of a 8192-token stream."""
     import dataclasses
-    fast = spec_small(2, lengths=[4096], H=4, seed=58)
+    from gated_delta_rule_depthwise_amd import binding as B
+    fast = spec_small(2 if gate == "gdn" else 5, lengths=[4096 if gate == "gdn" else 8192],
+                      H=4, seed=58)
     slow = dataclasses.replace(fast, gate_dist="slow")
     inp = inputs.make(fast)
+    if gate == "kda":
+        inp["g"] *= 4.0
     inp["g"][:, :2] = inputs.make(slow)["g"][:, :2]
     seg = run_gpu(inp)
     ser = run_gpu(inp, segmented=False)
+    S = B.gdn_segments(seg.params, seg.plan_kind, 1, fast.N, seg.ws_bytes)
+    assert S >= 3
+    assert warm_flags(seg, S) == [0.0, 0.0, 1.0, 1.0]
     ref = run_oracle(inp)
     compare(seg, ref)
     compare(ser, ref)
     assert rel_err(seg.o[:fast.N].cpu().numpy(), ser.o[:fast.N].cpu().numpy()) <= 2e-2
     assert rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy()) <= 2e-2
-
