@@ -935,6 +935,34 @@ __device__ __forceinline__ f32x8 ld_frag_t_qk(const float *X, int k0, int n0, in
 }
 
 
+// fp32 -> fp16 hi + lo: hi = x rounded to fp16, lo = (x - hi) rounded to fp16. hi is one
+// packed conversion per pair; x - hi comes from v_fma_mix_f32, which reads x as fp32 and hi
+// straight from its fp16 half (the difference is exact in fp32), and the lo pair is one more
+// packed conversion: the same bits as converting hi back, subtracting and converting again,
+// in 2 instructions per element instead of 4. (Full-register results only: an instruction
+// that writes half a register leaves a forwarding hazard the compiler cannot see in asm.)
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){x0, x1}, f16x2));
+    float d0, d1;
+    asm("v_fma_mix_f32 %0, %2, 1.0, -%4 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mix_f32 %1, %3, 1.0, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "=&v"(d0), "=&v"(d1)
+        : "v"(x0), "v"(x1), "v"(hi));
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){d0, d1}, f16x2));
+}
+__device__ __forceinline__ void split4(const f32x4 &x, f16x4 &hi, f16x4 &lo)
+{
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    hi = __builtin_bit_cast(f16x4, (u32x2){h0, h1});
+    lo = __builtin_bit_cast(f16x4, (u32x2){l0, l1});
+}
+
 // d += A B for 16x16 blocks with a 16-deep contraction in about fp32 accuracy:
 // a[i] = A[c][4g+i], b[i] = B[4g+i][c] (lane = 16g + c); d in the same D layout.
 template <bool SPLIT>
@@ -1002,11 +1030,7 @@ __device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, 
                                          const f32x4 &b, int lane)
 {
     f16x4 bh, bl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bh[i] = (f16)b[i];
-        bl[i] = (f16)(b[i] - (float)bh[i]);
-    }
+    split4(b, bh, bl);
     mm16_pre(d, X, ld, I, J, bh, bl, lane);
 }
 __device__ __forceinline__ void mm16_pre(f32x4 &d, const float *X, int ld, int I, int J,
@@ -1019,29 +1043,20 @@ __device__ __forceinline__ void mm16_pre(f32x4 &d, const float *X, int ld, int I
 }
 
 // fp32 D-layout value -> fp16 hi + lo
-__device__ __forceinline__ void split4(const f32x4 &x, f16x4 &hi, f16x4 &lo)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (f16)x[i];
-        lo[i] = (f16)(x[i] - (float)hi[i]);
-    }
-}
 
 // hi + lo operand pair of the B operand built from two D-layout accumulators
 template <typename T>
 __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
                                            typename Tr<T>::frag &hi, typename Tr<T>::frag &lo)
 {
-    hi = pack<T>(d0, d1);
     if constexpr (sizeof(T) == 2) {
-        f32x4 r0, r1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            r0[i] = d0[i] - (float)hi[i];
-            r1[i] = d1[i] - (float)hi[4 + i];
-        }
-        lo = pack<T>(r0, r1);
+        f16x4 h0, l0, h1, l1;
+        split4(d0, h0, l0);
+        split4(d1, h1, l1);
+        hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        hi = pack<T>(d0, d1);
     }
 }
 
@@ -1468,9 +1483,14 @@ __global__ void __launch_bounds__(NW * 64)
     // Fused front end: V is the conv + SiLU of the raw v rows (Vs is then the raw region),
     // computed here in fp32 for this lane's D-layout rows 16 I + 4 g + i and column; rows
     // at or past the chunk's end (Lc rows) are 0. Q h takes q's fp16 hi part.
-    auto kh_qh = [&](int cb, f32x4 (&x)[4], f32x4 (&o)[4], const float (&ar)[4][4],
-                     const T *Ks, const void *Qs, const void *Vs, int wave, int lane, int g4,
-                     int c16, int Lc) {
+    // Fused front end: WO (this chunk computes o, i.e. Q h) is a compile-time copy of each
+    // case, and a row block's fragment reads are all issued before its products with no
+    // branch between. (The register-path instances, which hold the next chunk's rows in
+    // registers, interleave reads and products: batching them would spill.)
+    auto kh_qh_wo = [&](auto wo, int cb, f32x4 (&x)[4], f32x4 (&o)[4],
+                        const float (&ar)[4][4], const T *Ks, const void *Qs, const void *Vs,
+                        int wave, int lane, int g4, int c16, int Lc) {
+        constexpr bool WO = decltype(wo)::value;
         const int vc = 16 * (wave * NCB + cb);  // this block's columns within Vs
         frag hf[DK / 32];
 #pragma unroll
@@ -1479,11 +1499,27 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 kh = zero4(), qh = zero4();
+            if constexpr (FRONT) {
+                frag kf[DK / 32], qf[WO ? DK / 32 : 1];
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                mma(kh, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), hf[kb]);
-                if (write_o)
-                    mma(qh, ld_frag_qk<DK>((const T *)Qs, 16 * I, 32 * kb, lane), hf[kb]);
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    kf[kb] = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
+                    if constexpr (WO)
+                        qf[kb] = ld_frag_qk<DK>((const T *)Qs, 16 * I, 32 * kb, lane);
+                }
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    mma(kh, kf[kb], hf[kb]);
+                    if constexpr (WO)
+                        mma(qh, qf[kb], hf[kb]);
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    mma(kh, ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane), hf[kb]);
+                    if (write_o)
+                        mma(qh, ld_frag_qk<DK>((const T *)Qs, 16 * I, 32 * kb, lane), hf[kb]);
+                }
             }
             float v[4];
             if constexpr (FRONT) {
@@ -1516,6 +1552,14 @@ __global__ void __launch_bounds__(NW * 64)
                 o[I][i] = arr * qh[i];
             }
         }
+    };
+    auto kh_qh = [&](int cb, f32x4 (&x)[4], f32x4 (&o)[4], const float (&ar)[4][4],
+                     const T *Ks, const void *Qs, const void *Vs, int wave, int lane, int g4,
+                     int c16, int Lc) {
+        if (!FRONT || write_o)
+            kh_qh_wo(std::true_type{}, cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16, Lc);
+        else
+            kh_qh_wo(std::false_type{}, cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16, Lc);
     };
 
     // A transition job stops once its transition has underflowed. Token t multiplies it by
@@ -2083,15 +2127,24 @@ __global__ void __launch_bounds__(NW * 64)
                 const int r = r0 + it * (NT / (DK / 4));
                 const int off = QK<T, DK>::at(r, c0 / 4);
                 T4 kd, kdl, ke, qe;
+                f32x4 dv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float e = __builtin_amdgcn_exp2f(gv[it][i]);
                     const float kx = (float)kv[it][i] + (C::KLO ? (float)klv[it][i] : 0.f);
-                    const float d = kx * __builtin_amdgcn_exp2f(gcv[i] - gv[it][i]);
-                    kd[i] = (T)d;
-                    kdl[i] = (T)(d - (float)kd[i]);
+                    dv[i] = kx * __builtin_amdgcn_exp2f(gcv[i] - gv[it][i]);
                     ke[i] = (T)(kx * e);
                     qe[i] = (T)((float)qv[it][i] * e);
+                }
+                if constexpr (SPLIT) {
+                    f16x4 h4, l4;
+                    split4(dv, h4, l4);
+                    kd = __builtin_bit_cast(T4, h4);
+                    kdl = __builtin_bit_cast(T4, l4);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        kd[i] = dv[i];
                 }
                 *reinterpret_cast<T4 *>(Kd + off) = kd;
                 if constexpr (C::KLO)
