@@ -366,9 +366,17 @@ __device__ __forceinline__ int find_stream(const Streams &s, int64_t t)
 
 constexpr int CH = 64;  // chunk length
 
+// Warm starts: a segment starts from h = 0 once the chunks before it bound the norm of
+// their transition by e^kWarmLogBound. The state it drops is then at most e^-40 (< 2^-57)
+// of the state's norm at the start of that window: far below the fp32 rounding (2^-24) of
+// every value the state feeds, unless the state shrank by more than 2^33 across the window.
+// (A transition job's early stop, which substitutes an exact zero, waits for e^-110: below
+// half the smallest fp32 subnormal.)
+constexpr float kWarmLogBound = -40.f;
+
 // One workgroup per (stream, head); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
 // it walks back from the boundary over the previous segment's chunks, four at a time (lane l
-// reading row l of each), until their log-gates sum below -110.
+// reading row l of each), until their log-gates sum below kWarmLogBound.
 __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
 {
     __shared__ int all_ok;  // cleared by a wave that finds a boundary without a window
@@ -406,7 +414,7 @@ __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
                     } else {
                         acc += sum;
                         ++w;
-                        if (acc < -110.f)
+                        if (acc < kWarmLogBound)
                             done = 1;
                     }
                 }
