@@ -264,9 +264,8 @@ def main() -> int:
         else:
             parts.append("chunk_kernel")
         if segs:
-            parts.append("segmented scan of %d segments: %swarm_plan_kernel + pass 1 + "
-                         "combine_kernel + pass 2; warm starts where the gates allow"
-                         % (segs, "gate_max_kernel + " if spec.gate == "kda" else ""))
+            parts.append("segmented scan of %d segments: warm_boundary_kernel + pass 1 + "
+                         "combine_kernel + pass 2; warm starts where the gates allow" % segs)
         if "gate" in avg_ms:
             parts.append("gate_kernel")
         kname = "the whole call: " + "; ".join(parts)

@@ -336,20 +336,13 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
 
 // the segment states, and for a fused front end without shared windows the windows that
 // warm-started streams stage for the combine kernel
-size_t seg_state_bytes(const gdn_params *p, int kda, int32_t B, int S)
-{
-    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S, p->H};
-    return align_up((size_t)lay.total() * sizeof(float)) +
-           (win_shared(p, kda) ? 0 : win_bytes(p, kda, B));
-}
-// ... and with the per-key-channel gate, each token's largest channel log-gate ([N][H]
-// floats) for the warm-start plan
-size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S, int64_t N)
+size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S)
 {
     if (S < 3)
         return 0;
-    return seg_state_bytes(p, kda, B, S) +
-           (kda && warm_capable(p) ? align_up((size_t)N * p->H * sizeof(float)) : 0);
+    const gdn::SegLayout lay{(int64_t)p->H * p->dk * p->dv, B, S, p->H};
+    return align_up((size_t)lay.total() * sizeof(float)) +
+           (win_shared(p, kda) ? 0 : win_bytes(p, kda, B));
 }
 
 struct Call {
@@ -413,7 +406,7 @@ int run(const Call &c)
         sp = seg_plan(p, c.kda, c.st.B, c.st.tps, p->dv / sh.nv, cu_count());
         warm = sp.S && warm_capable(p);
         const int64_t jobs1 = warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
-        if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.kda, c.st.B, sp.S, c.N) ||
+        if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.kda, c.st.B, sp.S) ||
                      grid * jobs1 > (int64_t)INT32_MAX))
             sp = SegPlan{0, 0, 0}, warm = false;
     }
@@ -472,19 +465,8 @@ int run(const Call &c)
     gdn::WarmArgs wa{};
     wa.dbg = dbg;
     ca.warm = warm;
-    // per-key-channel gate: the plan reads each token's largest channel log-gate (a bound
-    // on the norm of the token's transition), from a small kernel ahead of it
-    gdn::GateMaxArgs gm{};
     if (ca.warm) {
         wa.g = c.g, wa.beta = c.beta, wa.st = c.st, wa.H = p->H;
-        if (c.kda) {
-            gm.dbg = dbg;
-            gm.g = c.g;
-            gm.out = (float *)((char *)seg_ws + seg_state_bytes(p, c.kda, c.st.B, sp.S));
-            gm.n = c.N * p->H;
-            gm.dk = p->dk;
-            wa.g = gm.out;
-        }
         wa.nseg = sp.S, wa.seg0_len = sp.seg0_len, wa.seg_len = sp.seg_len;
         wa.seg_ws = seg_ws, wa.lay = lay;
     }
@@ -566,10 +548,8 @@ int run(const Call &c)
             ca.seg0_len = sp.seg0_len;
             ca.seg_len = sp.seg_len;
             ca.seg_ws = seg_ws;
-            if (ca.warm && c.kda && gdn::launch_gate_max(gm, c.stream) != hipSuccess)
-                return GDN_E_HIP;
             if (ca.warm && (c.kda || !(front && !fused_fe))) {
-                if (gdn::launch_warm_plan(wa, c.stream) != hipSuccess)
+                if (gdn::launch_warm_boundaries(wa, c.kda, p->dk, c.stream) != hipSuccess)
                     return GDN_E_HIP;
             }
             ca.pass = 1;
@@ -879,7 +859,7 @@ size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, i
     const Shape sh = pick_shape(p, kda);
     if (kind != GDN_KIND_VARLEN && p->dk == p->dv && sh.nv > 0 &&
         (int64_t)B * p->H * (p->dv / sh.nv) < cu_count() && max_tokens / B >= 3 * 64)
-        seg = seg_bytes(p, kda, B, kMaxSeg, max_tokens);
+        seg = seg_bytes(p, kda, B, kMaxSeg);
     if (kind == GDN_KIND_VARLEN)
         seg = order_bytes(B);
     return front_bytes(p, kda, max_tokens, B) + seg;
@@ -905,7 +885,7 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
     const Shape sh = pick_shape(p, kda);
     const SegPlan sp = seg_plan(p, kda, B, t_per_stream, p->dv / sh.nv, cu_count());
     const size_t need = front_bytes(p, kda, (int64_t)B * t_per_stream, B);
-    if (!sp.S || ws_bytes < need + seg_bytes(p, kda, B, sp.S, (int64_t)B * t_per_stream))
+    if (!sp.S || ws_bytes < need + seg_bytes(p, kda, B, sp.S))
         return 0;
     if (seg0_tokens)
         *seg0_tokens = sp.seg0_len;

@@ -30,8 +30,8 @@ struct GateArgs {
 // Slots of the segmented scan, each one [H][dk][dv] fp32 (dk == dv): H(b, s), s = 1..S-1;
 // B(b, s) and A(b, s), s = 1..S-2; then one flag per (b, s, head), 1.0 when the transition
 // job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0; then the
-// warm-start plan: per (b, head) the mode (1.0: every segment starts warm, no chain) and
-// per (b, s, head) the chunks of warm-up before segment s.
+// warm-start plan: per (b, s, head) the chunks of warm-up before segment s (0: none found;
+// a (stream, head) runs warm when every s = 1..S-1 found one).
 struct SegLayout {
     int64_t slot;  // floats per slot
     int32_t B, S, H;
@@ -51,20 +51,27 @@ struct SegLayout {
     {
         return (int64_t)B * (3 * S - 5) * slot + ((int64_t)b * S + s) * H + head;
     }
-    __host__ __device__ int64_t warm_mode(int b, int head) const
-    {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H + (int64_t)b * H + head;
-    }
     __host__ __device__ int64_t warm_chunks(int b, int s, int head) const
     {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H + (int64_t)B * H +
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H +
                ((int64_t)b * S + s) * H + head;
     }
     __host__ __device__ int64_t total() const
     {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * (2 * S + 1) * H;
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H;
     }
 };
+
+// Warm mode of a (stream, head): every boundary s = 1..S-1 found its window (the plan leaves
+// a positive chunk count, 0 where it found none).
+__device__ __forceinline__ bool warm_head(const float *seg_ws, const SegLayout &lay, int b,
+                                          int head)
+{
+    bool ok = true;
+    for (int s = 1; s < lay.S; ++s)
+        ok = ok && seg_ws[lay.warm_chunks(b, s, head)] > 0.f;
+    return ok;
+}
 
 // h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).
 // (Stream, head) pairs in warm mode have no chain: their last segment ran in the first
@@ -104,7 +111,7 @@ struct WindowCopyArgs {
 // Warm-start plan of a segmented call: per (stream, head), each chunk's total log-gate and
 // whether its betas lie in [0, 1.9]; per segment boundary the fewest chunks before it whose
 // log-gates sum below -40; warm mode when every boundary has such a window inside the
-// previous segment. With the per-key-channel gate, g holds each token's largest channel
+// previous segment. With the per-key-channel gate a token's bound is its largest channel
 // log-gate (the norm of a token's transition is at most its largest channel decay).
 struct WarmArgs {
     const int32_t *dbg;     // debug validation status (device), or nullptr
@@ -256,17 +263,10 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s);
-hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s);
-// Largest per-key-channel log-gate of each (token, head): out[t][h] = max_c g[t][h][c] over
-// n = N * H pairs; the warm-start plan of the per-channel gate runs on it.
-struct GateMaxArgs {
-    const int32_t *dbg;  // debug validation status (device), or nullptr
-    const float *g;      // [N][H][dk]
-    float *out;          // [N][H]
-    int64_t n;
-    int32_t dk;
-};
-hipError_t launch_gate_max(const GateMaxArgs &a, hipStream_t s);
+// The same plan with one workgroup per (stream, head, boundary), reading only the gates of
+// each boundary's window; with the per-key-channel gate (kda) a token's bound is its
+// largest channel log-gate (g is then [N][H][dk]).
+hipError_t launch_warm_boundaries(const WarmArgs &a, int kda, int dk, hipStream_t s);
 hipError_t launch_decode(int dtype, int kda, const DecodeArgs &a, hipStream_t s);
 // q/k windows of a decode step with Hqk < H (several workgroups read them): shifted after
 // the step by a pass of its own

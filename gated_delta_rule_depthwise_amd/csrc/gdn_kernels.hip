@@ -374,20 +374,17 @@ constexpr int CH = 64;  // chunk length
 // half the smallest fp32 subnormal.)
 constexpr float kWarmLogBound = -40.f;
 
-// One workgroup per (stream, head); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
+// The plan of one (stream, head) in one workgroup (extra workgroups of the float32 front
+// kernel); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
 // it walks back from the boundary over the previous segment's chunks, four at a time (lane l
 // reading row l of each), until their log-gates sum below kWarmLogBound.
 __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
 {
-    __shared__ int all_ok;  // cleared by a wave that finds a boundary without a window
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     const int S = a.nseg;
-    if (tid == 0)
-        all_ok = 1;
-    __syncthreads();
     for (int s = wv + 1; s <= S - 1; s += 4) {  // uniform per wave
         const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
         const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
@@ -420,22 +417,117 @@ __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
                 }
             }
         }
-        if (lane == 0) {
+        if (lane == 0)
             a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
-            if (done != 1)
-                all_ok = 0;
-        }
     }
-    __syncthreads();
-    if (tid == 0)
-        a.seg_ws[a.lay.warm_mode(b, head)] = all_ok ? 1.f : 0.f;
 }
 
-__global__ void __launch_bounds__(256) warm_plan_kernel(const WarmArgs a)
+// One workgroup per (stream, head, boundary s = 1..S-1): it walks back from the boundary over
+// the previous segment's chunks, RC chunks per round (all their gates requested at once),
+// and records the fewest chunks whose
+// bounds sum below kWarmLogBound (0: none inside the previous segment, or a beta outside
+// [0, 1.9] first). A token's bound is its log-gate, or with the per-key-channel gate its
+// largest channel log-gate: lanes take a share of a row's channels, a maximum over them,
+// then a sum over the chunk's rows. Only the gates of the window are read.
+template <bool KDA, int DK>
+__global__ void __launch_bounds__(KDA ? 1024 : 256) warm_boundary_kernel(const WarmArgs a)
 {
     if (debug_stop(a.dbg))
         return;
-    warm_plan_block(a, blockIdx.x);
+    // per round: GDN 4 chunks on 4 waves (one per wave, a row per lane); KDA 8 chunks on 16
+    // waves, two per chunk, 32 rows per wave read 8 rows per instruction with 8 lanes per
+    // row (whole 128-byte lines), 4 row groups of 8
+    constexpr int NWV = KDA ? 16 : 4, RC = KDA ? 8 : 4;
+    constexpr int PPL = KDA ? DK / 32 : 1;  // 16-byte pieces of a row per lane (KDA)
+    __shared__ float part[NWV];
+    __shared__ int bad_beta[NWV];
+    const int S = a.nseg;
+    const int bh = blockIdx.x / (S - 1), s = blockIdx.x - bh * (S - 1) + 1;
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int64_t start, end;
+    stream_bounds(a.st, b, start, end);
+    const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
+    const int64_t cp = s == 1 ? 0 : (a.seg0_len + (int64_t)(s - 2) * a.seg_len) / CH;
+    float acc = 0.f;
+    int w = 0, done = 0;  // done: 1 found, -1 not possible (uniform over the workgroup)
+    for (int64_t ctop = cs - 1; ctop >= cp && !done; ctop -= RC) {
+        float gv = 0.f;
+        bool bad_row = false;
+        if constexpr (KDA) {
+            const int64_t c = ctop - (wv >> 1);
+            const int r0 = (wv & 1) * 32 + (lane >> 3);  // + 8 rg
+            uint4 u[4][PPL];
+            bool in[4];
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int64_t r = start + c * CH + r0 + 8 * rg;
+                in[rg] = c >= cp && r < end;
+                const float *row = a.g + (r * a.H + head) * DK + 4 * (lane & 7);
+#pragma unroll
+                for (int q = 0; q < PPL; ++q)
+                    u[rg][q] = in[rg] ? load_stream16(row + 32 * q) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                float m = -__builtin_inff();
+#pragma unroll
+                for (int q = 0; q < PPL; ++q)
+                    m = fmaxf(m, fmaxf(fmaxf(__uint_as_float(u[rg][q].x),
+                                             __uint_as_float(u[rg][q].y)),
+                                       fmaxf(__uint_as_float(u[rg][q].z),
+                                             __uint_as_float(u[rg][q].w))));
+                m = fmaxf(m, __shfl_xor(m, 1));
+                m = fmaxf(m, __shfl_xor(m, 2));
+                m = fmaxf(m, __shfl_xor(m, 4));  // the row's largest channel log-gate
+                if ((lane & 7) == 0 && in[rg]) {
+                    gv += m;
+                    const float bv = a.beta[(start + c * CH + r0 + 8 * rg) * a.H + head];
+                    bad_row = bad_row || !(bv >= 0.f && bv <= 1.9f);
+                }
+            }
+        } else {
+            const int64_t c = ctop - wv;
+            const int64_t r = start + c * CH + lane;
+            if (c >= cp && r < end) {
+                gv = a.g[r * a.H + head];
+                const float bv = a.beta[r * a.H + head];
+                bad_row = !(bv >= 0.f && bv <= 1.9f);
+            }
+        }
+        const float sum = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gv)), 63));
+        const bool bad = __ballot(bad_row) != 0;
+        if (lane == 0) {
+            part[wv] = sum;
+            bad_beta[wv] = bad;
+        }
+        __syncthreads();
+        if (tid == 0) {
+#pragma unroll
+            for (int jj = 0; jj < RC; ++jj) {
+                const int64_t cc = ctop - jj;
+                const float csum = KDA ? part[2 * jj] + part[2 * jj + 1] : part[jj];
+                const int cbad = KDA ? bad_beta[2 * jj] | bad_beta[2 * jj + 1] : bad_beta[jj];
+                if (!done && cc >= cp) {
+                    if (cbad) {
+                        done = -1;
+                    } else {
+                        acc += csum;
+                        ++w;
+                        if (acc < kWarmLogBound)
+                            done = 1;
+                    }
+                }
+            }
+            bad_beta[0] = done;  // broadcast
+        }
+        __syncthreads();
+        done = bad_beta[0];
+        __syncthreads();
+    }
+    if (tid == 0)
+        a.seg_ws[a.lay.warm_chunks(b, s, head)] = done == 1 ? (float)w : 0.f;
 }
 
 template <typename T, typename TOUT, int K>
@@ -1149,7 +1241,7 @@ __global__ void __launch_bounds__(NW * 64)
         const int S = a.nseg;
         // warm mode of this (stream, head): uniform over the workgroup; the jobs it makes
         // redundant return before touching LDS or a barrier
-        const bool warm = a.warm && a.seg_ws[lay.warm_mode(b, head)] != 0.f;
+        const bool warm = a.warm && warm_head(a.seg_ws, lay, b, head);
         int seg;
         if (a.pass == 1) {
             if (job >= 2 * S - 3) {  // warm job of segment job - (2S - 4)
@@ -2456,7 +2548,7 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     const int BH = a.lay.B * a.H;
     const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
     const int b = bh / a.H, head = bh - b * a.H;
-    if (a.warm && a.seg_ws[a.lay.warm_mode(b, head)] != 0.f) {
+    if (a.warm && warm_head(a.seg_ws, a.lay, b, head)) {
         // every segment of this (stream, head) started warm in the first launch: no chain.
         // Its last segment left the final state in slot H(b, S-1) (and, with the front end
         // fused, the new windows in win_ws) because the job that read the initial state and
@@ -2572,11 +2664,22 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     }
 }
 
-hipError_t launch_warm_plan(const WarmArgs &a, hipStream_t s)
+hipError_t launch_warm_boundaries(const WarmArgs &a, int kda, int dk, hipStream_t s)
 {
-    if (a.nseg < 3 || a.seg0_len % CH || a.seg_len % CH)
+    const int64_t grid = (int64_t)a.st.B * a.H * (a.nseg - 1);
+    if (a.nseg < 3 || a.seg0_len % CH || a.seg_len % CH || grid > (int64_t)INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(warm_plan_kernel, dim3((unsigned)(a.st.B * a.H)), dim3(256), 0, s, a);
+    if (!kda)
+        hipLaunchKernelGGL((warm_boundary_kernel<false, 0>), dim3((unsigned)grid), dim3(256), 0,
+                           s, a);
+    else if (dk == 128)
+        hipLaunchKernelGGL((warm_boundary_kernel<true, 128>), dim3((unsigned)grid), dim3(1024),
+                           0, s, a);
+    else if (dk == 64)
+        hipLaunchKernelGGL((warm_boundary_kernel<true, 64>), dim3((unsigned)grid), dim3(1024),
+                           0, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -2664,38 +2767,6 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
         hipLaunchKernelGGL((combine_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
-    return hipGetLastError();
-}
-
-// Channel maximum of the per-key-channel log-gates: 8 lanes per (token, head), each
-// taking every eighth 4-channel group of the row, then a maximum over the 8.
-__global__ void __launch_bounds__(256) gate_max_kernel(const GateMaxArgs a)
-{
-    if (debug_stop(a.dbg))
-        return;
-    const int64_t pair = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int l = threadIdx.x & 7;
-    if (pair >= a.n)  // whole groups of 8 lanes leave together
-        return;
-    const float *row = a.g + pair * a.dk;
-    float m = -__builtin_inff();
-    for (int c = 4 * l; c < a.dk; c += 32) {
-        const uint4 u = load_stream16(row + c);
-        m = fmaxf(m, fmaxf(fmaxf(__uint_as_float(u.x), __uint_as_float(u.y)),
-                           fmaxf(__uint_as_float(u.z), __uint_as_float(u.w))));
-    }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    if (l == 0)
-        a.out[pair] = m;
-}
-
-hipError_t launch_gate_max(const GateMaxArgs &a, hipStream_t s)
-{
-    if (a.n < 1 || a.dk < 4 || a.dk % 4 || (a.n + 31) / 32 > (int64_t)INT32_MAX)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gate_max_kernel, dim3((unsigned)((a.n + 31) / 32)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -274,8 +274,7 @@ int gdn_chunk_table(const int32_t *cu_seqlens, int32_t B, int32_t chunk, int32_t
  *                   bf16 front-end calls run the front end inside the chunk kernel.
  *   GDN_PROF_RECUR  the fused chunk kernel (front end for bf16 rows, WY/UT preparation,
  *                   inter-chunk scan), the warm-start plan when it has no front kernel to
- *                   ride in, the chain of segment maps, the window copies, and for KDA
- *                   the per-token channel maxima of the log-gates that the plan reads
+ *                   ride in, the chain of segment maps and the window copies
  *   GDN_PROF_STATE  unused by prefill calls (the windows go out with the scan); kept so
  *                   that bucket numbers stay fixed
  *   GDN_PROF_GATE   the output gate when it runs as its own pass (the per-key-channel gate
@@ -313,8 +312,7 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
  * 1..S-1 from their start states. (The pages' chunked scan carries h serially across a
  * stream's chunks; the recurrence is affine in h, so the segment maps compose exactly up
  * to rounding.) A call whose ws_bytes covers the front end but not the segment states runs
- * unsegmented. For KDA (GDN_PLAN_KDA) with eps >= 0 the segment area also holds N * H
- * floats: each token's largest channel log-gate, for the warm-start plan below.
+ * unsegmented.
  *
  * Two shortcuts of the segmented scan depend on the gates, decided on the device: with keys
  * of unit length or less (eps >= 0), every token multiplies a segment's transition by a

@@ -259,14 +259,15 @@ def test_segmented_scan_fast_decay(case):
 
 
 def warm_flags(call, S):
-    """The warm-mode flag of each head of a single-stream segmented call: a float the
-    library's warm-start plan leaves in the workspace's segment area (after 3S - 5 state
-    slots and S x H transition flags), 1.0 where the head's segments start warm."""
+    """Whether each head of a single-stream segmented call ran warm: the library's
+    warm-start plan leaves, per boundary s = 1..S-1 and head, the chunks of warm-up it found
+    (0 for none) in the workspace's segment area, after 3S - 5 state slots and S x H
+    transition flags; a head runs warm when every boundary found some."""
     spec = call.spec
-    slot = spec.H * spec.dk * spec.dv
-    base = (3 * S - 5) * slot + S * spec.H
-    f = call.ws[:(base + spec.H) * 4].view(torch.float32)
-    return [float(x) for x in f[base:base + spec.H].cpu()]
+    H = spec.H
+    base = (3 * S - 5) * spec.H * spec.dk * spec.dv + S * H
+    f = call.ws[:(base + S * H) * 4].view(torch.float32).cpu()
+    return [float(all(f[base + s * H + h] > 0 for s in range(1, S))) for h in range(H)]
 
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
