@@ -367,12 +367,12 @@ __device__ __forceinline__ int find_stream(const Streams &s, int64_t t)
 constexpr int CH = 64;  // chunk length
 
 // Warm starts: a segment starts from h = 0 once the chunks before it bound the norm of
-// their transition by e^kWarmLogBound. The state it drops is then at most e^-40 (< 2^-57)
+// their transition by e^kWarmLogBound. The state it drops is then at most e^-32 (< 2^-46)
 // of the state's norm at the start of that window: far below the fp32 rounding (2^-24) of
-// every value the state feeds, unless the state shrank by more than 2^33 across the window.
+// every value the state feeds, unless the state shrank by more than 2^22 across the window.
 // (A transition job's early stop, which substitutes an exact zero, waits for e^-110: below
 // half the smallest fp32 subnormal.)
-constexpr float kWarmLogBound = -40.f;
+constexpr float kWarmLogBound = -32.f;
 
 // The plan of one (stream, head) in one workgroup (extra workgroups of the float32 front
 // kernel); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:
@@ -1309,17 +1309,6 @@ __global__ void __launch_bounds__(NW * 64)
 
     // state, D layout: hs[cb][mb][i] = h[16 mb + 4 g + i][colw + 16 cb + c]
     f32x4 hs[NCB][DK / 16];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int mb = 0; mb < DK / 16; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mb + 4 * (lane0 >> 4) + i;
-                const int col = colw + 16 * cb + (lane0 & 15);
-                hs[cb][mb][i] = hin ? hin[hoff + (int64_t)row * DV + col]
-                                    : (h_ident && row == col ? 1.f : 0.f);
-            }
 
     // Raw 16-byte vectors of the next chunk, loaded one chunk ahead so that the HBM latency
     // hides behind a whole chunk of work. Rows at or past the stream's end are never read.
@@ -1413,39 +1402,6 @@ __global__ void __launch_bounds__(NW * 64)
     // and the window keeps the last K - 1 raw inputs.
     const int Kt = FRONT ? a.conv_k : KC, Wn = Kt - 1, tap0 = KC - Kt;
     float wv[FRONT ? KC : 1];  // this lane's v column taps (fused front end)
-    if constexpr (FRONT) {
-        // q and k taps of this head into LDS, [tensor][tap][channel], times -log2(e): the
-        // conv then gives -z log2(e), the argument of the exp2 in the SiLU (see stage A)
-        for (int idx = tid0; idx < 2 * KC * DK; idx += NT) {
-            const int t = idx / (KC * DK), rem = idx - t * KC * DK, j = rem / DK;
-            ((float *)(smem + C::OFF_CW))[idx] =
-                j < tap0 ? 0.f
-                         : a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * Kt + j - tap0] *
-                               -kLog2e;
-        }
-#pragma unroll
-        for (int j = 0; j < KC; ++j)
-            wv[j] = j < tap0 ? 0.f
-                             : a.conv_w[(int64_t)v_channel(16 * wave0 + (lane0 & 15)) * Kt +
-                                        j - tap0];
-        // the stream's first chunk: raw rows 0 .. KC-2 are the carried window, after zeros
-        // in the rows a shorter window does not reach (multiplied by zero taps; never read
-        // from stale LDS)
-        if (start == sbeg && start < end) {
-            const TIN *cw = (const TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
-                                                            : a.conv_state);
-            constexpr int W = KC - 1;
-            for (int idx = tid0; idx < (2 * DK + NV) * W; idx += NT) {
-                const int ch = idx / W, j = idx - ch * W, e = j - (W - Wn);
-                if (ch < 2 * DK)
-                    *(TIN *)(smem + C::OFF_Q + C::raw_qk(ch >= DK, j) + (ch % DK) * 2) =
-                        e < 0 ? (TIN)0.f : cw[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + e];
-                else
-                    *(TIN *)(smem + C::OFF_V + C::raw_v(j) + (ch - 2 * DK) * 2) =
-                        e < 0 ? (TIN)0.f : cw[(int64_t)v_channel(ch - 2 * DK) * Wn + e];
-            }
-        }
-    }
     // The raw rows of the next chunk go out in three groups spread over the state stage
     // (group 0 at its start, 1 before P U, 2 before the state update): every workgroup
     // runs the same steps at about the same time, and the rows of a whole chunk requested
@@ -1507,8 +1463,54 @@ __global__ void __launch_bounds__(NW * 64)
             pb = (int)threadIdx.x < Lc ? (a.beta + (c0 * H + head))[go] : 0.f;
         }
     };
+    // the first chunk's rows are requested before the state, the taps and the carried
+    // window, whose loads the workgroup then waits for while the rows are in flight
     if (start < end)
         prefetch(start, (int)min((int64_t)CH, end - start));
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mb + 4 * (lane0 >> 4) + i;
+                const int col = colw + 16 * cb + (lane0 & 15);
+                hs[cb][mb][i] = hin ? hin[hoff + (int64_t)row * DV + col]
+                                    : (h_ident && row == col ? 1.f : 0.f);
+            }
+    if constexpr (FRONT) {
+        // q and k taps of this head into LDS, [tensor][tap][channel], times -log2(e): the
+        // conv then gives -z log2(e), the argument of the exp2 in the SiLU (see stage A)
+        for (int idx = tid0; idx < 2 * KC * DK; idx += NT) {
+            const int t = idx / (KC * DK), rem = idx - t * KC * DK, j = rem / DK;
+            ((float *)(smem + C::OFF_CW))[idx] =
+                j < tap0 ? 0.f
+                         : a.conv_w[(int64_t)qk_channel(t, rem - j * DK) * Kt + j - tap0] *
+                               -kLog2e;
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+            wv[j] = j < tap0 ? 0.f
+                             : a.conv_w[(int64_t)v_channel(16 * wave0 + (lane0 & 15)) * Kt +
+                                        j - tap0];
+        // the stream's first chunk: raw rows 0 .. KC-2 are the carried window, after zeros
+        // in the rows a shorter window does not reach (multiplied by zero taps; never read
+        // from stale LDS)
+        if (start == sbeg && start < end) {
+            const TIN *cw = (const TIN *)(a.conv_state_ptrs ? a.conv_state_ptrs[b]
+                                                            : a.conv_state);
+            constexpr int W = KC - 1;
+            for (int idx = tid0; idx < (2 * DK + NV) * W; idx += NT) {
+                const int ch = idx / W, j = idx - ch * W, e = j - (W - Wn);
+                if (ch < 2 * DK)
+                    *(TIN *)(smem + C::OFF_Q + C::raw_qk(ch >= DK, j) + (ch % DK) * 2) =
+                        e < 0 ? (TIN)0.f : cw[(int64_t)qk_channel(ch >= DK, ch % DK) * Wn + e];
+                else
+                    *(TIN *)(smem + C::OFF_V + C::raw_v(j) + (ch - 2 * DK) * 2) =
+                        e < 0 ? (TIN)0.f : cw[(int64_t)v_channel(ch - 2 * DK) * Wn + e];
+            }
+        }
+    }
 
     // o of a chunk is staged in LDS and written out during the next chunk's preparation
     // stage: vector loads and stores share one completion counter, so stores issued at the
