@@ -162,6 +162,8 @@ def main() -> int:
                     help="with the output gate (gated RMSNorm of o with z)")
     ap.add_argument("--qk-heads", type=int, default=0,
                     help="q/k heads shared by the value heads (0 = as many as value heads)")
+    ap.add_argument("--chunk", type=int, default=64,
+                    help="rows per chunk (32 runs on the instances that have it)")
     args = ap.parse_args()
     if args.profile_every <= 0:
         args.profile_every = max(1, args.steps // 5)
@@ -183,6 +185,9 @@ def main() -> int:
         if args.qk_heads:
             spec = dataclasses.replace(spec, Hqk=args.qk_heads,
                                        name=spec.name + "-qk%d" % args.qk_heads)
+        if args.chunk != 64:
+            spec = dataclasses.replace(spec, chunk=args.chunk,
+                                       name=spec.name + "-c%d" % args.chunk)
         return spec
 
     dev = "cuda"

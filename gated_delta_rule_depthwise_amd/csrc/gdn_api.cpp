@@ -102,7 +102,8 @@ bool fused_front(const gdn_params *p, int kda)
     if (p->conv_k < 2 || p->conv_k > 4 || p->dtype != GDN_BF16 || p->ld_qkv >= (1 << 24))
         return false;
     for (int nv : {128, 64})
-        if (p->dv % nv == 0 && gdn::chunk_instance_exists(3, p->dk, p->dv, kda, nv, 0, 0))
+        if (p->dv % nv == 0 &&
+            gdn::chunk_instance_exists(3, p->dk, p->dv, kda, nv, 0, 0, p->chunk))
             return true;
     return false;
 }
@@ -127,7 +128,8 @@ Shape pick_shape(const gdn_params *p, int kda)
 {
     const int ik = in_kind(p, kda);
     for (int nv : {128, 64}) {
-        if (p->dv % nv == 0 && gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0, 0))
+        if (p->dv % nv == 0 &&
+            gdn::chunk_instance_exists(ik, p->dk, p->dv, kda, nv, 0, 0, p->chunk))
             return Shape{nv, 0};
     }
     return Shape{0, 0};
@@ -145,7 +147,7 @@ int check_params(const gdn_params *p, int kda)
         return GDN_E_ARG;
     if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
         return GDN_E_UNSUPPORTED;
-    if (p->chunk != 64)
+    if (p->chunk != 64 && p->chunk != 32)  // 32: the instances that have it (pick_shape)
         return GDN_E_UNSUPPORTED;
     if (p->conv_k != 0 && (p->conv_k < 2 || p->conv_k > 4))
         return GDN_E_UNSUPPORTED;
@@ -394,7 +396,7 @@ int run(const Call &c)
     const int ik = in_kind(p, c.kda);
     // the output gate rides in the o flush where the instance stages o, else its own pass
     const int fused = p->z && gdn::chunk_instance_exists(ik, p->dk, p->dv, c.kda, sh.nv,
-                                                         sh.waves, 1);
+                                                         sh.waves, 1, p->chunk);
     const int64_t grid = BH * (p->dv / sh.nv);
     if (grid > (int64_t)INT32_MAX)
         return GDN_E_ARG;
@@ -540,8 +542,8 @@ int run(const Call &c)
         if (order && gdn::launch_stream_order(c.st.cu, c.st.B, order, c.stream) != hipSuccess)
             return GDN_E_HIP;
         if (!sp.S) {
-            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
-                                  (int)grid, c.stream) != hipSuccess)
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
+                                  ca, (int)grid, c.stream) != hipSuccess)
                 return GDN_E_HIP;
         } else {
             ca.nseg = sp.S;
@@ -554,8 +556,8 @@ int run(const Call &c)
             }
             ca.pass = 1;
             const int64_t jobs1 = ca.warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
-            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
-                                  (int)(grid * jobs1), c.stream) != hipSuccess)
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
+                                  ca, (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
             gdn::CombineArgs cb{};
             cb.dbg = dbg;
@@ -573,8 +575,8 @@ int run(const Call &c)
                 return GDN_E_HIP;
             ca.pass = 2;
             ca.window_items = 0;  // the windows went out with pass 1
-            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, ca,
-                                  (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
+            if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
+                                  ca, (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
                 return GDN_E_HIP;
         }
         if (shared) {  // every workgroup that read the old windows is done

@@ -252,13 +252,13 @@ __device__ __forceinline__ bool debug_stop(const int32_t *dbg)
 // launch error.
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 hipError_t launch_front(int dtype, const FrontArgs &a, hipStream_t s);
-// new carried conv windows; must run after every kernel that reads the old ones
-// in_kind: 0 = f32 rows, 1 = bf16 rows, 2 = fp16 activations written by the front end;
+// in_kind: 0 = f32 rows, 1 = bf16 rows, 3 = bf16 raw rows with the front end fused;
 // nv: dv columns per workgroup (the grid is B * H * dv / nv workgroups); waves: waves per
 // workgroup, 0 = the first compiled instance of that width; gate: the instance with the
-// output gate fused into its o flush (ChunkArgs z, ld_z, norm_w, norm_eps)
+// output gate fused into its o flush (ChunkArgs z, ld_z, norm_w, norm_eps); chunk: rows
+// per chunk (64, or 32 where an instance has it)
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
-                        const ChunkArgs &a, int grid, hipStream_t s);
+                        int chunk, const ChunkArgs &a, int grid, hipStream_t s);
 // the output gate as its own pass (dtype: element type of z, GDN_F32 or GDN_BF16)
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
@@ -275,7 +275,8 @@ hipError_t launch_decode_qk_window(int dtype, const DecodeArgs &a, hipStream_t s
 hipError_t launch_stream_order(const int32_t *cu, int32_t B, int32_t *order, hipStream_t s);
 hipError_t launch_chunk_table(const int32_t *cu, int32_t B, int32_t chunk, int32_t *table,
                               int64_t max_entries, int32_t *count, hipStream_t s);
-// 1 if the (in_kind, dk, dv, kda, nv, waves, gate) instance exists.
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate);
+// 1 if the (in_kind, dk, dv, kda, nv, waves, gate, chunk) instance exists.
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
+                          int chunk);
 
 }  // namespace gdn

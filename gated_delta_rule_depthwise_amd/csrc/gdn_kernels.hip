@@ -887,8 +887,9 @@ hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s)
 
 
 template <typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE = false,
-          bool FRONT = false>
+          bool FRONT = false, int CHK = 64>
 struct ChunkCfg {
+    static constexpr int CH = CHK;  // rows per chunk (64, or 32 without the fused front end)
     static constexpr int NV = 16 * NW * NCB;  // dv columns per workgroup (16*NCB per wave)
     // fp16 operands: T = (I+M)^-1 and P are applied as fp16 hi + lo pairs, and the
     // right-hand operands of T X and P U too, which keeps those products at about fp32
@@ -966,9 +967,10 @@ struct ChunkCfg {
     // 16 banks apart
     static constexpr int LDO = NV + (FRONT ? 4 : 16);
     // + the running log decay bound of a transition job (one float, padded to 16 bytes;
-    // scalar gate without the fused output gate only)
+    // scalar gate without the fused output gate only); per-key-channel gate: + e^(G_C) per
+    // channel
     static constexpr bool STOP = !KDA && !GATE;
-    static constexpr int OFF_O = OFF_G + 4 * CH * 4 + (STOP ? 16 : 0);
+    static constexpr int OFF_O = OFF_G + 4 * CH * 4 + (STOP ? 16 : 0) + (KDA ? DK * 4 : 0);
     // o is staged in LDS when it fits (not with the per-channel gate tile at 128 columns)
     static constexpr bool STAGE_O = OFF_O + CH * LDO * 4 <= 160 * 1024;
     // fused front end: the q and k conv taps of this head, [2][KC][DK] float
@@ -1165,10 +1167,13 @@ __device__ __forceinline__ void pack_split(const f32x4 &d0, const f32x4 &d1,
 // 1 = M only, 2 = P only. Diagonal blocks (0, 2, 5, 9) come first on waves 0-3, which
 // also invert them; two blocks below the diagonal are split between two waves so that
 // the waves without an inversion carry about as much as the ones with.
-template <int NW>
+template <int NW, int NB = 4>
 __device__ __forceinline__ int block_task(int wave, int j)
 {
-    if constexpr (NW == 8) {
+    if constexpr (NB == 2) {  // 32-row chunks: blocks 0 (0, 0), 1 (1, 0), 2 (1, 1)
+        constexpr int tab[8] = {0, 2, 1, -1, -1, -1, -1, -1};
+        return j == 0 ? tab[wave] : -1;
+    } else if constexpr (NW == 8) {
         constexpr int tab[8][2] = {{0, -1}, {2, -1}, {5, -1},      {9, -1},
                                    {1, 22}, {3, 23}, {4, 38}, {8, 39}};
         return tab[wave][j];
@@ -1179,14 +1184,18 @@ __device__ __forceinline__ int block_task(int wave, int j)
 }
 
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE,
-          bool FRONT>
+          bool FRONT, int CHK = 64>
 __global__ void __launch_bounds__(NW * 64)
     __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) chunk_kernel(const ChunkArgs a)
 {
     static_assert(sizeof(TIN) == sizeof(T), "16-byte loads fill whole operand vectors");
     static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     static_assert(!FRONT || std::is_same<TIN, bf16>::value, "fused front end: bf16 raw rows");
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
+    // rows per chunk and 16-row blocks per chunk: 64 (4 blocks), or 32 (2 blocks) on the
+    // register path without the output gate
+    constexpr int CH = CHK, NB = CH / 16;
+    static_assert(CH == 64 || (CH == 32 && !FRONT && !GATE), "chunk rows");
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT, CHK>;
     // the output gate normalises whole o rows, which the staged o holds
     static_assert(!GATE || (C::STAGE_O && C::NV == DV), "output gate needs staged o rows");
     // z comes in the caller's element type (bf16 also when the operands are fp16)
@@ -1589,8 +1598,8 @@ __global__ void __launch_bounds__(NW * 64)
     // case, and a row block's fragment reads are all issued before its products with no
     // branch between. (The register-path instances, which hold the next chunk's rows in
     // registers, interleave reads and products: batching them would spill.)
-    auto kh_qh_wo = [&](auto wo, int cb, f32x4 (&x)[4], f32x4 (&o)[4],
-                        const float (&ar)[4][4], const T *Ks, const void *Qs, const void *Vs,
+    auto kh_qh_wo = [&](auto wo, int cb, f32x4 (&x)[NB], f32x4 (&o)[NB],
+                        const float (&ar)[NB][4], const T *Ks, const void *Qs, const void *Vs,
                         int wave, int lane, int g4, int c16, int Lc) {
         constexpr bool WO = decltype(wo)::value;
         const int vc = 16 * (wave * NCB + cb);  // this block's columns within Vs
@@ -1599,7 +1608,7 @@ __global__ void __launch_bounds__(NW * 64)
         for (int kb = 0; kb < DK / 32; ++kb)
             hf[kb] = pack<T>(hs[cb][2 * kb], hs[cb][2 * kb + 1]);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < NB; ++I) {
             f32x4 kh = zero4(), qh = zero4();
             if constexpr (FRONT) {
                 frag kf[DK / 32], qf[WO ? DK / 32 : 1];
@@ -1655,7 +1664,7 @@ __global__ void __launch_bounds__(NW * 64)
             }
         }
     };
-    auto kh_qh = [&](int cb, f32x4 (&x)[4], f32x4 (&o)[4], const float (&ar)[4][4],
+    auto kh_qh = [&](int cb, f32x4 (&x)[NB], f32x4 (&o)[NB], const float (&ar)[NB][4],
                      const T *Ks, const void *Qs, const void *Vs, int wave, int lane, int g4,
                      int c16, int Lc) {
         if (!FRONT || write_o)
@@ -1936,17 +1945,17 @@ __global__ void __launch_bounds__(NW * 64)
             __syncthreads();
         }
         const float gC = graw[CH - 1];  // graw holds Gamma (written in stage A)
-        float gr[4][4];  // Gamma at the D-layout rows 16I + 4g + i of this lane
+        float gr[NB][4];  // Gamma at the D-layout rows 16I + 4g + i of this lane
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < NB; ++I) {
             const f32x4 v = *reinterpret_cast<const f32x4 *>(graw + 16 * I + 4 * g4);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 gr[I][i] = v[i];
         }
-        float gcol[4];   // Gamma at the D-layout columns 16J + c of this lane
+        float gcol[NB];  // Gamma at the D-layout columns 16J + c of this lane
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
+        for (int J = 0; J < NB; ++J)
             gcol[J] = graw[16 * J + c16];
 
         // The previous chunk's o goes out now, behind this stage's arithmetic; the next
@@ -1968,16 +1977,16 @@ __global__ void __launch_bounds__(NW * 64)
         // per-channel gate, whose tiles are rescaled after the preparation; measured -2%
         // per chunk on the segmented 4096-token stream)
         constexpr bool EARLY = NCB == 1 && !KDA;
-        float ar[4][4], dr[4][4];  // a_r = e^Gamma_r and a_C / a_r at this lane's rows
+        float ar[NB][4], dr[NB][4];  // a_r = e^Gamma_r and a_C / a_r at this lane's rows
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int I = 0; I < NB; ++I) {
             const f32x4 va = *reinterpret_cast<const f32x4 *>(ea + 16 * I + 4 * g4);
             const f32x4 vd = *reinterpret_cast<const f32x4 *>(ed + 16 * I + 4 * g4);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 ar[I][i] = va[i], dr[I][i] = vd[i];
         }
-        f32x4 xe[EARLY ? 4 : 1], oe[EARLY ? 4 : 1];
+        f32x4 xe[EARLY ? NB : 1], oe[EARLY ? NB : 1];
         if constexpr (EARLY)
             kh_qh(0, xe, oe, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
 
@@ -1987,10 +1996,10 @@ __global__ void __launch_bounds__(NW * 64)
         // the diagonal are spread over the other waves (8 waves) or the same ones (4 waves).
         // Both products of a block share the K_J operand. T_II and the off-diagonal M_IJ go
         // to the MT tile (fp16), P to Ps/Psl as an fp16 hi + lo pair.
-        constexpr int NJ = NW == 8 ? 2 : 3;
+        constexpr int NJ = NB == 2 ? 1 : NW == 8 ? 2 : 3;
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) {
-            const int code = block_task<NW>(wave, jb);
+            const int code = block_task<NW, NB>(wave, jb);
             if (code < 0)
                 break;
             const int p = code & 15, part = code >> 4;
@@ -2124,14 +2133,14 @@ __global__ void __launch_bounds__(NW * 64)
             const int s = 16 * J + c16;
             float gs = gcol[0];
 #pragma unroll
-            for (int jj = 1; jj < 4; ++jj)
+            for (int jj = 1; jj < NB; ++jj)
                 gs = J == jj ? gcol[jj] : gs;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * I + 4 * g4 + i;
                 float grr = gr[0][i];
 #pragma unroll
-                for (int ii = 1; ii < 4; ++ii)
+                for (int ii = 1; ii < NB; ++ii)
                     grr = I == ii ? gr[ii][i] : grr;
                 // decay e^(G_r - G_s) for s <= r (the per-channel gate has it inside the
                 // products); the masked upper part is discarded by the selects below
@@ -2199,18 +2208,17 @@ __global__ void __launch_bounds__(NW * 64)
             typedef T T4 __attribute__((ext_vector_type(4)));
             constexpr int NI = CH * (DK / 4) / NT;
             static_assert(NI * NT == CH * (DK / 4) && NT % (DK / 4) == 0, "rescale map");
-            static_assert(DK <= 2 * CH, "e^(G_C) fits over a and a_C / a");
+
             const int c0 = (tid % (DK / 4)) * 4, r0 = tid / (DK / 4);
             // (k = hi + lo; the K lo tile then takes the lo half of K e^(G_C - G))
             const f32x4 gcv = *reinterpret_cast<const f32x4 *>(Gk + (CH - 1) * LDG + c0);
-            // e^(G_C) per channel, for the state update, over a and a_C / a (which the
-            // per-channel gate does not use)
+            // e^(G_C) per channel, for the state update
             if (r0 == 0) {
                 f32x4 e;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     e[i] = __builtin_amdgcn_exp2f(gcv[i]);
-                *reinterpret_cast<f32x4 *>(ea + c0) = e;
+                *reinterpret_cast<f32x4 *>(graw + 4 * CH + c0) = e;
             }
             T4 kv[NI], klv[NI], qv[NI];
             f32x4 gv[NI];
@@ -2261,7 +2269,7 @@ __global__ void __launch_bounds__(NW * 64)
         // on the rescaled tiles, so that Q, K and the raw v rows are dead before the next
         // chunk's raw rows land on them
         constexpr bool LATE = FRONT && KDA;
-        f32x4 xl[LATE ? 4 : 1], ol[LATE ? 4 : 1];
+        f32x4 xl[LATE ? NB : 1], ol[LATE ? NB : 1];
         if constexpr (LATE) {
             kh_qh(0, xl, ol, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
             __syncthreads();
@@ -2283,14 +2291,14 @@ __global__ void __launch_bounds__(NW * 64)
         const float aC = ea[CH - 1];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 x[4], o[4];
+            f32x4 x[NB], o[NB];
             if constexpr (EARLY) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
+                for (int I = 0; I < NB; ++I)
                     x[I] = xe[I], o[I] = oe[I];
             } else if constexpr (LATE) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
+                for (int I = 0; I < NB; ++I)
                     x[I] = xl[I], o[I] = ol[I];
             } else {
                 kh_qh(cb, x, o, ar, Ks, Qs, Vs, wave, lane, g4, c16, L);
@@ -2301,10 +2309,10 @@ __global__ void __launch_bounds__(NW * 64)
             // U_I = T_II (beta X_I - sum_{J<I} M_IJ U_J), right-hand sides as hi + lo pairs
             // (fp16 operands: each U block is split into hi + lo once, for the later blocks
             // and for P U)
-            f32x4 u[4];
-            f16x4 uhs[4], uls[4];
+            f32x4 u[NB];
+            f16x4 uhs[NB], uls[NB];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int I = 0; I < NB; ++I) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int J = 0; J < I; ++J) {
@@ -2326,9 +2334,11 @@ __global__ void __launch_bounds__(NW * 64)
                 prefetch_group(cs + CH, pfL, 1);
             // O += P U with P and U as hi + lo pairs
             if (write_o) {
-                frag uh[2], ul[2];
+                // 32-deep column blocks of P (16-row pairs of U)
+                constexpr int NKB = NB / 2;
+                frag uh[NKB], ul[NKB];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     if constexpr (SPLIT) {
                         uh[kb] = __builtin_shufflevector(uhs[2 * kb], uhs[2 * kb + 1], 0, 1, 2,
                                                          3, 4, 5, 6, 7);
@@ -2339,9 +2349,9 @@ __global__ void __launch_bounds__(NW * 64)
                     }
                 }
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
+                for (int I = 0; I < NB; ++I) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
+                    for (int kb = 0; kb < NKB; ++kb) {
                         if (kb > (I >> 1))
                             continue;
                         const frag ph = ld_frag(Ps, LDT, 16 * I, 32 * kb, lane);
@@ -2367,7 +2377,7 @@ __global__ void __launch_bounds__(NW * 64)
             // h <- diag(e^G_C) h + (K . e^(G_C - G))^T U
             if constexpr (!KDA) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
+                for (int I = 0; I < NB; ++I)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         u[I][i] *= dr[I][i];
@@ -2376,13 +2386,16 @@ __global__ void __launch_bounds__(NW * 64)
             // the whole stream, and heavy-tailed states (max/RMS ~ 50) need U beyond fp16
             // (a single fp16 U left err(h) at 3.3% on such a state; the pair: 1.8%, for
             // 2-4% more time per chunk)
+            // (the 32-row halves of the chunk: two at 64 rows, one at 32)
             frag vf0, vf1, vl0, vl1;
             pack_split<T>(u[0], u[1], vf0, vl0);
-            pack_split<T>(u[2], u[3], vf1, vl1);
+            if constexpr (NB == 4)
+                pack_split<T>(u[2], u[3], vf1, vl1);
 #pragma unroll
             for (int mb = 0; mb < DK / 16; ++mb) {
                 if constexpr (KDA) {
-                    const f32x4 ec = *reinterpret_cast<const f32x4 *>(ea + 16 * mb + 4 * g4);
+                    const f32x4 ec =
+                        *reinterpret_cast<const f32x4 *>(graw + 4 * CH + 16 * mb + 4 * g4);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         hs[cb][mb][i] *= ec[i];
@@ -2393,16 +2406,19 @@ __global__ void __launch_bounds__(NW * 64)
                 }
                 const T *Kt = KDA ? Kd : Ks;
                 const frag k0 = ld_frag_t_qk<DK>(Kt, 0, 16 * mb, lane);
-                const frag k1 = ld_frag_t_qk<DK>(Kt, 32, 16 * mb, lane);
                 mma(hs[cb][mb], k0, vf0);
-                mma(hs[cb][mb], k1, vf1);
-                if constexpr (SPLIT) {
+                if constexpr (SPLIT)
                     mma(hs[cb][mb], k0, vl0);
-                    mma(hs[cb][mb], k1, vl1);
+                if constexpr (NB == 4) {
+                    const frag k1 = ld_frag_t_qk<DK>(Kt, 32, 16 * mb, lane);
+                    mma(hs[cb][mb], k1, vf1);
+                    if constexpr (SPLIT)
+                        mma(hs[cb][mb], k1, vl1);
                 }
                 if constexpr (C::KLO) {  // the k operand as an fp16 hi + lo pair as well
                     mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 0, 16 * mb, lane), vf0);
-                    mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 32, 16 * mb, lane), vf1);
+                    if constexpr (NB == 4)
+                        mma(hs[cb][mb], ld_frag_t_qk<DK>(Kl, 32, 16 * mb, lane), vf1);
                 }
             }
         }
@@ -2441,13 +2457,13 @@ __global__ void __launch_bounds__(NW * 64)
 }
 
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE,
-          bool FRONT>
+          bool FRONT, int CHK>
 hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 {
-    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
+    using C = ChunkCfg<T, DK, DV, NW, NCB, KDA, GATE, FRONT, CHK>;
     static_assert(C::BYTES <= 160 * 1024, "LDS budget");
     static_assert(DV % C::NV == 0, "slices");
-    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE, FRONT>;
+    auto kern = chunk_kernel<TIN, T, DK, DV, NW, NCB, KDA, GATE, FRONT, CHK>;
     static bool attr_set = false;  // per instance; same value on every device
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -2466,7 +2482,9 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 }
 
 // Instances: (input element, operand type, input kind, dk, dv, waves, column blocks of 16
-// per wave, per-channel gate, output gate fused, front end fused). Input kind: 0 = f32
+// per wave, per-channel gate, output gate fused, front end fused, rows per chunk). The
+// 32-row instances (register path, no output gate) exist for the chunk-size invariance of
+// the results; 64 rows is the default. Input kind: 0 = f32
 // rows, 1 = bf16 rows, 2 = fp16 activations of the front kernel, 3 = bf16 raw rows with the
 // conv front end fused into the load stage. A workgroup covers NW * NCB * 16 dv columns of one
 // (stream, head). The default (widest) shapes that stage o also come with the output gate
@@ -2475,49 +2493,54 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
 // a separate pass (gate_kernel), and so do the dk != dv shapes, whose value rows span two
 // workgroups (dv = 2 dk: two column slices of one (stream, head)).
 #define GDN_CHUNK_INSTANCES(X)                          \
-    X(bf16, f16, 1, 128, 128, 8, 1, false, false, false) \
-    X(bf16, f16, 1, 128, 128, 4, 2, false, false, false) \
-    X(bf16, f16, 1, 128, 128, 4, 1, false, false, false) \
-    X(bf16, f16, 1, 64, 64, 4, 1, false, false, false) \
-    X(float, float, 0, 64, 64, 4, 1, false, false, false) \
-    X(bf16, f16, 1, 128, 128, 8, 1, true, false, false) \
-    X(bf16, f16, 1, 128, 128, 4, 1, true, false, false) \
-    X(bf16, f16, 1, 64, 64, 4, 1, true, false, false) \
-    X(float, float, 0, 64, 64, 4, 1, true, false, false) \
-    X(bf16, f16, 1, 128, 128, 8, 1, false, true, false) \
-    X(bf16, f16, 1, 64, 64, 4, 1, false, true, false) \
-    X(float, float, 0, 64, 64, 4, 1, false, true, false) \
-    X(bf16, f16, 1, 64, 64, 4, 1, true, true, false) \
-    X(bf16, f16, 1, 128, 256, 8, 1, false, false, false) \
-    X(bf16, f16, 1, 128, 256, 8, 1, true, false, false) \
-    X(float, float, 0, 64, 128, 4, 1, false, false, false) \
-    X(float, float, 0, 64, 128, 4, 1, true, false, false) \
-    X(bf16, f16, 3, 128, 128, 8, 1, false, false, true) \
-    X(bf16, f16, 3, 64, 64, 4, 1, false, false, true) \
-    X(bf16, f16, 3, 128, 128, 8, 1, true, false, true) \
-    X(bf16, f16, 3, 64, 64, 4, 1, true, false, true) \
-    X(bf16, f16, 3, 128, 256, 8, 1, false, false, true) \
-    X(bf16, f16, 3, 128, 256, 8, 1, true, false, true)
+    X(bf16, f16, 1, 128, 128, 8, 1, false, false, false, 64) \
+    X(bf16, f16, 1, 128, 128, 4, 2, false, false, false, 64) \
+    X(bf16, f16, 1, 128, 128, 4, 1, false, false, false, 64) \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, false, false, 64) \
+    X(float, float, 0, 64, 64, 4, 1, false, false, false, 64) \
+    X(bf16, f16, 1, 128, 128, 8, 1, true, false, false, 64) \
+    X(bf16, f16, 1, 128, 128, 4, 1, true, false, false, 64) \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, false, false, 64) \
+    X(float, float, 0, 64, 64, 4, 1, true, false, false, 64) \
+    X(bf16, f16, 1, 128, 128, 8, 1, false, true, false, 64) \
+    X(bf16, f16, 1, 64, 64, 4, 1, false, true, false, 64) \
+    X(float, float, 0, 64, 64, 4, 1, false, true, false, 64) \
+    X(bf16, f16, 1, 64, 64, 4, 1, true, true, false, 64) \
+    X(bf16, f16, 1, 128, 256, 8, 1, false, false, false, 64) \
+    X(bf16, f16, 1, 128, 256, 8, 1, true, false, false, 64) \
+    X(float, float, 0, 64, 128, 4, 1, false, false, false, 64) \
+    X(float, float, 0, 64, 128, 4, 1, true, false, false, 64) \
+    X(bf16, f16, 3, 128, 128, 8, 1, false, false, true, 64) \
+    X(bf16, f16, 3, 64, 64, 4, 1, false, false, true, 64) \
+    X(bf16, f16, 3, 128, 128, 8, 1, true, false, true, 64) \
+    X(bf16, f16, 3, 64, 64, 4, 1, true, false, true, 64) \
+    X(bf16, f16, 3, 128, 256, 8, 1, false, false, true, 64) \
+    X(bf16, f16, 3, 128, 256, 8, 1, true, false, true, 64) \
+    X(bf16, f16, 1, 128, 128, 8, 1, false, false, false, 32) \
+    X(bf16, f16, 1, 128, 128, 8, 1, true, false, false, 32) \
+    X(float, float, 0, 64, 64, 4, 1, false, false, false, 32) \
+    X(float, float, 0, 64, 64, 4, 1, true, false, false, 32)
 
 // nv: dv columns per workgroup; waves: 0 = the default for that width; gate: the instance
-// with the output gate fused
+// with the output gate fused; chunk: rows per chunk
 hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
-                        const ChunkArgs &a, int grid, hipStream_t s)
+                        int chunk, const ChunkArgs &a, int grid, hipStream_t s)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F)                                       \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F, CK)                                   \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
-        (waves == 0 || waves == NW) && !gate == !G)                                    \
-        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD, G, F>(a, grid, s);
+        (waves == 0 || waves == NW) && !gate == !G && chunk == CK)                     \
+        return launch_chunk_t<TIN, T, DK, DV, NW, NCB, KD, G, F, CK>(a, grid, s);
     GDN_CHUNK_INSTANCES(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate)
+int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int waves, int gate,
+                          int chunk)
 {
-#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F)                                       \
+#define X(TIN, T, IK, DK, DV, NW, NCB, KD, G, F, CK)                                   \
     if (in_kind == IK && dk == DK && dv == DV && nv == 16 * NW * NCB && !kda == !KD && \
-        (waves == 0 || waves == NW) && !gate == !G)                                    \
+        (waves == 0 || waves == NW) && !gate == !G && chunk == CK)                     \
         return 1;
     GDN_CHUNK_INSTANCES(X)
 #undef X

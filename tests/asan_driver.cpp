@@ -90,7 +90,7 @@ int main()
     CHECK(gdn_prefill(nullptr, D, D, D, Df, Df, Df, nullptr, nullptr, D, 10, nullptr, 0,
                       nullptr) == GDN_E_ARG);
     gdn_params bad = f;
-    bad.chunk = 32;
+    bad.chunk = 16;
     CHECK(kda_prefill(&bad, D, D, D, Df, Df, Df, nullptr, nullptr, D, 10, nullptr, 0,
                       nullptr) == GDN_E_UNSUPPORTED);
     bad = f;

@@ -57,13 +57,26 @@ def test_workspace_bytes():
     pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)
     ws = B.gdn_workspace_bytes(pf, 1, 4096, B.GDN_KIND_SINGLE | B.GDN_PLAN_KDA)
     assert ws >= 4096 * 3 * 32 * 64 * 4 and ws % 256 == 0
-    # float32 rows: the front kernel and its fp32 activations
-    pf = B.params(32, 64, 64, conv_k=4, dtype=B.GDN_F32)
     assert B.gdn_workspace_bytes(pf, 1, 10, B.GDN_KIND_VARLEN) == 10 * 3 * 32 * 64 * 4 + 256
     assert B.gdn_workspace_bytes(B.params(32, 128, 128), 8, 16384, B.GDN_KIND_BATCHED) == 0
     assert B.gdn_workspace_bytes(p, 0, 4096, B.GDN_KIND_SINGLE) == 0
     assert B.gdn_workspace_bytes(p, 1, 0, B.GDN_KIND_SINGLE) == 0
     assert B.gdn_workspace_bytes(B.params(32, 96, 128), 1, 10, B.GDN_KIND_SINGLE) == 0
+
+
+def test_chunk_32():
+    """32-row chunks run where a 32-row instance exists (the register path: bf16 rows at
+    dk = dv = 128, fp32 rows at 64, either gate) and never segment; the fused bf16 front end
+    and other chunk lengths are refused."""
+    for kd in (0, B.GDN_PLAN_KDA):
+        for p in (B.params(32, 128, 128, chunk=32),
+                  B.params(2, 64, 64, chunk=32, dtype=B.GDN_F32),
+                  B.params(2, 64, 64, chunk=32, dtype=B.GDN_F32, conv_k=4)):
+            assert B.gdn_segments(p, B.GDN_KIND_SINGLE | kd, 1, 1 << 16, 1 << 40) == 0
+        assert B.gdn_segments(B.params(32, 128, 128, chunk=32, conv_k=4),
+                              B.GDN_KIND_SINGLE | kd, 1, 4096, 1 << 40) == B.GDN_E_UNSUPPORTED
+        assert B.gdn_segments(B.params(32, 128, 128, chunk=16),
+                              B.GDN_KIND_SINGLE | kd, 1, 4096, 1 << 40) == B.GDN_E_UNSUPPORTED
 
 
 def test_segment_plan():
@@ -145,7 +158,8 @@ def test_refusals_before_launch():
     assert _single(p, h=None) == B.GDN_E_ARG                 # null state
     assert _single(p, g=None) == B.GDN_E_ARG
     assert _single(p, q=FAKE + 2) == B.GDN_E_ARG             # misaligned rows
-    assert _single(B.params(2, 64, 64, chunk=32)) == B.GDN_E_UNSUPPORTED
+    assert _single(B.params(2, 64, 64, chunk=32)) == B.GDN_E_UNSUPPORTED    # no bf16 d=64 at 32
+    assert _single(B.params(2, 64, 64, chunk=16, dtype=B.GDN_F32)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 96, 96)) == B.GDN_E_UNSUPPORTED
     assert _single(B.params(2, 64, 128)) == B.GDN_E_UNSUPPORTED     # bf16 has 128 x 256
     assert _single(B.params(2, 128, 64, dtype=B.GDN_F32)) == B.GDN_E_UNSUPPORTED

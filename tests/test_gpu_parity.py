@@ -214,7 +214,7 @@ def test_refused_calls_leave_buffers_unchanged():
     s = torch.cuda.current_stream().cuda_stream
     p = call.params
     bad_chunk = B.gdn_params.from_buffer_copy(p)
-    bad_chunk.chunk = 32
+    bad_chunk.chunk = 16
     bad_ld = B.gdn_params.from_buffer_copy(p)
     bad_ld.ld_qkv = p.ld_qkv + 1
     # the front end's activations alone need N * cd float values
