@@ -1065,6 +1065,43 @@ __device__ __forceinline__ void split4(const f32x4 &x, f16x4 &hi, f16x4 &lo)
     lo = __builtin_bit_cast(f16x4, (u32x2){l0, l1});
 }
 
+// Widening with v_fma_mix_f32 (fp16 sources read straight from their half of a register,
+// one rounding to fp32, full-register results): the two fp32 values hi + lo of a packed
+// pair of fp16 hi halves and lo halves (exact: hi + lo needs at most 24 bits), and a
+// packed fp16 element times an fp32 factor. Each is one instruction per element where the
+// separate conversions and the add or multiply take three or two, with the same bits.
+__device__ __forceinline__ void widen_hl2(uint32_t hi, uint32_t lo, float &x0, float &x1)
+{
+    asm("v_fma_mix_f32 %0, %2, 1.0, %3 op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %1, %2, 1.0, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(x0), "=&v"(x1)
+        : "v"(hi), "v"(lo));
+}
+__device__ __forceinline__ void widen_mul2(uint32_t h2, float f0, float f1, float &x0, float &x1)
+{
+    asm("v_fma_mix_f32 %0, %2, %3, 0 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %1, %2, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(x0), "=&v"(x1)
+        : "v"(h2), "v"(f0), "v"(f1));
+}
+// the same over 4 elements (8-byte vectors of fp16)
+__device__ __forceinline__ f32x4 widen_hl4(const f16x4 &hi, const f16x4 &lo)
+{
+    const u32x2 h = __builtin_bit_cast(u32x2, hi), l = __builtin_bit_cast(u32x2, lo);
+    float x0, x1, x2, x3;
+    widen_hl2(h[0], l[0], x0, x1);
+    widen_hl2(h[1], l[1], x2, x3);
+    return f32x4{x0, x1, x2, x3};
+}
+__device__ __forceinline__ f32x4 widen_mul4(const f16x4 &v, const f32x4 &f)
+{
+    const u32x2 h = __builtin_bit_cast(u32x2, v);
+    float x0, x1, x2, x3;
+    widen_mul2(h[0], f[0], f[1], x0, x1);
+    widen_mul2(h[1], f[2], f[3], x2, x3);
+    return f32x4{x0, x1, x2, x3};
+}
+
 // d += A B for 16x16 blocks with a 16-deep contraction in about fp32 accuracy:
 // a[i] = A[c][4g+i], b[i] = B[4g+i][c] (lane = 16g + c); d in the same D layout.
 template <bool SPLIT>
@@ -1347,7 +1384,6 @@ __global__ void __launch_bounds__(NW * 64)
         gk_row[it] = wave0 * GRW + lane0 / GPR + it * NW * GRW;
         gk_off[it] = (gk_row[it] * H + head) * DK + (lane0 % GPR) * 4;
     }
-    const int gb_off = (tid0 & (CH - 1)) * H;  // this lane's row of the gates and betas
     // Fused front end: the raw rows of the chunk at c0 (Lc rows) and the KC - 1 rows before
     // it go straight into LDS by LDS-DMA, one 16-byte piece per lane (a wave instruction
     // fills up to 1 KiB): raw row rho of a region holds stream row c0 - (KC - 1) + rho: the
@@ -1463,10 +1499,12 @@ __global__ void __launch_bounds__(NW * 64)
             }
         }
         if (threadIdx.x < CH) {
-            // opaque per call: a 64-bit per-lane address held across the chunk loop would
-            // be spilled, and its reload waits for every load in flight
-            int go = gb_off;
-            asm volatile("" : "+v"(go));
+            // this lane's row of the gates and betas, derived from the thread index in each
+            // call: a per-lane offset held across the chunk loop is spilled, and its reload
+            // waits for every load and store in flight
+            int tx = threadIdx.x;
+            asm volatile("" : "+v"(tx));
+            const int go = (tx & (CH - 1)) * H;
             if constexpr (!KDA)
                 pg = (int)threadIdx.x < Lc ? (a.g + (c0 * H + head))[go] : 0.f;
             pb = (int)threadIdx.x < Lc ? (a.beta + (c0 * H + head))[go] : 0.f;
@@ -2034,21 +2072,6 @@ __global__ void __launch_bounds__(NW * 64)
                 const float *gs_ = Gk + (16 * J + c16) * LDG;
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    frag fk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
-                    frag fq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
-                    frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
-                    // k in about fp32 (hi + lo) before the factors are applied
-                    float kI[8], kJ[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        kI[i] = (float)fk[i], kJ[i] = (float)fb[i];
-                    if constexpr (C::KLO) {
-                        const frag fkl = ld_frag_qk<DK>(Kl, 16 * I, 32 * kb, lane);
-                        const frag fbl = ld_frag_qk<DK>(Kl, 16 * J, 32 * kb, lane);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            kI[i] += (float)fkl[i], kJ[i] += (float)fbl[i];
-                    }
                     const int c0 = 32 * kb + 4 * g4;
                     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(gb + c0);
                     const f32x4 b1 = *reinterpret_cast<const f32x4 *>(gb + c0 + 16);
@@ -2056,62 +2079,120 @@ __global__ void __launch_bounds__(NW * 64)
                     const f32x4 r1 = *reinterpret_cast<const f32x4 *>(gr_ + c0 + 16);
                     const f32x4 s0 = *reinterpret_cast<const f32x4 *>(gs_ + c0);
                     const f32x4 s1 = *reinterpret_cast<const f32x4 *>(gs_ + c0 + 16);
+                    f32x4 ea0, ea1, eb0, eb1;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float ea = __builtin_amdgcn_exp2f(r0[i] - b0[i]),
-                                    ea1 = __builtin_amdgcn_exp2f(r1[i] - b1[i]);
-                        fk[i] = (T)(kI[i] * ea);
-                        fk[4 + i] = (T)(kI[4 + i] * ea1);
-                        fq[i] = (T)((float)fq[i] * ea);
-                        fq[4 + i] = (T)((float)fq[4 + i] * ea1);
-                        fb[i] = (T)(kJ[i] * __builtin_amdgcn_exp2f(b0[i] - s0[i]));
-                        fb[4 + i] = (T)(kJ[4 + i] * __builtin_amdgcn_exp2f(b1[i] - s1[i]));
+                        ea0[i] = __builtin_amdgcn_exp2f(r0[i] - b0[i]);
+                        ea1[i] = __builtin_amdgcn_exp2f(r1[i] - b1[i]);
+                        eb0[i] = __builtin_amdgcn_exp2f(b0[i] - s0[i]);
+                        eb1[i] = __builtin_amdgcn_exp2f(b1[i] - s1[i]);
                     }
-                    if (do_m)
-                        mma(am, fk, fb);
-                    if (do_p)
-                        mma(ap, fq, fb);
+                    const frag fb = ld_frag_qk<DK>(Ks, 16 * J, 32 * kb, lane);
+                    if constexpr (SPLIT) {
+                        // k in about fp32 (hi + lo) before the factors are applied; the
+                        // fragment's elements 0-3 and 4-7 are channels c0 + 0..3, c0 + 16..19
+                        auto lo4 = [](const frag &f) {
+                            return __builtin_shufflevector(f, f, 0, 1, 2, 3);
+                        };
+                        auto hi4 = [](const frag &f) {
+                            return __builtin_shufflevector(f, f, 4, 5, 6, 7);
+                        };
+                        auto wid = [&](const frag &h, const frag *l, bool upper) {
+                            if constexpr (C::KLO)
+                                return upper ? widen_hl4(hi4(h), hi4(*l))
+                                             : widen_hl4(lo4(h), lo4(*l));
+                            else
+                                return __builtin_convertvector(upper ? hi4(h) : lo4(h), f32x4);
+                        };
+                        auto pack = [](const f32x4 &x0, const f32x4 &x1) {
+                            const f16x4 h0 = __builtin_convertvector(x0, f16x4);
+                            const f16x4 h1 = __builtin_convertvector(x1, f16x4);
+                            return __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        };
+                        frag fbl{};
+                        if constexpr (C::KLO)
+                            fbl = ld_frag_qk<DK>(Kl, 16 * J, 32 * kb, lane);
+                        const frag gbf = pack(wid(fb, &fbl, false) * eb0,
+                                              wid(fb, &fbl, true) * eb1);
+                        if (do_m) {
+                            const frag fk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
+                            frag fkl{};
+                            if constexpr (C::KLO)
+                                fkl = ld_frag_qk<DK>(Kl, 16 * I, 32 * kb, lane);
+                            mma(am, pack(wid(fk, &fkl, false) * ea0, wid(fk, &fkl, true) * ea1),
+                                gbf);
+                        }
+                        if (do_p) {
+                            const frag fq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
+                            mma(ap, pack(widen_mul4(lo4(fq), ea0), widen_mul4(hi4(fq), ea1)),
+                                gbf);
+                        }
+                    } else {
+                        frag fk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
+                        frag fq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
+                        frag fbs = fb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            fk[i] *= ea0[i];
+                            fk[4 + i] *= ea1[i];
+                            fq[i] *= ea0[i];
+                            fq[4 + i] *= ea1[i];
+                            fbs[i] *= eb0[i];
+                            fbs[4 + i] *= eb1[i];
+                        }
+                        if (do_m)
+                            mma(am, fk, fbs);
+                        if (do_p)
+                            mma(ap, fq, fbs);
+                    }
                 }
             } else {
                 // diagonal block: mid-block reference m = 16I + 8, so each factor spans at
                 // most 8 tokens of decay (exponents clamped at 80, 80 log2(e) in the log2
-                // units of Gk); the gated operands can
-                // exceed the fp16 range, so they go in fp32 range: fp32 MFMA for fp32 tiles,
-                // bf16 hi + lo pairs (about 16 mantissa bits) for fp16 tiles
+                // units of Gk). The gated operands can exceed the fp16 range, so the block's
+                // products run on fp32 MFMA, whose A and B elements of a lane come from one
+                // row and one channel: lane (g, c) takes row 16I + c and, over the 32 steps,
+                // channels 32g .. 32g + 31 (the contraction order is free), read as 4-element
+                // chunks of the tiles (k as its hi + lo pair).
                 const float *gm = Gk + (16 * I + 8) * LDG;
                 const float *grs = Gk + (16 * I + c16) * LDG;
                 if constexpr (SPLIT) {
+                    typedef T T4 __attribute__((ext_vector_type(4)));
+                    const int r = 16 * I + c16;
 #pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb) {
-                        const frag xk = ld_frag_qk<DK>(Ks, 16 * I, 32 * kb, lane);
-                        const frag xq = ld_frag_qk<DK>(Qs, 16 * I, 32 * kb, lane);
-                        frag xkl{};
+                    for (int jj = 0; jj < DK / 16; ++jj) {
+                        const int q4 = (DK / 16) * g4 + jj;  // 4-channel chunk
+                        const int off = QK<T, DK>::at(r, q4);
+                        const T4 kh4 = *reinterpret_cast<const T4 *>(Ks + off);
+                        const T4 qh4 = *reinterpret_cast<const T4 *>(Qs + off);
+                        T4 kl4{};
                         if constexpr (C::KLO)
-                            xkl = ld_frag_qk<DK>(Kl, 16 * I, 32 * kb, lane);
-                        const int c0 = 32 * kb + 4 * g4;
-                        bf16x8 kh_, kl_, qh_, ql_, bh, bl;
+                            kl4 = *reinterpret_cast<const T4 *>(Kl + off);
+                        const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(grs + 4 * q4);
+                        const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(gm + 4 * q4);
+                        f32x4 ea4, eb4;
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const int ch = c0 + (i < 4 ? i : 12 + i);
-                            const float d = grs[ch] - gm[ch];
-                            const float ea = __builtin_amdgcn_exp2f(fminf(d, kExpCap));
-                            const float kx = (float)xk[i] + (C::KLO ? (float)xkl[i] : 0.f);
-                            const float kv = kx * ea, qv = (float)xq[i] * ea;
-                            const float bv = kx * __builtin_amdgcn_exp2f(fminf(-d, kExpCap));
-                            kh_[i] = (bf16)kv;
-                            kl_[i] = (bf16)(kv - (float)kh_[i]);
-                            qh_[i] = (bf16)qv;
-                            ql_[i] = (bf16)(qv - (float)qh_[i]);
-                            bh[i] = (bf16)bv;
-                            bl[i] = (bf16)(bv - (float)bh[i]);
+                        for (int e = 0; e < 4; ++e) {
+                            const float d = gr4[e] - gm4[e];
+                            ea4[e] = __builtin_amdgcn_exp2f(fminf(d, kExpCap));
+                            eb4[e] = __builtin_amdgcn_exp2f(fminf(-d, kExpCap));
                         }
-                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bh, am, 0, 0, 0);
-                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh_, bl, am, 0, 0, 0);
-                        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl_, bh, am, 0, 0, 0);
+                        f32x4 kx4;
+                        if constexpr (C::KLO)
+                            kx4 = widen_hl4(__builtin_bit_cast(f16x4, kh4),
+                                            __builtin_bit_cast(f16x4, kl4));
+                        else
+                            kx4 = __builtin_convertvector(__builtin_bit_cast(f16x4, kh4), f32x4);
+                        const f32x4 ka4 = kx4 * ea4, kb4 = kx4 * eb4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            am = __builtin_amdgcn_mfma_f32_16x16x4f32(ka4[e], kb4[e], am, 0, 0, 0);
                         if (do_p) {
-                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bh, ap, 0, 0, 0);
-                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh_, bl, ap, 0, 0, 0);
-                            ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql_, bh, ap, 0, 0, 0);
+                            const f32x4 qa4 = widen_mul4(__builtin_bit_cast(f16x4, qh4), ea4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                ap = __builtin_amdgcn_mfma_f32_16x16x4f32(qa4[e], kb4[e], ap, 0,
+                                                                          0, 0);
                         }
                     }
                 } else {
@@ -2237,24 +2318,35 @@ __global__ void __launch_bounds__(NW * 64)
                 const int r = r0 + it * (NT / (DK / 4));
                 const int off = QK<T, DK>::at(r, c0 / 4);
                 T4 kd, kdl, ke, qe;
-                f32x4 dv;
+                f32x4 e4, d4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(gv[it][i]);
-                    const float kx = (float)kv[it][i] + (C::KLO ? (float)klv[it][i] : 0.f);
-                    dv[i] = kx * __builtin_amdgcn_exp2f(gcv[i] - gv[it][i]);
-                    ke[i] = (T)(kx * e);
-                    qe[i] = (T)((float)qv[it][i] * e);
+                    e4[i] = __builtin_amdgcn_exp2f(gv[it][i]);
+                    d4[i] = __builtin_amdgcn_exp2f(gcv[i] - gv[it][i]);
                 }
                 if constexpr (SPLIT) {
+                    const f16x4 k16 = __builtin_bit_cast(f16x4, kv[it]);
+                    f32x4 kx4;
+                    if constexpr (C::KLO)
+                        kx4 = widen_hl4(k16, __builtin_bit_cast(f16x4, klv[it]));
+                    else
+                        kx4 = __builtin_convertvector(k16, f32x4);
                     f16x4 h4, l4;
-                    split4(dv, h4, l4);
+                    split4(kx4 * d4, h4, l4);
                     kd = __builtin_bit_cast(T4, h4);
                     kdl = __builtin_bit_cast(T4, l4);
+                    ke = __builtin_bit_cast(T4, __builtin_convertvector(kx4 * e4, f16x4));
+                    qe = __builtin_bit_cast(
+                        T4, __builtin_convertvector(
+                                widen_mul4(__builtin_bit_cast(f16x4, qv[it]), e4), f16x4));
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        kd[i] = dv[i];
+                    for (int i = 0; i < 4; ++i) {
+                        const float kx = kv[it][i];
+                        kd[i] = kx * d4[i];
+                        ke[i] = kx * e4[i];
+                        qe[i] = qv[it][i] * e4[i];
+                    }
                 }
                 *reinterpret_cast<T4 *>(Kd + off) = kd;
                 if constexpr (C::KLO)
