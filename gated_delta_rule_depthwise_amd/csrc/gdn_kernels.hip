@@ -1477,6 +1477,14 @@ __global__ void __launch_bounds__(NW * 64)
                 prefetch_raw(c0, Lc, with_q, lane, wave, 1);
                 prefetch_raw(c0, Lc, with_q, lane, wave, 0);
             }
+        } else if (Lc == CH) {  // a whole chunk: only wave-uniform conditions
+#pragma unroll
+            for (int it = 0; it < NQK; ++it)
+                pq[it] = qk_isk[it] || with_q ? load_stream16(qk_src[it] + roff)
+                                              : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int it = 0; it < NVV; ++it)
+                pv[it] = !v_zero ? load_stream16(v_src[it] + roff) : make_uint4(0, 0, 0, 0);
         } else {
 #pragma unroll
             for (int it = 0; it < NQK; ++it)
@@ -1619,11 +1627,18 @@ __global__ void __launch_bounds__(NW * 64)
                                Z4<TZ>::get(z));
             }
         }
+        if (Lc == CH) {  // a whole chunk: no per-row test
 #pragma unroll
-        for (int it = 0; it < NR; ++it) {
-            const int r = it * RPP + tid / V4;
-            if (r < Lc)
-                store_stream16(ob + (c0 + r) * (int64_t)H * DV + 4 * j, ov[it]);
+            for (int it = 0; it < NR; ++it)
+                store_stream16(ob + (c0 + it * RPP + tid / V4) * (int64_t)H * DV + 4 * j,
+                               ov[it]);
+        } else {
+#pragma unroll
+            for (int it = 0; it < NR; ++it) {
+                const int r = it * RPP + tid / V4;
+                if (r < Lc)
+                    store_stream16(ob + (c0 + r) * (int64_t)H * DV + 4 * j, ov[it]);
+            }
         }
     };
 
@@ -1687,7 +1702,11 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
                     for (int j = 0; j < KC; ++j)
                         acc += wv[j] * xr[i + j];
-                    v[i] = 16 * I + 4 * g4 + i < Lc && !v_zero ? silu(acc) : 0.f;
+                    // computed on every lane and then selected: a branch around it per
+                    // element would cost more than the SiLU (stale rows never reach v)
+                    float sv = silu(acc);
+                    asm volatile("" : "+v"(sv));
+                    v[i] = 16 * I + 4 * g4 + i < Lc && !v_zero ? sv : 0.f;
                 }
             } else {
 #pragma unroll
@@ -1900,7 +1919,9 @@ __global__ void __launch_bounds__(NW * 64)
                     for (int m = 1; m < LPR; m <<= 1)
                         ss += __shfl_xor(ss, m);
                 }
-                mul = r < L ? mul * rsqrtf(ss + a.eps) : 0.f;
+                float rs = rsqrtf(ss + a.eps);  // on every lane, then selected
+                asm volatile("" : "+v"(rs));
+                mul = r < L ? mul * rs : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
@@ -1975,8 +1996,11 @@ __global__ void __launch_bounds__(NW * 64)
             __syncthreads();
             float add = 0.f;
 #pragma unroll
-            for (int pp = 0; pp < PARTS - 1; ++pp)
-                add += pp < part ? tot[pp * DK + c] : 0.f;
+            for (int pp = 0; pp < PARTS - 1; ++pp) {
+                float t = tot[pp * DK + c];  // read by every lane, then selected
+                asm volatile("" : "+v"(t));
+                add += pp < part ? t : 0.f;
+            }
 #pragma unroll
             for (int j = 0; j < RP; ++j)
                 Gk[(part * RP + j) * LDG + c] = xs[j] + add;
@@ -2212,6 +2236,9 @@ __global__ void __launch_bounds__(NW * 64)
                 }
             }
             const int s = 16 * J + c16;
+            // this lane's betas (rows 16 I + 4 g + i), read whether or not a row is used, so
+            // that the selects below stay selects
+            const f32x4 bet4 = *reinterpret_cast<const f32x4 *>(bet + 16 * I + 4 * g4);
             float gs = gcol[0];
 #pragma unroll
             for (int jj = 1; jj < NB; ++jj)
@@ -2233,7 +2260,7 @@ __global__ void __launch_bounds__(NW * 64)
                     if constexpr (SPLIT)
                         Psl[r * LDT + s] = (T)(pv_ - (float)phi);
                 }
-                const float mv = s < r ? bet[r] * dec * am[i] : 0.f;
+                const float mv = s < r ? bet4[i] * dec * am[i] : 0.f;
                 am[i] = mv;
                 if (I != J && do_m)
                     MTh[r * LDT + s] = (T)mv;
@@ -2453,13 +2480,22 @@ __global__ void __launch_bounds__(NW * 64)
                             mma(o[I], ld_frag(Psl, LDT, 16 * I, 32 * kb, lane), uh[kb]);
                         }
                     }
+                    const int col = 16 * (wave * NCB + cb) + c16;
+                    if constexpr (C::STAGE_O) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * I + 4 * g4 + i, col = 16 * (wave * NCB + cb) + c16;
-                        if constexpr (C::STAGE_O)
-                            Os[r * LDO + col] = o[I][i];
-                        else if (r < L)
-                            ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
+                        for (int i = 0; i < 4; ++i)
+                            Os[(16 * I + 4 * g4 + i) * LDO + col] = o[I][i];
+                    } else if (L == CH) {  // a whole chunk: no per-row test
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            ob[(cs + 16 * I + 4 * g4 + i) * (int64_t)H * DV + col] = o[I][i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 16 * I + 4 * g4 + i;
+                            if (r < L)
+                                ob[(cs + r) * (int64_t)H * DV + col] = o[I][i];
+                        }
                     }
                 }
             }
