@@ -1266,7 +1266,7 @@ __global__ void __launch_bounds__(NW * 64)
     const int H = a.H;
     const int BH = a.st.B * H;
     constexpr int NS = DV / NV;  // dv slices
-    const int job = blockIdx.x / (BH * NS), jr = blockIdx.x - job * (BH * NS);
+    const int jp = blockIdx.x / (BH * NS), jr = blockIdx.x - jp * (BH * NS);
     const int slice = jr / BH, bh = jr - slice * BH;
     const int bi = bh / H, head = bh - bi * H;
     const int b = a.order ? a.order[bi] : bi;  // varlen: longest streams dispatch first
@@ -1290,6 +1290,12 @@ __global__ void __launch_bounds__(NW * 64)
         const bool warm = a.warm && warm_head(a.seg_ws, lay, b, head);
         int seg;
         if (a.pass == 1) {
+            // Job order: 0 segment 0, 1..S-2 end states, S-1..2S-4 transitions, 2S-3..3S-5
+            // warm jobs of segments 1..S-1. With warm starts possible the grid puts the warm
+            // jobs right after segment 0 and the map jobs last: workgroups dispatch in grid
+            // order, and in warm mode the map jobs return at once, so they then neither sit
+            // in front of the warm jobs nor delay their start.
+            const int job = !a.warm || jp == 0 ? jp : jp < S ? 2 * S - 4 + jp : jp - S + 1;
             if (job >= 2 * S - 3) {  // warm job of segment job - (2S - 4)
                 if (!warm)
                     return;
@@ -1319,7 +1325,7 @@ __global__ void __launch_bounds__(NW * 64)
         } else {
             if (warm)
                 return;
-            seg = job + 1;
+            seg = jp + 1;
             hin = a.seg_ws + lay.h(b, seg);
             if (seg < S - 1)
                 hout = nullptr;
