@@ -1162,8 +1162,11 @@ __device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, 
 {
     const f16x4 a = *reinterpret_cast<const f16x4 *>(X + (16 * I + (lane & 15)) * ld + 16 * J +
                                                     4 * (lane >> 4));
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bh, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bl, d, 0, 0, 0);
+    // A B_hi + A B_lo as one 32-deep product of [A A] and [B_hi; B_lo] (the 16-deep product
+    // takes as long as the 32-deep one on gfx950)
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3),
+                                               __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               d, 0, 0, 0);
 }
 __device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, int J,
                                          const f32x4 &b, int lane)
