@@ -1157,6 +1157,16 @@ __device__ __forceinline__ f32x4 blk_a16(const float *X, int ld, int I, int J, i
 // its rounding adds no measurable error to o or h (the M blocks below the diagonal and the
 // inverted diagonal blocks enter U only through products with the split right-hand side),
 // while rounding B does. fp32 tiles use fp32 MFMA directly.
+// d += A (B_hi + B_lo) for a 16x16 A fragment already in registers (a[i] = A[c][4g+i]), as
+// one 32-deep product of [A A] and [B_hi; B_lo] (the 16-deep product takes as long as the
+// 32-deep one on gfx950)
+__device__ __forceinline__ void mm16_frag(f32x4 &d, const f16x4 &a, const f16x4 &bh,
+                                          const f16x4 &bl)
+{
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3),
+                                               __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               d, 0, 0, 0);
+}
 __device__ __forceinline__ void mm16_pre(f32x4 &d, const f16 *X, int ld, int I, int J,
                                          const f16x4 &bh, const f16x4 &bl, int lane)
 {
@@ -2450,24 +2460,44 @@ __global__ void __launch_bounds__(NW * 64)
             // and for P U)
             f32x4 u[NB];
             f16x4 uhs[NB], uls[NB];
+            // fp16 operands: the blocks of MT (T_II and M_IJ, J < I) and this lane's betas are
+            // all read before the substitution starts, so that its chain of dependent
+            // products waits on LDS once
+            f16x4 mt[SPLIT ? NB * (NB + 1) / 2 : 1];
+            f32x4 bt[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                bt[I] = *reinterpret_cast<const f32x4 *>(bet + 16 * I + 4 * g4);
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int J = 0; J <= I; ++J)
+                        mt[I * (I + 1) / 2 + J] = *reinterpret_cast<const f16x4 *>(
+                            (const T *)MTh + (16 * I + c16) * LDT + 16 * J + 4 * g4);
+                }
+            }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int J = 0; J < I; ++J) {
                     if constexpr (SPLIT)
-                        mm16_pre(acc, MTh, LDT, I, J, uhs[J], uls[J], lane);
+                        mm16_frag(acc, mt[I * (I + 1) / 2 + J], uhs[J], uls[J]);
                     else
                         mm16_pre(acc, MTh, LDT, I, J, u[J], lane);
                 }
                 f32x4 z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    z[i] = bet[16 * I + 4 * g4 + i] * x[I][i] - acc[i];
+                    z[i] = bt[I][i] * x[I][i] - acc[i];
                 u[I] = zero4();
-                mm16_pre(u[I], MTh, LDT, I, I, z, lane);
-                if constexpr (SPLIT)
+                if constexpr (SPLIT) {
+                    f16x4 zh, zl;
+                    split4(z, zh, zl);
+                    mm16_frag(u[I], mt[I * (I + 1) / 2 + I], zh, zl);
                     split4(u[I], uhs[I], uls[I]);
+                } else {
+                    mm16_pre(u[I], MTh, LDT, I, I, z, lane);
+                }
             }
             if (FRONT && pf)
                 prefetch_group(cs + CH, pfL, 1);
