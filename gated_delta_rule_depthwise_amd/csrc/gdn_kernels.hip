@@ -2099,6 +2099,108 @@ __global__ void __launch_bounds__(NW * 64)
             const int I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
             const int J = p - I * (I + 1) / 2;
             f32x4 am = zero4(), ap = zero4();
+            // D layout -> A layout through LDS, in this diagonal block's own corner of Ms or
+            // (fused front end) its own scratch block (no other wave touches it)
+            float *scr = C::XSCR ? Xs + 16 * I * C::LDX : Ms + 16 * I * LDF + 16 * I;
+            constexpr int lds = C::XSCR ? C::LDX : LDF;
+            auto to_a = [&](const f32x4 &d) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    scr[(4 * g4 + i) * lds + c16] = d[i];
+                return blk_a(scr, lds, 0, 0, lane);
+            };
+            // T_II = (I - N)^-1 with N = -M_II strictly lower (N^16 = 0):
+            // (I + N)(I + N^2)(I + N^4)(I + N^8), the products on fp32 MFMA; step(k) is
+            // called between the inverse's dependent steps (k = 0..3) to issue independent
+            // work into their latency
+            auto invert = [&](const f32x4 &m, auto step) {
+                f32x4 nb;  // N, D layout
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    nb[i] = -m[i];
+                const f32x4 na = to_a(nb);
+                step(0);
+                f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
+                mm16<false>(n2, na, nb);  // N^2
+                step(1);
+                mm16<false>(n3, na, n2);  // N^3
+                const f32x4 n2a = to_a(n2);
+                step(2);
+                mm16<false>(n4, n2a, n2);  // N^4
+                const f32x4 n4a = to_a(n4);
+                step(3);
+                mm16<false>(n8, n4a, n4);  // N^8
+                const f32x4 n8a = to_a(n8);
+                f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[i] = ((4 * g4 + i) == c16 ? 1.f : 0.f) + nb[i] + n2[i] + n3[i];
+                f32x4 y = x;
+                mm16<false>(y, n4a, x);  // (I + N^4) X
+                f32x4 z = y;
+                mm16<false>(z, n8a, y);  // (I + N^8) Y
+                return z;
+            };
+            if (!KDA && FRONT && I == J) {
+                // Diagonal block, scalar gate (fused front end; the register-path instances
+                // have no registers to hold K_I across the inverse): M_II first, then its
+                // inverse with P_II's products issued between the inverse's dependent steps,
+                // then P_II's stores.
+                const int base = 16 * I, s = base + c16;
+                frag kf[DK / 32];
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    kf[kb] = ld_frag_qk<DK>(Ks, base, 32 * kb, lane);
+                    mma(am, kf[kb], kf[kb]);
+                }
+                const f32x4 bet4 = *reinterpret_cast<const f32x4 *>(bet + base + 4 * g4);
+                float gs = gcol[0];
+#pragma unroll
+                for (int jj = 1; jj < NB; ++jj)
+                    gs = I == jj ? gcol[jj] : gs;
+                float dec[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = base + 4 * g4 + i;
+                    float grr = gr[0][i];
+#pragma unroll
+                    for (int ii = 1; ii < NB; ++ii)
+                        grr = I == ii ? gr[ii][i] : grr;
+                    dec[i] = __expf(grr - gs);  // e^(G_r - G_s); the upper part is masked
+                    am[i] = s < r ? bet4[i] * dec[i] * am[i] : 0.f;
+                }
+                auto p_step = [&](int kb) {  // the inverse has 4 steps, DK / 32 <= 4
+                    static_assert(DK / 32 <= 4, "P steps");
+                    if (!do_p || kb >= DK / 32)
+                        return;
+                    if constexpr (FRONT) {
+                        // Q K^T with q and k as fp16 hi + lo pairs (the lo x lo term is below
+                        // fp32 rounding)
+                        const frag qh8 = ld_frag_qk<DK>(Qs, base, 32 * kb, lane);
+                        mma(ap, qh8, kf[kb]);
+                        mma(ap, qh8, ld_frag_qk<DK>(Kl, base, 32 * kb, lane));
+                        mma(ap, ld_frag_qk<DK>(Ql, base, 32 * kb, lane), kf[kb]);
+                    } else {
+                        mma(ap, ld_frag_qk<DK>(Qs, base, 32 * kb, lane), kf[kb]);
+                    }
+                };
+                const f32x4 z = invert(am, p_step);
+                if (do_p) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = base + 4 * g4 + i;
+                        const float pv_ = s <= r ? dec[i] * ap[i] : 0.f;
+                        const T phi = (T)pv_;
+                        Ps[r * LDT + s] = phi;
+                        if constexpr (SPLIT)
+                            Psl[r * LDT + s] = (T)(pv_ - (float)phi);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    MTh[(base + 4 * g4 + i) * LDT + base + c16] = (T)z[i];
+                continue;
+            }
             if constexpr (!KDA) {
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
@@ -2296,44 +2398,10 @@ __global__ void __launch_bounds__(NW * 64)
                     MTh[r * LDT + s] = (T)mv;
             }
             if (I == J) {
-                // T_II = (I - N)^-1 with N = -M_II strictly lower (N^16 = 0):
-                // (I + N)(I + N^2)(I + N^4)(I + N^8), the products on fp32 MFMA. A-layout
-                // operands go through this block's own corner of Ms (no other wave touches
-                // it).
-                const int base = 16 * I;
-                // this block's corner of Ms, or (fused front end) its own scratch block
-                float *scr = C::XSCR ? Xs + base * C::LDX : Ms + base * LDF + base;
-                constexpr int lds = C::XSCR ? C::LDX : LDF;
-                auto to_a = [&](const f32x4 &d) {  // D layout -> A layout through LDS
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        scr[(4 * g4 + i) * lds + c16] = d[i];
-                    return blk_a(scr, lds, 0, 0, lane);
-                };
-                f32x4 nb;  // N, D layout
+                const f32x4 z = invert(am, [](int) {});
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    nb[i] = -am[i];
-                const f32x4 na = to_a(nb);
-                f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
-                mm16<false>(n2, na, nb);  // N^2
-                mm16<false>(n3, na, n2);  // N^3
-                const f32x4 n2a = to_a(n2);
-                mm16<false>(n4, n2a, n2);  // N^4
-                const f32x4 n4a = to_a(n4);
-                mm16<false>(n8, n4a, n4);  // N^8
-                const f32x4 n8a = to_a(n8);
-                f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    x[i] = ((4 * g4 + i) == c16 ? 1.f : 0.f) + nb[i] + n2[i] + n3[i];
-                f32x4 y = x;
-                mm16<false>(y, n4a, x);  // (I + N^4) X
-                f32x4 z = y;
-                mm16<false>(z, n8a, y);  // (I + N^8) Y
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    MTh[(base + 4 * g4 + i) * LDT + base + c16] = (T)z[i];
+                    MTh[(16 * I + 4 * g4 + i) * LDT + 16 * I + c16] = (T)z[i];
             }
         }
         __syncthreads();
