@@ -264,14 +264,23 @@ struct QK {
     }
 };
 
-// ld_frag for a Q/K tile
+// ld_frag for a Q/K tile. row0 is a multiple of 16 and k0 of 32, so the permutation of a
+// lane's chunks depends on the lane alone: the offset is row0 * LD + k0 plus a lane part
+// (the same in every call, so the compiler keeps one address per tile and folds the rest
+// into the instruction's offset), and chunk ch + 4 sits 16 elements after chunk ch.
+template <int DK>
+__device__ __forceinline__ int qk_lane_part(int lane)
+{
+    using L = QK<f16, DK>;
+    return (lane & 15) * L::LD + ((lane >> 4) ^ ((lane >> 2) & 3)) * 4;
+}
 template <int DK>
 __device__ __forceinline__ f16x8 ld_frag_qk(const f16 *X, int row0, int k0, int lane)
 {
     using L = QK<f16, DK>;
-    const int r = row0 + (lane & 15), ch = k0 / 4 + (lane >> 4);
-    const f16x4 lo = *reinterpret_cast<const f16x4 *>(X + L::at(r, ch));
-    const f16x4 hi = *reinterpret_cast<const f16x4 *>(X + L::at(r, ch + 4));
+    const f16 *p = X + row0 * L::LD + k0 + qk_lane_part<DK>(lane);
+    const f16x4 lo = *reinterpret_cast<const f16x4 *>(p);
+    const f16x4 hi = *reinterpret_cast<const f16x4 *>(p + 16);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 template <int DK>
@@ -1020,13 +1029,14 @@ __device__ __forceinline__ f32x8 ld_frag_t(const float *X, int ld, int k0, int n
 template <int DK>
 __device__ __forceinline__ f16x8 ld_frag_t_qk(const f16 *X, int k0, int n0, int lane)
 {
+    // k0 is a multiple of 16 and n0 of 16: the chunk permutation of row k0 + 4g + s/4 is g,
+    // so the offset is k0 * LD + n0 plus a lane part, and the second read is 16 rows on
     using L = QK<f16, DK>;
     const int g = lane >> 4, s = lane & 15;
-    const int r = k0 + 4 * g + (s >> 2), ch = n0 / 4 + (s & 3);
+    const f16 *p = X + k0 * L::LD + n0 + (4 * g + (s >> 2)) * L::LD + ((s & 3) ^ g) * 4;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + L::at(r, ch)));
-    const s16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + L::at(r + 16, ch)));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * L::LD));
     const f16x4 flo = __builtin_bit_cast(f16x4, lo), fhi = __builtin_bit_cast(f16x4, hi);
     return __builtin_shufflevector(flo, fhi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
