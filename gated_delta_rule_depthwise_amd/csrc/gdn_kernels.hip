@@ -1780,23 +1780,12 @@ __global__ void __launch_bounds__(NW * 64)
         // Thread coordinates and tile addresses are re-derived from opaque copies in every
         // chunk: otherwise the compiler hoists each per-lane LDS address out of the loop
         // and holds a register for every one of them across all stages.
-        int zo = 0, zq = 0, zkl = 0, zql = 0, tz = threadIdx.x;
+        int zo = 0, tz = threadIdx.x;
         asm volatile("" : "+s"(zo));
-        if constexpr (FRONT && !KDA) {
-            // the Q, Q lo and K lo tiles from bases of their own: with one base the compiler
-            // pairs reads at the same place of two tiles into one instruction and then moves
-            // registers to assemble each fragment (measured on the instance with both lo
-            // tiles; the others come out shorter with the one base)
-            asm volatile("" : "+s"(zq));
-            asm volatile("" : "+s"(zkl));
-            asm volatile("" : "+s"(zql));
-        } else {
-            zq = zkl = zql = zo;
-        }
         asm volatile("" : "+v"(tz));
         const int tid = tz, lane = tz & 63, g4 = lane >> 4, c16 = lane & 15;
         const int wave = __builtin_amdgcn_readfirstlane(tz >> 6);
-        T *Qs = (T *)(smem + zq + C::OFF_Q);
+        T *Qs = (T *)(smem + zo + C::OFF_Q);
         T *Ks = (T *)(smem + zo + C::OFF_K);
         T *Vs = (T *)(smem + zo + C::OFF_V);
         T *Ps = (T *)(smem + zo + C::OFF_P);
@@ -1809,8 +1798,8 @@ __global__ void __launch_bounds__(NW * 64)
         float *ea = graw + 2 * CH;  // a_r = e^Gamma_r
         float *ed = graw + 3 * CH;  // a_C / a_r
         float *Os = (float *)(smem + zo + C::OFF_O);
-        T *Kl = (T *)(smem + zkl + C::OFF_KL);     // fused front end: K lo
-        T *Ql = (T *)(smem + zql + C::OFF_QL);     // fused front end: Q lo
+        T *Kl = (T *)(smem + zo + C::OFF_KL);      // fused front end: K lo
+        T *Ql = (T *)(smem + zo + C::OFF_QL);      // fused front end: Q lo
         float *Xs = (float *)(smem + zo + C::OFF_X);  // fused front end: inversion scratch
 
         // the previous chunk's z tile (LDS-DMA, counted like the prefetch loads) lands
