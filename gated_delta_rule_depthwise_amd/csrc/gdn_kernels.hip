@@ -988,12 +988,16 @@ struct ChunkCfg {
     // norm weights of the NV columns
     static constexpr int OFF_Z = OFF_CW + (FRONT ? 2 * KC * DK * 4 : 0);
     static constexpr int ZROW = NV * (int)sizeof(T);
-    static constexpr int OFF_W = OFF_Z + (GATE ? CH * ZROW : 0);
+    // fused front end with the output gate: no LDS left for a z tile; each thread holds
+    // the z values of its o flush in registers instead
+    static constexpr bool ZREG = GATE && FRONT;
+    static constexpr int OFF_W = OFF_Z + (GATE && !ZREG ? CH * ZROW : 0);
     static constexpr int BYTES = OFF_W + (GATE ? NV * 4 : 0);
     // the raw q|k rows land on the dead tiles at the start of the layout
     static_assert(!FRONT || RR * RQK <= (KDA ? OFF_KL : OFF_K), "raw q|k rows fit");
-    static_assert(!FRONT || (SPLIT && !GATE && NCB == 1 && (STAGE_O || KDA)),
-                  "fused front end: fp16 operands, one column block per wave, no output gate");
+    static_assert(!FRONT || (SPLIT && !(GATE && KDA) && NCB == 1 && (STAGE_O || KDA)),
+                  "fused front end: fp16 operands, one column block per wave, the output "
+                  "gate with the scalar gate only");
 };
 
 // Operand fragment that runs down the columns of a row-major LDS tile X[k][n]:
@@ -1609,9 +1613,22 @@ __global__ void __launch_bounds__(NW * 64)
     constexpr int V4 = NV / 4, RPP = NT / V4, NR = CH / RPP;
     static_assert(NT % V4 == 0 && CH % RPP == 0 && (V4 == 16 || V4 == 32), "o row map");
     constexpr int LZ = C::ZROW / 16, RL = 64 / LZ;
-    static_assert(!GATE || ((LZ == 8 || LZ == 16) && (CH / RL) % NW == 0), "z tile map");
+    static_assert(!GATE || C::ZREG || ((LZ == 8 || LZ == 16) && (CH / RL) % NW == 0),
+                  "z tile map");
+    // z in registers (fused front end): thread tid holds z of rows it * RPP + tid / V4,
+    // columns 4 (tid % V4) .. +3 -- the values its flush of that chunk's o gates
+    typename Z4<TZ>::raw zr[C::ZREG ? NR : 1];
     const TZ *zg = GATE ? (const TZ *)a.z + head * DV : nullptr;
     auto load_z = [&](int64_t c0, int Lc, int lane, int wave) {
+        if constexpr (C::ZREG) {
+            const int tid = threadIdx.x, j = tid % V4;
+#pragma unroll
+            for (int it = 0; it < NR; ++it) {
+                const int r = it * RPP + tid / V4;
+                zr[it] = r < Lc ? Z4<TZ>::load(zg + (c0 + r) * a.ld_z + 4 * j) : Z4<TZ>::zero();
+            }
+            return;
+        }
         typedef __attribute__((address_space(1))) void gptr;
         typedef __attribute__((address_space(3))) void lptr;
         constexpr int NZI = CH / RL / NW;  // loads per wave
@@ -1650,8 +1667,10 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
             for (int it = 0; it < NR; ++it) {
                 const int r = it * RPP + tid / V4;
-                const typename Z4<TZ>::raw z = *reinterpret_cast<const typename Z4<TZ>::raw *>(
-                    smem + C::OFF_Z + r * C::ZROW + 4 * j * (int)sizeof(TZ));
+                const typename Z4<TZ>::raw z =
+                    C::ZREG ? zr[it]
+                            : *reinterpret_cast<const typename Z4<TZ>::raw *>(
+                                  smem + C::OFF_Z + r * C::ZROW + 4 * j * (int)sizeof(TZ));
                 ov[it] = gate4(ov[it], rsqrtf(ss[it] * (1.f / DV) + a.norm_eps), w,
                                Z4<TZ>::get(z));
             }
@@ -2756,7 +2775,9 @@ hipError_t launch_chunk_t(const ChunkArgs &a, int grid, hipStream_t s)
     X(float, float, 0, 64, 128, 4, 1, false, false, false, 64) \
     X(float, float, 0, 64, 128, 4, 1, true, false, false, 64) \
     X(bf16, f16, 3, 128, 128, 8, 1, false, false, true, 64) \
+    X(bf16, f16, 3, 128, 128, 8, 1, false, true, true, 64) \
     X(bf16, f16, 3, 64, 64, 4, 1, false, false, true, 64) \
+    X(bf16, f16, 3, 64, 64, 4, 1, false, true, true, 64) \
     X(bf16, f16, 3, 128, 128, 8, 1, true, false, true, 64) \
     X(bf16, f16, 3, 64, 64, 4, 1, true, false, true, 64) \
     X(bf16, f16, 3, 128, 256, 8, 1, false, false, true, 64) \

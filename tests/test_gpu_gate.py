@@ -1,10 +1,10 @@
 """Parity of the output gate (gated RMSNorm of o with z) with the oracle.
 
 The reference output is the oracle's o passed through the oracle's gated RMSNorm. Where the
-chunk kernel stages whole o rows and a z tile in LDS the gate runs in its o flush; the
-per-key-channel instances at dk = dv = 128 and in fp32 run it as its own pass
-(gate_kernel); the decode kernel applies it to the row it finishes. Every kind is covered
-below.
+chunk kernel stages whole o rows the gate runs in its o flush, with z from an LDS tile or,
+in the scalar gate's fused front end, from registers; the per-key-channel instances at
+dk = dv = 128 and in fp32 run it as its own pass (gate_kernel); the decode kernel applies
+it to the row it finishes. Every kind is covered below.
 """
 import dataclasses
 
@@ -58,6 +58,7 @@ def gated_err(y, y_ref, o_ref, z, w, eps):
 
 CASES = {
     "gdn-bf16-front-d128": dict(base=2, lengths=[777], H=4),
+    "gdn-bf16-front-d64": dict(base=2, lengths=[777], H=4, dk=64, dv=64),
     "gdn-bf16-d128": dict(base=3, lengths=[300], H=3),
     "gdn-f32-d64": dict(base=1, lengths=[333], H=2, h0_std=0.1),
     "kda-bf16-front-d128": dict(base=5, lengths=[500], H=2),
@@ -82,15 +83,17 @@ def test_gated_prefill_matches_oracle(name):
 
 
 def test_gate_pass_only_where_o_is_not_staged():
-    """The per-key-channel instances at 128 columns and in fp32, and every call whose front
-    end runs inside the scan (its tiles leave no room for a z tile), gate in a pass of
-    their own; the others gate in the o flush and record nothing in that profile bucket."""
+    """The per-key-channel instances at 128 columns and in fp32, and calls whose front end
+    runs inside the scan with the per-key-channel gate, gate in a pass of their own; the
+    others gate in the o flush (with the scalar gate's fused front end, z in registers: its
+    tiles leave no room for a z tile) and record nothing in that profile bucket."""
     for base, kw, want in ((5, dict(lengths=[200], H=2), 1),
                            (5, dict(lengths=[200], H=2, front_end=False), 1),
                            (1, dict(lengths=[200], H=2, gate="kda"), 1),
                            (1, dict(lengths=[200], H=2), 0),
                            (3, dict(lengths=[200], H=2), 0),
-                           (2, dict(lengths=[200], H=2), 1)):
+                           (2, dict(lengths=[200], H=2), 0),
+                           (2, dict(lengths=[200], H=2, dk=64, dv=64), 0)):
         spec = spec_small(base, out_gate=True, seed=22, **kw)
         inp = inputs.make(spec)
         B.gdn_profile_read()
