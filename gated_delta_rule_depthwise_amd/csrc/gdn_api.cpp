@@ -209,6 +209,8 @@ size_t front_bytes(const gdn_params *p, int kda, int64_t max_tokens, int32_t B)
 // transition (the same recurrence from h = I with v = 0); a small kernel chains
 // h_{s+1} = A_s h_s + b_s; a second launch runs segments 1..S-1 from their start states.
 constexpr int kMaxSeg = 12;
+// the kernels read a (stream, head)'s S - 1 warm-start counts one per lane of a wave
+static_assert(kMaxSeg - 1 <= 64, "segment boundaries per wave");
 
 int cu_count()
 {

@@ -62,15 +62,21 @@ struct SegLayout {
     }
 };
 
-// Warm mode of a (stream, head): every boundary s = 1..S-1 found its window (the plan leaves
-// a positive chunk count, 0 where it found none).
-__device__ __forceinline__ bool warm_head(const float *seg_ws, const SegLayout &lay, int b,
-                                          int head)
+// The plan's warm-up chunk count of boundary s = lane + 1 (1 past the last boundary): whole
+// waves read all S - 1 <= 64 counts with one load each, so they arrive after one memory
+// latency, not S - 1 dependent ones.
+__device__ __forceinline__ float warm_lane_count(const float *seg_ws, const SegLayout &lay,
+                                                 int b, int head)
 {
-    bool ok = true;
-    for (int s = 1; s < lay.S; ++s)
-        ok = ok && seg_ws[lay.warm_chunks(b, s, head)] > 0.f;
-    return ok;
+    const int s = (int)(threadIdx.x & 63) + 1;
+    return s < lay.S ? seg_ws[lay.warm_chunks(b, s, head)] : 1.f;
+}
+
+// Warm mode of a (stream, head), from warm_lane_count of every lane: each boundary found its
+// window (the plan leaves a positive chunk count, 0 where it found none).
+__device__ __forceinline__ bool warm_head(float lane_count)
+{
+    return __ballot(!(lane_count > 0.f)) == 0;
 }
 
 // h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).

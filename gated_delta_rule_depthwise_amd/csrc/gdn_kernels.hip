@@ -1314,7 +1314,8 @@ __global__ void __launch_bounds__(NW * 64)
         const int S = a.nseg;
         // warm mode of this (stream, head): uniform over the workgroup; the jobs it makes
         // redundant return before touching LDS or a barrier
-        const bool warm = a.warm && warm_head(a.seg_ws, lay, b, head);
+        const float wcount = a.warm ? warm_lane_count(a.seg_ws, lay, b, head) : 0.f;
+        const bool warm = a.warm && warm_head(wcount);
         int seg;
         if (a.pass == 1) {
             // Job order: 0 segment 0, 1..S-2 end states, S-1..2S-4 transitions, 2S-3..3S-5
@@ -1333,7 +1334,10 @@ __global__ void __launch_bounds__(NW * 64)
                 // orders the two workgroups, so it goes to slot H(b, S-1) (unused in warm
                 // mode), and the combine kernel, the next launch, copies it over.
                 hout = seg < S - 1 ? nullptr : a.seg_ws + lay.h(b, S - 1);
-                warm_rows = (int64_t)a.seg_ws[lay.warm_chunks(b, seg, head)] * CH;
+                warm_rows = (int64_t)__builtin_bit_cast(
+                                float, __builtin_amdgcn_readlane(
+                                           __builtin_bit_cast(int, wcount), seg - 1)) *
+                            CH;
                 win_staged = true;
             } else {
                 if (warm && job > 0)
@@ -2839,7 +2843,7 @@ __global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
     const int BH = a.lay.B * a.H;
     const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
     const int b = bh / a.H, head = bh - b * a.H;
-    if (a.warm && warm_head(a.seg_ws, a.lay, b, head)) {
+    if (a.warm && warm_head(warm_lane_count(a.seg_ws, a.lay, b, head))) {
         // every segment of this (stream, head) started warm in the first launch: no chain.
         // Its last segment left the final state in slot H(b, S-1) (and, with the front end
         // fused, the new windows in win_ws) because the job that read the initial state and
