@@ -206,8 +206,9 @@ size_t front_bytes(const gdn_params *p, int kda, int64_t max_tokens, int32_t B)
 // With few (stream, head) pairs most CUs would idle while each workgroup walks its stream
 // chunk by chunk. Streams of equal length are then cut into S segments: one launch runs
 // segment 0 and, for every inner segment, its end state from h = 0 and its dk x dk
-// transition (the same recurrence from h = I with v = 0); a small kernel chains
-// h_{s+1} = A_s h_s + b_s; a second launch runs segments 1..S-1 from their start states.
+// transition (the same recurrence from h = I with v = 0); a second launch chains
+// h_{s+1} = A_s h_s + b_s in workgroups at the front of its grid and runs segments 1..S-1
+// from their start states.
 constexpr int kMaxSeg = 12;
 // the kernels read a (stream, head)'s S - 1 warm-start counts one per lane of a wave
 static_assert(kMaxSeg - 1 <= 64, "segment boundaries per wave");
@@ -339,7 +340,7 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
 }
 
 // the segment states, and for a fused front end without shared windows the windows that
-// warm-started streams stage for the combine kernel
+// warm-started streams stage for the second launch's chain workgroups to copy
 size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S)
 {
     if (S < 3)
@@ -411,7 +412,8 @@ int run(const Call &c)
         warm = sp.S && warm_capable(p);
         const int64_t jobs1 = warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
         if (sp.S && (c.ws_bytes < need + seg_bytes(p, c.kda, c.st.B, sp.S) ||
-                     grid * jobs1 > (int64_t)INT32_MAX))
+                     grid * jobs1 > (int64_t)INT32_MAX ||
+                     BH * (p->dv / 16) + grid * (sp.S - 1) > (int64_t)INT32_MAX))
             sp = SegPlan{0, 0, 0}, warm = false;
     }
 
@@ -561,24 +563,14 @@ int run(const Call &c)
             if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
                                   ca, (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
-            gdn::CombineArgs cb{};
-            cb.dbg = dbg;
-            cb.seg_ws = ca.seg_ws;
-            cb.lay = lay;
-            cb.warm = ca.warm;
-            cb.H = p->H, cb.dk = p->dk, cb.dv = p->dv;
-            cb.h = c.h, cb.h_ptrs = c.h_ptrs;
-            cb.win_ws = shared ? nullptr : win_ws;  // shared windows: the copy below
-            cb.conv_state = c.conv_state, cb.conv_state_ptrs = c.conv_state_ptrs;
-            cb.cd = (int32_t)conv_dim(p);
-            cb.Hqk = qk_heads(p);
-            cb.conv_k = p->conv_k;
-            if (gdn::launch_combine(cb, c.stream) != hipSuccess)
-                return GDN_E_HIP;
+            // the chain's workgroups (one per stream, head and 16 state columns) ahead of
+            // the jobs of segments 1..S-1
             ca.pass = 2;
             ca.window_items = 0;  // the windows went out with pass 1
+            ca.chain_groups = (int32_t)(BH * (p->dv / 16));
             if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
-                                  ca, (int)(grid * (sp.S - 1)), c.stream) != hipSuccess)
+                                  ca, (int)(ca.chain_groups + grid * (sp.S - 1)),
+                                  c.stream) != hipSuccess)
                 return GDN_E_HIP;
         }
         if (shared) {  // every workgroup that read the old windows is done

@@ -31,7 +31,8 @@ struct GateArgs {
 // B(b, s) and A(b, s), s = 1..S-2; then one flag per (b, s, head), 1.0 when the transition
 // job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0; then the
 // warm-start plan: per (b, s, head) the chunks of warm-up before segment s (0: none found;
-// a (stream, head) runs warm when every s = 1..S-1 found one).
+// a (stream, head) runs warm when every s = 1..S-1 found one); then per (b, head) eight int
+// flags, one per 16 state columns (dv <= 128), set when the chain of those columns is done.
 struct SegLayout {
     int64_t slot;  // floats per slot
     int32_t B, S, H;
@@ -56,9 +57,14 @@ struct SegLayout {
         return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H +
                ((int64_t)b * S + s) * H + head;
     }
+    __host__ __device__ int64_t chain_done(int b, int head, int cbk) const
+    {
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H +
+               ((int64_t)b * H + head) * 8 + cbk;
+    }
     __host__ __device__ int64_t total() const
     {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H;
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H + (int64_t)B * H * 8;
     }
 };
 
@@ -78,29 +84,6 @@ __device__ __forceinline__ bool warm_head(float lane_count)
 {
     return __ballot(!(lane_count > 0.f)) == 0;
 }
-
-// h(b, s+1) = A(b, s) h(b, s) + B(b, s) for s = 1..S-2, per (stream, head, 16 columns).
-// (Stream, head) pairs in warm mode have no chain: their last segment ran in the first
-// launch, beside the job that read the stream's initial state, so it left its end state in
-// slot H(b, S-1) (and, with the front end fused, the new conv windows in win_ws); this
-// kernel, the first to run after that launch, copies them to the caller's buffers.
-struct CombineArgs {
-    const int32_t *dbg;     // debug validation status (device), or nullptr
-    float *seg_ws;
-    SegLayout lay;
-    int32_t H, dk, dv;
-    int32_t warm;
-    float *h;                       // single stream state (h_ptrs == nullptr)
-    float *const *h_ptrs;
-    // fused front end in warm mode: the new windows of every stream, [B][cd][conv_k-1]
-    // bf16, to copy to the caller's windows (nullptr: nothing to copy here)
-    const void *win_ws;
-    void *conv_state;
-    void *const *conv_state_ptrs;
-    int32_t cd;
-    int32_t Hqk;     // q/k heads
-    int32_t conv_k;
-};
 
 // The staged windows [B][cd][W] (bf16) of a fused front-end call copied to the caller's;
 // a zero-length stream wrote none and keeps its window.
@@ -173,14 +156,18 @@ struct ChunkArgs {
     // stream. pass 1: job 0 runs segment 0 from the stream's state (o written, end state to
     // slot H(b, 1)); jobs 1..S-2 run segment j from h = 0 (end state to slot B(b, j)); jobs
     // S-1..2S-4 run segment j-(S-2) from h = I with v = 0 (end state, the segment's
-    // transition, to slot A(b, j-(S-2))). pass 2: job j runs segment j+1 from slot H(b, j+1)
-    // (o written; the last segment's end state to the stream's state). Segment 0 holds
+    // transition, to slot A(b, j-(S-2))). pass 2: chain_groups workgroups first, which
+    // chain h(b, s+1) = A(b, s) h(b, s) + B(b, s) into slots H(b, 2..S-1), then job j runs
+    // segment j+1 from slot H(b, j+1) (o written; the last segment's end state to the
+    // stream's state), for j >= 1 once the chain of its columns is done. Segment 0 holds
     // seg0_len tokens, segments 1..S-2 seg_len each, segment S-1 the rest of the stream.
     int32_t pass;
     int32_t nseg;           // S
+    int32_t chain_groups;   // pass 2: B * H * dv / 16
     // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
     // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
-    // the map jobs, the chain and pass 2 then return at once
+    // the map jobs and the jobs of pass 2 then return at once, and the chain's workgroups
+    // only copy the final state (and windows) over
     int32_t warm;
     // set by the launch: workgroups [0, job_groups) are jobs; the rest update the front
     // end's carried windows (window_items = streams x channels, 0 when there is none)
@@ -202,7 +189,7 @@ struct ChunkArgs {
     // taps): the conv taps, the carried windows (read by the job holding a stream's first
     // chunk) and where the job that ends a stream puts the new windows: the caller's
     // windows, or win_ws when a later kernel must copy them there -- in warm mode (the
-    // combine kernel, after the launch that read the old windows) and when several
+    // chain's workgroups, after the launch that read the old windows) and when several
     // workgroups read one window (win_shared: q/k heads shared by value heads, or dv
     // slices; window_copy_kernel at the end of the call).
     const float *conv_w;            // [cd][conv_k]
@@ -267,7 +254,6 @@ hipError_t launch_chunk(int in_kind, int dk, int dv, int kda, int nv, int waves,
                         int chunk, const ChunkArgs &a, int grid, hipStream_t s);
 // the output gate as its own pass (dtype: element type of z, GDN_F32 or GDN_BF16)
 hipError_t launch_gate(int dtype, const GateArgs &a, hipStream_t s);
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s);
 // The same plan with one workgroup per (stream, head, boundary), reading only the gates of
 // each boundary's window; with the per-key-channel gate (kda) a token's bound is its

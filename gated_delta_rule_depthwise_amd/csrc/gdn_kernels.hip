@@ -5,7 +5,7 @@
 // "split_prefill.rs" (the batched and varlen entry points):
 //
 //  * chunk_kernel: one workgroup per (stream, head, dv slice) walks the stream's chunks in
-//    order (or, for few long streams, one segment of them; see combine_kernel). Per chunk:
+//    order (or, for few long streams, one segment of them; see chain_block). Per chunk:
 //    the load stage brings the chunk's rows into LDS tiles -- with the front end fused
 //    (bf16 raw rows), the causal depthwise conv + SiLU, the L2 of q and k and the q scale
 //    run here in fp32 on raw rows that arrived by LDS-DMA one chunk ahead; otherwise the
@@ -21,8 +21,9 @@
 //    dv != dk, 2 or 3 taps, the output gate): conv + SiLU, L2 and q scale written once as
 //    packed activations (fp32 for float32 rows, fp16 for bf16 rows). The carried windows
 //    are then advanced by extra workgroups of the first chunk-kernel launch.
-//  * combine_kernel: the chain of segment maps of the segmented scan, and the hand-over of
-//    warm-started streams' final states and windows.
+//  * chain_block: the chain of segment maps of the segmented scan, and the hand-over of
+//    warm-started streams' final states and windows, run by workgroups at the front of the
+//    chunk kernel's second launch of a segmented call.
 //  * decode lives in gdn_decode.hip.
 //
 // MFMA fragment convention (v_mfma_f32_16x16x32_f16, and 8 x v_mfma_f32_16x16x4_f32 for
@@ -1247,6 +1248,172 @@ __device__ __forceinline__ int block_task(int wave, int j)
     }
 }
 
+// ------------------------------------------------------------------------------------
+// segmented scan: chain the segment maps, h(b, s+1) = A(b, s) h(b, s) + B(b, s)
+
+// Polls of a bounded wait: about a second at most, far beyond the chain's few
+// microseconds. The chain's workgroups precede their waiters in the grid, and workgroups
+// dispatch in grid order, so the flags are set while a waiter polls; the bound keeps every
+// wave finite regardless.
+constexpr int kChainPolls = 1 << 20;
+
+// Waits until the n <= 64 flags f[0..n) are nonzero (lane l polls f[l]); loads after it see
+// what the workgroups that set them wrote before setting them. Called by whole waves.
+__device__ __forceinline__ void wait_flags(const int *f, int n)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    bool ok = lane >= n;
+    for (int it = 0; it < kChainPolls; ++it) {
+        if (!ok)
+            ok = __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        if (__ballot(!ok) == 0)
+            break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// The chain of one (stream, head, 16 state columns), blk = column block * B*H + (stream,
+// head), by a workgroup of NWV waves at the front of the second launch. The 16 columns of
+// h(b, s) sit in LDS; wave w computes row blocks w, w + NWV, ... of the next state with fp32
+// MFMA (one block per wave at dk = 128 with 8 waves: the chain is latency-bound). The A and
+// B blocks a wave needs for step s+1 are loaded into registers while step s computes, so
+// each step waits on memory once at most. When the last step is stored, the column block's
+// flag (reset by job 0 of the first launch) releases the second launch's jobs of segments
+// 2..S-1, which wait for it before they read their start states.
+// A (stream, head) in warm mode has no chain: its last segment ran in the first launch,
+// beside the job that read the stream's initial state, so it left its end state in slot
+// H(b, S-1) (and, with the front end fused and windows not shared, the new windows in
+// win_ws); the workgroup copies its share to the caller's buffers.
+template <int DK, int NWV>
+__device__ __forceinline__ void chain_block(const ChunkArgs &a, const SegLayout &lay, int blk,
+                                            unsigned char *lds)
+{
+    constexpr int NRB = DK / 16, RBW = (NRB + NWV - 1) / NWV;  // row blocks, per wave
+    float(*hsm)[20] = reinterpret_cast<float(*)[20]>(lds);     // rows 4 apart 16 banks apart
+    float *zf = reinterpret_cast<float *>(lds + DK * 20 * sizeof(float));
+    // Workgroups go to the 8 XCDs round-robin by index: with the column block as the slow
+    // index, the column blocks of one (stream, head) share an XCD (B*H a multiple of 8),
+    // so that XCD's L2 serves that head's A to all of them.
+    const int BH = lay.B * a.H;
+    const int cbk = blk / BH, bh = blk - cbk * BH;
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int64_t hoff = (int64_t)head * DK * DK;
+    float *state = a.h_ptrs ? a.h_ptrs[b] : a.h;
+    if (a.warm && warm_head(warm_lane_count(a.seg_ws, lay, b, head))) {
+        const float *src = a.seg_ws + lay.h(b, lay.S - 1) + hoff;
+        for (int idx = threadIdx.x; idx < DK * 16; idx += NWV * 64) {
+            const int64_t e = (int64_t)(idx >> 4) * DK + 16 * cbk + (idx & 15);
+            state[hoff + e] = src[e];
+        }
+        if (a.win_ws && !a.win_shared) {  // bf16 windows [cd][W]; this head's q, k, v channels
+            const int W = a.conv_k - 1, hq = head / a.qk_group, Hqk = a.H / a.qk_group;
+            const int nch = 2 * DK + DK, per = (nch * W + DK / 16 - 1) / (DK / 16);
+            const uint16_t *ws = (const uint16_t *)a.win_ws + (int64_t)b * a.cd * W;
+            uint16_t *cw = (uint16_t *)(a.conv_state_ptrs ? a.conv_state_ptrs[b] : a.conv_state);
+            for (int e = cbk * per + (int)threadIdx.x; e < min((cbk + 1) * per, nch * W);
+                 e += NWV * 64) {
+                const int ch = e / W, j = e - W * ch;
+                const int gc = ch < 2 * DK ? (ch >= DK ? Hqk * DK : 0) + hq * DK + ch % DK
+                                           : 2 * Hqk * DK + head * DK + ch - 2 * DK;
+                cw[(int64_t)gc * W + j] = ws[(int64_t)gc * W + j];
+            }
+        }
+        return;  // the second launch's jobs of a warm (stream, head) return without waiting
+    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int col0 = 16 * cbk;
+    const int S = lay.S;
+    const float *h1 = a.seg_ws + lay.h(b, 1) + hoff;
+    for (int idx = tid; idx < DK * 16; idx += NWV * 64)
+        hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
+    // the zero-transition flags of every step, read once (visible after the first barrier)
+    if (tid < S - 2)
+        zf[tid] = a.seg_ws[lay.zero_flag(b, tid + 1, head)];
+
+    // A step whose transition job found A(b, s) zero is h(b, s+1) = B(b, s): no A to load, no
+    // product, and no wait for h(b, s) (the flag is the same for the whole workgroup).
+    auto zero_at = [&](int s) { return zf[s - 1] != 0.f; };
+    // A blocks and B rows of the next two steps (ring of 2), so a step's loads have two
+    // steps' time to arrive
+    f32x4 av[2][RBW][NRB], bv[2][RBW];
+    auto load = [&](int s, int slot, bool flags_known) {
+        const float *A = a.seg_ws + lay.as(b, s) + hoff;  // [dk][dk]
+        const float *Bm = a.seg_ws + lay.bs(b, s) + hoff;
+        const bool za = flags_known && zero_at(s);
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave + NWV * j;
+            if (rb < NRB) {
+                if (!za) {
+#pragma unroll
+                    for (int kb = 0; kb < NRB; ++kb)
+                        av[slot][j][kb] = blk_a(A, DK, rb, kb, lane);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    bv[slot][j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
+            }
+        }
+    };
+    auto step = [&](int s, int slot) {
+        const bool zs = zero_at(s);
+        f32x4 acc[RBW];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave + NWV * j;
+            acc[j] = bv[slot][j];
+            if (rb < NRB && !zs) {
+#pragma unroll
+                for (int kb = 0; kb < NRB; ++kb) {
+                    const float *hc = &hsm[16 * kb + 4 * g4][c16];
+                    mm16<false>(acc[j], av[slot][j][kb], f32x4{hc[0], hc[20], hc[40], hc[60]});
+                }
+            }
+        }
+        if (s + 2 <= S - 2)
+            load(s + 2, slot, true);
+        if (!zs)
+            __syncthreads();  // every wave has read h(b, s)
+        float *Hn = a.seg_ws + lay.h(b, s + 1) + hoff;
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave + NWV * j;
+            if (rb < NRB) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * g4 + i;
+                    hsm[r][c16] = acc[j][i];
+                    Hn[(int64_t)r * DK + col0 + c16] = acc[j][i];
+                }
+            }
+        }
+        // the next step reads h(b, s+1) from every wave's rows unless its transition is zero
+        // (each wave writes the same rows in every step, so a zero step needs no wait)
+        if (s + 1 <= S - 2 && !zero_at(s + 1))
+            __syncthreads();
+    };
+    // the first two steps' blocks are requested before the flags are visible (A included)
+    load(1, 0, false);
+    if (S - 2 >= 2)
+        load(2, 1, false);
+    __syncthreads();  // h(b, 1) and the flags
+    // the ring slot is a compile-time index: steps go in pairs
+    for (int s = 1; s <= S - 2; s += 2) {
+        step(s, 0);
+        if (s + 1 <= S - 2)
+            step(s + 1, 1);
+    }
+    // every wave's stores of the chain reach the agent-coherent level, then one flag
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(reinterpret_cast<int *>(a.seg_ws + lay.chain_done(b, head, cbk)), 1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename TIN, typename T, int DK, int DV, int NW, int NCB, bool KDA, bool GATE,
           bool FRONT, int CHK = 64>
 __global__ void __launch_bounds__(NW * 64)
@@ -1290,10 +1457,20 @@ __global__ void __launch_bounds__(NW * 64)
                          (int64_t)(blockIdx.x - a.job_groups) * NT + tid0);
         return;
     }
+    int gid = blockIdx.x;
+    if (a.chain_groups) {  // second launch of a segmented call: the chain's workgroups first
+        if (gid < a.chain_groups) {
+            if constexpr (DK == DV && (DK == 64 || DK == 128))
+                chain_block<DK, NW>(a, SegLayout{(int64_t)a.H * DK * DV, a.st.B, a.nseg, a.H},
+                                    gid, smem);
+            return;
+        }
+        gid -= a.chain_groups;
+    }
     const int H = a.H;
     const int BH = a.st.B * H;
     constexpr int NS = DV / NV;  // dv slices
-    const int jp = blockIdx.x / (BH * NS), jr = blockIdx.x - jp * (BH * NS);
+    const int jp = gid / (BH * NS), jr = gid - jp * (BH * NS);
     const int slice = jr / BH, bh = jr - slice * BH;
     const int bi = bh / H, head = bh - bi * H;
     const int b = a.order ? a.order[bi] : bi;  // varlen: longest streams dispatch first
@@ -1309,6 +1486,7 @@ __global__ void __launch_bounds__(NW * 64)
     bool h_ident = false, v_zero = false, write_o = true;
     float *zflag = nullptr;  // transition jobs: whether their transition was found zero
     int64_t warm_rows = 0;   // warm jobs: rows run from h = 0 before the segment, without o
+    const int *chain_flags = nullptr;  // second-launch jobs: the chain flags of their columns
     if (a.pass != 0) {
         const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg, H};
         const int S = a.nseg;
@@ -1332,7 +1510,7 @@ __global__ void __launch_bounds__(NW * 64)
                 // The last segment's end state is the stream's final state. Job 0 of this
                 // launch reads the stream's initial state from the same buffer and nothing
                 // orders the two workgroups, so it goes to slot H(b, S-1) (unused in warm
-                // mode), and the combine kernel, the next launch, copies it over.
+                // mode), and the chain's workgroups of the next launch copy it over.
                 hout = seg < S - 1 ? nullptr : a.seg_ws + lay.h(b, S - 1);
                 warm_rows = (int64_t)__builtin_bit_cast(
                                 float, __builtin_amdgcn_readlane(
@@ -1342,6 +1520,9 @@ __global__ void __launch_bounds__(NW * 64)
             } else {
                 if (warm && job > 0)
                     return;
+                if (job == 0 && tid0 < NV / 16)  // this job's columns: chain not done yet
+                    reinterpret_cast<int *>(
+                        a.seg_ws + lay.chain_done(b, head, slice * (NV / 16)))[tid0] = 0;
                 seg = job <= S - 2 ? job : job - (S - 2);
                 if (job > 0) {
                     hin = nullptr;
@@ -1358,6 +1539,9 @@ __global__ void __launch_bounds__(NW * 64)
                 return;
             seg = jp + 1;
             hin = a.seg_ws + lay.h(b, seg);
+            if (seg >= 2)  // slot H(b, seg) comes from the chain of this launch
+                chain_flags = reinterpret_cast<const int *>(
+                    a.seg_ws + lay.chain_done(b, head, slice * (NV / 16)));
             if (seg < S - 1)
                 hout = nullptr;
         }
@@ -1559,6 +1743,8 @@ __global__ void __launch_bounds__(NW * 64)
     // window, whose loads the workgroup then waits for while the rows are in flight
     if (start < end)
         prefetch(start, (int)min((int64_t)CH, end - start));
+    if (chain_flags)  // (uniform) every wave, before it reads its share of the start state
+        wait_flags(chain_flags, NV / 16);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -2817,148 +3003,6 @@ int chunk_instance_exists(int in_kind, int dk, int dv, int kda, int nv, int wave
     return 0;
 }
 
-// ------------------------------------------------------------------------------------
-// segmented scan: chain the segment maps, h(b, s+1) = A(b, s) h(b, s) + B(b, s)
-
-// waves per workgroup: one 16-row block of the next state each at dk = 128
-#ifndef GDN_CB_WAVES
-#define GDN_CB_WAVES 8
-#endif
-
-// One workgroup per (stream, head, 16 state columns). The 16 columns of h(b, s) sit in LDS;
-// wave w computes row blocks w, w + NWV, ... of the next state with fp32 MFMA (one block
-// per wave at dk = 128: the chain is latency-bound, 8 waves cut it 11% against 4). The A and B blocks a
-// wave needs for step s+1 are loaded into registers while step s computes, so each step
-// waits on memory once at most.
-template <int DK, int NWV>
-__global__ void __launch_bounds__(NWV * 64) combine_kernel(const CombineArgs a)
-{
-    if (debug_stop(a.dbg))
-        return;
-    constexpr int NRB = DK / 16, RBW = (NRB + NWV - 1) / NWV;  // row blocks, per wave
-    __shared__ float hsm[DK][20];  // 20 floats: rows 4 apart 16 banks apart
-    // Workgroups go to the 8 XCDs round-robin by index: with the column block as the slow
-    // index, the column blocks of one (stream, head) share an XCD (B*H a multiple of 8),
-    // so that XCD's L2 serves that head's A to all of them.
-    const int BH = a.lay.B * a.H;
-    const int cbk = blockIdx.x / BH, bh = blockIdx.x - cbk * BH;
-    const int b = bh / a.H, head = bh - b * a.H;
-    if (a.warm && warm_head(warm_lane_count(a.seg_ws, a.lay, b, head))) {
-        // every segment of this (stream, head) started warm in the first launch: no chain.
-        // Its last segment left the final state in slot H(b, S-1) (and, with the front end
-        // fused, the new windows in win_ws) because the job that read the initial state and
-        // the old windows ran in that same launch; copy this workgroup's share over.
-        const int64_t hoff = (int64_t)head * DK * DK;
-        const float *src = a.seg_ws + a.lay.h(b, a.lay.S - 1) + hoff;
-        float *dst = (a.h_ptrs ? a.h_ptrs[b] : a.h) + hoff;
-        for (int idx = threadIdx.x; idx < DK * 16; idx += NWV * 64) {
-            const int64_t e = (int64_t)(idx >> 4) * DK + 16 * cbk + (idx & 15);
-            dst[e] = src[e];
-        }
-        if (a.win_ws) {  // bf16 windows [cd][W]; this head's q, k and v channels
-            const int W = a.conv_k - 1, hq = head / (a.H / a.Hqk);
-            const int nch = 2 * DK + DK, per = (nch * W + DK / 16 - 1) / (DK / 16);
-            const uint16_t *ws = (const uint16_t *)a.win_ws + (int64_t)b * a.cd * W;
-            uint16_t *cw = (uint16_t *)(a.conv_state_ptrs ? a.conv_state_ptrs[b] : a.conv_state);
-            for (int e = cbk * per + (int)threadIdx.x; e < min((cbk + 1) * per, nch * W);
-                 e += NWV * 64) {
-                const int ch = e / W, j = e - W * ch;
-                const int gc = ch < 2 * DK ? (ch >= DK ? a.Hqk * DK : 0) + hq * DK + ch % DK
-                                           : 2 * a.Hqk * DK + head * DK + ch - 2 * DK;
-                cw[(int64_t)gc * W + j] = ws[(int64_t)gc * W + j];
-            }
-        }
-        return;
-    }
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g4 = lane >> 4, c16 = lane & 15;
-    const int64_t hoff = (int64_t)head * DK * DK;
-    const int col0 = 16 * cbk;
-    const int S = a.lay.S;
-    const float *h1 = a.seg_ws + a.lay.h(b, 1) + hoff;
-    for (int idx = tid; idx < DK * 16; idx += NWV * 64)
-        hsm[idx >> 4][idx & 15] = h1[(int64_t)(idx >> 4) * DK + col0 + (idx & 15)];
-    // the zero-transition flags of every step, read once (visible after the first barrier)
-    __shared__ float zf[32];
-    if (tid < S - 2 && tid < 32)
-        zf[tid] = a.seg_ws[a.lay.zero_flag(b, tid + 1, head)];
-
-    // A step whose transition job found A(b, s) zero is h(b, s+1) = B(b, s): no A to load, no
-    // product, and no wait for h(b, s) (the flag is the same for the whole workgroup).
-    auto zero_at = [&](int s) { return zf[s - 1] != 0.f; };
-    // A blocks and B rows of the next two steps (ring of 2), so a step's loads have two
-    // steps' time to arrive
-    f32x4 av[2][RBW][NRB], bv[2][RBW];
-    auto load = [&](int s, int slot, bool flags_known) {
-        const float *A = a.seg_ws + a.lay.as(b, s) + hoff;  // [dk][dk]
-        const float *Bm = a.seg_ws + a.lay.bs(b, s) + hoff;
-        const bool za = flags_known && zero_at(s);
-#pragma unroll
-        for (int j = 0; j < RBW; ++j) {
-            const int rb = wave + NWV * j;
-            if (rb < NRB) {
-                if (!za) {
-#pragma unroll
-                    for (int kb = 0; kb < NRB; ++kb)
-                        av[slot][j][kb] = blk_a(A, DK, rb, kb, lane);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    bv[slot][j][i] = Bm[(int64_t)(16 * rb + 4 * g4 + i) * DK + col0 + c16];
-            }
-        }
-    };
-    auto step = [&](int s, int slot) {
-        const bool zs = zero_at(s);
-        f32x4 acc[RBW];
-#pragma unroll
-        for (int j = 0; j < RBW; ++j) {
-            const int rb = wave + NWV * j;
-            acc[j] = bv[slot][j];
-            if (rb < NRB && !zs) {
-#pragma unroll
-                for (int kb = 0; kb < NRB; ++kb) {
-                    const float *hc = &hsm[16 * kb + 4 * g4][c16];
-                    mm16<false>(acc[j], av[slot][j][kb], f32x4{hc[0], hc[20], hc[40], hc[60]});
-                }
-            }
-        }
-        if (s + 2 <= S - 2)
-            load(s + 2, slot, true);
-        if (!zs)
-            __syncthreads();  // every wave has read h(b, s)
-        float *Hn = a.seg_ws + a.lay.h(b, s + 1) + hoff;
-#pragma unroll
-        for (int j = 0; j < RBW; ++j) {
-            const int rb = wave + NWV * j;
-            if (rb < NRB) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * g4 + i;
-                    hsm[r][c16] = acc[j][i];
-                    Hn[(int64_t)r * DK + col0 + c16] = acc[j][i];
-                }
-            }
-        }
-        // the next step reads h(b, s+1) from every wave's rows unless its transition is zero
-        // (each wave writes the same rows in every step, so a zero step needs no wait)
-        if (s + 1 <= S - 2 && !zero_at(s + 1))
-            __syncthreads();
-    };
-    // the first two steps' blocks are requested before the flags are visible (A included)
-    load(1, 0, false);
-    if (S - 2 >= 2)
-        load(2, 1, false);
-    __syncthreads();  // h(b, 1) and the flags
-    // the ring slot is a compile-time index: steps go in pairs
-    for (int s = 1; s <= S - 2; s += 2) {
-        step(s, 0);
-        if (s + 1 <= S - 2)
-            step(s + 1, 1);
-    }
-}
-
 hipError_t launch_warm_boundaries(const WarmArgs &a, int kda, int dk, hipStream_t s)
 {
     const int64_t grid = (int64_t)a.st.B * a.H * (a.nseg - 1);
@@ -3047,21 +3091,6 @@ hipError_t launch_window_copy(const WindowCopyArgs &a, hipStream_t s)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(window_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        a);
-    return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
-{
-    if (a.dk > 128 || a.dk % 16 || a.dv % 16 || a.dk != a.dv || a.lay.S < 3)
-        return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)a.lay.B * a.H * (a.dv / 16);
-    if (a.dk == 128)
-        hipLaunchKernelGGL((combine_kernel<128, GDN_CB_WAVES>), dim3((unsigned)grid),
-                           dim3(GDN_CB_WAVES * 64), 0, s, a);
-    else if (a.dk == 64)
-        hipLaunchKernelGGL((combine_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    else
-        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
