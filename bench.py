@@ -6,7 +6,10 @@ end when the workload has one, L2, chunk preparation, inter-chunk scan, state wr
 The default workload is GDN with the conv front end, 1 stream of T=4096 tokens, H=32,
 dk=dv=128, chunk 64 (seeded synthetic bf16 inputs). Inputs are resident in HBM when timing
 starts; several input copies are rotated so that a step never finds its inputs in the
-256 MB Infinity Cache from the previous step.
+256 MB Infinity Cache from the previous step. The GPU's clocks reach their sustained level
+only after some tens of milliseconds of load, so by default the warm-up runs about 100 ms
+of steps and the timed region about 100 ms (at least 20 and 40 steps); ``--warmup`` and
+``--steps`` fix the counts instead, and the JSON line reports the counts used.
 
 ``--decode gdn|kda`` times the decode step instead: one call advances 64 streams by one
 token each (front end, one recurrence step on each stream's 2 MiB state, window update);
@@ -146,8 +149,10 @@ def cpu_baseline(spec, inp, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0: about 100 ms of them, at least 40)")
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps first (-1: about 100 ms of them, at least 20)")
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--profile-every", type=int, default=0,
@@ -165,8 +170,6 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=64,
                     help="rows per chunk (32 runs on the instances that have it)")
     args = ap.parse_args()
-    if args.profile_every <= 0:
-        args.profile_every = max(1, args.steps // 5)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -207,10 +210,30 @@ def main() -> int:
     calls = [first] + [type(first)(inp, dev) for _ in range(copies - 1)]
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        rc = calls[i % copies]()
-        if rc != 0:
-            raise RuntimeError("libgdn status %d (%s)" % (rc, B.gdn_status_string(rc)))
+    def run_steps(n, first_step=0):
+        for i in range(first_step, first_step + n):
+            rc = calls[i % copies]()
+            if rc != 0:
+                raise RuntimeError("libgdn status %d (%s)" % (rc, B.gdn_status_string(rc)))
+
+    done = 0
+    if args.warmup < 0 or args.steps <= 0:
+        # step counts from the duration of 5 steps (clocks not yet ramped: an overestimate)
+        run_steps(5)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        run_steps(5, 5)
+        torch.cuda.synchronize()
+        done = 10
+        n100 = math.ceil(0.1 / max((time.perf_counter() - tp) / 5, 1e-6))
+        if args.warmup < 0:
+            args.warmup = max(20, 10 + n100)
+        if args.steps <= 0:
+            args.steps = max(40, n100)
+    run_steps(max(0, args.warmup - done), done)
+    args.warmup = max(args.warmup, done)  # untimed steps run
+    if args.profile_every <= 0:
+        args.profile_every = max(1, args.steps // 5)
     torch.cuda.synchronize()
     B.gdn_profile_read()          # drop anything recorded so far
     torch.cuda.synchronize()
@@ -270,7 +293,8 @@ def main() -> int:
             parts.append("chunk_kernel")
         if segs:
             parts.append("segmented scan of %d segments: warm_boundary_kernel + pass 1 + "
-                         "combine_kernel + pass 2; warm starts where the gates allow" % segs)
+                         "pass 2 (the chain of segment maps in its first workgroups); warm "
+                         "starts where the gates allow" % segs)
         if "gate" in avg_ms:
             parts.append("gate_kernel")
         kname = "the whole call: " + "; ".join(parts)
