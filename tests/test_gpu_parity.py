@@ -236,7 +236,7 @@ def test_refused_calls_leave_buffers_unchanged():
 
 
 @pytest.mark.parametrize("case", ["gdn-front-T4096-H4", "gdn-bf16-T3000-H2",
-                                  "batched-2x2048-H2"])
+                                  "batched-2x2048-H2", "f32-front-d64-T2048-H2"])
 def test_segmented_scan_fast_decay(case):
     """Fast decay (log-gates -softplus(N(0,1))): each inner segment's transition underflows
     within its first chunks, so the transition jobs stop early and write zeros. The call
@@ -245,6 +245,10 @@ def test_segmented_scan_fast_decay(case):
     spec = {"gdn-front-T4096-H4": lambda: spec_small(2, lengths=[4096], H=4, seed=56),
             "gdn-bf16-T3000-H2": lambda: spec_small(3, lengths=[3000], H=2, seed=57),
             "batched-2x2048-H2": lambda: spec_small(3, lengths=[2048, 2048], H=2, seed=59),
+            # float32 rows: the front kernel first, then the segmented scan
+            "f32-front-d64-T2048-H2": lambda: spec_small(1, lengths=[2048], H=2,
+                                                         front_end=True, h0_std=0.1,
+                                                         gate_dist="softplus", seed=60),
             }[case]()
     inp = inputs.make(spec)
     seg = run_gpu(inp)
