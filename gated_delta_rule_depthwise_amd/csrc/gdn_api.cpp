@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <utility>
@@ -560,6 +561,13 @@ int run(const Call &c)
             }
             ca.pass = 1;
             const int64_t jobs1 = ca.warm ? 3 * sp.S - 4 : 2 * sp.S - 3;
+            // the warm-start plan above cleared the read flags: the last warm job writes the
+            // final state and windows itself
+            ca.direct_final = ca.warm;
+            // a flag wait outlasts any job it waits for: 2^20 polls plus 256 per chunk of the
+            // stream (a chunk step outlasts 256 poll sleeps)
+            ca.wait_polls = (int32_t)std::min<int64_t>(
+                INT32_MAX, (int64_t)(1 << 20) + 256 * ((c.st.tps + 63) / 64));
             if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
                                   ca, (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;

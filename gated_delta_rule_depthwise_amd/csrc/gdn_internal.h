@@ -31,8 +31,8 @@ struct GateArgs {
 // B(b, s) and A(b, s), s = 1..S-2; then one flag per (b, s, head), 1.0 when the transition
 // job of (b, s, head) found A(b, s) to be zero (it then wrote zeros), else 0.0; then the
 // warm-start plan: per (b, s, head) the chunks of warm-up before segment s (0: none found;
-// a (stream, head) runs warm when every s = 1..S-1 found one); then per (b, head) eight int
-// flags, one per 16 state columns (dv <= 128), set when the chain of those columns is done.
+// a (stream, head) runs warm when every s = 1..S-1 found one); then 16 int flags per (b,
+// head) that order workgroups of one launch (see the kFlag offsets below).
 struct SegLayout {
     int64_t slot;  // floats per slot
     int32_t B, S, H;
@@ -57,15 +57,24 @@ struct SegLayout {
         return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * S * H +
                ((int64_t)b * S + s) * H + head;
     }
-    __host__ __device__ int64_t chain_done(int b, int head, int cbk) const
+    __host__ __device__ int64_t flags(int b, int head) const
     {
         return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H +
-               ((int64_t)b * H + head) * 8 + cbk;
+               ((int64_t)b * H + head) * 16;
+    }
+    __host__ __device__ int64_t chain_done(int b, int head, int cbk) const
+    {
+        return flags(b, head) + kFlagChain + cbk;
     }
     __host__ __device__ int64_t total() const
     {
-        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H + (int64_t)B * H * 8;
+        return (int64_t)B * (3 * S - 5) * slot + (int64_t)B * 2 * S * H + (int64_t)B * H * 16;
     }
+    // Flag offsets within a (stream, head)'s 16 (dv slices <= 2):
+    //   kFlagChain + c   the chain of state columns 16c..16c+15 is done (c < 8; second launch)
+    //   kFlagRead + sl   job 0 has read the initial state and windows of slice sl (first
+    //                    launch, calls with a warm-start plan)
+    static constexpr int kFlagChain = 0, kFlagRead = 8;
 };
 
 // The plan's warm-up chunk count of boundary s = lane + 1 (1 past the last boundary): whole
@@ -164,6 +173,11 @@ struct ChunkArgs {
     int32_t pass;
     int32_t nseg;           // S
     int32_t chain_groups;   // pass 2: B * H * dv / 16
+    // calls with a warm-start plan (which clears the read flags first): the last warm job
+    // writes the final state and windows to the caller's buffers itself, once job 0 of the
+    // same launch has read the initial ones (a bounded wait of at most wait_polls polls)
+    int32_t direct_final;
+    int32_t wait_polls;
     // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
     // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
     // the map jobs and the jobs of pass 2 then return at once, and the chain's workgroups

@@ -392,6 +392,8 @@ __device__ __forceinline__ void warm_plan_block(const WarmArgs &a, int bh)
 {
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid < 16)  // the read flags the scan's first launch orders two of its jobs by
+        reinterpret_cast<int *>(a.seg_ws + a.lay.flags(b, head))[tid] = 0;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     const int S = a.nseg;
@@ -455,6 +457,8 @@ __global__ void __launch_bounds__(KDA ? 1024 : 256) warm_boundary_kernel(const W
     const int bh = blockIdx.x / (S - 1), s = blockIdx.x - bh * (S - 1) + 1;
     const int b = bh / a.H, head = bh - b * a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (s == 1 && tid < 16)  // the read flags the scan's first launch orders two jobs by
+        reinterpret_cast<int *>(a.seg_ws + a.lay.flags(b, head))[tid] = 0;
     int64_t start, end;
     stream_bounds(a.st, b, start, end);
     const int64_t cs = (a.seg0_len + (int64_t)(s - 1) * a.seg_len) / CH;
@@ -1251,19 +1255,16 @@ __device__ __forceinline__ int block_task(int wave, int j)
 // ------------------------------------------------------------------------------------
 // segmented scan: chain the segment maps, h(b, s+1) = A(b, s) h(b, s) + B(b, s)
 
-// Polls of a bounded wait: about a second at most, far beyond the chain's few
-// microseconds. The chain's workgroups precede their waiters in the grid, and workgroups
-// dispatch in grid order, so the flags are set while a waiter polls; the bound keeps every
-// wave finite regardless.
-constexpr int kChainPolls = 1 << 20;
-
-// Waits until the n <= 64 flags f[0..n) are nonzero (lane l polls f[l]); loads after it see
-// what the workgroups that set them wrote before setting them. Called by whole waves.
-__device__ __forceinline__ void wait_flags(const int *f, int n)
+// Waits until the n <= 64 flags f[0..n) are nonzero (lane l polls f[l], at most polls
+// times, ChunkArgs::wait_polls); loads after it see what the workgroups that set them wrote
+// before setting them. Called by whole waves. Every flag is set by a workgroup that
+// precedes its waiters in the grid, and workgroups dispatch in grid order, so the flags are
+// set while a waiter polls; the bound keeps every wave finite regardless.
+__device__ __forceinline__ void wait_flags(const int *f, int n, int polls)
 {
     const int lane = (int)(threadIdx.x & 63);
     bool ok = lane >= n;
-    for (int it = 0; it < kChainPolls; ++it) {
+    for (int it = 0; it < polls; ++it) {
         if (!ok)
             ok = __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
         if (__ballot(!ok) == 0)
@@ -1284,7 +1285,8 @@ __device__ __forceinline__ void wait_flags(const int *f, int n)
 // A (stream, head) in warm mode has no chain: its last segment ran in the first launch,
 // beside the job that read the stream's initial state, so it left its end state in slot
 // H(b, S-1) (and, with the front end fused and windows not shared, the new windows in
-// win_ws); the workgroup copies its share to the caller's buffers.
+// win_ws); the workgroup copies its share to the caller's buffers (with direct_final that
+// job waited for the read and wrote them itself).
 template <int DK, int NWV>
 __device__ __forceinline__ void chain_block(const ChunkArgs &a, const SegLayout &lay, int blk,
                                             unsigned char *lds)
@@ -1301,6 +1303,8 @@ __device__ __forceinline__ void chain_block(const ChunkArgs &a, const SegLayout 
     const int64_t hoff = (int64_t)head * DK * DK;
     float *state = a.h_ptrs ? a.h_ptrs[b] : a.h;
     if (a.warm && warm_head(warm_lane_count(a.seg_ws, lay, b, head))) {
+        if (a.direct_final)
+            return;
         const float *src = a.seg_ws + lay.h(b, lay.S - 1) + hoff;
         for (int idx = threadIdx.x; idx < DK * 16; idx += NWV * 64) {
             const int64_t e = (int64_t)(idx >> 4) * DK + 16 * cbk + (idx & 15);
@@ -1487,6 +1491,8 @@ __global__ void __launch_bounds__(NW * 64)
     float *zflag = nullptr;  // transition jobs: whether their transition was found zero
     int64_t warm_rows = 0;   // warm jobs: rows run from h = 0 before the segment, without o
     const int *chain_flags = nullptr;  // second-launch jobs: the chain flags of their columns
+    // direct_final: job 0 sets, and the last warm job waits for, this slice's read flag
+    int read_role = 0;  // 1: set it, 2: wait for it
     if (a.pass != 0) {
         const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg, H};
         const int S = a.nseg;
@@ -1508,15 +1514,21 @@ __global__ void __launch_bounds__(NW * 64)
                 seg = job - (2 * S - 4);
                 hin = nullptr;
                 // The last segment's end state is the stream's final state. Job 0 of this
-                // launch reads the stream's initial state from the same buffer and nothing
-                // orders the two workgroups, so it goes to slot H(b, S-1) (unused in warm
-                // mode), and the chain's workgroups of the next launch copy it over.
+                // launch reads the stream's initial state from the same buffer, so it goes to
+                // slot H(b, S-1) (unused in warm mode), and the chain's workgroups of the
+                // next launch copy it over; with direct_final the job waits for job 0's read
+                // flag and writes the caller's state and windows itself.
                 hout = seg < S - 1 ? nullptr : a.seg_ws + lay.h(b, S - 1);
                 warm_rows = (int64_t)__builtin_bit_cast(
                                 float, __builtin_amdgcn_readlane(
                                            __builtin_bit_cast(int, wcount), seg - 1)) *
                             CH;
                 win_staged = true;
+                if (a.direct_final && seg == S - 1) {
+                    hout = state;
+                    win_staged = false;
+                    read_role = 2;
+                }
             } else {
                 if (warm && job > 0)
                     return;
@@ -1524,6 +1536,8 @@ __global__ void __launch_bounds__(NW * 64)
                     reinterpret_cast<int *>(
                         a.seg_ws + lay.chain_done(b, head, slice * (NV / 16)))[tid0] = 0;
                 seg = job <= S - 2 ? job : job - (S - 2);
+                if (job == 0 && a.direct_final)
+                    read_role = 1;
                 if (job > 0) {
                     hin = nullptr;
                     write_o = false;
@@ -1744,7 +1758,7 @@ __global__ void __launch_bounds__(NW * 64)
     if (start < end)
         prefetch(start, (int)min((int64_t)CH, end - start));
     if (chain_flags)  // (uniform) every wave, before it reads its share of the start state
-        wait_flags(chain_flags, NV / 16);
+        wait_flags(chain_flags, NV / 16, a.wait_polls);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -1983,6 +1997,23 @@ __global__ void __launch_bounds__(NW * 64)
                                                          __builtin_bit_cast(int, ((const float *)(
                                                              smem + C::OFF_G))[4 * CH]))) < -110.f;
     };
+    if (read_role) {  // (uniform) direct_final
+        int *rf = reinterpret_cast<int *>(
+                      a.seg_ws + SegLayout{(int64_t)H * DK * DV, a.st.B, a.nseg, H}.flags(b, head)) +
+                  SegLayout::kFlagRead + slice;
+        if (read_role == 1) {
+            // job 0: every wave's loads of the initial state and windows are done
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid0 == 0)
+                __hip_atomic_store(rf, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            // the last warm job, which writes the caller's state and windows: job 0 has read
+            // them. Both start in the first round of workgroups, so this waits for little
+            // more than job 0's first loads, and nothing inside the chunk loop has to check.
+            wait_flags(rf, 1, a.wait_polls);
+        }
+    }
     for (int64_t cs = start; cs < end && !(cs > start && underflowed()); cs += CH) {
         const int L = (int)min((int64_t)CH, end - cs);
         write_o = cs >= o_start;  // this chunk computes o
