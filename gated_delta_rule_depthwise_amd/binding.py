@@ -31,7 +31,8 @@ EXPORTS = ("gdn_prefill", "gdn_prefill_noalloc", "gdn_noalloc_scratch_bytes", "k
            "gdn_prefill_batched", "gdn_prefill_varlen",
            "kda_prefill_batched", "kda_prefill_varlen", "gdn_decode", "kda_decode",
            "gdn_chunk_table", "gdn_profile_enable", "gdn_profile_read", "gdn_workspace_bytes",
-           "gdn_segments", "gdn_segment_plan", "gdn_status_string", "gdn_debug_validate")
+           "gdn_segments", "gdn_segment_plan", "gdn_status_string", "gdn_debug_validate",
+           "gdn_debug_flag_polls")
 GDN_BAD_CU_START, GDN_BAD_CU_ORDER, GDN_BAD_CU_TOTAL, GDN_BAD_CU_MAXLEN = 1, 2, 4, 8
 GDN_BAD_KDA_GATE = 16
 GDN_PROF_FRONT = 0
@@ -98,6 +99,8 @@ def load(path: str = SO):
         lib.gdn_segment_plan.restype = ctypes.c_int
         lib.gdn_debug_validate.argtypes = [_vp]
         lib.gdn_debug_validate.restype = ctypes.c_int
+        lib.gdn_debug_flag_polls.argtypes = [ctypes.c_int32]
+        lib.gdn_debug_flag_polls.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         for name in ("gdn_prefill", "kda_prefill", "gdn_prefill_batched",
@@ -233,3 +236,8 @@ def gdn_debug_validate(status):
     """Turn the device-side input checks on (status: a device int32 tensor or pointer) or
     off (None)."""
     return load().gdn_debug_validate(_p(status))
+
+
+def gdn_debug_flag_polls(polls):
+    """Bound the segmented scan's flag waits (polls >= 0) or restore the default (-1)."""
+    return load().gdn_debug_flag_polls(int(polls))

@@ -76,6 +76,9 @@ struct Stage {
     }
 };
 
+// flag-wait bound of the segmented scan (-1: computed per call): see gdn_debug_flag_polls
+std::atomic<int32_t> flag_polls{-1};
+
 // debug validation status word (device), or nullptr: see gdn_debug_validate
 std::atomic<int32_t *> debug_status{nullptr};
 
@@ -568,6 +571,8 @@ int run(const Call &c)
             // stream (a chunk step outlasts 256 poll sleeps)
             ca.wait_polls = (int32_t)std::min<int64_t>(
                 INT32_MAX, (int64_t)(1 << 20) + 256 * ((c.st.tps + 63) / 64));
+            if (flag_polls.load() >= 0)
+                ca.wait_polls = flag_polls.load();
             if (gdn::launch_chunk(ik, p->dk, p->dv, c.kda, sh.nv, sh.waves, fused, p->chunk,
                                   ca, (int)(grid * jobs1), c.stream) != hipSuccess)
                 return GDN_E_HIP;
@@ -907,6 +912,14 @@ int gdn_segments(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per_str
 int gdn_debug_validate(int32_t *status)
 {
     debug_status.store(status);
+    return GDN_OK;
+}
+
+int gdn_debug_flag_polls(int32_t polls)
+{
+    if (polls < -1)
+        return GDN_E_ARG;
+    flag_polls.store(polls);
     return GDN_OK;
 }
 

@@ -74,7 +74,9 @@ struct SegLayout {
     //   kFlagChain + c   the chain of state columns 16c..16c+15 is done (c < 8; second launch)
     //   kFlagRead + sl   job 0 has read the initial state and windows of slice sl (first
     //                    launch, calls with a warm-start plan)
-    static constexpr int kFlagChain = 0, kFlagRead = 8;
+    //   kFlagFallback + sl   the last warm job gave up waiting for that and left the final
+    //                    state (and windows) in slot H(b, S-1) for the second launch to copy
+    static constexpr int kFlagChain = 0, kFlagRead = 8, kFlagFallback = 10;
 };
 
 // The plan's warm-up chunk count of boundary s = lane + 1 (1 past the last boundary): whole

@@ -1259,8 +1259,9 @@ __device__ __forceinline__ int block_task(int wave, int j)
 // times, ChunkArgs::wait_polls); loads after it see what the workgroups that set them wrote
 // before setting them. Called by whole waves. Every flag is set by a workgroup that
 // precedes its waiters in the grid, and workgroups dispatch in grid order, so the flags are
-// set while a waiter polls; the bound keeps every wave finite regardless.
-__device__ __forceinline__ void wait_flags(const int *f, int n, int polls)
+// set while a waiter polls; the bound keeps every wave finite regardless. Returns whether
+// every flag was seen set.
+__device__ __forceinline__ bool wait_flags(const int *f, int n, int polls)
 {
     const int lane = (int)(threadIdx.x & 63);
     bool ok = lane >= n;
@@ -1272,6 +1273,7 @@ __device__ __forceinline__ void wait_flags(const int *f, int n, int polls)
         __builtin_amdgcn_s_sleep(8);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return __ballot(!ok) == 0;
 }
 
 // The chain of one (stream, head, 16 state columns), blk = column block * B*H + (stream,
@@ -1286,8 +1288,9 @@ __device__ __forceinline__ void wait_flags(const int *f, int n, int polls)
 // beside the job that read the stream's initial state, so it left its end state in slot
 // H(b, S-1) (and, with the front end fused and windows not shared, the new windows in
 // win_ws); the workgroup copies its share to the caller's buffers (with direct_final that
-// job waited for the read and wrote them itself).
-template <int DK, int NWV>
+// job waited for the read and wrote them itself, unless its wait gave up: then it took the
+// slot and set the fallback flag of its dv slice, and the copy happens here).
+template <int DK, int NWV, int NV>
 __device__ __forceinline__ void chain_block(const ChunkArgs &a, const SegLayout &lay, int blk,
                                             unsigned char *lds)
 {
@@ -1303,7 +1306,9 @@ __device__ __forceinline__ void chain_block(const ChunkArgs &a, const SegLayout 
     const int64_t hoff = (int64_t)head * DK * DK;
     float *state = a.h_ptrs ? a.h_ptrs[b] : a.h;
     if (a.warm && warm_head(warm_lane_count(a.seg_ws, lay, b, head))) {
-        if (a.direct_final)
+        if (a.direct_final &&
+            reinterpret_cast<const int *>(a.seg_ws + lay.flags(b, head))
+                    [SegLayout::kFlagFallback + 16 * cbk / NV] == 0)
             return;
         const float *src = a.seg_ws + lay.h(b, lay.S - 1) + hoff;
         for (int idx = threadIdx.x; idx < DK * 16; idx += NWV * 64) {
@@ -1465,8 +1470,8 @@ __global__ void __launch_bounds__(NW * 64)
     if (a.chain_groups) {  // second launch of a segmented call: the chain's workgroups first
         if (gid < a.chain_groups) {
             if constexpr (DK == DV && (DK == 64 || DK == 128))
-                chain_block<DK, NW>(a, SegLayout{(int64_t)a.H * DK * DV, a.st.B, a.nseg, a.H},
-                                    gid, smem);
+                chain_block<DK, NW, NV>(
+                    a, SegLayout{(int64_t)a.H * DK * DV, a.st.B, a.nseg, a.H}, gid, smem);
             return;
         }
         gid -= a.chain_groups;
@@ -1998,9 +2003,9 @@ __global__ void __launch_bounds__(NW * 64)
                                                              smem + C::OFF_G))[4 * CH]))) < -110.f;
     };
     if (read_role) {  // (uniform) direct_final
-        int *rf = reinterpret_cast<int *>(
-                      a.seg_ws + SegLayout{(int64_t)H * DK * DV, a.st.B, a.nseg, H}.flags(b, head)) +
-                  SegLayout::kFlagRead + slice;
+        const SegLayout lay{(int64_t)H * DK * DV, a.st.B, a.nseg, H};
+        int *rf = reinterpret_cast<int *>(a.seg_ws + lay.flags(b, head)) + SegLayout::kFlagRead +
+                  slice;
         if (read_role == 1) {
             // job 0: every wave's loads of the initial state and windows are done
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -2011,7 +2016,14 @@ __global__ void __launch_bounds__(NW * 64)
             // the last warm job, which writes the caller's state and windows: job 0 has read
             // them. Both start in the first round of workgroups, so this waits for little
             // more than job 0's first loads, and nothing inside the chunk loop has to check.
-            wait_flags(rf, 1, a.wait_polls);
+            // Should the wait give up, the job takes the slot and the staging area instead
+            // and flags it, and the second launch copies them over.
+            if (!wait_flags(rf, 1, a.wait_polls)) {
+                hout = a.seg_ws + lay.h(b, lay.S - 1);
+                win_staged = true;
+                if (tid0 == 0)
+                    rf[SegLayout::kFlagFallback - SegLayout::kFlagRead] = 1;
+            }
         }
     }
     for (int64_t cs = start; cs < end && !(cs > start && underflowed()); cs += CH) {

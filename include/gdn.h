@@ -366,6 +366,20 @@ int gdn_segment_plan(const gdn_params *p, int32_t kind, int32_t B, int64_t t_per
 #define GDN_BAD_KDA_GATE 16  /* a per-key-channel log-gate above 0 or NaN, in a real row */
 int gdn_debug_validate(int32_t *status);
 
+/*
+ * Debug bound of the segmented scan's flag waits. Inside one launch some workgroups wait
+ * for flags that earlier workgroups of the grid set (the last warm-started segment waits
+ * until the job that reads the stream's initial state and windows has read them; jobs of
+ * the second launch wait for the chain of segment maps). Each wait polls a bounded number of
+ * times, by default about a second's worth plus room for the longest job, and the last
+ * warm-started segment falls back to a copy by the second launch when its wait gives up.
+ * polls >= 0 replaces the bound for every later call (0: the last warm-started segment
+ * takes the fallback at once; a chained segment would proceed without its start state, so
+ * this is for tests of warm-started calls); -1 restores the default. The setting is
+ * process-wide. Returns GDN_OK, or GDN_E_ARG for polls < -1.
+ */
+int gdn_debug_flag_polls(int32_t polls);
+
 /* Static description of a status code. */
 const char *gdn_status_string(int status);
 

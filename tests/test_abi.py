@@ -32,6 +32,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_debug_flag_polls_setting():
+    """The flag-wait bound is a host-side setting: polls >= 0 or -1 (default) are taken,
+    anything below -1 is refused."""
+    assert B.gdn_debug_flag_polls(-2) == B.GDN_E_ARG
+    assert B.gdn_debug_flag_polls(5) == B.GDN_OK
+    assert B.gdn_debug_flag_polls(-1) == B.GDN_OK
+
+
 def test_status_strings():
     for code in (B.GDN_OK, B.GDN_E_ARG, B.GDN_E_UNSUPPORTED, B.GDN_E_WORKSPACE, B.GDN_E_HIP):
         assert B.gdn_status_string(code) not in ("", "unknown status")
