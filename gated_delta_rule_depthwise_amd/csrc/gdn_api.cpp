@@ -343,8 +343,8 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
     return seg_search(nc, U, ncu, max_s);
 }
 
-// the segment states, and for a fused front end without shared windows the windows that
-// warm-started streams stage for the second launch's chain workgroups to copy
+// the segment states, and for a fused front end without shared windows the windows that a
+// warm-started stream stages when its last job falls back to the second launch's copy
 size_t seg_bytes(const gdn_params *p, int kda, int32_t B, int S)
 {
     if (S < 3)

@@ -183,7 +183,8 @@ struct ChunkArgs {
     // warm starts (scalar gate, unit keys): pass 1 also holds S-1 warm jobs (segments
     // 1..S-1 from h = 0 a few chunks early), run when the (stream, head) is in warm mode;
     // the map jobs and the jobs of pass 2 then return at once, and the chain's workgroups
-    // only copy the final state (and windows) over
+    // only copy the final state (and windows) over where the last warm job left them in the
+    // workspace (without direct_final, or when its wait gave up)
     int32_t warm;
     // set by the launch: workgroups [0, job_groups) are jobs; the rest update the front
     // end's carried windows (window_items = streams x channels, 0 when there is none)
@@ -204,8 +205,9 @@ struct ChunkArgs {
     // Front end fused into the load stage (q, k, v are the raw bf16 conv inputs, conv_k
     // taps): the conv taps, the carried windows (read by the job holding a stream's first
     // chunk) and where the job that ends a stream puts the new windows: the caller's
-    // windows, or win_ws when a later kernel must copy them there -- in warm mode (the
-    // chain's workgroups, after the launch that read the old windows) and when several
+    // windows, or win_ws when a later kernel must copy them there -- in warm mode without
+    // direct_final or when its wait gave up (the chain's workgroups, after the launch that
+    // read the old windows) and when several
     // workgroups read one window (win_shared: q/k heads shared by value heads, or dv
     // slices; window_copy_kernel at the end of the call).
     const float *conv_w;            // [cd][conv_k]
