@@ -302,27 +302,40 @@ def test_segmented_scan_mixed_warm_and_chain(gate):
     assert rel_err(seg.h.cpu().numpy(), ser.h.cpu().numpy()) <= 2e-2
 
 
-def test_segmented_warm_fallback_copy():
+@pytest.mark.parametrize("case", ["gdn-front-T4096-H4", "gdn-front-batched-2x2048-H2",
+                                  "kda-front-T8192-H2"])
+def test_segmented_warm_fallback_copy(case):
     """The last warm-started segment writes the caller's state and windows once job 0 of the
     same launch has flagged that it read them. With the flag waits bounded at 0 polls
     (gdn_debug_flag_polls) that wait gives up at once: the segment leaves its end state and
     windows in the workspace, flags it, and the second launch copies them over. o, the final
-    state and the windows equal the default path's bit for bit."""
+    states and the windows equal the default path's bit for bit (single stream, equal-length
+    streams with per-stream states and windows, and the per-key-channel gate, whose
+    log-gates are scaled by 4 so that the warm windows fit in a segment)."""
     from gated_delta_rule_depthwise_amd import binding as B
-    spec = spec_small(2, lengths=[4096], H=4, seed=56)
+    spec = {"gdn-front-T4096-H4": lambda: spec_small(2, lengths=[4096], H=4, seed=56),
+            "gdn-front-batched-2x2048-H2": lambda: spec_small(2, lengths=[2048, 2048], H=2,
+                                                              seed=61),
+            "kda-front-T8192-H2": lambda: spec_small(5, lengths=[8192], H=2, seed=62)}[case]()
     inp = inputs.make(spec)
+    if spec.gate == "kda":
+        inp["g"] *= 4.0
     direct = run_gpu(inp)
-    S = B.gdn_segments(direct.params, direct.plan_kind, 1, spec.N, direct.ws_bytes)
-    assert S >= 3 and warm_flags(direct, S) == [1.0] * spec.H
+    S = B.gdn_segments(direct.params, direct.plan_kind, spec.B, spec.N // spec.B,
+                       direct.ws_bytes)
+    assert S >= 3
+    if spec.B == 1:
+        assert warm_flags(direct, S) == [1.0] * spec.H
     assert B.gdn_debug_flag_polls(0) == 0
     try:
         fallback = run_gpu(inp)
     finally:
         assert B.gdn_debug_flag_polls(-1) == 0
-    # the fallback flags (one per dv slice, after the plan's counts) of every head
-    base = (3 * S - 5) * spec.H * spec.dk * spec.dv + 2 * S * spec.H
-    f = fallback.ws[:(base + spec.H * 16) * 4].view(torch.int32).cpu()
-    assert [int(f[base + h * 16 + 10]) for h in range(spec.H)] == [1] * spec.H
+    # the fallback flags (one per dv slice, after the plan's counts) of every stream and head
+    BH = spec.B * spec.H
+    base = (3 * S - 5) * spec.B * spec.H * spec.dk * spec.dv + spec.B * 2 * S * spec.H
+    f = fallback.ws[:(base + BH * 16) * 4].view(torch.int32).cpu()
+    assert [int(f[base + bh * 16 + 10]) for bh in range(BH)] == [1] * BH
     assert torch.equal(fallback.o[:spec.N], direct.o[:spec.N])
     assert torch.equal(fallback.h, direct.h)
     assert torch.equal(fallback.conv_state, direct.conv_state)
