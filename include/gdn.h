@@ -38,12 +38,14 @@
  *     heavy-tailed outputs.) The dense products run on MFMA with fp32 accumulation, with
  *     fp16 operands for bf16 inputs (hi + lo pairs where a single fp16 rounding would
  *     show in o or h) and fp32 operands for float32 inputs.
- *   - Front end: with bf16 rows, 4 taps, one q/k head per value head, dk == dv, no output
- *     gate and ld_qkv < 2^24, the conv + SiLU + L2 run inside the scan's load stage in
- *     fp32 straight from the raw rows (no activation buffer; k, and with the scalar gate
- *     q, enter the products as fp16 hi + lo pairs, v in fp32). Every other front-end call runs the
- *     front end as a kernel of its own that hands the scan fp16 (bf16 rows) or fp32
- *     activations through the workspace.
+ *   - Front end: with bf16 rows, 2 to 4 taps and ld_qkv < 2^24, on the shapes with a fused
+ *     instance (dk = dv = 128 or 64, and dk = 128 with dv = 256; either gate, shared q/k
+ *     heads included), the conv + SiLU + L2 run inside the scan's load stage in fp32
+ *     straight from the raw rows (no activation buffer; k, and with the scalar gate q,
+ *     enter the products as fp16 hi + lo pairs, v in fp32); the scalar gate's output gate
+ *     then rides in the same kernel's o flush. A bf16 front-end call outside those is
+ *     refused with GDN_E_UNSUPPORTED; with float32 rows the front end runs as a kernel of
+ *     its own that hands the scan fp32 activations through the workspace.
  *   - Errors: every check below runs on the host before anything is enqueued; on error
  *     nothing is launched and no buffer changes (the pages refuse a bad token count before
  *     any launch). GDN_E_HIP reports a failed launch.
