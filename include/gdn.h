@@ -42,10 +42,10 @@
  *     instance (dk = dv = 128 or 64, and dk = 128 with dv = 256; either gate, shared q/k
  *     heads included), the conv + SiLU + L2 run inside the scan's load stage in fp32
  *     straight from the raw rows (no activation buffer; k, and with the scalar gate q,
- *     enter the products as fp16 hi + lo pairs, v in fp32); the scalar gate's output gate
- *     then rides in the same kernel's o flush. A bf16 front-end call outside those is
- *     refused with GDN_E_UNSUPPORTED; with float32 rows the front end runs as a kernel of
- *     its own that hands the scan fp32 activations through the workspace.
+ *     enter the products as fp16 hi + lo pairs, v in fp32); at dk = dv the scalar gate's
+ *     output gate then rides in the same kernel's o flush. A bf16 front-end call outside
+ *     those is refused with GDN_E_UNSUPPORTED; with float32 rows the front end runs as a
+ *     kernel of its own that hands the scan fp32 activations through the workspace.
  *   - Errors: every check below runs on the host before anything is enqueued; on error
  *     nothing is launched and no buffer changes (the pages refuse a bad token count before
  *     any launch). GDN_E_HIP reports a failed launch.
