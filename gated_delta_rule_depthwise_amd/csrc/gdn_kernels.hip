@@ -2364,6 +2364,16 @@ __global__ void __launch_bounds__(NW * 64)
             // (I + N)(I + N^2)(I + N^4)(I + N^8), the products on fp32 MFMA; step(k) is
             // called between the inverse's dependent steps (k = 0..3) to issue independent
             // work into their latency
+            // After a step, which may branch around its work, the inverse reads the fp32
+            // MFMA result issued before it: the wait states that read needs are kept here,
+            // at the join, since the compiler counted them only along the path through the
+            // step's work (on the other path the d = 64 instance read the result too early
+            // and got wrong transitions and end states whenever a chunk computed no o).
+            auto settle = [] {
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
             auto invert = [&](const f32x4 &m, auto step) {
                 f32x4 nb;  // N, D layout
 #pragma unroll
@@ -2374,12 +2384,15 @@ __global__ void __launch_bounds__(NW * 64)
                 f32x4 n2 = zero4(), n3 = zero4(), n4 = zero4(), n8 = zero4();
                 mm16<false>(n2, na, nb);  // N^2
                 step(1);
+                settle();
                 mm16<false>(n3, na, n2);  // N^3
                 const f32x4 n2a = to_a(n2);
                 step(2);
+                settle();
                 mm16<false>(n4, n2a, n2);  // N^4
                 const f32x4 n4a = to_a(n4);
                 step(3);
+                settle();
                 mm16<false>(n8, n4a, n4);  // N^8
                 const f32x4 n8a = to_a(n8);
                 f32x4 x;  // (I + N)(I + N^2) = I + N + N^2 + N^3
@@ -2850,6 +2863,14 @@ __global__ void __launch_bounds__(NW * 64)
                         }
                     }
                     const int col = 16 * (wave * NCB + cb) + c16;
+                    if constexpr (!C::STAGE_O) {
+                        // The stores below sit behind a branch on the chunk's length. The wait
+                        // states an MFMA result needs before it is read are kept here, ahead
+                        // of that branch: the compiler counted them only along one path.
+                        __builtin_amdgcn_sched_barrier(0);
+                        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     if constexpr (C::STAGE_O) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)

@@ -63,3 +63,43 @@ def test_sweep_case_matches_oracle(i):
         compare(call, ref, o_metric=ref["o_metric"])
     else:
         compare(call, ref)
+
+
+def _seg_case(i):
+    """A long single stream or two equal ones with few heads, so that the scan segments:
+    per head fast or slow decay (warm-started segments, chained ones, or both in one call),
+    either gate, with or without the front end and the output gate."""
+    rng = np.random.default_rng([78, i])
+    dtype = ["bf16", "f32"][rng.integers(2)]
+    dk = [64, 128][rng.integers(2)] if dtype == "bf16" else 64
+    gate = ["gdn", "kda"][rng.integers(2)]
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(700, 3000 if gate == "gdn" else 4000))
+    kw = dict(lengths=[T] * B, H=int(rng.integers(1, 4)), dk=dk, dv=dk, dtype=dtype,
+              gate=gate, front_end=bool(rng.integers(2)), conv_k=int(rng.integers(2, 5)),
+              out_gate=bool(rng.integers(2)), h0_std=0.1, seed=2000 + i)
+    slow = rng.integers(2, size=kw["H"]).astype(bool)  # heads that decay slowly
+    return kw, slow
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_segmented_sweep_matches_oracle(i):
+    from gated_delta_rule_depthwise_amd import binding as B
+    kw, slow = _seg_case(i)
+    spec = spec_small(1, **kw)
+    inp = inputs.make(spec)
+    if spec.gate == "kda":
+        inp["g"] *= 4.0  # warm windows that fit the segments of these shorter streams
+    if slow.any():
+        sl = inputs.make(dataclasses.replace(spec, gate_dist="slow"))["g"]
+        idx = [h for h in range(spec.H) if slow[h]]
+        inp["g"][:, idx] = sl[:, idx]
+    call = run_gpu(inp)
+    S = B.gdn_segments(call.params, call.plan_kind, spec.B, spec.N // spec.B, call.ws_bytes)
+    print("%s S=%d slow heads %s" % (spec.name, S, slow.tolist()), flush=True)
+    ref = run_oracle(inp)
+    if spec.out_gate:
+        ref = gated(inp, ref)
+        compare(call, ref, o_metric=ref["o_metric"])
+    else:
+        compare(call, ref)
