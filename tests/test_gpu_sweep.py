@@ -44,7 +44,7 @@ def _case(i):
     return kw, eps
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(256))
 def test_sweep_case_matches_oracle(i):
     kw, eps = _case(i)
     spec = spec_small(1, **kw)
@@ -82,7 +82,7 @@ def _seg_case(i):
     return kw, slow
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(96))
 def test_segmented_sweep_matches_oracle(i):
     from gated_delta_rule_depthwise_amd import binding as B
     kw, slow = _seg_case(i)
