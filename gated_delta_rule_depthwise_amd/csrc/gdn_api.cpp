@@ -340,7 +340,19 @@ SegPlan seg_plan(const gdn_params *p, int kda, int32_t B, int64_t tps, int nslic
     const int64_t U = (int64_t)B * p->H * nslices;
     const int max_s = warm_capable(p) && ncu / U >= 3 ? (int)(ncu / U) : 0;
     (void)kda;
-    return seg_search(nc, U, ncu, max_s);
+    SegPlan sp = seg_search(nc, U, ncu, max_s);
+    if (max_s > 0 && sp.S > 0) {
+        // A call that can start warm runs segment 0 and the S - 1 warm jobs side by side,
+        // each warm job w chunks longer than its segment: equal segments give the shortest
+        // critical path, L + w, for every w up to the segment length L (a longer segment 0
+        // only pays off when the segments chain). The last segment takes what is left.
+        const int64_t S = sp.S;
+        int64_t l = (nc + S - 1) / S;
+        if (nc - (S - 1) * l < 1)
+            l = nc / S;
+        sp.seg0_len = sp.seg_len = l * 64;
+    }
+    return sp;
 }
 
 // the segment states, and for a fused front end without shared windows the windows that a

@@ -110,7 +110,7 @@ struct WindowCopyArgs {
 
 // Warm-start plan of a segmented call: per (stream, head), each chunk's total log-gate and
 // whether its betas lie in [0, 1.9]; per segment boundary the fewest chunks before it whose
-// log-gates sum below -32; warm mode when every boundary has such a window inside the
+// log-gates sum below -16; warm mode when every boundary has such a window inside the
 // previous segment. With the per-key-channel gate a token's bound is its largest channel
 // log-gate (the norm of a token's transition is at most its largest channel decay).
 struct WarmArgs {

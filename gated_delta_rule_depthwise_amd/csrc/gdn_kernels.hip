@@ -377,12 +377,13 @@ __device__ __forceinline__ int find_stream(const Streams &s, int64_t t)
 constexpr int CH = 64;  // chunk length
 
 // Warm starts: a segment starts from h = 0 once the chunks before it bound the norm of
-// their transition by e^kWarmLogBound. The state it drops is then at most e^-32 (< 2^-46)
-// of the state's norm at the start of that window: far below the fp32 rounding (2^-24) of
-// every value the state feeds, unless the state shrank by more than 2^22 across the window.
-// (A transition job's early stop, which substitutes an exact zero, waits for e^-110: below
-// half the smallest fp32 subnormal.)
-constexpr float kWarmLogBound = -32.f;
+// their transition by e^kWarmLogBound. The state it drops is then at most e^-16 (< 2^-23)
+// of the state's norm at the start of that window: the fp32 rounding of that state, and
+// below the precision of the hi + lo operand pairs (about 2^-22) through which every chunk
+// already passes the state, unless the state shrank by orders of magnitude across the
+// window. (A transition job's early stop, which substitutes an exact zero, waits for e^-110:
+// below half the smallest fp32 subnormal.)
+constexpr float kWarmLogBound = -16.f;
 
 // The plan of one (stream, head) in one workgroup (extra workgroups of the float32 front
 // kernel); see WarmArgs. Wave w takes boundaries w + 1, w + 5, ...:

@@ -322,12 +322,14 @@ int gdn_profile_read(double *ms_total, int64_t *launches, int32_t nbuckets);
  * beta_t lies in [0, 1.9]. Once a running sum of these log-gates is below -110 the
  * transition is zero in fp32: with the scalar gate a transition job then stops and writes
  * zeros, and the chain copies that step's end state. And when every segment boundary of a
- * (stream, head) has a window of chunks inside the previous segment whose sum is below -32,
+ * (stream, head) has a window of chunks inside the previous segment whose sum is below -16,
  * each segment starts from a zero state that many chunks early ("warm start"), all in the
- * first launch, with no chain. The state a warm start drops is at most e^-32 (< 2^-46) of
- * the state's norm at the start of that window, far below the fp32 rounding of the values
- * it feeds unless the state shrank by more than 2^22 across the window. Slowly decaying
- * heads take the chain; one call may hold both. */
+ * first launch, with no chain. The state a warm start drops is at most e^-16 (< 2^-23) of
+ * the state's norm at the start of that window: the fp32 rounding of that state, and below
+ * the precision of the hi + lo operand pairs that carry the state through every chunk,
+ * unless the state shrank by orders of magnitude across the window. Segments of calls that
+ * can start warm are of equal length. Slowly decaying heads take the chain; one call may
+ * hold both. */
 size_t gdn_workspace_bytes(const gdn_params *p, int32_t B, int64_t max_tokens, int32_t kind);
 
 /* Segments per stream (S >= 3, or 0 for an unsegmented scan) that a single (kind

@@ -114,11 +114,12 @@ def test_segment_plan():
     assert B.gdn_segments(pk, kda, 1, 16384, wk) >= 3
     # A call with unit keys (L2 in the call) may start every segment warm, so its plan
     # keeps segment 0 and the warm jobs of all (stream, head) pairs in one round: S <= CUs
-    # / (streams * heads) = 8 on 256 CUs. Without L2 the segments always chain, with no such
-    # cap: the KDA plan is then 9 segments of 40, 27 x 7 and 27 chunks.
+    # / (streams * heads) = 8 on 256 CUs, in equal segments (each warm job runs its
+    # segment plus its warm-up beside segment 0). Without L2 the segments always chain,
+    # with no such cap: the KDA plan is then 9 segments of 40, 27 x 7 and 27 chunks.
     S_g, _, _ = B.gdn_segment_plan(pk, B.GDN_KIND_SINGLE, 1, 16384, wk)
     assert 3 <= S_g <= 8
-    assert B.gdn_segment_plan(pk, kda, 1, 16384, wk) == (8, 39 * 64, 31 * 64)
+    assert B.gdn_segment_plan(pk, kda, 1, 16384, wk) == (8, 32 * 64, 32 * 64)
     pn = B.params(32, 128, 128, conv_k=4, eps=-1.0)
     wn = B.gdn_workspace_bytes(pn, 1, 16384, kda)
     assert B.gdn_segment_plan(pn, kda, 1, 16384, wn) == (9, 40 * 64, 27 * 64)
